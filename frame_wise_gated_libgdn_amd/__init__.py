@@ -1,0 +1,177 @@
+"""Python binding of libgdn, the frame-wise Gated DeltaNet recurrence on MI355X (gfx950).
+
+Argument marshalling only: every step of the recurrence runs in the HIP kernels of
+``libgdn.so`` (built from ``csrc/``), reached through the C ABI declared in
+``include/libgdn.h``. PyTorch supplies device memory and the current HIP stream. There is no
+CPU fallback: if the shared library is missing or fails to load, every call raises.
+
+Recurrence (gen-hub.ru, "NVIDIA SANA-WM: минутное 720p видео с одной видеокарты", section
+"Архитектура: четыре нетривиальных решения"), per (b, h), c = 1/sqrt(D*S) by default:
+    R = V_f - gamma_f (c K_f) M;  M <- gamma_f M + beta_f (c K_f)^T R;  O_f = Q_f M.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "forward_framewise",
+           "step_frame", "abi_version", "GDN_F32", "GDN_BF16"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
+          4: "GDN_ERR_STRIDE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
+          8: "GDN_ERR_HIP"}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code, message):
+        self.code = code
+        self.name = STATUS.get(code, "GDN_ERR_%d" % code)
+        super().__init__("%s: %s" % (self.name, message))
+
+
+class Problem(ctypes.Structure):
+    """Mirror of gdn_problem (include/libgdn.h)."""
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32),
+                ("frames", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("use_delta", ctypes.c_int32), ("key_scale", ctypes.c_float),
+                ("qkv_stride_b", ctypes.c_int64), ("qkv_stride_h", ctypes.c_int64),
+                ("qkv_stride_t", ctypes.c_int64), ("o_stride_b", ctypes.c_int64),
+                ("o_stride_h", ctypes.c_int64), ("o_stride_t", ctypes.c_int64)]
+
+
+_lock = threading.Lock()
+_lib = None
+_vp = ctypes.c_void_p
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgdn.so (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise ImportError("libgdn.so is not built at %s; run __graft_entry__.build()"
+                                  % _LIB_PATH)
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.POINTER(Problem)
+            lib.gdn_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+            lib.gdn_workspace_size.restype = ctypes.c_int
+            for fn in (lib.gdn_forward_framewise, lib.gdn_step_frame):
+                fn.argtypes = [P] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
+                fn.restype = ctypes.c_int
+            lib.gdn_status_string.argtypes = [ctypes.c_int]
+            lib.gdn_status_string.restype = ctypes.c_char_p
+            lib.gdn_last_error_message.restype = ctypes.c_char_p
+            lib.gdn_abi_version.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return int(load().gdn_abi_version())
+
+
+def _check(code):
+    if code != 0:
+        raise GdnError(code, load().gdn_last_error_message().decode(errors="replace"))
+
+
+def workspace_size(p: Problem, step_mode: bool) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().gdn_workspace_size(ctypes.byref(p), int(bool(step_mode)), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise GdnError(3, "Q/K/V must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _problem(q, o, F, use_delta, key_scale):
+    B, H, T, D = q.shape
+    if T % F:
+        raise GdnError(2, "token count %d is not a whole number of frames (F=%d)" % (T, F))
+    if q.stride(3) != 1 or o.stride(3) != 1:
+        raise GdnError(4, "the head dimension must be contiguous")
+    return Problem(B, H, D, T // F, F, _dtype_code(q), int(bool(use_delta)),
+                   0.0 if key_scale is None else float(key_scale),
+                   q.stride(0), q.stride(1), q.stride(2), o.stride(0), o.stride(1), o.stride(2))
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(p, step_mode, workspace, device):
+    import torch
+    need = workspace_size(p, step_mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def forward_framewise(q, k, v, gamma, beta, state=None, *, use_delta=True, key_scale=None,
+                      out=None, state_out=None, return_state=True, workspace=None, stream=None):
+    """All frames: q, k, v [B, H, F*S, D] (D contiguous, any other strides, same strides for
+    all three); gamma, beta fp32 [B, H, F]; state fp32 [B, H, D, D] or None (zero).
+    Returns (o, state_out); o has q's shape and dtype, state_out is None when
+    return_state is False."""
+    import torch
+    B, H, T, D = q.shape
+    F = gamma.shape[2]
+    if k.stride() != q.stride() or v.stride() != q.stride() or k.shape != q.shape \
+            or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise GdnError(4, "q, k and v must share shape, dtype and strides")
+    if out is None:
+        out = torch.empty((B, H, T, D), dtype=q.dtype, device=q.device)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    p = _problem(q, out, F, use_delta, key_scale)
+    ws, nbytes = _workspace(p, False, workspace, q.device)
+    _check(load().gdn_forward_framewise(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                        _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),
+                                        _ptr(ws), nbytes, _stream(stream)))
+    return out, state_out
+
+
+def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_scale=None,
+               out=None, state_out=None, workspace=None, stream=None):
+    """One frame: q, k, v [B, H, S, D]; gamma, beta fp32 [B, H]; state fp32 [B, H, D, D].
+    Returns (o, new_state) when commit, else (o, None). state_out may be `state` itself."""
+    import torch
+    B, H, S, D = q.shape
+    if k.stride() != q.stride() or v.stride() != q.stride() or k.shape != q.shape \
+            or v.shape != q.shape:
+        raise GdnError(4, "q, k and v must share shape and strides")
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=q.dtype, device=q.device)
+    if commit and state_out is None:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    if not commit:
+        state_out = None
+    p = _problem(q, out, 1, use_delta, key_scale)
+    ws, nbytes = _workspace(p, True, workspace, q.device)
+    _check(load().gdn_step_frame(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                 _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out), _ptr(ws),
+                                 nbytes, _stream(stream)))
+    return out, state_out

@@ -1,0 +1,242 @@
+// C ABI of libgdn: argument validation, workspace planning and the launch sequence.
+// Everything here runs on the host before any device work; the arithmetic is in
+// gdn_kernels.hip.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "../../include/libgdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Splits chosen from the shape only, so that the workspace size is a pure function of it.
+struct Plan {
+    int nsplit, split_tokens;   // partial-product kernel
+    int nchunk, chunk_tokens;   // output kernel
+    size_t part_bytes, mt_bytes;
+};
+
+constexpr int kTargetGroups = 2048;  // workgroups wanted per parallel launch (256 CUs x 8)
+
+Plan make_plan(const gdn_problem& p, int step_mode) {
+    Plan pl;
+    const int64_t D = p.head_dim, S = p.tokens_per_frame;
+    const int64_t BH = (int64_t)p.batch * p.heads;
+    const int64_t F = step_mode ? 1 : p.frames;
+    const int64_t esz = p.dtype == GDN_BF16 ? 2 : 4;
+    const int64_t tiles64 = (S + 63) / 64;
+    int64_t want;
+    if (step_mode) {
+        // one split per 256 tokens: enough workgroups for a single frame of a few heads
+        want = (S + 255) / 256;
+    } else {
+        want = (kTargetGroups + BH * F - 1) / (BH * F);
+    }
+    want = std::max<int64_t>(1, std::min<int64_t>(want, tiles64));
+    pl.split_tokens = (int)(((tiles64 + want - 1) / want) * 64);
+    pl.nsplit = (int)((S + pl.split_tokens - 1) / pl.split_tokens);
+
+    const int64_t tiles16 = (S + 15) / 16;
+    int64_t wc = (kTargetGroups + BH * F - 1) / (BH * F);
+    wc = std::max<int64_t>(1, std::min<int64_t>(wc, (tiles16 + 3) / 4));
+    pl.chunk_tokens = (int)(((tiles16 + wc - 1) / wc) * 16);
+    pl.nchunk = (int)((S + pl.chunk_tokens - 1) / pl.chunk_tokens);
+
+    const int64_t nout = (!step_mode && p.use_delta) ? 2 : 1;
+    pl.part_bytes = (size_t)(BH * F * pl.nsplit * nout * D * D * 4);
+    pl.mt_bytes = (size_t)(BH * F * D * D * esz);
+    return pl;
+}
+
+gdn_status check_sizes(const gdn_problem* p, int step_mode) {
+    if (!p) return fail(GDN_ERR_NULL, "problem descriptor is NULL");
+    if (p->batch < 1 || p->heads < 1 || p->tokens_per_frame < 1 || (!step_mode && p->frames < 1))
+        return fail(GDN_ERR_SHAPE, "sizes must be >= 1 (B=%d H=%d S=%d F=%d)", p->batch, p->heads,
+                    p->tokens_per_frame, p->frames);
+    const int D = p->head_dim;
+    if (D != 16 && D != 32 && D != 64 && D != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "head_dim %d not supported (16, 32, 64, 128)", D);
+    if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
+    const int64_t F = step_mode ? 1 : p->frames;
+    const int64_t BH = (int64_t)p->batch * p->heads;
+    // grid sizes: BH * F * splits must fit a 1-D grid; token indices f*S+s must fit int32 math
+    if (BH * F * ((p->tokens_per_frame + 63) / 64) > (int64_t)1 << 30 ||
+        F * (int64_t)p->tokens_per_frame > ((int64_t)1 << 31) - 1)
+        return fail(GDN_ERR_SHAPE, "problem too large for one call");
+    return GDN_OK;
+}
+
+// Byte extent [lo, hi) touched by a strided [B,H,T,D] tensor.
+struct Span {
+    const char* lo;
+    const char* hi;
+};
+Span span_of(const void* base, int64_t B, int64_t H, int64_t T, int64_t D, int64_t sb, int64_t sh,
+             int64_t st, int64_t esz) {
+    const int64_t last = (B - 1) * sb + (H - 1) * sh + (T - 1) * st + (D - 1);
+    return {(const char*)base, (const char*)base + (last + 1) * esz};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Strides must be non-negative and rows of distinct (b, h, t) must not overlap.
+bool layout_ok(int64_t B, int64_t H, int64_t T, int64_t D, int64_t sb, int64_t sh, int64_t st) {
+    if (sb < 0 || sh < 0 || st < 0) return false;
+    struct Dim { int64_t n, s; } d[4] = {{B, sb}, {H, sh}, {T, st}, {D, 1}};
+    Dim v[4];
+    int k = 0;
+    for (auto& x : d)
+        if (x.n > 1) v[k++] = x;
+    std::sort(v, v + k, [](const Dim& a, const Dim& b) { return a.s < b.s; });
+    int64_t extent = 1;
+    for (int i = 0; i < k; ++i) {
+        if (v[i].s < extent) return false;
+        extent = v[i].s * (v[i].n - 1) + extent;
+    }
+    return true;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k, const void* v,
+               const float* gamma, const float* beta, const float* state_in, void* o,
+               float* state_out, void* ws, size_t ws_bytes, void* stream) {
+    g_msg[0] = '\0';
+    gdn_status s = check_sizes(p, step_mode);
+    if (s != GDN_OK) return s;
+    const int64_t B = p->batch, H = p->heads, D = p->head_dim, S = p->tokens_per_frame;
+    const int64_t F = step_mode ? 1 : p->frames;
+    const int64_t T = F * S;
+    const int64_t esz = p->dtype == GDN_BF16 ? 2 : 4;
+    if (!q || !k || !v || !o || !gamma || !beta)
+        return fail(GDN_ERR_NULL, "q, k, v, o, gamma and beta are required");
+    if (step_mode && !state_in) return fail(GDN_ERR_NULL, "state_in is required in step mode");
+    if (!layout_ok(B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t))
+        return fail(GDN_ERR_STRIDE, "q/k/v strides (%lld, %lld, %lld) overlap rows or are negative",
+                    (long long)p->qkv_stride_b, (long long)p->qkv_stride_h, (long long)p->qkv_stride_t);
+    if (!layout_ok(B, H, T, D, p->o_stride_b, p->o_stride_h, p->o_stride_t))
+        return fail(GDN_ERR_STRIDE, "o strides (%lld, %lld, %lld) overlap rows or are negative",
+                    (long long)p->o_stride_b, (long long)p->o_stride_h, (long long)p->o_stride_t);
+    for (const void* ptr : {q, k, v, (const void*)o})
+        if (!aligned(ptr, 16)) return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+    const int64_t strides[6] = {p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t,
+                                p->o_stride_b,   p->o_stride_h,   p->o_stride_t};
+    for (int64_t st : strides)
+        if (st % 8) return fail(GDN_ERR_ALIGN, "strides must be multiples of 8 elements");
+    for (const void* ptr : {(const void*)gamma, (const void*)beta, (const void*)state_in,
+                            (const void*)state_out})
+        if (ptr && !aligned(ptr, 4)) return fail(GDN_ERR_ALIGN, "gates and states must be 4-byte aligned");
+
+    const Plan pl = make_plan(*p, step_mode);
+    const size_t need = align256(pl.part_bytes) + pl.mt_bytes;
+
+    const Span sq = span_of(q, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
+    const Span sk = span_of(k, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
+    const Span sv = span_of(v, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
+    const Span so = span_of(o, B, H, T, D, p->o_stride_b, p->o_stride_h, p->o_stride_t, esz);
+    const Span sg = {(const char*)gamma, (const char*)(gamma + B * H * F)};
+    const Span sbt = {(const char*)beta, (const char*)(beta + B * H * F)};
+    const Span none = {nullptr, nullptr};
+    const Span sw = ws ? Span{(const char*)ws, (const char*)ws + need} : none;
+    const Span si = state_in ? Span{(const char*)state_in, (const char*)(state_in + B * H * D * D)} : none;
+    const Span sso = state_out ? Span{(const char*)state_out, (const char*)(state_out + B * H * D * D)} : none;
+    for (Span in : {sq, sk, sv, sg, sbt, si, sw})
+        if (overlap(so, in)) return fail(GDN_ERR_ALIAS, "o overlaps an input or the workspace");
+    for (Span in : {sq, sk, sv, sg, sbt, so, si})
+        if (overlap(sw, in)) return fail(GDN_ERR_ALIAS, "workspace overlaps an input or output");
+    if (state_out) {
+        for (Span in : {sq, sk, sv, sg, sbt, so, sw})
+            if (overlap(sso, in)) return fail(GDN_ERR_ALIAS, "state_out overlaps another buffer");
+        if (state_in && state_in != state_out && overlap(sso, si))
+            return fail(GDN_ERR_ALIAS, "state_out partially overlaps state_in");
+    }
+    if (!ws || ws_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    ws ? ws_bytes : (size_t)0);
+    if (!aligned(ws, 256)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+    gdn::Launch L;
+    L.B = (int)B; L.H = (int)H; L.D = (int)D; L.S = (int)S; L.F = (int)F;
+    L.bf16 = p->dtype == GDN_BF16;
+    L.use_delta = p->use_delta != 0;
+    L.c = p->key_scale > 0.f ? p->key_scale : (float)(1.0 / std::sqrt((double)D * (double)S));
+    L.q = q; L.k = k; L.v = v; L.o = o;
+    L.sb = p->qkv_stride_b; L.sh = p->qkv_stride_h; L.st = p->qkv_stride_t;
+    L.ob = p->o_stride_b; L.oh = p->o_stride_h; L.ot = p->o_stride_t;
+    L.gamma = gamma; L.beta = beta; L.state_in = state_in; L.state_out = state_out;
+    L.part = (float*)ws;
+    L.mt = (char*)ws + align256(pl.part_bytes);
+    L.nsplit = pl.nsplit; L.split_tokens = pl.split_tokens;
+    L.nchunk = pl.nchunk; L.chunk_tokens = pl.chunk_tokens;
+    L.stream = (hipStream_t)stream;
+    const hipError_t e = step_mode ? gdn::launch_step(L) : gdn::launch_forward(L);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_workspace_size(const gdn_problem* p, int step_mode, size_t* bytes_out) {
+    g_msg[0] = '\0';
+    if (!bytes_out) return fail(GDN_ERR_NULL, "bytes_out is NULL");
+    gdn_status s = check_sizes(p, step_mode);
+    if (s != GDN_OK) return s;
+    const Plan pl = make_plan(*p, step_mode);
+    *bytes_out = align256(pl.part_bytes) + pl.mt_bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_forward_framewise(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                 const float* gamma, const float* beta, const float* state_in,
+                                 void* o, float* state_out, void* workspace, size_t workspace_bytes,
+                                 void* hip_stream) {
+    return run(0, p, q, k, v, gamma, beta, state_in, o, state_out, workspace, workspace_bytes,
+               hip_stream);
+}
+
+gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, const void* v,
+                          const float* gamma, const float* beta, const float* state_in, void* o,
+                          float* state_out, void* workspace, size_t workspace_bytes,
+                          void* hip_stream) {
+    return run(1, p, q, k, v, gamma, beta, state_in, o, state_out, workspace, workspace_bytes,
+               hip_stream);
+}
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "null pointer";
+    case GDN_ERR_SHAPE: return "bad shape";
+    case GDN_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case GDN_ERR_STRIDE: return "bad strides";
+    case GDN_ERR_ALIGN: return "misaligned pointer or stride";
+    case GDN_ERR_ALIAS: return "overlapping buffers";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* gdn_last_error_message(void) { return g_msg; }
+
+int gdn_abi_version(void) { return LIBGDN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+/*
+ * libgdn.h -- C ABI of libgdn, the frame-wise Gated DeltaNet (GDN) recurrence on AMD MI355X
+ * (gfx950).
+ *
+ * The operation
+ * -------------
+ * Gen-hub.ru, "NVIDIA SANA-WM: минутное 720p видео с одной видеокарты", section
+ * "Архитектура: четыре нетривиальных решения": SANA-WM's GDN blocks process video frame by
+ * frame with a recurrent state of fixed size D x D per head; a decay gate gamma lowers the
+ * weight of older frames, a delta-rule correction writes only the difference between the target
+ * value and the state's current prediction, and keys are scaled by 1/sqrt(D*S) (D = head dim,
+ * S = spatial tokens per frame). The pages describe this in words; libgdn computes, per (batch
+ * b, head h), with M the D x D fp32 state (row = key dim, column = value dim):
+ *
+ *     for f = 0 .. F-1:
+ *         Kt  = c K_f                         c = key_scale, default 1/sqrt(D*S)
+ *         R   = V_f - gamma_f Kt M            (R = V_f when use_delta == 0)
+ *         M   = gamma_f M + beta_f Kt^T R
+ *         O_f = Q_f M
+ *
+ * Frames are causal; the S tokens of one frame all read the same state, so attention is
+ * bidirectional inside a frame. With gamma = beta = 1 and use_delta = 0 this is SANA-Video's
+ * block-causal cumulative linear attention (talk "SANA-Video: Efficient Video Generation with
+ * Block Linear Diffusion Transformer", ICLR 2026 oral, passage on the block KV cache).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory. Every pointer is a device pointer on the current HIP device, owned by the caller.
+ *   libgdn allocates nothing, keeps no state between calls and may be called from several
+ *   host threads at once (distinct workspaces).
+ * Asynchrony. Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and the
+ *   call returns; buffers must stay valid until the stream has passed the call.
+ * Layouts. Q, K, V, O of one (b, h) are token-major rows of D contiguous elements; token
+ *   t = f*S + s. Element (b, h, t, d) of Q/K/V is at
+ *       base + b*qkv_stride_b + h*qkv_stride_h + t*qkv_stride_t + d      (elements)
+ *   and of O at the same with the o_stride_* values. Head-major [B,H,T,D] and token-major
+ *   [B,T,H,D] storage are both expressible. Gates gamma, beta are fp32 [B][H][F] contiguous
+ *   (step: [B][H]). States are fp32 [B][H][D][D] contiguous, row = key dim.
+ * Types. Q, K, V, O are all GDN_F32 or all GDN_BF16; states and gates are always fp32;
+ *   arithmetic accumulates in fp32; bf16 outputs are rounded to nearest even.
+ * Supported shapes. D in {16, 32, 64, 128}; B, H, S, F >= 1; B*H*F*S*max-stride must fit the
+ *   int64 element index. Pointers to Q, K, V, O must be 16-byte aligned, the strides multiples
+ *   of 8 elements (GDN_ERR_ALIGN otherwise); gates and states 16-byte aligned.
+ * Gate values are not checked (that would cost a device pass); the documented domain is
+ *   gamma in (0, 1], beta in [0, 1]. NaN and Inf inputs propagate.
+ * Errors. Argument errors are found on the host before anything is enqueued: the call then
+ *   returns a non-zero gdn_status, writes nothing and records a message for
+ *   gdn_last_error_message() (per host thread). A failed launch returns GDN_ERR_HIP with the
+ *   HIP error text in that message. Nothing throws or aborts across this ABI. Device faults
+ *   surface at the caller's next synchronisation, as for any HIP call.
+ * Determinism. Results are bitwise identical from run to run for the same inputs, shapes and
+ *   workspace (fixed-order reductions, no floating-point atomics).
+ */
+#ifndef LIBGDN_H
+#define LIBGDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LIBGDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,         /* a required pointer is NULL */
+    GDN_ERR_SHAPE = 2,        /* a size is < 1 or too large */
+    GDN_ERR_UNSUPPORTED = 3,  /* head_dim or dtype not supported */
+    GDN_ERR_STRIDE = 4,       /* a stride is negative or rows of one tensor overlap */
+    GDN_ERR_ALIGN = 5,        /* pointer or stride alignment violated */
+    GDN_ERR_ALIAS = 6,        /* an output overlaps an input (other than the allowed in-place state) */
+    GDN_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than gdn_workspace_size() */
+    GDN_ERR_HIP = 8           /* a HIP runtime call failed */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef struct {
+    int32_t batch;             /* B */
+    int32_t heads;             /* H */
+    int32_t head_dim;          /* D in {16, 32, 64, 128} */
+    int32_t tokens_per_frame;  /* S */
+    int32_t frames;            /* F (gdn_step_frame ignores it: one frame) */
+    int32_t dtype;             /* gdn_dtype of Q, K, V, O */
+    int32_t use_delta;         /* 1: gated delta rule; 0: M = gamma M + beta Kt^T V */
+    float   key_scale;         /* c; <= 0 selects 1/sqrt(D*S) */
+    int64_t qkv_stride_b, qkv_stride_h, qkv_stride_t;   /* elements */
+    int64_t o_stride_b, o_stride_h, o_stride_t;         /* elements */
+} gdn_problem;
+
+/*
+ * Workspace bytes needed by gdn_forward_framewise (step_mode = 0) or gdn_step_frame
+ * (step_mode = 1) for this problem. The step-mode size does not depend on `frames`.
+ * Validates the sizes in `p` (not the pointers or strides).
+ */
+gdn_status gdn_workspace_size(const gdn_problem* p, int step_mode, size_t* bytes_out);
+
+/*
+ * All F frames of every (b, h) in one call (the recurrence above).
+ *   q, k, v      inputs, layout as above
+ *   gamma, beta  fp32 [B][H][F]
+ *   state_in     fp32 [B][H][D][D], or NULL for a zero initial state
+ *   o            output, layout as above; must not overlap any input
+ *   state_out    fp32 [B][H][D][D] state after frame F-1, or NULL; may equal state_in exactly
+ *   workspace    device scratch of at least gdn_workspace_size(p, 0) bytes, 256-byte aligned;
+ *                its contents on entry do not matter and are undefined afterwards
+ */
+gdn_status gdn_forward_framewise(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                 const float* gamma, const float* beta, const float* state_in,
+                                 void* o, float* state_out,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * One frame for streaming / autoregressive rollout: compute the frame's contribution, add it
+ * to the cached state, produce the frame's output, and cache the new state only when asked
+ * (the block KV cache passage of the SANA-Video talk; the chunk-causal and distilled
+ * autoregressive modes of the gen-hub.ru article, section "Три режима на любой вкус"; frame
+ * by frame streaming in SANA-Streaming, jefxiong.cn digest item 1).
+ *   q, k, v, o   one frame: t = s in [0, S); strides as above
+ *   gamma, beta  fp32 [B][H]
+ *   state_in     fp32 [B][H][D][D], required
+ *   state_out    NULL: the new state is not committed (a denoising pass that will be redone);
+ *                otherwise it receives the new state and may equal state_in exactly
+ *   workspace    at least gdn_workspace_size(p, 1) bytes, 256-byte aligned
+ */
+gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, const void* v,
+                          const float* gamma, const float* beta, const float* state_in,
+                          void* o, float* state_out,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Static text for a status code (never NULL). */
+const char* gdn_status_string(gdn_status s);
+
+/* Detail of the last failure on the calling host thread ("" if none). */
+const char* gdn_last_error_message(void);
+
+/* LIBGDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGDN_H */

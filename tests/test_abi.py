@@ -1,0 +1,164 @@
+"""C-ABI boundary on the CPU: the library loads, exports what the header declares, and rejects
+bad arguments on the host before any device work (fake device addresses are safe here because
+every call below fails validation first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import frame_wise_gated_libgdn_amd as gdn
+import gdn_synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libgdn.h")
+
+A = 1 << 20  # a 16-byte (and 256-byte) aligned fake address; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = gdn.load()
+    names = declared_functions()
+    assert {"gdn_forward_framewise", "gdn_step_frame", "gdn_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), "missing export " + n
+
+
+def test_abi_version_and_status_strings():
+    assert gdn.abi_version() == 1
+    lib = gdn.load()
+    for code in range(9):
+        assert lib.gdn_status_string(code)
+    assert lib.gdn_status_string(99) == b"unknown status"
+
+
+def prob(B=1, H=2, D=64, S=40, F=3, dtype=gdn.GDN_BF16, delta=1, layout="head"):
+    T = F * S
+    if layout == "head":
+        st = (H * T * D, T * D, D)
+    else:
+        st = (T * H * D, D, H * D)
+    return gdn.Problem(B, H, D, S, F, dtype, delta, 0.0, *st, *st)
+
+
+def call(p, step=False, q=A, k=2 * A, v=3 * A, g=4 * A, b=5 * A, si=None, o=6 * A, so=None,
+         ws=8 * A, wsb=1 << 40):
+    lib = gdn.load()
+    fn = lib.gdn_step_frame if step else lib.gdn_forward_framewise
+    pp = None if p is None else ctypes.byref(p)
+    return fn(pp, q, k, v, g, b, si, o, so, ws, wsb, None)
+
+
+def msg():
+    return gdn.load().gdn_last_error_message().decode()
+
+
+@pytest.mark.parametrize("name", gdn_synth.WORKLOAD_ORDER)
+def test_workspace_size_for_workloads(name):
+    w = gdn_synth.WORKLOADS[name]
+    p = gdn.Problem(w.B, w.H, w.D, w.S, 1 if w.step_mode else w.F,
+                    gdn.GDN_F32 if w.dtype == "f32" else gdn.GDN_BF16, int(w.use_delta), 0.0,
+                    0, 0, w.D, 0, 0, w.D)
+    n = gdn.workspace_size(p, w.step_mode)
+    assert n > 0
+    if not w.step_mode:
+        esz = w.elem_bytes()
+        # per-frame states plus at least one fp32 partial per frame
+        assert n >= w.B * w.H * w.F * w.D * w.D * (esz + 4 * (2 if w.use_delta else 1))
+
+
+def test_step_workspace_independent_of_frames():
+    # constant memory in video length (the fixed D x D state of the pages)
+    sizes = {gdn.workspace_size(prob(F=f), True) for f in (1, 10, 961, 100000)}
+    assert len(sizes) == 1
+
+
+def test_forward_workspace_grows_with_frames():
+    assert gdn.workspace_size(prob(F=20), False) > gdn.workspace_size(prob(F=10), False)
+
+
+def test_null_problem():
+    assert call(None) == 1
+    assert "NULL" in msg()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, 2), ("heads", 0, 2), ("tokens_per_frame", 0, 2), ("frames", 0, 2),
+    ("head_dim", 48, 3), ("head_dim", 256, 3), ("dtype", 7, 3),
+])
+def test_bad_sizes(field, value, code):
+    p = prob()
+    setattr(p, field, value)
+    assert call(p) == code
+    assert msg()
+    n = ctypes.c_size_t(123)
+    assert gdn.load().gdn_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == code
+    assert n.value == 123
+
+
+def test_step_ignores_frames_and_requires_state():
+    p = prob(F=0)
+    assert call(p, step=True) == 1  # state_in missing (frames is not checked in step mode)
+    assert "state_in" in msg()
+
+
+def test_null_tensor_pointers():
+    assert call(prob(), q=None) == 1
+    assert call(prob(), o=None) == 1
+    assert call(prob(), g=None) == 1
+
+
+def test_misaligned_pointers_and_strides():
+    assert call(prob(), k=2 * A + 8) == 5
+    p = prob()
+    p.qkv_stride_t = 68
+    p.qkv_stride_h = 68 * 120
+    assert call(p) == 5
+    assert call(prob(), ws=8 * A + 16) == 5
+    assert call(prob(), g=4 * A + 2) == 5
+
+
+def test_bad_strides():
+    p = prob()
+    p.qkv_stride_t = 32  # rows of 64 elements overlap
+    assert call(p) == 4
+    p = prob()
+    p.o_stride_h = -p.o_stride_h
+    assert call(p) == 4
+    p = prob(H=2)
+    p.qkv_stride_h = 64  # heads interleave with tokens
+    assert call(p) == 4
+
+
+def test_token_major_layout_accepted_until_workspace_check():
+    p = prob(layout="token")
+    assert call(p, wsb=16) == 7
+    assert "workspace" in msg()
+
+
+def test_workspace_missing_or_small():
+    p = prob()
+    need = gdn.workspace_size(p, False)
+    assert call(p, wsb=need - 1) == 7
+    assert call(p, ws=None) == 7
+
+
+def test_aliasing():
+    p = prob()
+    assert call(p, o=A) == 6                      # o == q
+    assert call(p, o=A + 1024) == 6               # o overlaps q
+    assert call(p, so=8 * A + 256) == 6           # state_out inside the workspace
+    assert call(p, si=7 * A, so=7 * A + 4096) == 6  # partial overlap of the states
+    assert call(p, ws=6 * A + 4096) == 6          # workspace overlaps o
+
+
+def test_in_place_state_passes_alias_checks():
+    # exact in-place commit is allowed: the call only fails later, at the workspace check
+    p = prob()
+    assert call(p, si=7 * A, so=7 * A, wsb=16) == 7

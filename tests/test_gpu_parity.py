@@ -1,0 +1,211 @@
+"""GPU path (through the C ABI) against the CPU oracle, element by element.
+
+Tolerance: max|d| / max|ref| <= 1e-4 for fp32 inputs, <= 1e-2 for bf16 inputs (fp32 state).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import frame_wise_gated_libgdn_amd as gdn  # noqa: E402
+import gdn_synth  # noqa: E402
+import oracle  # noqa: E402
+from gpu_util import TOL, rel_err, random_qkv, to_dev, to_np  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# --------------------------------------------------------------------------- generator
+def test_generator_device_matches_host():
+    w = gdn_synth.WORKLOADS["gdn_720p_60s_bf16"]
+    gen = gdn_synth.TorchGen(DEV)
+    dst = torch.empty((2 * w.S, w.D), dtype=torch.bfloat16, device=DEV)
+    gen.fill_normal(dst, w.seed, gdn_synth.TID_K, 0, 5, 100, w.S, w.D)
+    host = np.concatenate([gdn_synth.f32_to_bf16_bits(
+        gdn_synth.normal_slice(w.seed, gdn_synth.TID_K, 0, 5, f, w.S, w.D)) for f in (100, 101)])
+    got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, host)
+
+
+# --------------------------------------------------------------------------- workloads
+def run_workload_forward(w, layout="head"):
+    q, k, v = gdn_synth.qkv_torch(w, DEV, layout=layout)
+    g, b = gdn_synth.gates_torch(w, DEV)
+    o, st = gdn.forward_framewise(q, k, v, g, b, use_delta=w.use_delta)
+    torch.cuda.synchronize()
+    return o, st
+
+
+@pytest.mark.parametrize("layout", ["head", "token"])
+def test_tiny_f32_full(layout):
+    w = gdn_synth.WORKLOADS["tiny_f32"]
+    say("tiny_f32 layout", layout)
+    o, st = run_workload_forward(w, layout)
+    (qc, kc, vc), _ = gdn_synth.qkv_cpu(w)
+    gc, bc = gdn_synth.gates_cpu(w)
+    ro, rs = oracle.forward(qc, kc, vc, gc, bc)
+    assert rel_err(to_np(o), ro) <= TOL["f32"]
+    assert rel_err(to_np(st), rs) <= TOL["f32"]
+
+
+def test_block_causal_bf16_full():
+    w = gdn_synth.WORKLOADS["block_causal_bf16"]
+    say("block_causal_bf16 full")
+    o, st = run_workload_forward(w)
+    (qc, kc, vc), _ = gdn_synth.qkv_cpu(w)
+    gc, bc = gdn_synth.gates_cpu(w)
+    ro, rs = oracle.forward(qc, kc, vc, gc, bc, use_delta=False)
+    e1, e2 = rel_err(to_np(o), ro), rel_err(to_np(st), rs)
+    say("  O err %.3e state err %.3e" % (e1, e2))
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+def test_gdn_880x81_bf16_sampled_heads():
+    w = gdn_synth.WORKLOADS["gdn_880x81_bf16"]
+    say("gdn_880x81_bf16 full launch, oracle on heads 0 and 15")
+    o, st = run_workload_forward(w)
+    heads = [0, 15]
+    (qc, kc, vc), _ = gdn_synth.qkv_cpu(w, heads=heads)
+    gc, bc = gdn_synth.gates_cpu(w, heads=heads)
+    ro, rs = oracle.forward(qc, kc, vc, gc, bc)
+    e1 = rel_err(to_np(o[:, heads]), ro)
+    e2 = rel_err(to_np(st[:, heads]), rs)
+    say("  O err %.3e state err %.3e" % (e1, e2))
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+# --------------------------------------------------------------------------- shape sweep
+SWEEP = [
+    # B, H, D, S, F, dtype, delta, layout
+    (1, 1, 16, 1, 1, "f32", True, "head"),
+    (1, 2, 16, 17, 3, "f32", True, "token"),
+    (2, 1, 32, 100, 2, "f32", True, "head"),
+    (1, 3, 64, 65, 3, "f32", False, "head"),
+    (1, 1, 128, 33, 2, "f32", True, "head"),
+    (1, 1, 16, 5, 4, "bf16", True, "head"),
+    (1, 2, 32, 64, 3, "bf16", True, "token"),
+    (2, 3, 64, 130, 4, "bf16", True, "head"),
+    (1, 2, 64, 77, 5, "bf16", False, "token"),
+    (1, 2, 128, 1, 6, "bf16", True, "head"),
+    (1, 9, 128, 200, 3, "bf16", True, "head"),
+    (1, 2, 128, 1000, 2, "bf16", False, "head"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=["-".join(map(str, c)) for c in SWEEP])
+def test_forward_sweep(case):
+    B, H, D, S, F, dt, delta, layout = case
+    say("forward sweep", case)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    q, k, v = random_qkv(rng, (B, H, F * S, D), dt)
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    s0 = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    o, st = gdn.forward_framewise(to_dev(q, dt, DEV, layout), to_dev(k, dt, DEV, layout),
+                                  to_dev(v, dt, DEV, layout), torch.from_numpy(g).to(DEV),
+                                  torch.from_numpy(b).to(DEV), torch.from_numpy(s0).to(DEV),
+                                  use_delta=delta)
+    torch.cuda.synchronize()
+    ro, rs = oracle.forward(q, k, v, g, b, s0, use_delta=delta)
+    e1, e2 = rel_err(to_np(o), ro), rel_err(to_np(st), rs)
+    say("  O err %.3e state err %.3e" % (e1, e2))
+    assert e1 <= TOL[dt] and e2 <= TOL[dt]
+
+
+STEP_SWEEP = [
+    (1, 2, 16, 16, "f32", True),
+    (1, 1, 32, 70, "f32", False),
+    (1, 2, 128, 300, "f32", True),
+    (2, 2, 16, 9, "bf16", True),
+    (1, 3, 64, 257, "bf16", True),
+    (1, 2, 64, 100, "bf16", False),
+    (1, 4, 128, 700, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", STEP_SWEEP, ids=["-".join(map(str, c)) for c in STEP_SWEEP])
+def test_step_sweep(case):
+    B, H, D, S, dt, delta = case
+    say("step sweep", case)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    q, k, v = random_qkv(rng, (B, H, S, D), dt)
+    g = rng.uniform(0.85, 1.0, (B, H)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H)).astype(np.float32)
+    s0 = (0.3 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    dq, dk, dv = (to_dev(x, dt, DEV) for x in (q, k, v))
+    dg, db, ds = (torch.from_numpy(x).to(DEV) for x in (g, b, s0))
+    o, st = gdn.step_frame(dq, dk, dv, dg, db, ds, commit=True, use_delta=delta)
+    o2, none = gdn.step_frame(dq, dk, dv, dg, db, ds, commit=False, use_delta=delta)
+    torch.cuda.synchronize()
+    assert none is None
+    ro, rs = oracle.step(q, k, v, g, b, s0, use_delta=delta)
+    e1, e2 = rel_err(to_np(o), ro), rel_err(to_np(st), rs)
+    say("  O err %.3e state err %.3e" % (e1, e2))
+    assert e1 <= TOL[dt] and e2 <= TOL[dt]
+    assert torch.equal(o, o2), "uncommitted pass must give the same output"
+    assert np.array_equal(to_np(ds), s0), "state_in must not change"
+
+
+def test_step_in_place_commit():
+    rng = np.random.default_rng(5)
+    B, H, D, S = 1, 2, 64, 96
+    q, k, v = random_qkv(rng, (B, H, S, D), "bf16")
+    g = rng.uniform(0.9, 1.0, (B, H)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H)).astype(np.float32)
+    s0 = (0.3 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    ds = torch.from_numpy(s0).to(DEV)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV)]
+    o_ref, s_ref = gdn.step_frame(*args, ds.clone())
+    o, s = gdn.step_frame(*args, ds, state_out=ds)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == ds.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(ds, s_ref)
+
+
+def test_step_chain_equals_forward_and_oracle():
+    rng = np.random.default_rng(6)
+    B, H, D, S, F = 1, 3, 128, 120, 5
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    dq, dk, dv = (to_dev(x, "bf16", DEV) for x in (q, k, v))
+    dg, db = torch.from_numpy(g).to(DEV), torch.from_numpy(b).to(DEV)
+    of, sf = gdn.forward_framewise(dq, dk, dv, dg, db)
+    state = torch.zeros((B, H, D, D), dtype=torch.float32, device=DEV)
+    outs = []
+    for f in range(F):
+        sl = slice(f * S, (f + 1) * S)
+        o, state = gdn.step_frame(dq[:, :, sl], dk[:, :, sl], dv[:, :, sl],
+                                  dg[:, :, f].contiguous(), db[:, :, f].contiguous(), state)
+        outs.append(o)
+    torch.cuda.synchronize()
+    os_ = torch.cat(outs, dim=2)
+    ro, rs = oracle.forward(q, k, v, g, b)
+    assert rel_err(to_np(os_), ro) <= TOL["bf16"]
+    assert rel_err(to_np(state), rs) <= TOL["bf16"]
+    assert rel_err(to_np(of), to_np(os_)) <= TOL["bf16"]
+    assert rel_err(to_np(sf), to_np(state)) <= TOL["bf16"]
+
+
+def test_determinism_bitwise():
+    rng = np.random.default_rng(8)
+    B, H, D, S, F = 1, 4, 128, 333, 4
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV)]
+    o1, s1 = gdn.forward_framewise(*args)
+    o2, s2 = gdn.forward_framewise(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
