@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Throughput of the frame-wise GDN forward on one MI355X, with its roofline and a CPU baseline.
+
+One step = one gdn_forward_framewise call over the whole workload (all frames, all heads):
+the partial-product kernel, the frame scan and the output kernel. Inputs are synthetic,
+seeded and generated on the device before timing (resident in HBM).
+
+Prints one JSON line. Extra objects:
+  roofline      the dominant kernel's algorithmic HBM bytes per launch / its mean duration,
+                timed with HIP events recorded on the launch stream inside the library
+                (gdn_set_stage_events); `traffic` comes from the committed rocprofv3 counter
+                summary when it was taken on the current kernel source, else null.
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
+  stream        streaming step mode (gdn_step_frame): 4 denoising passes per frame, state
+                committed after the last; per-frame latency and frames/s.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+KERNELS = ["gram_kernel", "scan_kernel", "output_kernel"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gdn_720p_60s_bf16.json")
+KERNEL_SRC = os.path.join(ROOT, "frame_wise_gated_libgdn_amd", "csrc", "gdn_kernels.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t through the HIP runtime that torch already loaded (same soname)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def new(self):
+        e = ctypes.c_void_p()
+        assert self.rt.hipEventCreate(ctypes.byref(e)) == 0
+        self.made.append(e.value)
+        return e.value
+
+    def record(self, e, stream):
+        assert self.rt.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        assert self.rt.hipEventSynchronize(b) == 0
+        out = ctypes.c_float()
+        assert self.rt.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return float(out.value)
+
+    def close(self):
+        for e in self.made:
+            self.rt.hipEventDestroy(e)
+        self.made = []
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gdn_720p_60s_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="target CPU time (wall x threads) of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--stream-frames", type=int, default=240)
+    ap.add_argument("--copy-calib-gib", type=float, default=0.0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def source_sha():
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def traffic_for(kernel, workload):
+    """Counter-derived HBM bytes per launch (GB), if measured on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_sha() or t.get("workload") != workload:
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else round(k["hbm_gb_per_launch"], 3)
+
+
+def copy_calibration(gib):
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+
+
+def cpu_baseline(w, seconds):
+    import numpy as np
+    import gdn_synth
+    import oracle
+    nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
+    heads = list(range(w.H))
+
+    def run(nf):
+        (q, k, v), _ = gdn_synth.qkv_cpu(w, heads=heads, frames=range(nf))
+        g, b = gdn_synth.gates_cpu(w, heads=heads, frames=range(nf))
+        t = time.perf_counter()
+        oracle.forward(q, k, v, g, b, use_delta=w.use_delta, nthreads=nthreads)
+        return time.perf_counter() - t
+
+    t1 = run(1)
+    nf = int(max(1, min(16, w.F, round(seconds / max(t1 * nthreads, 1e-6)))))
+    log("cpu baseline: 1 frame took %.2f s; timing %d frames on %d threads" % (t1, nf, nthreads))
+    t = run(nf) if nf > 1 else t1
+    tokens = w.B * nf * w.S
+    return {"value": round(tokens / t, 1), "unit": "tokens/s", "cores": nthreads,
+            "kind": "oracle", "seconds": round(t, 2),
+            "sample": "all %d heads of batch 0, frames 0-%d of %s (S=%d, D=%d): fp64 oracle, "
+                      "OpenMP over heads" % (w.H, nf - 1, w.name, w.S, w.D)}
+
+
+def stream_mode(dev, nframes, ev, stream):
+    """Streaming step mode: per frame 4 passes from the same incoming state, commit on the last."""
+    import numpy as np
+    import torch
+    import frame_wise_gated_libgdn_amd as gdn
+    import gdn_synth
+    w = gdn_synth.WORKLOADS["stream_720p_bf16"]
+    nframes = min(nframes, w.F)
+    gen = gdn_synth.TorchGen(dev)
+    passes = []
+    for p in range(w.passes):
+        q, k, v = gdn_synth.qkv_torch(w, dev, frames=(0, nframes), pass_=p, gen=gen)
+        g, b = gdn_synth.gates_torch(w, dev, pass_=p)
+        # per-frame gates as contiguous [B, H] slices
+        passes.append((q, k, v, g.permute(2, 0, 1).contiguous(), b.permute(2, 0, 1).contiguous()))
+    state = torch.zeros((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device=dev)
+    wsz = gdn.workspace_size(gdn.Problem(w.B, w.H, w.D, w.S, 1, gdn.GDN_BF16, 1, 0.0,
+                                         0, 0, w.D, 0, 0, w.D), True)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+
+    def frame(f):
+        sl = slice(f * w.S, (f + 1) * w.S)
+        for p in range(w.passes):
+            q, k, v, g, b = passes[p]
+            last = p == w.passes - 1
+            gdn.step_frame(q[:, :, sl], k[:, :, sl], v[:, :, sl], g[f], b[f], state,
+                           commit=last, out=o, state_out=state if last else None, workspace=ws)
+
+    for f in range(min(3, nframes)):  # warm-up on a scratch copy of the state
+        frame(f)
+    state.zero_()
+    torch.cuda.synchronize()
+    marks = [ev.new() for _ in range(nframes + 1)]
+    ev.record(marks[0], stream)
+    for f in range(nframes):
+        frame(f)
+        ev.record(marks[f + 1], stream)
+    lat = np.array([ev.ms(marks[f], marks[f + 1]) for f in range(nframes)])
+    total = ev.ms(marks[0], marks[-1])
+    return {"workload": w.name, "frames": nframes, "passes_per_frame": w.passes,
+            "frame_latency_ms": {"median": round(float(np.median(lat)), 4),
+                                 "p90": round(float(np.percentile(lat, 90)), 4),
+                                 "max": round(float(lat.max()), 4)},
+            "frames_per_s": round(nframes / (total / 1e3), 1),
+            "pass_us_median": round(float(np.median(lat)) * 1e3 / w.passes, 2)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(asked for --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import frame_wise_gated_libgdn_amd as gdn
+    import gdn_synth
+    if args.copy_calib_gib > 0:
+        copy_calibration(args.copy_calib_gib)
+        return
+    gdn.load()
+    w = gdn_synth.WORKLOADS[args.workload]
+    assert not w.step_mode, "the forward bench needs a forward workload"
+    dev = torch.device("cuda:0")
+    log("generating %s inputs on the device" % w.name)
+    t = time.perf_counter()
+    q, k, v = gdn_synth.qkv_torch(w, dev)
+    g, b = gdn_synth.gates_torch(w, dev)
+    torch.cuda.synchronize()
+    log("inputs ready in %.1f s" % (time.perf_counter() - t))
+    o = torch.empty_like(q)
+    st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    p = gdn.Problem(w.B, w.H, w.D, w.S, w.F, gdn.GDN_BF16 if w.dtype == "bf16" else gdn.GDN_F32,
+                    int(w.use_delta), 0.0, *q.stride()[:3], *o.stride()[:3])
+    ws = torch.empty(gdn.workspace_size(p, False), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def call():
+        gdn.forward_framewise(q, k, v, g, b, use_delta=w.use_delta, out=o, state_out=st,
+                              workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    log("warm-up done (%d steps)" % args.warmup)
+
+    ev = HipEvents()
+    stage = [[ev.new() for _ in range(4)] for _ in range(args.steps)]
+    t0, t1 = ev.new(), ev.new()
+    torch.cuda.synchronize()
+    ev.record(t0, sh)
+    for i in range(args.steps):
+        gdn.set_stage_events(stage[i])
+        call()
+    gdn.set_stage_events(None)
+    ev.record(t1, sh)
+    torch.cuda.synchronize()
+    total_ms = ev.ms(t0, t1)
+    ms = total_ms / args.steps
+    kms = {KERNELS[j]: sum(ev.ms(stage[i][j], stage[i][j + 1]) for i in range(args.steps))
+           / args.steps for j in range(3)}
+    log("timed %d steps: %.3f ms/step; stages %s" % (args.steps, ms,
+                                                      {k_: round(x, 3) for k_, x in kms.items()}))
+
+    esz = w.elem_bytes()
+    tokens = w.B * w.F * w.S
+    bytes_alg = 4 * w.B * w.H * w.F * w.S * w.D * esz          # Q, K, V read + O written
+    flops_alg = (6 if w.use_delta else 4) * w.B * w.H * w.F * w.S * w.D * w.D
+    per_kernel_bytes = {"gram_kernel": bytes_alg // 2, "output_kernel": bytes_alg // 2,
+                        "scan_kernel": 0}
+    dom = max(("gram_kernel", "output_kernel"), key=lambda n: kms[n])
+    achieved = per_kernel_bytes[dom] / (kms[dom] * 1e-3) / 1e9
+    t_roof_ms = max(bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    result = {
+        "metric": "GDN tokens/sec at 961x3520-token 720p shape; % of HBM/MFMA roofline",
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D,
+                   "tokens_per_frame": w.S, "frames": w.F, "tokens": tokens,
+                   "use_delta": w.use_delta, "layout": "head-major [B,H,T,D]",
+                   "state": "fp32", "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm", "kernel": dom,
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for(dom, w.name), "traffic_unit": "GB per launch",
+            "algorithmic_gb_per_launch": round(per_kernel_bytes[dom] / 1e9, 3),
+            "kernel_ms": {k_: round(x, 4) for k_, x in kms.items()},
+            "call": {"bytes_alg_gb": round(bytes_alg / 1e9, 3),
+                     "flops_alg_tf": round(flops_alg / 1e12, 4),
+                     "t_roof_ms": round(t_roof_ms, 4),
+                     "frac_of_roofline": round(t_roof_ms / ms, 4),
+                     "achieved_gb_s": round(bytes_alg / (ms * 1e-3) / 1e9, 1),
+                     "achieved_tflops": round(flops_alg / (ms * 1e-3) / 1e12, 2)},
+        },
+    }
+    ev.close()
+    del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    if not args.no_stream:
+        ev2 = HipEvents()
+        log("streaming step mode: %d frames x 4 passes" % args.stream_frames)
+        result["stream"] = stream_mode(dev, args.stream_frames, ev2, sh)
+        ev2.close()
+        log("stream done: %s" % result["stream"]["frame_latency_ms"])
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

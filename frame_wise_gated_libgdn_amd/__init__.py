@@ -16,7 +16,7 @@ import os
 import threading
 
 __all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "forward_framewise",
-           "step_frame", "abi_version", "GDN_F32", "GDN_BF16"]
+           "step_frame", "abi_version", "set_stage_events", "GDN_F32", "GDN_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -62,6 +62,10 @@ def load():
             if not os.path.exists(_LIB_PATH):
                 raise ImportError("libgdn.so is not built at %s; run __graft_entry__.build()"
                                   % _LIB_PATH)
+            # torch ships its own HIP runtime (same soname). Loading torch first makes
+            # libgdn.so bind to that copy, so streams and pointers from torch are valid here;
+            # loading libgdn.so first would map a second runtime into the process.
+            import torch  # noqa: F401
             lib = ctypes.CDLL(_LIB_PATH)
             P = ctypes.POINTER(Problem)
             lib.gdn_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -73,12 +77,24 @@ def load():
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_last_error_message.restype = ctypes.c_char_p
             lib.gdn_abi_version.restype = ctypes.c_int
+            lib.gdn_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+            lib.gdn_set_stage_events.restype = ctypes.c_int
             _lib = lib
     return _lib
 
 
 def abi_version() -> int:
     return int(load().gdn_abi_version())
+
+
+def set_stage_events(handles):
+    """Arm (list of up to 4 hipEvent_t handles as ints) or disarm (None) the per-kernel stage
+    events of later calls on this host thread."""
+    if not handles:
+        _check(load().gdn_set_stage_events(None, 0))
+        return
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    _check(load().gdn_set_stage_events(arr, len(handles)))
 
 
 def _check(code):
@@ -116,6 +132,17 @@ def _problem(q, o, F, use_delta, key_scale):
                    q.stride(0), q.stride(1), q.stride(2), o.stride(0), o.stride(1), o.stride(2))
 
 
+def _check_f32(name, t, shape):
+    """Gates and states cross the ABI as contiguous fp32 arrays."""
+    import torch
+    if t is None:
+        return
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise GdnError(4, "%s must be a contiguous float32 tensor of shape %s (got %s %s%s)"
+                       % (name, tuple(shape), t.dtype, tuple(t.shape),
+                          "" if t.is_contiguous() else ", non-contiguous"))
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -146,6 +173,10 @@ def forward_framewise(q, k, v, gamma, beta, state=None, *, use_delta=True, key_s
         out = torch.empty((B, H, T, D), dtype=q.dtype, device=q.device)
     if state_out is None and return_state:
         state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _check_f32("gamma", gamma, (B, H, F))
+    _check_f32("beta", beta, (B, H, F))
+    _check_f32("state", state, (B, H, D, D))
+    _check_f32("state_out", state_out, (B, H, D, D))
     p = _problem(q, out, F, use_delta, key_scale)
     ws, nbytes = _workspace(p, False, workspace, q.device)
     _check(load().gdn_forward_framewise(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
@@ -169,6 +200,10 @@ def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_
         state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     if not commit:
         state_out = None
+    _check_f32("gamma", gamma, (B, H))
+    _check_f32("beta", beta, (B, H))
+    _check_f32("state", state, (B, H, D, D))
+    _check_f32("state_out", state_out, (B, H, D, D))
     p = _problem(q, out, 1, use_delta, key_scale)
     ws, nbytes = _workspace(p, True, workspace, q.device)
     _check(load().gdn_step_frame(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),

@@ -14,6 +14,8 @@
 namespace {
 
 thread_local char g_msg[512] = "";
+thread_local hipEvent_t g_ev[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local int g_nev = 0;
 
 gdn_status fail(gdn_status s, const char* fmt, ...) {
     va_list ap;
@@ -185,6 +187,8 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     L.nsplit = pl.nsplit; L.split_tokens = pl.split_tokens;
     L.nchunk = pl.nchunk; L.chunk_tokens = pl.chunk_tokens;
     L.stream = (hipStream_t)stream;
+    L.nev = g_nev;
+    for (int i = 0; i < 4; ++i) L.ev[i] = g_ev[i];
     const hipError_t e = step_mode ? gdn::launch_step(L) : gdn::launch_forward(L);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
@@ -218,6 +222,16 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                           void* hip_stream) {
     return run(1, p, q, k, v, gamma, beta, state_in, o, state_out, workspace, workspace_bytes,
                hip_stream);
+}
+
+gdn_status gdn_set_stage_events(void* const* events, int count) {
+    g_msg[0] = '\0';
+    if (count < 0 || count > 4) return fail(GDN_ERR_SHAPE, "count must be 0..4, got %d", count);
+    if (count > 0 && !events) return fail(GDN_ERR_NULL, "events is NULL");
+    if (!events) count = 0;
+    for (int i = 0; i < 4; ++i) g_ev[i] = i < count ? (hipEvent_t)events[i] : nullptr;
+    g_nev = count;
+    return GDN_OK;
 }
 
 const char* gdn_status_string(gdn_status s) {

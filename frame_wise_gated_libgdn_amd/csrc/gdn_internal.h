@@ -25,6 +25,8 @@ struct Launch {
     int nchunk;          // S chunks of the output kernel
     int chunk_tokens;    // tokens per output chunk (multiple of 16)
     hipStream_t stream;
+    hipEvent_t ev[4];    // optional stage events (nev of them)
+    int nev;
 };
 
 // Enqueue the whole forward (all frames) / one streaming step. Return the HIP error of the

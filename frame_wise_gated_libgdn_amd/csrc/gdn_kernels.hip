@@ -282,19 +282,36 @@ __global__ __launch_bounds__(NT) void scan_kernel(Launch L) {
             if (active) Ms[0][row * NC + r16] = Mc[it][q];
         }
 
+    // Next frame's Ghat (whole D x D, float4 per thread) and Bhat (this wave's C-layout
+    // entries), summed over the S splits. The split loop is outermost so that all loads of one
+    // split are independent and in flight together.
     f32x4 gpre[GV];
-    auto load_g = [&](int f) {
+    float bpre[IT][4];
+    auto load_next = [&](int f) {
         const float* src = part_bh + (int64_t)f * L.nsplit * pstride;
+        for (int p = 0; p < L.nsplit; ++p) {
+            const float* sp = src + p * pstride;
+            if (DELTA) {
 #pragma unroll
-        for (int v = 0; v < GV; ++v) {
-            const int i4 = tid + v * NT;
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (i4 * 4 < D * D)
-                for (int p = 0; p < L.nsplit; ++p) s += *(const f32x4*)(src + p * pstride + 4 * i4);
-            gpre[v] = s;
+                for (int v = 0; v < GV; ++v) {
+                    const int i4 = tid + v * NT;
+                    const f32x4 x = i4 * 4 < D * D ? *(const f32x4*)(sp + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    gpre[v] = p == 0 ? x : gpre[v] + x;
+                }
+            }
+            if (active) {
+                const float* bp = sp + (DELTA ? D * D : 0);
+#pragma unroll
+                for (int it = 0; it < IT; ++it)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float x = bp[((wave * IT + it) * 16 + 4 * g + q) * D + col];
+                        bpre[it][q] = p == 0 ? x : bpre[it][q] + x;
+                    }
+            }
         }
     };
-    if (DELTA) load_g(0);
+    load_next(0);
 
     int cur = 0;
     for (int f = 0; f < L.F; ++f) {
@@ -308,20 +325,14 @@ __global__ __launch_bounds__(NT) void scan_kernel(Launch L) {
                 }
             }
         }
+        float Bc[IT][4];
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Bc[it][q] = bpre[it][q];
         __syncthreads();
-        if (DELTA && f + 1 < L.F) load_g(f + 1);
+        if (f + 1 < L.F) load_next(f + 1);
         if (active) {
-            const float* pf = part_bh + (int64_t)f * L.nsplit * pstride + (DELTA ? D * D : 0);
-            float Bc[IT][4];
-#pragma unroll
-            for (int it = 0; it < IT; ++it)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int row = (wave * IT + it) * 16 + 4 * g + q;
-                    float s = 0.f;
-                    for (int p = 0; p < L.nsplit; ++p) s += pf[p * pstride + row * D + col];
-                    Bc[it][q] = s;
-                }
             f32x4 acc[IT];
 #pragma unroll
             for (int it = 0; it < IT; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -620,25 +631,38 @@ __global__ __launch_bounds__(NT) void step_reduce_kernel(Launch L) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Optional stage events (tracing): event i is recorded after kernel i (event 0 before the first).
+static inline void mark(const Launch& L, int i) {
+    if (i < L.nev && L.ev[i]) (void)hipEventRecord(L.ev[i], L.stream);
+}
+
 template <typename T, int D, bool DELTA> static hipError_t fwd(const Launch& L) {
     const int BH = L.B * L.H;
+    mark(L, 0);
     hipLaunchKernelGGL((gram_kernel<T, D, DELTA>), dim3(BH * L.F * L.nsplit), dim3(NT), 0,
                        L.stream, L);
+    mark(L, 1);
     const int units = (BH + 7) / 8 * 8 * (D / 16);
     hipLaunchKernelGGL((scan_kernel<T, D, DELTA>), dim3(units), dim3(NT), 0, L.stream, L);
+    mark(L, 2);
     hipLaunchKernelGGL((output_kernel<T, D>), dim3(BH * L.F * L.nchunk), dim3(NT), 0, L.stream, L);
+    mark(L, 3);
     return hipGetLastError();
 }
 
 template <typename T, int D, bool DELTA> static hipError_t stp(const Launch& L) {
     const int BH = L.B * L.H;
+    mark(L, 0);
     hipLaunchKernelGGL((step_partial_kernel<T, D, DELTA>), dim3(BH * L.nsplit), dim3(NT), 0,
                        L.stream, L);
+    mark(L, 1);
     constexpr int NB = (D * D / 4 + NT - 1) / NT;
     hipLaunchKernelGGL((step_reduce_kernel<T, D>), dim3(BH * NB), dim3(NT), 0, L.stream, L);
+    mark(L, 2);
     Launch L1 = L;
     L1.F = 1;
     hipLaunchKernelGGL((output_kernel<T, D>), dim3(BH * L.nchunk), dim3(NT), 0, L.stream, L1);
+    mark(L, 3);
     return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@
  *   arithmetic accumulates in fp32; bf16 outputs are rounded to nearest even.
  * Supported shapes. D in {16, 32, 64, 128}; B, H, S, F >= 1; B*H*F*S*max-stride must fit the
  *   int64 element index. Pointers to Q, K, V, O must be 16-byte aligned, the strides multiples
- *   of 8 elements (GDN_ERR_ALIGN otherwise); gates and states 16-byte aligned.
+ *   of 8 elements, gates and states 4-byte aligned (GDN_ERR_ALIGN otherwise).
  * Gate values are not checked (that would cost a device pass); the documented domain is
  *   gamma in (0, 1], beta in [0, 1]. NaN and Inf inputs propagate.
  * Errors. Argument errors are found on the host before anything is enqueued: the call then
@@ -129,6 +129,16 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                           const float* gamma, const float* beta, const float* state_in,
                           void* o, float* state_out,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Instrumentation (tracing). Arms HIP events on the calling host thread: every later
+ * gdn_forward_framewise / gdn_step_frame call on this thread records events[0] on its stream
+ * before its first kernel and events[i] after its i-th kernel (i = 1 .. count-1; the forward
+ * runs three kernels -- products, scan, output -- and a step runs three -- partial, reduce,
+ * output). `events` holds hipEvent_t handles created by the caller; count 0 or events NULL
+ * disarms. count must be 0..4. The events are only recorded, never waited on.
+ */
+gdn_status gdn_set_stage_events(void* const* events, int count);
 
 /* Static text for a status code (never NULL). */
 const char* gdn_status_string(gdn_status s);
