@@ -450,9 +450,11 @@ __global__ __launch_bounds__(NT, 2) void output_kernel(Launch L) {
 
 // ----------------------------------------------------------------------------------------
 // Kernel 4: one frame, partial sums over the split's tokens of U = K^T R, with
-// R = V - (gamma c) K M (delta) or R = V (no delta). M (state_in) enters the prediction
-// product rounded to the I/O type. K and V of each 64-token chunk are staged transposed in LDS;
-// the prediction's K rows are read directly.
+// R = V - (gamma c) K M (delta) or R = V (no delta). The prediction P = K M runs on MFMA with M
+// (state_in) rounded to the I/O type. For bf16 data U is accumulated as K^T V + K^T (-gamma c P):
+// V is an exact bf16 input and only the small prediction term is rounded to bf16. For fp32
+// data R is formed in fp32. K and V of each 64-token chunk are staged transposed in LDS; the
+// prediction's K rows are read directly.
 // Token grouping inside a step of the U product: for bf16, a 32-token group is two 16-token
 // tiles; lane group g holds tokens {4g..4g+3} of the first tile and {16+4g..16+4g+3} of the
 // second (exactly the rows of the prediction's C fragments). For fp32, step q of a 16-token
@@ -520,13 +522,13 @@ __global__ __launch_bounds__(NT) void step_partial_kernel(Launch L) {
         if (!active) continue;
 #pragma unroll 1
         for (int tg = 0; tg < X::SC; tg += TG) {
-            // residual R (fp32, C layout): rows 4g+q of each 16-token tile, column (wave tile jl, r16)
-            float R[RT][JW][4];
+            // prediction P = K M (fp32, C layout): rows 4g+q of each 16-token tile, column
+            // (wave tile jl, r16)
+            f32x4 pr[RT][JW];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                f32x4 pr[JW];
 #pragma unroll
-                for (int jl = 0; jl < JW; ++jl) pr[jl] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int jl = 0; jl < JW; ++jl) pr[rt][jl] = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (DELTA) {
                     const int s = c0 + tg + rt * 16 + r16;
                     const bool ok = s < t1;
@@ -537,57 +539,53 @@ __global__ __launch_bounds__(NT) void step_partial_kernel(Launch L) {
                                 ? ld_frag<T>(kb + (int64_t)s * L.st + ks * MM::KS + g * MM::KL)
                                 : zero_frag<T>();
 #pragma unroll
-                        for (int jl = 0; jl < JW; ++jl) pr[jl] = MM::run(ak, bm[jl][ks], pr[jl]);
+                        for (int jl = 0; jl < JW; ++jl) pr[rt][jl] = MM::run(ak, bm[jl][ks], pr[rt][jl]);
                     }
                 }
+            }
+            if constexpr (sizeof(T) == 2) {
+                // U += K^T V + K^T (-gamma c P): V enters exactly (bf16 input); only the
+                // prediction term is rounded to bf16 for the MFMA.
 #pragma unroll
                 for (int jl = 0; jl < JW; ++jl) {
                     const int vrow = D + (wave * JW + jl) * 16 + r16;
-                    const int tok = tg + rt * 16 + 4 * g;
-                    float vv[4];
-                    if constexpr (sizeof(T) == 2) {
-                        const u32x2 u = *(const u32x2*)(lds + X::addr(vrow, tok));
-                        vv[0] = __builtin_bit_cast(float, u[0] << 16);
-                        vv[1] = __builtin_bit_cast(float, u[0] & 0xFFFF0000u);
-                        vv[2] = __builtin_bit_cast(float, u[1] << 16);
-                        vv[3] = __builtin_bit_cast(float, u[1] & 0xFFFF0000u);
-                    } else {
-                        const f32x4 u = *(const f32x4*)(lds + X::addr(vrow, tok));
-                        vv[0] = u[0]; vv[1] = u[1]; vv[2] = u[2]; vv[3] = u[3];
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) R[rt][jl][q] = DELTA ? vv[q] - gc * pr[jl][q] : vv[q];
-                }
-            }
-            // U += K^T R over this token group
-            if constexpr (sizeof(T) == 2) {
-                bf16x8 br[JW];
-#pragma unroll
-                for (int jl = 0; jl < JW; ++jl)
-                    br[jl] = __builtin_bit_cast(
-                        bf16x8, u32x4{pack_bf16x2(R[0][jl][0], R[0][jl][1]),
-                                      pack_bf16x2(R[0][jl][2], R[0][jl][3]),
-                                      pack_bf16x2(R[1][jl][0], R[1][jl][1]),
-                                      pack_bf16x2(R[1][jl][2], R[1][jl][3])});
-#pragma unroll
-                for (int it = 0; it < TJ; ++it) {
-                    const int krow = it * 16 + r16;
-                    const u32x2 lo = *(const u32x2*)(lds + X::addr(krow, tg + 4 * g));
-                    const u32x2 hi = *(const u32x2*)(lds + X::addr(krow, tg + 16 + 4 * g));
-                    const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-                    for (int jl = 0; jl < JW; ++jl) acc[it][jl] = MM::run(ak, br[jl], acc[it][jl]);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
+                    const u32x2 vlo = *(const u32x2*)(lds + X::addr(vrow, tg + 4 * g));
+                    const u32x2 vhi = *(const u32x2*)(lds + X::addr(vrow, tg + 16 + 4 * g));
+                    const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{vlo[0], vlo[1], vhi[0], vhi[1]});
+                    bf16x8 bp;
+                    if (DELTA)
+                        bp = __builtin_bit_cast(
+                            bf16x8, u32x4{pack_bf16x2(-gc * pr[0][jl][0], -gc * pr[0][jl][1]),
+                                          pack_bf16x2(-gc * pr[0][jl][2], -gc * pr[0][jl][3]),
+                                          pack_bf16x2(-gc * pr[1][jl][0], -gc * pr[1][jl][1]),
+                                          pack_bf16x2(-gc * pr[1][jl][2], -gc * pr[1][jl][3])});
 #pragma unroll
                     for (int it = 0; it < TJ; ++it) {
-                        const float ak = *(const float*)(lds + X::addr(it * 16 + r16, tg + 4 * g + q));
-#pragma unroll
-                        for (int jl = 0; jl < JW; ++jl)
-                            acc[it][jl] = Mma<float>::run(ak, R[0][jl][q], acc[it][jl]);
+                        const int krow = it * 16 + r16;
+                        const u32x2 lo = *(const u32x2*)(lds + X::addr(krow, tg + 4 * g));
+                        const u32x2 hi = *(const u32x2*)(lds + X::addr(krow, tg + 16 + 4 * g));
+                        const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                        acc[it][jl] = MM::run(ak, bv, acc[it][jl]);
+                        if (DELTA) acc[it][jl] = MM::run(ak, bp, acc[it][jl]);
                     }
+                }
+            } else {
+                // fp32 data: the residual R = V - gamma c P is formed and contracted in fp32
+#pragma unroll
+                for (int jl = 0; jl < JW; ++jl) {
+                    const int vrow = D + (wave * JW + jl) * 16 + r16;
+                    const f32x4 vv = *(const f32x4*)(lds + X::addr(vrow, tg + 4 * g));
+                    float R[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) R[q] = DELTA ? vv[q] - gc * pr[0][jl][q] : vv[q];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int it = 0; it < TJ; ++it) {
+                            const float ak = *(const float*)(lds + X::addr(it * 16 + r16, tg + 4 * g + q));
+                            acc[it][jl] = Mma<float>::run(ak, R[q], acc[it][jl]);
+                        }
+                }
             }
         }
     }

@@ -93,7 +93,12 @@ def forward(q, k, v, gamma, beta, state_in=None, *, use_delta=True, key_scale=No
     """All frames. q, k, v: [B, H, F*S, D]; gamma, beta: [B, H, F]; state_in: [B, H, D, D].
 
     Returns (o [B, H, F*S, D], state_out [B, H, D, D]) as fp64 arrays.
+    lib="numpy" runs the frame-streaming numpy variant (oracle/stream.py) instead of the C code.
     """
+    if isinstance(lib, str) and lib == "numpy":
+        from . import stream
+        return stream.forward(q, k, v, gamma, beta, state_in, use_delta=use_delta,
+                              key_scale=key_scale)
     q, k, v, gamma, beta = map(_f64, (q, k, v, gamma, beta))
     B, H, T, D = q.shape
     F = gamma.shape[2]
@@ -118,6 +123,12 @@ def step(q, k, v, gamma, beta, state_in, *, commit=True, use_delta=True, key_sca
 
     Returns (o, state_out); state_out is None when commit is False.
     """
+    if isinstance(lib, str) and lib == "numpy":
+        from . import stream
+        o, so = stream.forward(q, k, v, np.asarray(gamma)[..., None], np.asarray(beta)[..., None],
+                               np.asarray(state_in, np.float64), use_delta=use_delta,
+                               key_scale=key_scale)
+        return o, (so if commit else None)
     q, k, v, gamma, beta, st = map(_f64, (q, k, v, gamma, beta, state_in))
     B, H, S, D = q.shape
     o = np.empty_like(q)

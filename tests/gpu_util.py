@@ -41,3 +41,46 @@ def to_dev(x, dtype, dev, layout="head"):
 
 def to_np(t):
     return t.float().cpu().numpy()
+
+
+class HostFrames:
+    """Host-side inputs of one (b, h) slice of a workload, frame by frame, generated ahead of
+    use by a thread pool (numpy releases the GIL in the hashing and table lookups).
+
+    Calling it with f returns (q_f, k_f, v_f, gamma_f, beta_f): [S, D] fp32 values (rounded
+    through bf16 for bf16 workloads) and fp32 gates; pass_of(f) selects the pass for frame f.
+    """
+
+    def __init__(self, w, b, h, count, pass_of=None, frame_of=None, workers=8, ahead=48):
+        from concurrent.futures import ThreadPoolExecutor
+        self.w, self.b, self.h = w, b, h
+        self.pass_of = pass_of or (lambda f: 0)
+        self.frame_of = frame_of or (lambda f: f)
+        self.pool = ThreadPoolExecutor(workers)
+        self.ahead = ahead
+        self.count = count
+        self.fut = {}
+
+    def _make(self, i):
+        w, b, h = self.w, self.b, self.h
+        f, p = self.frame_of(i), self.pass_of(i)
+        out = []
+        for tid in (gdn_synth.TID_Q, gdn_synth.TID_K, gdn_synth.TID_V):
+            relu = w.relu_qk and tid != gdn_synth.TID_V
+            z = gdn_synth.normal_slice(w.seed, tid, b, h, f, w.S, w.D, p, relu)
+            if w.dtype == "bf16":
+                z = gdn_synth.bf16_bits_to_f32(gdn_synth.f32_to_bf16_bits(z))
+            out.append(z)
+        g, bt = gdn_synth.gates_cpu(w, heads=[h], frames=[f], pass_=p)
+        return out[0], out[1], out[2], float(g[b, 0, 0]), float(bt[b, 0, 0])
+
+    def __call__(self, i):
+        for j in range(i, min(self.count, i + self.ahead)):
+            if j not in self.fut:
+                self.fut[j] = self.pool.submit(self._make, j)
+        return self.fut.pop(i).result()
+
+    def close(self):
+        for fu in self.fut.values():
+            fu.cancel()
+        self.pool.shutdown(wait=True)

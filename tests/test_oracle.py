@@ -13,6 +13,30 @@ def test_pin(pin):
     pin()
 
 
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin_streaming_variant(pin):
+    # the frame-streaming numpy variant used for full-length workloads
+    pin(lib="numpy")
+
+
+def test_streaming_variant_keeps_selected_frames():
+    from oracle import stream
+    rng = np.random.default_rng(4)
+    D, S, F = 8, 6, 7
+    q, k, v = (rng.standard_normal((1, 1, F * S, D)) for _ in range(3))
+    g = rng.uniform(0.9, 1, (1, 1, F))
+    b = rng.uniform(0, 1, (1, 1, F))
+    ref, ref_s = oracle.forward(q, k, v, g, b)
+
+    def src(f):
+        sl = slice(f * S, (f + 1) * S)
+        return q[0, 0, sl], k[0, 0, sl], v[0, 0, sl], g[0, 0, f], b[0, 0, f]
+    outs, M = stream.forward_frames(src, F, D, S, keep={0, 6})
+    assert sorted(outs) == [0, 6]
+    assert np.allclose(outs[6], ref[0, 0, 6 * S:], rtol=0, atol=1e-12)
+    assert np.allclose(M, ref_s[0, 0], rtol=0, atol=1e-12)
+
+
 def test_oracle_rejects_bad_sizes():
     z = np.zeros((1, 1, 4, 2))
     g = np.ones((1, 1, 2))
