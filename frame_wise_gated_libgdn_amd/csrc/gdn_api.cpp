@@ -31,7 +31,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     int nsplit, split_tokens;   // partial-product kernel
     int nchunk, chunk_tokens;   // output kernel
-    size_t part_bytes, mt_bytes;
+    size_t canon_bytes, part_bytes, mt_bytes;
+    size_t total() const { return align256(canon_bytes) + align256(part_bytes) + mt_bytes; }
 };
 
 constexpr int kTargetGroups = 2048;  // workgroups wanted per parallel launch (256 CUs x 8)
@@ -60,8 +61,14 @@ Plan make_plan(const gdn_problem& p, int step_mode) {
     pl.chunk_tokens = (int)(((tiles16 + wc - 1) / wc) * 16);
     pl.nchunk = (int)((S + pl.chunk_tokens - 1) / pl.chunk_tokens);
 
+    // forward: per-frame record for the scan ([Ghat hi | Ghat lo | Bhat^T] or [Bhat^T]), fp32
+    // partials only when a frame is split, per-frame states; step: per-split partials, state
     const int64_t nout = (!step_mode && p.use_delta) ? 2 : 1;
-    pl.part_bytes = (size_t)(BH * F * pl.nsplit * nout * D * D * 4);
+    // per-frame record: Ghat hi/lo planes in MFMA-fragment order (D/16 x 2 x ceil(D/32) KB)
+    // plus Bhat (4 D^2 bytes)
+    const int64_t rec = (p.use_delta ? (D / 16) * 2 * ((D + 31) / 32) * 1024 : 0) + 4 * D * D;
+    pl.canon_bytes = step_mode ? 0 : (size_t)(BH * F * rec);
+    pl.part_bytes = (step_mode || pl.nsplit > 1) ? (size_t)(BH * F * pl.nsplit * nout * D * D * 4) : 0;
     pl.mt_bytes = (size_t)(BH * F * D * D * esz);
     return pl;
 }
@@ -146,7 +153,7 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
         if (ptr && !aligned(ptr, 4)) return fail(GDN_ERR_ALIGN, "gates and states must be 4-byte aligned");
 
     const Plan pl = make_plan(*p, step_mode);
-    const size_t need = align256(pl.part_bytes) + pl.mt_bytes;
+    const size_t need = pl.total();
 
     const Span sq = span_of(q, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
     const Span sk = span_of(k, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
@@ -182,8 +189,9 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     L.sb = p->qkv_stride_b; L.sh = p->qkv_stride_h; L.st = p->qkv_stride_t;
     L.ob = p->o_stride_b; L.oh = p->o_stride_h; L.ot = p->o_stride_t;
     L.gamma = gamma; L.beta = beta; L.state_in = state_in; L.state_out = state_out;
-    L.part = (float*)ws;
-    L.mt = (char*)ws + align256(pl.part_bytes);
+    L.canon = ws;
+    L.part = (float*)((char*)ws + align256(pl.canon_bytes));
+    L.mt = (char*)ws + align256(pl.canon_bytes) + align256(pl.part_bytes);
     L.nsplit = pl.nsplit; L.split_tokens = pl.split_tokens;
     L.nchunk = pl.nchunk; L.chunk_tokens = pl.chunk_tokens;
     L.stream = (hipStream_t)stream;
@@ -204,7 +212,7 @@ gdn_status gdn_workspace_size(const gdn_problem* p, int step_mode, size_t* bytes
     gdn_status s = check_sizes(p, step_mode);
     if (s != GDN_OK) return s;
     const Plan pl = make_plan(*p, step_mode);
-    *bytes_out = align256(pl.part_bytes) + pl.mt_bytes;
+    *bytes_out = pl.total();
     return GDN_OK;
 }
 

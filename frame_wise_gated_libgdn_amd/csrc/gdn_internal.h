@@ -18,7 +18,8 @@ struct Launch {
     int64_t ob, oh, ot;  // O strides
     const float *gamma, *beta, *state_in;
     float* state_out;
-    float* part;         // workspace: per-split fp32 partial products
+    void* canon;         // workspace: per-frame record handed from the products kernel to the scan
+    float* part;         // workspace: per-split fp32 partial products (when nsplit > 1)
     void* mt;            // workspace: materialised per-frame states, transposed, in the I/O type
     int nsplit;          // S splits of the partial-product kernel
     int split_tokens;    // tokens per split (multiple of 64)

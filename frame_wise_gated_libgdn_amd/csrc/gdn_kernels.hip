@@ -8,7 +8,8 @@
 //   1. gram_kernel   -- fully parallel over (b, h, f[, S split]). Stages K_f, V_f through LDS,
 //                       contracts over the frame's tokens on MFMA:
 //                         Ghat_f = gamma_f beta_f c^2 K_f^T K_f,  Bhat_f = beta_f c K_f^T V_f
-//                       (gates and key scale applied in the epilogue).
+//                       (gates and key scale applied in the epilogue); combine_kernel sums
+//                       S-split partials when a frame was split.
 //   2. scan_kernel   -- the serial part: M_f = gamma_f M - Ghat_f M + Bhat_f. This is the update
 //                       above with the residual expanded (Kt^T (V - g Kt M) = Kt^T V - g Kt^T Kt M),
 //                       so the frame-to-frame chain only touches D x D matrices; one workgroup
@@ -161,10 +162,52 @@ template <typename T, int D> struct XStage {
     }
 };
 
+// Per-frame record handed from the products kernel to the scan, in fragment-major order so
+// that every scan load instruction reads 1 KB of contiguous memory (64 lanes x 16 B):
+//   Ghat planes (delta only): for wave w (state rows 16w..16w+15), plane p (hi, lo), k step ks,
+//     lane l = 16 g + r: 8 bf16 = Ghat[16 w + r][32 ks + 8 g .. + 8]  (k past D never read)
+//   Bhat: for column block cb, wave w, lane l = 16 g + r: 4 fp32 = Bhat[16 w + 4 g + q][16 cb + r]
+template <int D> __host__ __device__ constexpr int rec_ksn() { return (D + 31) / 32; }
+template <int D, bool DELTA> __host__ __device__ constexpr int rec_g_bytes() {
+    return DELTA ? (D / 16) * 2 * rec_ksn<D>() * 1024 : 0;
+}
+template <int D, bool DELTA> __host__ __device__ constexpr int canon_bytes() {
+    return rec_g_bytes<D, DELTA>() + 4 * D * D;
+}
+// bf16 element offset of Ghat[m][k] in plane p
+template <int D> __device__ __forceinline__ int rec_g_off(int p, int m, int k) {
+    const int frag = ((m >> 4) * 2 + p) * rec_ksn<D>() + (k >> 5);
+    const int lane = ((k & 31) >> 3) * 16 + (m & 15);
+    return (frag * 64 + lane) * 8 + (k & 7);
+}
+// fp32 element offset of Bhat[i][j] within the Bhat part
+template <int D> __device__ __forceinline__ int rec_b_off(int i, int j) {
+    const int frag = (j >> 4) * (D / 16) + (i >> 4);
+    const int lane = ((i & 15) >> 2) * 16 + (j & 15);
+    return (frag * 64 + lane) * 4 + (i & 3);
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): 4 values to two bf16 planes (8 B each).
+__device__ __forceinline__ void store_split4(bf16* hi, bf16* lo, f32x4 x) {
+    uint32_t h[2], l[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const float a = x[2 * c], b = x[2 * c + 1];
+        h[c] = pack_bf16x2(a, b);
+        const float ah = __builtin_bit_cast(float, h[c] << 16);
+        const float bh = __builtin_bit_cast(float, h[c] & 0xFFFF0000u);
+        l[c] = pack_bf16x2(a - ah, b - bh);
+    }
+    *(u32x2*)hi = u32x2{h[0], h[1]};
+    *(u32x2*)lo = u32x2{l[0], l[1]};
+}
+
 // ----------------------------------------------------------------------------------------
-// Kernel 1: per (b, h, f, split) partial products over the split's tokens
-//   delta:    part = [ gamma beta c^2 K^T K | beta c K^T V ]   (two D x D fp32 blocks)
-//   no delta: part = [ beta c K^T V ]
+// Kernel 1: per (b, h, f, split) products over the split's tokens
+//   delta:    Ghat = gamma beta c^2 K^T K and Bhat = beta c K^T V
+//   no delta: Bhat = beta c K^T V
+// With one split the kernel writes the scan's per-frame record directly; otherwise fp32
+// partials that combine_kernel sums.
 template <typename T, int D, bool DELTA>
 __global__ __launch_bounds__(NT, 2) void gram_kernel(Launch L) {
     using MM = Mma<T>;
@@ -228,150 +271,190 @@ __global__ __launch_bounds__(NT, 2) void gram_kernel(Launch L) {
     const int gi = bh * L.F + f;
     const float gm = L.gamma[gi], bt = L.beta[gi];
     const float sG = gm * bt * L.c * L.c, sB = bt * L.c;
-    float* out = L.part + ((int64_t)gi * L.nsplit + p) * (int64_t)(NOUT * D);
+    // Lane (r16, g) holds out[i0 + q][col], q = 0..3. It is stored transposed, [col][i0 .. i0+3]
+    // (16 contiguous bytes): for Bhat this is Bhat^T; Ghat is symmetric, so its transposed
+    // store is Ghat itself.
+    if (L.nsplit == 1) {
+        // final per-frame record: [Ghat hi bf16 | Ghat lo bf16 | Bhat^T fp32] (no delta: [Bhat^T])
+        char* rec = (char*)L.canon + (int64_t)gi * canon_bytes<D, DELTA>();
+        bf16* grec = (bf16*)rec;
+        float* brec = (float*)(rec + rec_g_bytes<D, DELTA>());
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-        const int i0 = (wi * MI + mi) * 16 + 4 * g;
+        for (int mi = 0; mi < MI; ++mi) {
+            const int i0 = (wi * MI + mi) * 16 + 4 * g;
 #pragma unroll
-        for (int mj = 0; mj < MJ; ++mj) {
-            const int col = (wj * MJ + mj) * 16 + r16;
-            const bool isG = DELTA && col < D;
-            const float s = isG ? sG : sB;
-            float* dst = out + (isG ? 0 : (DELTA ? D * D : 0)) + (isG ? col : col - (DELTA ? D : 0));
+            for (int mj = 0; mj < MJ; ++mj) {
+                const int col = (wj * MJ + mj) * 16 + r16;
+                const f32x4 a = acc[mi][mj];
+                if (DELTA && col < D) {
+                    // Ghat[col][i0 .. i0+3] (symmetric), 4 consecutive k of one fragment
+                    store_split4(grec + rec_g_off<D>(0, col, i0), grec + rec_g_off<D>(1, col, i0), a * sG);
+                } else {
+                    *(f32x4*)(brec + rec_b_off<D>(i0, col - (DELTA ? D : 0))) = a * sB;
+                }
+            }
+        }
+    } else {
+        // fp32 partial of split p: [Ghat | Bhat^T] (no delta: [Bhat^T]), summed by combine_kernel
+        float* out = L.part + ((int64_t)gi * L.nsplit + p) * (int64_t)(NOUT * D);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dst[(i0 + q) * D] = acc[mi][mj][q] * s;
+        for (int mi = 0; mi < MI; ++mi) {
+            const int i0 = (wi * MI + mi) * 16 + 4 * g;
+#pragma unroll
+            for (int mj = 0; mj < MJ; ++mj) {
+                const int col = (wj * MJ + mj) * 16 + r16;
+                const float sc = DELTA && col < D ? sG : sB;
+                *(f32x4*)(out + col * D + i0) = acc[mi][mj] * sc;
+            }
         }
     }
 }
 
+// Sum of the S-split partials of each (b, h, f) into the final per-frame record (only when the
+// products kernel ran with more than one split). Fixed order over the splits.
+template <int D, bool DELTA>
+__global__ __launch_bounds__(NT) void combine_kernel(Launch L) {
+    constexpr int NOUT = DELTA ? 2 * D : D;
+    constexpr int NV = NOUT * D / 4;             // float4 per frame
+    constexpr int NB = (NV + NT - 1) / NT;
+    const int gi = blockIdx.x / NB;
+    const int v = (blockIdx.x % NB) * NT + threadIdx.x;
+    if (v >= NV) return;
+    const float* src = L.part + (int64_t)gi * L.nsplit * NOUT * D + 4 * v;
+    f32x4 s = *(const f32x4*)src;
+    for (int p = 1; p < L.nsplit; ++p) s += *(const f32x4*)(src + (int64_t)p * NOUT * D);
+    char* rec = (char*)L.canon + (int64_t)gi * canon_bytes<D, DELTA>();
+    const int e = 4 * v;                          // element index in [Ghat | Bhat^T], row-major [col][i]
+    if (DELTA && e < D * D) {
+        const int m = e / D, k = e % D;          // Ghat[m][k .. k+3]
+        bf16* grec = (bf16*)rec;
+        store_split4(grec + rec_g_off<D>(0, m, k), grec + rec_g_off<D>(1, m, k), s);
+    } else {
+        const int eb = e - (DELTA ? D * D : 0);
+        const int j = eb / D, i = eb % D;        // Bhat[i .. i+3][j]
+        *(f32x4*)((float*)(rec + rec_g_bytes<D, DELTA>()) + rec_b_off<D>(i, j)) = s;
+    }
+}
+
 // ----------------------------------------------------------------------------------------
-// Kernel 2: the frame-serial scan. One workgroup per (b, h, 16 value columns).
-// Workgroup w lands on XCD w % 8 (round-robin dispatch); all column blocks of one head are
-// given ids with the same residue so that they share one XCD's L2 for Ghat_f.
-template <typename T, int D, bool DELTA>
-__global__ __launch_bounds__(NT) void scan_kernel(Launch L) {
+// Kernel 2: the frame-serial scan M_f = gamma_f M - Ghat_f M + Bhat_f, for 16 value columns of
+// one head per workgroup (columns of M evolve independently, so no workgroup waits on
+// another). One wave per 16 state rows. Ghat M runs on bf16 MFMA with both operands split
+// into hi + lo bf16 (hi.hi + hi.lo + lo.hi; the dropped lo.lo term is ~2^-16 of the product);
+// M stays fp32 in registers (C layout) and its hi/lo planes are kept transposed in LDS as the
+// B operand. Each wave's operands of the next P frames (its Ghat rows, its Bhat entries, gamma)
+// sit in a register ring, loaded P frames ahead of use.
+// Workgroup w lands on XCD w % 8 (round-robin dispatch); all column blocks of one head get ids
+// with the same residue so that they share one XCD's L2 for Ghat_f.
+template <int D, bool DELTA> struct ScanSlot {
+    static constexpr int KSN = (D + 31) / 32;
+    bf16x8 a[DELTA ? 2 : 1][DELTA ? KSN : 1];  // Ghat rows of this wave: [hi/lo][k step]
+    f32x4 bh;                                   // Bhat[16 w + 4 g + q][col]
+};
+constexpr int kGammaSeg = 4000;  // frames per gamma staging (a multiple of the scan ring size)
+
+template <typename T, int D, bool DELTA, int P>
+__global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
     constexpr int NC = 16;              // value columns per workgroup
     constexpr int NCB = D / NC;         // column blocks per head
-    constexpr int TI = D / 16;
-    constexpr int NW = TI < 4 ? TI : 4; // waves that hold state rows
-    constexpr int IT = TI / NW;         // 16-row tiles per wave
-    constexpr int GP = D + 4;           // padded Ghat row (floats)
-    constexpr int GV = (D * D / 4 + NT - 1) / NT;  // float4 of Ghat per thread
-    constexpr int NOUT = DELTA ? 2 * D : D;
-    __shared__ __attribute__((aligned(16))) float Gs[DELTA ? D * GP : 4];
-    __shared__ __attribute__((aligned(16))) float Ms[2][D * NC];
+    constexpr int KSN = (D + 31) / 32;  // bf16 k steps (padded past D with zeros)
+    constexpr int MR = D + 8;           // row length (bf16) of the transposed state planes
+    constexpr int REC = canon_bytes<D, DELTA>();
+    __shared__ __attribute__((aligned(16))) bf16 Ms[2][2][NC * MR];  // [buffer][hi, lo][col][k]
+    // gamma_f of the current chunk of frames. Gammas come through LDS rather than scalar loads:
+    // a scalar load in the frame loop would share the LDS wait counter and expose a full memory
+    // round trip in every frame.
+    __shared__ float Gam[kGammaSeg];
 
     const int w = blockIdx.x, xcd = w & 7, slot = w >> 3;
     const int bh = (slot / NCB) * 8 + xcd, cb = slot % NCB;
     if (bh >= L.B * L.H) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    const bool active = wave < NW;
     const int col = cb * NC + r16;
-    const int64_t pstride = (int64_t)NOUT * D;  // floats per partial
-    const float* part_bh = L.part + (int64_t)bh * L.F * L.nsplit * pstride;
-    T* mt_bh = (T*)L.mt + (int64_t)bh * L.F * D * D;
+    const int row0 = wave * 16 + 4 * g;  // this lane's 4 state rows
+    const int F = L.F;
+    const char* rec_bh = (const char*)L.canon + (int64_t)bh * F * REC;
+    T* mt_bh = (T*)L.mt + (int64_t)bh * F * D * D;
 
-    float Mc[IT][4];
+    float Mc[4];
 #pragma unroll
-    for (int it = 0; it < IT; ++it)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = ((active ? wave : 0) * IT + it) * 16 + 4 * g + q;
-            Mc[it][q] = L.state_in ? L.state_in[((int64_t)bh * D + row) * D + col] : 0.f;
-            if (active) Ms[0][row * NC + r16] = Mc[it][q];
-        }
+    for (int q = 0; q < 4; ++q)
+        Mc[q] = L.state_in ? L.state_in[((int64_t)bh * D + row0 + q) * D + col] : 0.f;
+    store_split4(&Ms[0][0][r16 * MR + row0], &Ms[0][1][r16 * MR + row0], f32x4{Mc[0], Mc[1], Mc[2], Mc[3]});
 
-    // Next frame's Ghat (whole D x D, float4 per thread) and Bhat (this wave's C-layout
-    // entries), summed over the S splits. The split loop is outermost so that all loads of one
-    // split are independent and in flight together.
-    f32x4 gpre[GV];
-    float bpre[IT][4];
-    auto load_next = [&](int f) {
-        const float* src = part_bh + (int64_t)f * L.nsplit * pstride;
-        for (int p = 0; p < L.nsplit; ++p) {
-            const float* sp = src + p * pstride;
-            if (DELTA) {
+    // The ring has P + 1 slots: right after a frame's barrier the slot freed by the previous
+    // frame is refilled with frame f + P, so the loads stream while this frame's MFMAs run.
+    // The frame loop body is branch-free so that the compiler keeps the ring's loads in flight
+    // across iterations: loads past the last frame re-read frame F-1, and a frame past the end
+    // leaves M unchanged and rewrites M_{F-1} into its own slot.
+    constexpr int R = P + 1;
+    ScanSlot<D, DELTA> ring[R];
+    auto issue = [&](ScanSlot<D, DELTA>& r, int f) {
+        f = min(f, F - 1);
+        const char* rec = rec_bh + (int64_t)f * REC;
+        if constexpr (DELTA) {
 #pragma unroll
-                for (int v = 0; v < GV; ++v) {
-                    const int i4 = tid + v * NT;
-                    const f32x4 x = i4 * 4 < D * D ? *(const f32x4*)(sp + 4 * i4) : f32x4{0.f, 0.f, 0.f, 0.f};
-                    gpre[v] = p == 0 ? x : gpre[v] + x;
-                }
-            }
-            if (active) {
-                const float* bp = sp + (DELTA ? D * D : 0);
-#pragma unroll
-                for (int it = 0; it < IT; ++it)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float x = bp[((wave * IT + it) * 16 + 4 * g + q) * D + col];
-                        bpre[it][q] = p == 0 ? x : bpre[it][q] + x;
-                    }
+            for (int ks = 0; ks < KSN; ++ks) {
+                const bool in = ks * 32 + g * 8 < D;
+                const char* fr = rec + ((wave * 2) * KSN + ks) * 1024 + lane * 16;
+                r.a[0][ks] = in ? ld_frag<bf16>((const bf16*)fr) : zero_frag<bf16>();
+                r.a[1][ks] = in ? ld_frag<bf16>((const bf16*)(fr + KSN * 1024)) : zero_frag<bf16>();
             }
         }
+        r.bh = *(const f32x4*)(rec + rec_g_bytes<D, DELTA>() + ((cb * (D / 16) + wave) * 64 + lane) * 16);
     };
-    load_next(0);
+#pragma unroll
+    for (int u = 0; u < P; ++u) issue(ring[u], u);
 
+    static_assert(kGammaSeg % R == 0, "segments must hold whole ring cycles");
+    const float* gam_bh = L.gamma + (int64_t)bh * F;
     int cur = 0;
-    for (int f = 0; f < L.F; ++f) {
-        if (DELTA) {
+    for (int sb = 0; sb < F; sb += kGammaSeg) {
+        __syncthreads();  // the previous segment's gammas are no longer read
+        for (int t = threadIdx.x; t < kGammaSeg; t += blockDim.x) Gam[t] = gam_bh[min(sb + t, F - 1)];
+      for (int f0 = sb; f0 < sb + kGammaSeg && f0 < F; f0 += R) {
 #pragma unroll
-            for (int v = 0; v < GV; ++v) {
-                const int i4 = tid + v * NT;
-                if (i4 * 4 < D * D) {
-                    const int row = (4 * i4) / D, c4 = (4 * i4) % D;
-                    *(f32x4*)&Gs[row * GP + c4] = gpre[v];
-                }
-            }
-        }
-        float Bc[IT][4];
+        for (int u = 0; u < R; ++u) {
+            const int f = f0 + u;
+            const bool valid = f < F;  // uniform
+            {
+                __syncthreads();  // planes of M_{f-1} complete; readers of the other buffer done
+                issue(ring[(u + P) % R], f + P);  // the slot of frame f - 1
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (DELTA) {
+                    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int it = 0; it < IT; ++it)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) Bc[it][q] = bpre[it][q];
-        __syncthreads();
-        if (f + 1 < L.F) load_next(f + 1);
-        if (active) {
-            f32x4 acc[IT];
-#pragma unroll
-            for (int it = 0; it < IT; ++it) acc[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (DELTA) {
-#pragma unroll 8
-                for (int ks = 0; ks < D / 4; ++ks) {
-                    const float bm = Ms[cur][(4 * ks + g) * NC + r16];
-#pragma unroll
-                    for (int it = 0; it < IT; ++it) {
-                        const float ag = Gs[((wave * IT + it) * 16 + r16) * GP + 4 * ks + g];
-                        acc[it] = Mma<float>::run(ag, bm, acc[it]);
+                    for (int ks = 0; ks < KSN; ++ks) {
+                        const int k = ks * 32 + g * 8;
+                        const bf16x8 mh = k < D ? ld_frag<bf16>(&Ms[cur][0][r16 * MR + k]) : zero_frag<bf16>();
+                        const bf16x8 ml = k < D ? ld_frag<bf16>(&Ms[cur][1][r16 * MR + k]) : zero_frag<bf16>();
+                        acc = Mma<bf16>::run(ring[u].a[0][ks], mh, acc);
+                        a1 = Mma<bf16>::run(ring[u].a[0][ks], ml, a1);
+                        a2 = Mma<bf16>::run(ring[u].a[1][ks], mh, a2);
                     }
+                    acc += a1 + a2;
                 }
-            }
-            const float gm = L.gamma[bh * L.F + f];
-            T* mt = mt_bh + ((int64_t)f * D + col) * D;
-#pragma unroll
-            for (int it = 0; it < IT; ++it) {
-                const int row0 = (wave * IT + it) * 16 + 4 * g;
+                const float gm = Gam[f - sb];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    Mc[it][q] = gm * Mc[it][q] - acc[it][q] + Bc[it][q];
-                    Ms[cur ^ 1][(row0 + q) * NC + r16] = Mc[it][q];
+                    const float mn = gm * Mc[q] - acc[q] + ring[u].bh[q];
+                    Mc[q] = valid ? mn : Mc[q];
                 }
-                store4(mt + row0, Mc[it][0], Mc[it][1], Mc[it][2], Mc[it][3]);
+                const f32x4 mv = {Mc[0], Mc[1], Mc[2], Mc[3]};
+                if constexpr (DELTA)
+                    store_split4(&Ms[cur ^ 1][0][r16 * MR + row0], &Ms[cur ^ 1][1][r16 * MR + row0], mv);
+                const int fs = min(f, F - 1);
+                store4(mt_bh + ((int64_t)fs * D + col) * D + row0, Mc[0], Mc[1], Mc[2], Mc[3]);
+                cur ^= 1;
             }
         }
-        cur ^= 1;
-        __syncthreads();
+      }
     }
 
-    if (active && L.state_out) {
+    if (L.state_out) {
 #pragma unroll
-        for (int it = 0; it < IT; ++it)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = (wave * IT + it) * 16 + 4 * g + q;
-                L.state_out[((int64_t)bh * D + row) * D + col] = Mc[it][q];
-            }
+        for (int q = 0; q < 4; ++q) L.state_out[((int64_t)bh * D + row0 + q) * D + col] = Mc[q];
     }
 }
 
@@ -629,6 +712,8 @@ __global__ __launch_bounds__(NT) void step_reduce_kernel(Launch L) {
 }
 
 // ----------------------------------------------------------------------------------------
+constexpr int kScanAhead = 4;  // frames of scan operands kept in flight
+
 // Optional stage events (tracing): event i is recorded after kernel i (event 0 before the first).
 static inline void mark(const Launch& L, int i) {
     if (i < L.nev && L.ev[i]) (void)hipEventRecord(L.ev[i], L.stream);
@@ -639,9 +724,14 @@ template <typename T, int D, bool DELTA> static hipError_t fwd(const Launch& L) 
     mark(L, 0);
     hipLaunchKernelGGL((gram_kernel<T, D, DELTA>), dim3(BH * L.F * L.nsplit), dim3(NT), 0,
                        L.stream, L);
+    if (L.nsplit > 1) {
+        constexpr int NB = ((DELTA ? 2 * D : D) * D / 4 + NT - 1) / NT;
+        hipLaunchKernelGGL((combine_kernel<D, DELTA>), dim3(BH * L.F * NB), dim3(NT), 0, L.stream, L);
+    }
     mark(L, 1);
     const int units = (BH + 7) / 8 * 8 * (D / 16);
-    hipLaunchKernelGGL((scan_kernel<T, D, DELTA>), dim3(units), dim3(NT), 0, L.stream, L);
+    hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead>), dim3(units), dim3(64 * (D / 16)), 0,
+                       L.stream, L);
     mark(L, 2);
     hipLaunchKernelGGL((output_kernel<T, D>), dim3(BH * L.F * L.nchunk), dim3(NT), 0, L.stream, L);
     mark(L, 3);
