@@ -1,15 +1,17 @@
 #!/usr/bin/env python3
 """Throughput of the frame-wise GDN forward on one MI355X, with its roofline and a CPU baseline.
 
-One step = one gdn_forward_framewise call over the whole workload (all frames, all heads):
-the partial-product kernel, the frame scan and the output kernel. Inputs are synthetic,
-seeded and generated on the device before timing (resident in HBM).
+One step = one gdn_forward_framewise call over the whole workload (all frames, all heads) with
+the library's schedule for it (fused single pass at this size; --schedule staged times the
+three-pass order: products, frame scan, outputs). Inputs are synthetic, seeded and generated on
+the device before timing (resident in HBM).
 
 Prints one JSON line. Extra objects:
-  roofline      the dominant kernel's algorithmic HBM bytes per launch / its mean duration,
-                timed with HIP events recorded on the launch stream inside the library
-                (gdn_set_stage_events); `traffic` comes from the committed rocprofv3 counter
-                summary when it was taken on the current kernel source, else null.
+  roofline      the dominant kernel's algorithmic HBM bytes per launch / its mean launch
+                duration, timed with HIP events that the library records around each launch on
+                the stream the launch runs on (gdn_set_trace); `traffic` comes from the committed
+                rocprofv3 counter summary when it was taken on the current kernel source and
+                launch plan, else null.
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
   stream        streaming step mode (gdn_step_frame): 4 denoising passes per frame, state
                 committed after the last; per-frame latency and frames/s.
@@ -29,7 +31,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
-KERNELS = ["gram_kernel", "scan_kernel", "output_kernel"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gdn_720p_60s_bf16.json")
 KERNEL_SRC = os.path.join(ROOT, "frame_wise_gated_libgdn_amd", "csrc", "gdn_kernels.hip")
 
@@ -83,6 +84,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--stream-frames", type=int, default=240)
+    ap.add_argument("--schedule", default="auto", choices=["auto", "staged", "fused"],
+                    help="forward schedule (auto: the library's choice)")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="only run a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -93,14 +96,16 @@ def source_sha():
         return hashlib.sha256(fh.read()).hexdigest()
 
 
-def traffic_for(kernel, workload):
-    """Counter-derived HBM bytes per launch (GB), if measured on the current kernel source."""
+def traffic_for(kernel, workload, plan):
+    """Counter-derived HBM bytes per launch (GB), if measured on the current kernel source with
+    the same launch plan."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != source_sha() or t.get("workload") != workload:
+    if t.get("source_sha256") != source_sha() or t.get("workload") != workload \
+            or t.get("plan") != plan:
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else round(k["hbm_gb_per_launch"], 3)
@@ -216,46 +221,67 @@ def main():
     o = torch.empty_like(q)
     st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
     p = gdn.Problem(w.B, w.H, w.D, w.S, w.F, gdn.GDN_BF16 if w.dtype == "bf16" else gdn.GDN_F32,
-                    int(w.use_delta), 0.0, *q.stride()[:3], *o.stride()[:3])
+                    int(w.use_delta), 0.0, *q.stride()[:3], *o.stride()[:3],
+                    gdn.SCHEDULES[args.schedule])
     ws = torch.empty(gdn.workspace_size(p, False), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
     def call():
         gdn.forward_framewise(q, k, v, g, b, use_delta=w.use_delta, out=o, state_out=st,
-                              workspace=ws, stream=stream)
+                              workspace=ws, stream=stream, schedule=args.schedule)
 
+    ev = HipEvents()
+    # one traced warm-up call gives the launch plan (kernel, stream, units of each launch)
+    probe = [ev.new() for _ in range(2 * 256)]
+    gdn.set_trace(probe)
+    call()
+    plan = gdn.read_trace()
+    gdn.set_trace(None)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    log("warm-up done (%d steps)" % args.warmup)
+    log("warm-up done (%d steps); %d launches per step: %s" % (
+        args.warmup, len(plan), " ".join("%s%s:%d" % (k_[0], "'" if s_ else "", u)
+                                          for k_, s_, u in plan)))
 
-    ev = HipEvents()
-    stage = [[ev.new() for _ in range(4)] for _ in range(args.steps)]
+    nl = len(plan)
+    trace = [[ev.new() for _ in range(2 * nl)] for _ in range(args.steps)]
     t0, t1 = ev.new(), ev.new()
     torch.cuda.synchronize()
     ev.record(t0, sh)
     for i in range(args.steps):
-        gdn.set_stage_events(stage[i])
+        gdn.set_trace(trace[i])
         call()
-    gdn.set_stage_events(None)
+    gdn.set_trace(None)
     ev.record(t1, sh)
     torch.cuda.synchronize()
     total_ms = ev.ms(t0, t1)
     ms = total_ms / args.steps
-    kms = {KERNELS[j]: sum(ev.ms(stage[i][j], stage[i][j + 1]) for i in range(args.steps))
-           / args.steps for j in range(3)}
-    log("timed %d steps: %.3f ms/step; stages %s" % (args.steps, ms,
-                                                      {k_: round(x, 3) for k_, x in kms.items()}))
-
     esz = w.elem_bytes()
+    # algorithmic HBM bytes per (b, h, frame) item: a products item streams K and V (gram) or
+    # Q and O (outputs); a fused item streams all four
+    unit_bytes = {"products": 2 * w.S * w.D * esz, "fused": 4 * w.S * w.D * esz}
+    per = {}                                    # kernel -> [launches, ms, units]
+    for i in range(args.steps):
+        for j, (kname, _, units) in enumerate(plan):
+            acc = per.setdefault(kname, [0, 0.0, 0])
+            acc[0] += 1
+            acc[1] += ev.ms(trace[i][2 * j], trace[i][2 * j + 1])
+            acc[2] += units
+    kms = {k_: a[1] / args.steps for k_, a in per.items()}
+    log("timed %d steps: %.3f ms/step; summed launch ms per step %s" % (
+        args.steps, ms, {k_: round(x, 3) for k_, x in kms.items()}))
+
     tokens = w.B * w.F * w.S
     bytes_alg = 4 * w.B * w.H * w.F * w.S * w.D * esz          # Q, K, V read + O written
     flops_alg = (6 if w.use_delta else 4) * w.B * w.H * w.F * w.S * w.D * w.D
-    per_kernel_bytes = {"gram_kernel": bytes_alg // 2, "output_kernel": bytes_alg // 2,
-                        "scan_kernel": 0}
-    dom = max(("gram_kernel", "output_kernel"), key=lambda n: kms[n])
-    achieved = per_kernel_bytes[dom] / (kms[dom] * 1e-3) / 1e9
+    dom = max((k_ for k_ in per if k_ in unit_bytes), key=lambda k_: per[k_][1])
+    n_l, ms_l, units_l = per[dom]
+    launch_ms = ms_l / n_l
+    launch_bytes = units_l * unit_bytes[dom] / n_l
+    achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
+    plan_key = [[k_, s_, u] for k_, s_, u in plan]
     t_roof_ms = max(bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
     result = {
         "metric": "GDN tokens/sec at 961x3520-token 720p shape; % of HBM/MFMA roofline",
@@ -275,12 +301,16 @@ def main():
                    "use_delta": w.use_delta, "layout": "head-major [B,H,T,D]",
                    "state": "fp32", "parallelism": "single GPU"},
         "roofline": {
-            "bound": "hbm", "kernel": dom,
+            "bound": "hbm", "kernel": dom + "_kernel",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_for(dom, w.name), "traffic_unit": "GB per launch",
-            "algorithmic_gb_per_launch": round(per_kernel_bytes[dom] / 1e9, 3),
-            "kernel_ms": {k_: round(x, 4) for k_, x in kms.items()},
+            "traffic": traffic_for(dom + "_kernel", w.name, plan_key),
+            "traffic_unit": "GB per launch",
+            "algorithmic_gb_per_launch": round(launch_bytes / 1e9, 4),
+            "launch_ms": round(launch_ms, 4),
+            "launches_per_step": {k_: a[0] // args.steps for k_, a in per.items()},
+            "kernel_ms_per_step": {k_: round(x, 4) for k_, x in kms.items()},
+            "schedule": args.schedule,
             "call": {"bytes_alg_gb": round(bytes_alg / 1e9, 3),
                      "flops_alg_tf": round(flops_alg / 1e12, 4),
                      "t_roof_ms": round(t_roof_ms, 4),

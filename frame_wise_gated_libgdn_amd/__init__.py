@@ -16,7 +16,8 @@ import os
 import threading
 
 __all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "forward_framewise",
-           "step_frame", "abi_version", "set_stage_events", "GDN_F32", "GDN_BF16"]
+           "step_frame", "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES",
+           "GDN_F32", "GDN_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -25,6 +26,9 @@ GDN_F32, GDN_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_STRIDE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
           8: "GDN_ERR_HIP"}
+KERNEL_NAMES = {0: "products", 1: "combine", 2: "scan", 3: "step_partial", 4: "step_reduce",
+                5: "fused_reset", 6: "fused"}
+SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
 
 
 class GdnError(RuntimeError):
@@ -42,7 +46,13 @@ class Problem(ctypes.Structure):
                 ("use_delta", ctypes.c_int32), ("key_scale", ctypes.c_float),
                 ("qkv_stride_b", ctypes.c_int64), ("qkv_stride_h", ctypes.c_int64),
                 ("qkv_stride_t", ctypes.c_int64), ("o_stride_b", ctypes.c_int64),
-                ("o_stride_h", ctypes.c_int64), ("o_stride_t", ctypes.c_int64)]
+                ("o_stride_h", ctypes.c_int64), ("o_stride_t", ctypes.c_int64),
+                ("schedule", ctypes.c_int32)]
+
+
+class TraceEntry(ctypes.Structure):
+    """Mirror of gdn_trace_entry (include/libgdn.h)."""
+    _fields_ = [("kernel", ctypes.c_int32), ("stream", ctypes.c_int32), ("units", ctypes.c_int64)]
 
 
 _lock = threading.Lock()
@@ -77,8 +87,10 @@ def load():
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_last_error_message.restype = ctypes.c_char_p
             lib.gdn_abi_version.restype = ctypes.c_int
-            lib.gdn_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
-            lib.gdn_set_stage_events.restype = ctypes.c_int
+            lib.gdn_set_trace.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+            lib.gdn_set_trace.restype = ctypes.c_int
+            lib.gdn_trace_read.argtypes = [ctypes.POINTER(TraceEntry), ctypes.c_int]
+            lib.gdn_trace_read.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -87,14 +99,31 @@ def abi_version() -> int:
     return int(load().gdn_abi_version())
 
 
-def set_stage_events(handles):
-    """Arm (list of up to 4 hipEvent_t handles as ints) or disarm (None) the per-kernel stage
-    events of later calls on this host thread."""
+def set_trace(handles):
+    """Arm the launch trace of later calls on this host thread with hipEvent_t handles (ints,
+    an even number: a start and an end event per launch), or disarm it (None / empty)."""
+    global _trace_arr
     if not handles:
-        _check(load().gdn_set_stage_events(None, 0))
+        _trace_arr = None
+        _check(load().gdn_set_trace(None, 0))
         return
-    arr = (ctypes.c_void_p * len(handles))(*handles)
-    _check(load().gdn_set_stage_events(arr, len(handles)))
+    if len(handles) % 2:
+        raise GdnError(2, "trace events come in pairs")
+    _trace_arr = (ctypes.c_void_p * len(handles))(*handles)
+    _check(load().gdn_set_trace(_trace_arr, len(handles) // 2))
+
+
+_trace_arr = None
+
+
+def read_trace():
+    """Launches of the last call on this thread while the trace was armed:
+    list of (kernel name, stream index, units)."""
+    lib = load()
+    n = lib.gdn_trace_read(None, 0)
+    arr = (TraceEntry * max(n, 1))()
+    n = lib.gdn_trace_read(arr, n)
+    return [(KERNEL_NAMES.get(e.kernel, str(e.kernel)), e.stream, e.units) for e in arr[:n]]
 
 
 def _check(code):
@@ -121,7 +150,7 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _problem(q, o, F, use_delta, key_scale):
+def _problem(q, o, F, use_delta, key_scale, schedule=0):
     B, H, T, D = q.shape
     if T % F:
         raise GdnError(2, "token count %d is not a whole number of frames (F=%d)" % (T, F))
@@ -129,7 +158,16 @@ def _problem(q, o, F, use_delta, key_scale):
         raise GdnError(4, "the head dimension must be contiguous")
     return Problem(B, H, D, T // F, F, _dtype_code(q), int(bool(use_delta)),
                    0.0 if key_scale is None else float(key_scale),
-                   q.stride(0), q.stride(1), q.stride(2), o.stride(0), o.stride(1), o.stride(2))
+                   q.stride(0), q.stride(1), q.stride(2), o.stride(0), o.stride(1), o.stride(2),
+                   _schedule_code(schedule))
+
+
+def _schedule_code(schedule):
+    if isinstance(schedule, int):
+        return schedule
+    if schedule not in SCHEDULES:
+        raise GdnError(2, "schedule must be one of %s, got %r" % (sorted(SCHEDULES), schedule))
+    return SCHEDULES[schedule]
 
 
 def _check_f32(name, t, shape):
@@ -158,9 +196,12 @@ def _workspace(p, step_mode, workspace, device):
 
 
 def forward_framewise(q, k, v, gamma, beta, state=None, *, use_delta=True, key_scale=None,
-                      out=None, state_out=None, return_state=True, workspace=None, stream=None):
+                      out=None, state_out=None, return_state=True, workspace=None, stream=None,
+                      schedule="auto"):
     """All frames: q, k, v [B, H, F*S, D] (D contiguous, any other strides, same strides for
     all three); gamma, beta fp32 [B, H, F]; state fp32 [B, H, D, D] or None (zero).
+    schedule: "auto", "staged" (products, scan, outputs as three passes) or "fused" (one pass;
+    bf16 with D = 64 or 128).
     Returns (o, state_out); o has q's shape and dtype, state_out is None when
     return_state is False."""
     import torch
@@ -177,7 +218,7 @@ def forward_framewise(q, k, v, gamma, beta, state=None, *, use_delta=True, key_s
     _check_f32("beta", beta, (B, H, F))
     _check_f32("state", state, (B, H, D, D))
     _check_f32("state_out", state_out, (B, H, D, D))
-    p = _problem(q, out, F, use_delta, key_scale)
+    p = _problem(q, out, F, use_delta, key_scale, schedule)
     ws, nbytes = _workspace(p, False, workspace, q.device)
     _check(load().gdn_forward_framewise(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                         _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),

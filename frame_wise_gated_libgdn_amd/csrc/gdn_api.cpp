@@ -14,8 +14,6 @@
 namespace {
 
 thread_local char g_msg[512] = "";
-thread_local hipEvent_t g_ev[4] = {nullptr, nullptr, nullptr, nullptr};
-thread_local int g_nev = 0;
 
 gdn_status fail(gdn_status s, const char* fmt, ...) {
     va_list ap;
@@ -27,18 +25,35 @@ gdn_status fail(gdn_status s, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Splits chosen from the shape only, so that the workspace size is a pure function of it.
+// Schedule and splits chosen from the problem only, so that the workspace size is a pure
+// function of it.
 struct Plan {
+    bool fused;                 // forward: fused single pass (else staged)
     int nsplit, split_tokens;   // partial-product kernel
     int nchunk, chunk_tokens;   // output kernel
-    size_t canon_bytes, part_bytes, mt_bytes;
-    size_t total() const { return align256(canon_bytes) + align256(part_bytes) + mt_bytes; }
+    size_t canon_bytes, part_bytes, mt_bytes;   // staged forward and step
+    size_t ctl_bytes, chain_bytes;              // fused forward
+    size_t total() const {
+        return fused ? align256(ctl_bytes) + chain_bytes
+                     : align256(canon_bytes) + align256(part_bytes) + mt_bytes;
+    }
 };
+
+// The fused forward pays off once there are enough (b, h, f) items to fill the chip.
+constexpr int64_t kFusedMinItems = 1024;
+
+bool choose_fused(const gdn_problem& p, int step_mode) {
+    if (step_mode || !gdn::fused_supported(p.dtype == GDN_BF16, p.head_dim)) return false;
+    if (p.schedule == GDN_SCHEDULE_FUSED) return true;
+    if (p.schedule == GDN_SCHEDULE_STAGED) return false;
+    return (int64_t)p.batch * p.heads * p.frames >= kFusedMinItems;
+}
 
 constexpr int kTargetGroups = 2048;  // workgroups wanted per parallel launch (256 CUs x 8)
 
 Plan make_plan(const gdn_problem& p, int step_mode) {
-    Plan pl;
+    Plan pl{};
+    pl.fused = choose_fused(p, step_mode);
     const int64_t D = p.head_dim, S = p.tokens_per_frame;
     const int64_t BH = (int64_t)p.batch * p.heads;
     const int64_t F = step_mode ? 1 : p.frames;
@@ -70,6 +85,10 @@ Plan make_plan(const gdn_problem& p, int step_mode) {
     pl.canon_bytes = step_mode ? 0 : (size_t)(BH * F * rec);
     pl.part_bytes = (step_mode || pl.nsplit > 1) ? (size_t)(BH * F * pl.nsplit * nout * D * D * 4) : 0;
     pl.mt_bytes = (size_t)(BH * F * D * D * esz);
+    // fused: ticket counter, time-out flag and one frame flag per (b, h); two fp32 state
+    // buffers per (b, h)
+    pl.ctl_bytes = (size_t)(2 + BH) * 4;
+    pl.chain_bytes = (size_t)(2 * BH * D * D * 4);
     return pl;
 }
 
@@ -83,6 +102,11 @@ gdn_status check_sizes(const gdn_problem* p, int step_mode) {
         return fail(GDN_ERR_UNSUPPORTED, "head_dim %d not supported (16, 32, 64, 128)", D);
     if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
         return fail(GDN_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
+    if (p->schedule < GDN_SCHEDULE_AUTO || p->schedule > GDN_SCHEDULE_FUSED)
+        return fail(GDN_ERR_SHAPE, "schedule must be 0, 1 or 2, got %d", p->schedule);
+    if (!step_mode && p->schedule == GDN_SCHEDULE_FUSED &&
+        !gdn::fused_supported(p->dtype == GDN_BF16, D))
+        return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs bf16 data and D = 64 or 128");
     const int64_t F = step_mode ? 1 : p->frames;
     const int64_t BH = (int64_t)p->batch * p->heads;
     // grid sizes: BH * F * splits must fit a 1-D grid; token indices f*S+s must fit int32 math
@@ -180,7 +204,7 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
                     ws ? ws_bytes : (size_t)0);
     if (!aligned(ws, 256)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
 
-    gdn::Launch L;
+    gdn::Launch L{};
     L.B = (int)B; L.H = (int)H; L.D = (int)D; L.S = (int)S; L.F = (int)F;
     L.bf16 = p->dtype == GDN_BF16;
     L.use_delta = p->use_delta != 0;
@@ -189,15 +213,23 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     L.sb = p->qkv_stride_b; L.sh = p->qkv_stride_h; L.st = p->qkv_stride_t;
     L.ob = p->o_stride_b; L.oh = p->o_stride_h; L.ot = p->o_stride_t;
     L.gamma = gamma; L.beta = beta; L.state_in = state_in; L.state_out = state_out;
-    L.canon = ws;
-    L.part = (float*)((char*)ws + align256(pl.canon_bytes));
-    L.mt = (char*)ws + align256(pl.canon_bytes) + align256(pl.part_bytes);
+    if (pl.fused) {
+        L.ctl = (int*)ws;
+        L.chain = (float*)((char*)ws + align256(pl.ctl_bytes));
+    } else {
+        L.canon = ws;
+        L.part = (float*)((char*)ws + align256(pl.canon_bytes));
+        L.mt = (char*)ws + align256(pl.canon_bytes) + align256(pl.part_bytes);
+    }
     L.nsplit = pl.nsplit; L.split_tokens = pl.split_tokens;
     L.nchunk = pl.nchunk; L.chunk_tokens = pl.chunk_tokens;
-    L.stream = (hipStream_t)stream;
-    L.nev = g_nev;
-    for (int i = 0; i < 4; ++i) L.ev[i] = g_ev[i];
-    const hipError_t e = step_mode ? gdn::launch_step(L) : gdn::launch_forward(L);
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (step_mode) {
+        e = gdn::run_step(L, st);
+    } else {
+        e = gdn::run_forward(L, pl.fused, st);
+    }
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
 }
@@ -232,14 +264,16 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                hip_stream);
 }
 
-gdn_status gdn_set_stage_events(void* const* events, int count) {
+gdn_status gdn_set_trace(void* const* events, int pairs) {
     g_msg[0] = '\0';
-    if (count < 0 || count > 4) return fail(GDN_ERR_SHAPE, "count must be 0..4, got %d", count);
-    if (count > 0 && !events) return fail(GDN_ERR_NULL, "events is NULL");
-    if (!events) count = 0;
-    for (int i = 0; i < 4; ++i) g_ev[i] = i < count ? (hipEvent_t)events[i] : nullptr;
-    g_nev = count;
+    if (pairs < 0 || pairs > (1 << 16)) return fail(GDN_ERR_SHAPE, "pairs must be 0..65536, got %d", pairs);
+    if (pairs > 0 && !events) return fail(GDN_ERR_NULL, "events is NULL");
+    gdn::set_trace(events, events ? pairs : 0);
     return GDN_OK;
+}
+
+int gdn_trace_read(gdn_trace_entry* entries, int capacity) {
+    return gdn::read_trace(entries, capacity < 0 ? 0 : capacity);
 }
 
 const char* gdn_status_string(gdn_status s) {

@@ -1,12 +1,15 @@
-// Internal interface between the C-ABI layer (gdn_api.cpp) and the kernels (gdn_kernels.hip).
+// Internal interface between the C-ABI layer (gdn_api.cpp), the launch runtime
+// (gdn_runtime.cpp) and the kernels (gdn_kernels.hip).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/libgdn.h"
+
 namespace gdn {
 
-// Argument bundle of one launch sequence. Strides are in elements.
+// Argument bundle of the kernels. Strides are in elements; frame indices are absolute.
 struct Launch {
     int B, H, D, S, F;
     int bf16;            // 1: Q/K/V/O are bf16; 0: fp32
@@ -21,18 +24,38 @@ struct Launch {
     void* canon;         // workspace: per-frame record handed from the products kernel to the scan
     float* part;         // workspace: per-split fp32 partial products (when nsplit > 1)
     void* mt;            // workspace: materialised per-frame states, transposed, in the I/O type
-    int nsplit;          // S splits of the partial-product kernel
+    int* ctl;            // workspace (fused): [0] ticket counter, [1] wait time-out flag,
+                         //   [2 + bh] last frame of (b, h) whose state is published
+    float* chain;        // workspace (fused): published states, [2][B*H][D][D] fp32, [c][n] order
+    int nsplit;          // S splits of the gram products
     int split_tokens;    // tokens per split (multiple of 64)
-    int nchunk;          // S chunks of the output kernel
+    int nchunk;          // S chunks of the output products
     int chunk_tokens;    // tokens per output chunk (multiple of 16)
-    hipStream_t stream;
-    hipEvent_t ev[4];    // optional stage events (nev of them)
-    int nev;
+    // frame ranges of one launch
+    int g0, gn;          // gram products (and combine) over frames [g0, g0 + gn)
+    int o0, on;          // output products over frames [o0, o0 + on)
+    int s0, s1;          // scan over frames [s0, s1)
+    const float* scan_in;  // state before frame s0 (NULL: zero)
+    float* scan_out;       // state after frame s1 - 1 (NULL: not stored)
 };
 
-// Enqueue the whole forward (all frames) / one streaming step. Return the HIP error of the
-// launches (hipSuccess when all were enqueued).
-hipError_t launch_forward(const Launch& L);
-hipError_t launch_step(const Launch& L);
+// Kernels the runtime can launch (also the trace kinds of the C ABI).
+enum Kernel {
+    K_PRODUCTS = 0, K_COMBINE = 1, K_SCAN = 2, K_STEP_PARTIAL = 3, K_STEP_REDUCE = 4,
+    K_FUSED_RESET = 5, K_FUSED = 6
+};
+
+// Whether the fused single-pass forward has a kernel for this type / head size.
+bool fused_supported(int bf16, int D);
+
+// Enqueue one kernel on `s`. Returns the HIP error of the launch.
+hipError_t launch_kernel(Kernel k, const Launch& L, hipStream_t s);
+
+// gdn_runtime.cpp: the launch order of a forward (staged: products, scan, outputs; or fused)
+// and of a step, all on stream `s`.
+hipError_t run_forward(const Launch& L, bool fused, hipStream_t s);
+hipError_t run_step(const Launch& L, hipStream_t s);
+void set_trace(void* const* events, int pairs);
+int read_trace(gdn_trace_entry* out, int capacity);
 
 }  // namespace gdn

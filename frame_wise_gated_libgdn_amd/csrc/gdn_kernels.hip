@@ -4,8 +4,8 @@
 // "Архитектура: четыре нетривиальных решения"), per (b, h), c = key scale:
 //     R = V_f - gamma_f (c K_f) M,   M <- gamma_f M + beta_f (c K_f)^T R,   O_f = Q_f M.
 //
-// Forward (all frames), three kernels:
-//   1. gram_kernel   -- fully parallel over (b, h, f[, S split]). Stages K_f, V_f through LDS,
+// Forward (all frames):
+//   1. gram products -- fully parallel over (b, h, f[, S split]). Stages K_f, V_f through LDS,
 //                       contracts over the frame's tokens on MFMA:
 //                         Ghat_f = gamma_f beta_f c^2 K_f^T K_f,  Bhat_f = beta_f c K_f^T V_f
 //                       (gates and key scale applied in the epilogue); combine_kernel sums
@@ -15,16 +15,21 @@
 //                       so the frame-to-frame chain only touches D x D matrices; one workgroup
 //                       owns 16 value columns of one head (columns of M evolve independently), so
 //                       no workgroup waits on another. Writes each M_f (transposed, I/O type).
-//   3. output_kernel -- fully parallel O_f = Q_f M_f on MFMA.
+//   3. output products -- fully parallel O_f = Q_f M_f on MFMA.
+// Gram and output items share one kernel (products_kernel), so the host runtime can pipeline
+// the frames in chunks: the products of chunk c, the scan of chunk c - 1 and the outputs of
+// chunk c - 2 are in flight together.
 // Step (one frame from a cached state), the update as written:
 //   4. step_partial_kernel -- per S split: P = K M (MFMA), R = V - (gamma c) P, U_p = K^T R (MFMA).
 //   5. step_reduce_kernel  -- M' = gamma M + beta c sum_p U_p; state_out; transposed copy.
-//   then output_kernel with one frame.
+//   then the output products of the one frame.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16 for bf16 data, v_mfma_f32_16x16x4_f32 for fp32 data; fp32
 // accumulation throughout. Lane l = 16 g + r of a wave holds A row r / B column r and the
 // contraction slice [KL g, KL g + KL) of each KS-long step; C row 4 g + q, column r in
 // register q. The contraction order inside a step is free as long as A and B agree.
+#include <type_traits>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -34,6 +39,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NT = 256;  // threads per workgroup (4 waves of 64)
 
@@ -207,9 +213,9 @@ __device__ __forceinline__ void store_split4(bf16* hi, bf16* lo, f32x4 x) {
 //   delta:    Ghat = gamma beta c^2 K^T K and Bhat = beta c K^T V
 //   no delta: Bhat = beta c K^T V
 // With one split the kernel writes the scan's per-frame record directly; otherwise fp32
-// partials that combine_kernel sums.
+// partials that combine_kernel sums. Item blk covers frame g0 + (blk / nsplit) % gn.
 template <typename T, int D, bool DELTA>
-__global__ __launch_bounds__(NT, 2) void gram_kernel(Launch L) {
+__device__ __forceinline__ void gram_body(const Launch& L, int blk) {
     using MM = Mma<T>;
     using X = XTile<T, D>;
     constexpr int NOUT = DELTA ? 2 * D : D;
@@ -221,10 +227,9 @@ __global__ __launch_bounds__(NT, 2) void gram_kernel(Launch L) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    int blk = blockIdx.x;
     const int p = blk % L.nsplit;
     blk /= L.nsplit;
-    const int f = blk % L.F, bh = blk / L.F;
+    const int f = L.g0 + blk % L.gn, bh = blk / L.gn;
     const int b = bh / L.H, h = bh % L.H;
     const int64_t fo = (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * L.S * L.st;
     const T* kb = (const T*)L.k + fo;
@@ -310,14 +315,15 @@ __global__ __launch_bounds__(NT, 2) void gram_kernel(Launch L) {
     }
 }
 
-// Sum of the S-split partials of each (b, h, f) into the final per-frame record (only when the
-// products kernel ran with more than one split). Fixed order over the splits.
+// Sum of the S-split partials of each (b, h, f), f in [g0, g0 + gn), into the final per-frame
+// record (only when the products ran with more than one split). Fixed order over the splits.
 template <int D, bool DELTA>
 __global__ __launch_bounds__(NT) void combine_kernel(Launch L) {
     constexpr int NOUT = DELTA ? 2 * D : D;
     constexpr int NV = NOUT * D / 4;             // float4 per frame
     constexpr int NB = (NV + NT - 1) / NT;
-    const int gi = blockIdx.x / NB;
+    const int it = blockIdx.x / NB;
+    const int gi = (it / L.gn) * L.F + L.g0 + it % L.gn;  // (b h, frame) of item it
     const int v = (blockIdx.x % NB) * NT + threadIdx.x;
     if (v >= NV) return;
     const float* src = L.part + (int64_t)gi * L.nsplit * NOUT * D + 4 * v;
@@ -337,8 +343,8 @@ __global__ __launch_bounds__(NT) void combine_kernel(Launch L) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Kernel 2: the frame-serial scan M_f = gamma_f M - Ghat_f M + Bhat_f, for 16 value columns of
-// one head per workgroup (columns of M evolve independently, so no workgroup waits on
+// Kernel 2: the frame-serial scan M_f = gamma_f M - Ghat_f M + Bhat_f over frames [s0, s1), for
+// 16 value columns of one head per workgroup (columns of M evolve independently, so no workgroup waits on
 // another). One wave per 16 state rows. Ghat M runs on bf16 MFMA with both operands split
 // into hi + lo bf16 (hi.hi + hi.lo + lo.hi; the dropped lo.lo term is ~2^-16 of the product);
 // M stays fp32 in registers (C layout) and its hi/lo planes are kept transposed in LDS as the
@@ -373,25 +379,25 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
     const int r16 = lane & 15, g = lane >> 4;
     const int col = cb * NC + r16;
     const int row0 = wave * 16 + 4 * g;  // this lane's 4 state rows
-    const int F = L.F;
+    const int F = L.F, s0 = L.s0, s1 = L.s1;
     const char* rec_bh = (const char*)L.canon + (int64_t)bh * F * REC;
     T* mt_bh = (T*)L.mt + (int64_t)bh * F * D * D;
 
     float Mc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        Mc[q] = L.state_in ? L.state_in[((int64_t)bh * D + row0 + q) * D + col] : 0.f;
+        Mc[q] = L.scan_in ? L.scan_in[((int64_t)bh * D + row0 + q) * D + col] : 0.f;
     store_split4(&Ms[0][0][r16 * MR + row0], &Ms[0][1][r16 * MR + row0], f32x4{Mc[0], Mc[1], Mc[2], Mc[3]});
 
     // The ring has P + 1 slots: right after a frame's barrier the slot freed by the previous
     // frame is refilled with frame f + P, so the loads stream while this frame's MFMAs run.
     // The frame loop body is branch-free so that the compiler keeps the ring's loads in flight
-    // across iterations: loads past the last frame re-read frame F-1, and a frame past the end
-    // leaves M unchanged and rewrites M_{F-1} into its own slot.
+    // across iterations: loads past the last frame s1-1 re-read it, and a frame past the end
+    // leaves M unchanged and rewrites M_{s1-1} into its own slot.
     constexpr int R = P + 1;
     ScanSlot<D, DELTA> ring[R];
     auto issue = [&](ScanSlot<D, DELTA>& r, int f) {
-        f = min(f, F - 1);
+        f = min(f, s1 - 1);
         const char* rec = rec_bh + (int64_t)f * REC;
         if constexpr (DELTA) {
 #pragma unroll
@@ -405,19 +411,19 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
         r.bh = *(const f32x4*)(rec + rec_g_bytes<D, DELTA>() + ((cb * (D / 16) + wave) * 64 + lane) * 16);
     };
 #pragma unroll
-    for (int u = 0; u < P; ++u) issue(ring[u], u);
+    for (int u = 0; u < P; ++u) issue(ring[u], s0 + u);
 
     static_assert(kGammaSeg % R == 0, "segments must hold whole ring cycles");
     const float* gam_bh = L.gamma + (int64_t)bh * F;
     int cur = 0;
-    for (int sb = 0; sb < F; sb += kGammaSeg) {
+    for (int sb = s0; sb < s1; sb += kGammaSeg) {
         __syncthreads();  // the previous segment's gammas are no longer read
-        for (int t = threadIdx.x; t < kGammaSeg; t += blockDim.x) Gam[t] = gam_bh[min(sb + t, F - 1)];
-      for (int f0 = sb; f0 < sb + kGammaSeg && f0 < F; f0 += R) {
+        for (int t = threadIdx.x; t < kGammaSeg; t += blockDim.x) Gam[t] = gam_bh[min(sb + t, s1 - 1)];
+      for (int f0 = sb; f0 < sb + kGammaSeg && f0 < s1; f0 += R) {
 #pragma unroll
         for (int u = 0; u < R; ++u) {
             const int f = f0 + u;
-            const bool valid = f < F;  // uniform
+            const bool valid = f < s1;  // uniform
             {
                 __syncthreads();  // planes of M_{f-1} complete; readers of the other buffer done
                 issue(ring[(u + P) % R], f + P);  // the slot of frame f - 1
@@ -444,7 +450,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
                 const f32x4 mv = {Mc[0], Mc[1], Mc[2], Mc[3]};
                 if constexpr (DELTA)
                     store_split4(&Ms[cur ^ 1][0][r16 * MR + row0], &Ms[cur ^ 1][1][r16 * MR + row0], mv);
-                const int fs = min(f, F - 1);
+                const int fs = min(f, s1 - 1);
                 store4(mt_bh + ((int64_t)fs * D + col) * D + row0, Mc[0], Mc[1], Mc[2], Mc[3]);
                 cur ^= 1;
             }
@@ -452,9 +458,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
       }
     }
 
-    if (L.state_out) {
+    // Each lane rewrites exactly the entries it read from scan_in, so scan_out may equal it.
+    if (L.scan_out) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) L.state_out[((int64_t)bh * D + row0 + q) * D + col] = Mc[q];
+        for (int q = 0; q < 4; ++q) L.scan_out[((int64_t)bh * D + row0 + q) * D + col] = Mc[q];
     }
 }
 
@@ -471,15 +478,14 @@ template <typename T, int D> __device__ __forceinline__ int out_col(int jt, int 
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(NT, 2) void output_kernel(Launch L) {
+__device__ __forceinline__ void output_body(const Launch& L, int blk) {
     using MM = Mma<T>;
     constexpr int TJ = D / 16, KSN = (D + MM::KS - 1) / MM::KS;  // contraction padded to KS
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    int blk = blockIdx.x;
     const int ch = blk % L.nchunk;
     blk /= L.nchunk;
-    const int f = blk % L.F, bh = blk / L.F;
+    const int f = L.o0 + blk % L.on, bh = blk / L.on;
     const int b = bh / L.H, h = bh % L.H;
     const T* mt = (const T*)L.mt + ((int64_t)bh * L.F + f) * D * D;
     const T* qf = (const T*)L.q + (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * L.S * L.st;
@@ -526,6 +532,318 @@ __global__ __launch_bounds__(NT, 2) void output_kernel(Launch L) {
 #pragma unroll
                 for (int jt = 0; jt < TJ; ++jt)
                     store4(orow + 16 * jt + 4 * g, acc[jt][0], acc[jt][1], acc[jt][2], acc[jt][3]);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------------------
+// Products kernel: the gram items of frames [g0, g0 + gn) followed by the output items of
+// frames [o0, o0 + on). Both kinds of item only stream Q/K/V/O through MFMA, so one launch can
+// carry the products of one chunk of frames and the outputs of an earlier chunk whose states
+// are ready, and the frame-serial scan of the chunk in between runs beside it.
+template <typename T, int D, bool DELTA>
+__global__ __launch_bounds__(NT, 2) void products_kernel(Launch L) {
+    const int ng = L.B * L.H * L.gn * L.nsplit;
+    if ((int)blockIdx.x < ng)
+        gram_body<T, D, DELTA>(L, blockIdx.x);
+    else
+        output_body<T, D>(L, blockIdx.x - ng);
+}
+
+// ----------------------------------------------------------------------------------------
+// Fused forward (bf16 data, D = 64 or 128): one workgroup per (b, h, f) computes
+//   1. the frame's products Ghat_f, Bhat_f (as gram_body, all S tokens, K and V staged in LDS),
+//   2. the state step M_f = gamma_f M_{f-1} + Bhat_f - Ghat_f M_{f-1} on MFMA, once M_{f-1} of
+//      the same (b, h) is published, then publishes M_f,
+//   3. the frame's outputs O_f = Q_f M_f.
+// Nothing per frame goes through HBM except Q/K/V/O themselves and the D x D state handed from
+// frame to frame, so the frame-serial chain hides under the streaming of the other frames.
+//
+// Ordering and progress. Each workgroup takes a ticket from a counter; ticket t is frame
+// t / BH of (b h) = t % BH, so a workgroup only ever waits for a smaller ticket, whose
+// workgroup is already running (it took its ticket first) and waits only for smaller tickets
+// in turn: the chain always completes whatever order the hardware dispatches workgroups in.
+// The wait is bounded (kSpinLimit polls); on time-out the workgroup raises ctl[1], continues
+// with a NaN state so the failure is visible in every later output, and still publishes, so
+// the kernel always ends.
+//
+// Memory ordering: the state and the frame flags move only through device-coherent accesses
+// (the sc1 cache policy, which the compiler also uses for agent-scope atomics: coherent across
+// the chip's L2 caches on their own, so no cache write-back or invalidation is needed, which
+// would also flush the streaming outputs of every other workgroup). The publisher's waves wait
+// until their state stores have completed, meet at a barrier, and one lane then stores the
+// frame index; the consumer's lane polls the flag, and its waves issue their state loads only
+// after the barrier that follows a successful poll. States alternate between two buffers per
+// (b, h): frame f + 2 overwrites the buffer of frame f only after frame f + 1, the only reader
+// of it, has published. A state buffer is laid out in the lanes' own order ([wave][nb][cb]
+// [lane][4 fp32]: producer and consumer use the same mapping), so that every access
+// instruction covers 1 KB of contiguous memory.
+//
+// Wave w owns the key rows n in [w D/4, (w+1) D/4) of Ghat (as columns: Ghat is symmetric),
+// of Bhat and of the state step. With tile (kb, nb) of Ghat in C layout -- lane (r, g) holds
+// Ghat[16 kb + 4 g + q][n0 + 16 nb + r] -- symmetry makes it the A operand slice for rows
+// n0 + 16 nb + r and k = 16 kb + 4 g + q, so the step's A operand needs no data movement: a
+// 32-long MFMA k step ks takes tiles 2 ks and 2 ks + 1 in its lane slots 0-3 and 4-7. The B
+// operand (M_{f-1} split into bf16 hi + lo) is laid out in LDS with the same k order.
+constexpr int kSpinLimit = 1 << 20;  // polls of about a microsecond each
+constexpr int kCoherent = 16;        // cache-policy operand of the buffer intrinsics: sc1
+
+// Buffer resource over `bytes` bytes at p (raw dword access; accesses past the end read zero)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+__global__ void fused_reset_kernel(int* ctl, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) ctl[i] = i < 2 ? 0 : -1;
+}
+
+template <int D, bool DELTA>
+__global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
+    using MM = Mma<bf16>;
+    using X = XTile<bf16, D>;
+    static_assert(D == 64 || D == 128, "fused path: D = 64 or 128");
+    constexpr int NR = D / 4;       // key rows per wave
+    constexpr int NB = NR / 16;     // 16-row blocks per wave
+    constexpr int CB = D / 16;      // 16-column (value) blocks
+    constexpr int KB = D / 16;      // 16-long k blocks of Ghat
+    constexpr int MR = D + 8;       // LDS row length (bf16) of the state planes
+    constexpr int PLANE = D * MR;
+    constexpr int LDS_BYTES = X::BYTES > 4 * PLANE ? X::BYTES : 4 * PLANE;
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+    __shared__ int s_ticket, s_ok;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    if (tid == 0) s_ticket = atomicAdd(&L.ctl[0], 1);
+    __syncthreads();
+    const int BH = L.B * L.H, F = L.F, S = L.S;
+    const int f = s_ticket / BH, bh = s_ticket % BH;
+    const int b = bh / L.H, h = bh % L.H;
+    const int nw = wave * NR;       // first key row of this wave
+
+    // ---- 1. products over the frame's tokens
+    const int64_t fo = (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * S * L.st;
+    f32x4 gacc[DELTA ? KB : 1][NB], bacc[NB][CB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int kb = 0; kb < (DELTA ? KB : 1); ++kb) gacc[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) bacc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    {
+        const bf16* kp = (const bf16*)L.k + fo;
+        const bf16* vp = (const bf16*)L.v + fo;
+        XStage<bf16, D> stg;
+        stg.load(kp, vp, L.st, 0, S, tid);
+        for (int c0 = 0; c0 < S; c0 += X::SC) {
+            __syncthreads();  // readers of the previous chunk are done
+            stg.store(lds, tid);
+            __syncthreads();
+            if (c0 + X::SC < S) stg.load(kp, vp, L.st, c0 + X::SC, S, tid);
+#pragma unroll
+            for (int ks = 0; ks < X::SC / MM::KS; ++ks) {
+                const int tok = ks * MM::KS + g * MM::KL;
+                bf16x8 kn[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    kn[nb] = ld_frag<bf16>((const bf16*)(lds + X::addr(nw + 16 * nb + r16, tok)));
+                if constexpr (DELTA) {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const bf16x8 ki = ld_frag<bf16>((const bf16*)(lds + X::addr(16 * kb + r16, tok)));
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) gacc[kb][nb] = MM::run(ki, kn[nb], gacc[kb][nb]);
+                    }
+                }
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const bf16x8 vc = ld_frag<bf16>((const bf16*)(lds + X::addr(D + 16 * cb + r16, tok)));
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) bacc[nb][cb] = MM::run(kn[nb], vc, bacc[nb][cb]);
+                }
+            }
+        }
+    }
+    const int gi = bh * F + f;
+    const float gm = L.gamma[gi], bt = L.beta[gi];
+    const float sG = gm * bt * L.c * L.c, sB = bt * L.c;
+    // -Ghat as bf16 hi + lo (A operand of the step), Bhat scaled in place
+    uint32_t gh[DELTA ? KB : 1][NB][2], gl[DELTA ? KB : 1][NB][2];
+    if constexpr (DELTA) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const float x = -sG * gacc[kb][nb][2 * c2], y = -sG * gacc[kb][nb][2 * c2 + 1];
+                    const uint32_t hh = pack_bf16x2(x, y);
+                    gh[kb][nb][c2] = hh;
+                    gl[kb][nb][c2] = pack_bf16x2(x - __builtin_bit_cast(float, hh << 16),
+                                                 y - __builtin_bit_cast(float, hh & 0xFFFF0000u));
+                }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) bacc[nb][cb] *= sB;
+
+    // ---- 2. wait for M_{f-1} of this (b, h)
+    int* flag = L.ctl + 2 + bh;
+    if (tid == 0) {
+        int ok = 1;
+        if (f > 0) {
+            int polls = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < f - 1) {
+                if (++polls > kSpinLimit) {
+                    ok = 0;
+                    __hip_atomic_store(&L.ctl[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(4);
+            }
+        }
+        s_ok = ok;
+    }
+    __syncthreads();  // also: the last chunk's LDS readers are done (planes reuse that space)
+    const bool ok = s_ok != 0;
+
+    // M_{f-1}[n][c] at this lane's C-layout positions: n = nw + 16 nb + 4 g + q, c = 16 cb + r.
+    // All loads are issued before any is used (one uniform branch around the whole batch).
+    f32x4 mp[NB][CB];
+    if (f > 0) {
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_over(L.chain + ((int64_t)((f - 1) & 1) * BH + bh) * D * D, D * D * 4);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                mp[nb][cb] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rs, (((wave * NB + nb) * CB + cb) * 64 + lane) * 16, 0, kCoherent));
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    mp[nb][cb][q] = L.state_in
+                                        ? L.state_in[((int64_t)bh * D + nw + 16 * nb + 4 * g + q) * D + 16 * cb + r16]
+                                        : 0.f;
+    }
+    bf16* Ph = (bf16*)lds;
+    bf16* Pl = Ph + PLANE;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int kb = (nw + 16 * nb) >> 4;
+        const int pos = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int c = 16 * cb + r16;
+            const float nan = __builtin_nanf("");
+            const f32x4 m = ok ? mp[nb][cb] : f32x4{nan, nan, nan, nan};
+            bacc[nb][cb] += gm * m;
+            if constexpr (DELTA) store_split4(Ph + c * MR + pos, Pl + c * MR + pos, m);
+        }
+    }
+    if constexpr (DELTA) {
+        __syncthreads();
+        // three passes (hi.hi, hi.lo, lo.hi) per k step, each over all NB x CB accumulators, so
+        // that consecutive MFMAs never depend on each other
+#pragma unroll
+        for (int ks = 0; ks < KB / 2; ++ks) {
+            bf16x8 ah[NB], al[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                ah[nb] = __builtin_bit_cast(bf16x8, u32x4{gh[2 * ks][nb][0], gh[2 * ks][nb][1],
+                                                         gh[2 * ks + 1][nb][0], gh[2 * ks + 1][nb][1]});
+                al[nb] = __builtin_bit_cast(bf16x8, u32x4{gl[2 * ks][nb][0], gl[2 * ks][nb][1],
+                                                         gl[2 * ks + 1][nb][0], gl[2 * ks + 1][nb][1]});
+            }
+#pragma unroll
+            for (int pass = 0; pass < 3; ++pass) {
+                const bf16* plane = pass == 1 ? Pl : Ph;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const bf16x8 m = ld_frag<bf16>(plane + (16 * cb + r16) * MR + 32 * ks + 8 * g);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        bacc[nb][cb] = MM::run(pass == 2 ? al[nb] : ah[nb], m, bacc[nb][cb]);
+                }
+            }
+        }
+    }
+
+    // ---- publish M_f
+    {
+        const __amdgpu_buffer_rsrc_t rd =
+            buffer_over(L.chain + ((int64_t)(f & 1) * BH + bh) * D * D, D * D * 4);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bacc[nb][cb]), rd,
+                                                       (((wave * NB + nb) * CB + cb) * 64 + lane) * 16, 0,
+                                                       kCoherent);
+        if (f == F - 1 && L.state_out) {
+            float* so = L.state_out + (int64_t)bh * D * D;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) so[(nw + 16 * nb + 4 * g + q) * D + 16 * cb + r16] = bacc[nb][cb][q];
+        }
+    }
+    __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's state stores are done
+    __syncthreads();  // ... and every wave's; also: the planes are no longer read
+    if (tid == 0) __hip_atomic_store(flag, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // ---- 3. O_f = Q_f M_f (as output_body, with bf16(M_f)^T from LDS)
+    bf16* Mt = (bf16*)lds;  // [c][n]
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const f32x4 x = bacc[nb][cb];
+            store4(Mt + (16 * cb + r16) * MR + nw + 16 * nb + 4 * g, x[0], x[1], x[2], x[3]);
+        }
+    __syncthreads();
+    constexpr int TJ = D / 16, KSN = D / MM::KS;
+    bf16x8 am[TJ][KSN];
+#pragma unroll
+    for (int jt = 0; jt < TJ; ++jt)
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks)
+            am[jt][ks] = ld_frag<bf16>(Mt + out_col<bf16, D>(jt, r16) * MR + ks * MM::KS + g * MM::KL);
+    const bf16* qf = (const bf16*)L.q + fo;
+    bf16* of = (bf16*)L.o + (int64_t)b * L.ob + (int64_t)h * L.oh + (int64_t)f * S * L.ot;
+    for (int s0 = wave * 16; s0 < S; s0 += 4 * 16) {
+        const int s = s0 + r16;
+        const bool in = s < S;
+        bf16x8 bq[KSN];
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks)
+            bq[ks] = in ? ld_frag<bf16>(qf + (int64_t)s * L.st + ks * MM::KS + g * MM::KL) : zero_frag<bf16>();
+        f32x4 acc[TJ];
+#pragma unroll
+        for (int jt = 0; jt < TJ; ++jt) {
+            acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KSN; ++ks) acc[jt] = MM::run(am[jt][ks], bq[ks], acc[jt]);
+        }
+        if (in) {
+            bf16* orow = of + (int64_t)s * L.ot;
+#pragma unroll
+            for (int p = 0; p < TJ / 2; ++p) {
+                const f32x4 x = acc[2 * p], y = acc[2 * p + 1];
+                st16(orow + 32 * p + 8 * g,
+                     u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                           pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])});
             }
         }
     }
@@ -714,69 +1032,69 @@ __global__ __launch_bounds__(NT) void step_reduce_kernel(Launch L) {
 // ----------------------------------------------------------------------------------------
 constexpr int kScanAhead = 4;  // frames of scan operands kept in flight
 
-// Optional stage events (tracing): event i is recorded after kernel i (event 0 before the first).
-static inline void mark(const Launch& L, int i) {
-    if (i < L.nev && L.ev[i]) (void)hipEventRecord(L.ev[i], L.stream);
-}
-
-template <typename T, int D, bool DELTA> static hipError_t fwd(const Launch& L) {
+template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, const Launch& L,
+                                                                 hipStream_t s) {
     const int BH = L.B * L.H;
-    mark(L, 0);
-    hipLaunchKernelGGL((gram_kernel<T, D, DELTA>), dim3(BH * L.F * L.nsplit), dim3(NT), 0,
-                       L.stream, L);
-    if (L.nsplit > 1) {
-        constexpr int NB = ((DELTA ? 2 * D : D) * D / 4 + NT - 1) / NT;
-        hipLaunchKernelGGL((combine_kernel<D, DELTA>), dim3(BH * L.F * NB), dim3(NT), 0, L.stream, L);
+    switch (k) {
+    case K_PRODUCTS: {
+        const int64_t n = (int64_t)BH * ((int64_t)L.gn * L.nsplit + (int64_t)L.on * L.nchunk);
+        if (n == 0) return hipSuccess;
+        hipLaunchKernelGGL((products_kernel<T, D, DELTA>), dim3((unsigned)n), dim3(NT), 0, s, L);
+        break;
     }
-    mark(L, 1);
-    const int units = (BH + 7) / 8 * 8 * (D / 16);
-    hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead>), dim3(units), dim3(64 * (D / 16)), 0,
-                       L.stream, L);
-    mark(L, 2);
-    hipLaunchKernelGGL((output_kernel<T, D>), dim3(BH * L.F * L.nchunk), dim3(NT), 0, L.stream, L);
-    mark(L, 3);
+    case K_COMBINE: {
+        constexpr int NB = ((DELTA ? 2 * D : D) * D / 4 + NT - 1) / NT;
+        if (L.gn == 0) return hipSuccess;
+        hipLaunchKernelGGL((combine_kernel<D, DELTA>), dim3(BH * L.gn * NB), dim3(NT), 0, s, L);
+        break;
+    }
+    case K_SCAN: {
+        if (L.s1 <= L.s0) return hipSuccess;
+        const int units = (BH + 7) / 8 * 8 * (D / 16);
+        hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead>), dim3(units), dim3(64 * (D / 16)),
+                           0, s, L);
+        break;
+    }
+    case K_FUSED_RESET: {
+        const int n = 2 + BH;
+        hipLaunchKernelGGL(fused_reset_kernel, dim3((n + NT - 1) / NT), dim3(NT), 0, s, L.ctl, n);
+        break;
+    }
+    case K_FUSED: {
+        if constexpr (std::is_same<T, bf16>::value && (D == 64 || D == 128)) {
+            hipLaunchKernelGGL((fused_kernel<D, DELTA>), dim3(BH * L.F), dim3(NT), 0, s, L);
+        } else {
+            return hipErrorInvalidValue;
+        }
+        break;
+    }
+    case K_STEP_PARTIAL:
+        hipLaunchKernelGGL((step_partial_kernel<T, D, DELTA>), dim3(BH * L.nsplit), dim3(NT), 0, s, L);
+        break;
+    case K_STEP_REDUCE: {
+        constexpr int NB = (D * D / 4 + NT - 1) / NT;
+        hipLaunchKernelGGL((step_reduce_kernel<T, D>), dim3(BH * NB), dim3(NT), 0, s, L);
+        break;
+    }
+    default:
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
-template <typename T, int D, bool DELTA> static hipError_t stp(const Launch& L) {
-    const int BH = L.B * L.H;
-    mark(L, 0);
-    hipLaunchKernelGGL((step_partial_kernel<T, D, DELTA>), dim3(BH * L.nsplit), dim3(NT), 0,
-                       L.stream, L);
-    mark(L, 1);
-    constexpr int NB = (D * D / 4 + NT - 1) / NT;
-    hipLaunchKernelGGL((step_reduce_kernel<T, D>), dim3(BH * NB), dim3(NT), 0, L.stream, L);
-    mark(L, 2);
-    Launch L1 = L;
-    L1.F = 1;
-    hipLaunchKernelGGL((output_kernel<T, D>), dim3(BH * L.nchunk), dim3(NT), 0, L.stream, L1);
-    mark(L, 3);
-    return hipGetLastError();
+bool fused_supported(int bf16_data, int D) { return bf16_data && (D == 64 || D == 128); }
+
+hipError_t launch_kernel(Kernel k, const Launch& L, hipStream_t s) {
+    const bool dl = L.use_delta != 0;
+#define GDN_CASE(T, D) \
+    case D: return dl ? launch<T, D, true>(k, L, s) : launch<T, D, false>(k, L, s);
+    if (L.bf16) {
+        switch (L.D) { GDN_CASE(bf16, 16) GDN_CASE(bf16, 32) GDN_CASE(bf16, 64) GDN_CASE(bf16, 128) }
+    } else {
+        switch (L.D) { GDN_CASE(float, 16) GDN_CASE(float, 32) GDN_CASE(float, 64) GDN_CASE(float, 128) }
+    }
+#undef GDN_CASE
+    return hipErrorInvalidValue;
 }
-
-
-#define GDN_DISPATCH(FN, L)                                                                  \
-    do {                                                                                     \
-        const bool dl = (L).use_delta != 0;                                                  \
-        if ((L).bf16) {                                                                      \
-            switch ((L).D) {                                                                 \
-            case 16: return dl ? FN<bf16, 16, true>(L) : FN<bf16, 16, false>(L);             \
-            case 32: return dl ? FN<bf16, 32, true>(L) : FN<bf16, 32, false>(L);             \
-            case 64: return dl ? FN<bf16, 64, true>(L) : FN<bf16, 64, false>(L);             \
-            case 128: return dl ? FN<bf16, 128, true>(L) : FN<bf16, 128, false>(L);          \
-            }                                                                                \
-        } else {                                                                             \
-            switch ((L).D) {                                                                 \
-            case 16: return dl ? FN<float, 16, true>(L) : FN<float, 16, false>(L);           \
-            case 32: return dl ? FN<float, 32, true>(L) : FN<float, 32, false>(L);           \
-            case 64: return dl ? FN<float, 64, true>(L) : FN<float, 64, false>(L);           \
-            case 128: return dl ? FN<float, 128, true>(L) : FN<float, 128, false>(L);        \
-            }                                                                                \
-        }                                                                                    \
-        return hipErrorInvalidValue;                                                         \
-    } while (0)
-
-hipError_t launch_forward(const Launch& L) { GDN_DISPATCH(fwd, L); }
-hipError_t launch_step(const Launch& L) { GDN_DISPATCH(stp, L); }
 
 }  // namespace gdn

@@ -26,10 +26,12 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory. Every pointer is a device pointer on the current HIP device, owned by the caller.
- *   libgdn allocates nothing, keeps no state between calls and may be called from several
- *   host threads at once (distinct workspaces).
+ *   libgdn allocates no device memory and keeps no data between calls; it may be called from
+ *   several host threads at once (distinct workspaces).
  * Asynchrony. Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and the
- *   call returns; buffers must stay valid until the stream has passed the call.
+ *   call returns; buffers must stay valid until the stream has passed the call. Each call only
+ *   launches kernels on `hip_stream` (no memset or copy nodes, so it can be captured into a
+ *   HIP graph). Two calls that share a workspace must not run concurrently.
  * Layouts. Q, K, V, O of one (b, h) are token-major rows of D contiguous elements; token
  *   t = f*S + s. Element (b, h, t, d) of Q/K/V is at
  *       base + b*qkv_stride_b + h*qkv_stride_h + t*qkv_stride_t + d      (elements)
@@ -61,7 +63,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 1
+#define LIBGDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -77,6 +79,20 @@ typedef enum {
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
+/*
+ * How a forward is run. Both schedules compute the same recurrence; results agree to rounding
+ * (the state step of both splits Ghat and M into bf16 hi + lo parts; the order of fp32
+ * additions differs).
+ *   STAGED  products of every frame (Ghat_f, Bhat_f) into the workspace, then the frame-serial
+ *           scan over those D x D records, then the outputs of every frame. Any dtype and D.
+ *   FUSED   one pass: each (b, h, f) is a workgroup that computes its frame's products, waits
+ *           for the state of frame f-1 of the same (b, h), applies the step, publishes M_f and
+ *           writes O_f; only Q/K/V/O and the D x D states cross HBM. bf16 with D = 64 or 128
+ *           (GDN_ERR_UNSUPPORTED otherwise).
+ *   AUTO    FUSED where supported and B*H*F >= 1024, else STAGED.
+ */
+typedef enum { GDN_SCHEDULE_AUTO = 0, GDN_SCHEDULE_STAGED = 1, GDN_SCHEDULE_FUSED = 2 } gdn_schedule;
+
 typedef struct {
     int32_t batch;             /* B */
     int32_t heads;             /* H */
@@ -88,6 +104,7 @@ typedef struct {
     float   key_scale;         /* c; <= 0 selects 1/sqrt(D*S) */
     int64_t qkv_stride_b, qkv_stride_h, qkv_stride_t;   /* elements */
     int64_t o_stride_b, o_stride_h, o_stride_t;         /* elements */
+    int32_t schedule;          /* forward only, a gdn_schedule; ignored in step mode */
 } gdn_problem;
 
 /*
@@ -131,14 +148,36 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                           void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * Instrumentation (tracing). Arms HIP events on the calling host thread: every later
- * gdn_forward_framewise / gdn_step_frame call on this thread records events[0] on its stream
- * before its first kernel and events[i] after its i-th kernel (i = 1 .. count-1; the forward
- * runs three kernels -- products, scan, output -- and a step runs three -- partial, reduce,
- * output). `events` holds hipEvent_t handles created by the caller; count 0 or events NULL
- * disarms. count must be 0..4. The events are only recorded, never waited on.
+ * Instrumentation (launch trace). gdn_set_trace arms `pairs` pairs of caller-created,
+ * timing-enabled hipEvent_t handles on the calling host thread: in every later
+ * gdn_forward_framewise / gdn_step_frame call on this thread, kernel launch i (i < pairs) is
+ * bracketed by events[2i] before and events[2i+1] after it, recorded on the stream the kernel
+ * runs on, so hipEventElapsedTime(events[2i], events[2i+1]) is that launch's duration. The
+ * events are only recorded, never waited on. pairs 0 disarms; pairs must be 0..65536. Not for
+ * use during graph capture.
+ * gdn_trace_read returns the number of launches of the last call on this thread while armed
+ * (launches beyond `pairs` are listed but not timed) and copies up to `capacity` entries.
  */
-gdn_status gdn_set_stage_events(void* const* events, int count);
+typedef enum {
+    GDN_KERNEL_PRODUCTS = 0,      /* staged: gram products or outputs of frames */
+    GDN_KERNEL_COMBINE = 1,       /* staged: sum of S-split partial products */
+    GDN_KERNEL_SCAN = 2,          /* staged: frame-serial state scan */
+    GDN_KERNEL_STEP_PARTIAL = 3,  /* step: per-split K^T R */
+    GDN_KERNEL_STEP_REDUCE = 4,   /* step: state update */
+    GDN_KERNEL_FUSED_RESET = 5,   /* fused: clears the ticket counter and frame flags */
+    GDN_KERNEL_FUSED = 6          /* fused: products, state step and outputs of every frame */
+} gdn_kernel_kind;
+
+typedef struct {
+    int32_t kernel;   /* gdn_kernel_kind */
+    int32_t stream;   /* stream of the launch: 0 = the caller's (the only one used) */
+    int64_t units;    /* (b, h, frame) items. A PRODUCTS item moves 2*S*D elements of Q/K/V/O
+                         (K and V read, or Q read and O written); a FUSED item moves 4*S*D
+                         (K, V, Q read, O written) */
+} gdn_trace_entry;
+
+gdn_status gdn_set_trace(void* const* events, int pairs);
+int gdn_trace_read(gdn_trace_entry* entries, int capacity);
 
 /* Static text for a status code (never NULL). */
 const char* gdn_status_string(gdn_status s);

@@ -84,3 +84,36 @@ class HostFrames:
         for fu in self.fut.values():
             fu.cancel()
         self.pool.shutdown(wait=True)
+
+
+class HipEvents:
+    """Timing-enabled hipEvent_t handles through the HIP runtime that torch already loaded."""
+
+    def __init__(self):
+        import ctypes
+        import torch  # noqa: F401  (loads the runtime)
+        self.ct = ctypes
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def new(self):
+        e = self.ct.c_void_p()
+        assert self.rt.hipEventCreate(self.ct.byref(e)) == 0
+        self.made.append(e.value)
+        return e.value
+
+    def ms(self, a, b):
+        assert self.rt.hipEventSynchronize(b) == 0
+        out = self.ct.c_float()
+        assert self.rt.hipEventElapsedTime(self.ct.byref(out), a, b) == 0
+        return float(out.value)
+
+    def close(self):
+        for e in self.made:
+            self.rt.hipEventDestroy(e)
+        self.made = []

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 1
+    assert gdn.abi_version() == 2
     lib = gdn.load()
     for code in range(9):
         assert lib.gdn_status_string(code)
@@ -67,9 +67,13 @@ def test_workspace_size_for_workloads(name):
                     0, 0, w.D, 0, 0, w.D)
     n = gdn.workspace_size(p, w.step_mode)
     assert n > 0
-    if not w.step_mode:
+    fused = (w.dtype == "bf16" and w.D in (64, 128) and w.B * w.H * w.F >= 1024)
+    if not w.step_mode and fused:
+        # two fp32 D x D states per (b, h)
+        assert n >= 2 * w.B * w.H * w.D * w.D * 4
+    elif not w.step_mode:
         esz = w.elem_bytes()
-        # per-frame states plus at least one fp32 partial per frame
+        # per-frame states plus at least one fp32 record per frame
         assert n >= w.B * w.H * w.F * w.D * w.D * (esz + 4 * (2 if w.use_delta else 1))
 
 
@@ -100,6 +104,46 @@ def test_bad_sizes(field, value, code):
     n = ctypes.c_size_t(123)
     assert gdn.load().gdn_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == code
     assert n.value == 123
+
+
+def test_bad_schedule():
+    p = prob()
+    p.schedule = 3
+    assert call(p) == 2
+    assert "schedule" in msg()
+    p = prob(dtype=gdn.GDN_F32)
+    p.schedule = 2  # fused needs bf16
+    assert call(p) == 3
+    p = prob(D=32)
+    p.schedule = 2  # and D = 64 or 128
+    assert call(p) == 3
+    p = prob(D=32)
+    p.schedule = 2
+    assert call(p, step=True, si=7 * A, wsb=16) == 7  # step mode ignores the schedule
+
+
+def test_schedule_workspace():
+    staged, fused = prob(F=30), prob(F=30)
+    staged.schedule, fused.schedule = 1, 2
+    ns, nf = gdn.workspace_size(staged, False), gdn.workspace_size(fused, False)
+    # fused: only two D x D fp32 states per (b, h) plus flags, independent of the frame count
+    assert nf < ns
+    fused.frames = 3000
+    assert gdn.workspace_size(fused, False) == nf
+    assert gdn.workspace_size(prob(F=30), False) == ns     # auto: staged for 60 items
+    assert gdn.workspace_size(prob(F=3000), False) == nf   # and fused for 6000
+
+
+def test_trace_arming_validation():
+    lib = gdn.load()
+    assert lib.gdn_set_trace(None, 0) == 0
+    assert lib.gdn_set_trace(None, 3) == 1
+    assert lib.gdn_set_trace(None, -1) == 2
+    # a call that fails validation launches nothing
+    gdn.set_trace([0x10, 0x20])
+    assert call(prob(), q=None) == 1
+    assert gdn.read_trace() == []
+    gdn.set_trace(None)
 
 
 def test_step_ignores_frames_and_requires_state():

@@ -13,7 +13,7 @@ torch = pytest.importorskip("torch")
 import frame_wise_gated_libgdn_amd as gdn  # noqa: E402
 import gdn_synth  # noqa: E402
 import oracle  # noqa: E402
-from gpu_util import TOL, rel_err, random_qkv, to_dev, to_np  # noqa: E402
+from gpu_util import TOL, HipEvents, rel_err, random_qkv, to_dev, to_np  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -37,10 +37,10 @@ def test_generator_device_matches_host():
 
 
 # --------------------------------------------------------------------------- workloads
-def run_workload_forward(w, layout="head"):
+def run_workload_forward(w, layout="head", schedule="auto"):
     q, k, v = gdn_synth.qkv_torch(w, DEV, layout=layout)
     g, b = gdn_synth.gates_torch(w, DEV)
-    o, st = gdn.forward_framewise(q, k, v, g, b, use_delta=w.use_delta)
+    o, st = gdn.forward_framewise(q, k, v, g, b, use_delta=w.use_delta, schedule=schedule)
     torch.cuda.synchronize()
     return o, st
 
@@ -57,10 +57,11 @@ def test_tiny_f32_full(layout):
     assert rel_err(to_np(st), rs) <= TOL["f32"]
 
 
-def test_block_causal_bf16_full():
+@pytest.mark.parametrize("schedule", ["staged", "fused"])
+def test_block_causal_bf16_full(schedule):
     w = gdn_synth.WORKLOADS["block_causal_bf16"]
-    say("block_causal_bf16 full")
-    o, st = run_workload_forward(w)
+    say("block_causal_bf16 full", schedule)
+    o, st = run_workload_forward(w, schedule=schedule)
     (qc, kc, vc), _ = gdn_synth.qkv_cpu(w)
     gc, bc = gdn_synth.gates_cpu(w)
     ro, rs = oracle.forward(qc, kc, vc, gc, bc, use_delta=False)
@@ -69,10 +70,11 @@ def test_block_causal_bf16_full():
     assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
 
 
-def test_gdn_880x81_bf16_sampled_heads():
+@pytest.mark.parametrize("schedule", ["staged", "fused"])
+def test_gdn_880x81_bf16_sampled_heads(schedule):
     w = gdn_synth.WORKLOADS["gdn_880x81_bf16"]
-    say("gdn_880x81_bf16 full launch, oracle on heads 0 and 15")
-    o, st = run_workload_forward(w)
+    say("gdn_880x81_bf16 full launch, oracle on heads 0 and 15,", schedule)
+    o, st = run_workload_forward(w, schedule=schedule)
     heads = [0, 15]
     (qc, kc, vc), _ = gdn_synth.qkv_cpu(w, heads=heads)
     gc, bc = gdn_synth.gates_cpu(w, heads=heads)
@@ -119,6 +121,91 @@ def test_forward_sweep(case):
     e1, e2 = rel_err(to_np(o), ro), rel_err(to_np(st), rs)
     say("  O err %.3e state err %.3e" % (e1, e2))
     assert e1 <= TOL[dt] and e2 <= TOL[dt]
+
+
+# --------------------------------------------------------------------------- schedules
+# The fused single-pass forward (bf16, D = 64 / 128) against the oracle and against the staged
+# schedule (same products; the state step sums in another order, so states agree to fp32
+# rounding and outputs to bf16 rounding).
+FUSED = [
+    # B, H, D, S, F, delta, initial state, layout
+    (1, 2, 128, 200, 10, True, True, "head"),
+    (2, 3, 64, 130, 7, True, False, "token"),
+    (1, 1, 128, 1, 5, True, True, "head"),        # one token per frame
+    (1, 2, 128, 96, 9, False, True, "head"),
+    (1, 4, 64, 77, 12, False, False, "head"),
+    (1, 3, 128, 64, 60, True, True, "head"),      # a long chain of frames
+    (1, 16, 128, 3520, 3, True, True, "head"),    # the 720p frame size
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=["-".join(map(str, c)) for c in FUSED])
+def test_fused_forward(case):
+    B, H, D, S, F, delta, with_state, layout = case
+    say("fused forward", case)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    s0 = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32) if with_state else None
+    args = [to_dev(x, "bf16", DEV, layout) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                                  torch.from_numpy(b).to(DEV)]
+    ds = None if s0 is None else torch.from_numpy(s0).to(DEV)
+    o1, st1 = gdn.forward_framewise(*args, ds, use_delta=delta, schedule="fused")
+    o2, st2 = gdn.forward_framewise(*args, ds, use_delta=delta, schedule="staged")
+    torch.cuda.synchronize()
+    ro, rs = oracle.forward(q, k, v, g, b, s0, use_delta=delta)
+    e1, e2 = rel_err(to_np(o1), ro), rel_err(to_np(st1), rs)
+    d1, d2 = rel_err(to_np(o1), to_np(o2)), rel_err(to_np(st1), to_np(st2))
+    say("  O err %.3e state err %.3e; vs staged O %.3e state %.3e" % (e1, e2, d1, d2))
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+    assert d2 <= 1e-5 and d1 <= 1e-2
+
+
+def test_fused_in_place_state_and_determinism():
+    rng = np.random.default_rng(11)
+    B, H, D, S, F = 1, 2, 128, 50, 9
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    s0 = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV)]
+    ds = torch.from_numpy(s0).to(DEV)
+    o_ref, s_ref = gdn.forward_framewise(*args, ds.clone(), schedule="fused")
+    o, s = gdn.forward_framewise(*args, ds, state_out=ds, schedule="fused")
+    torch.cuda.synchronize()
+    assert s.data_ptr() == ds.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(ds, s_ref)
+
+
+def test_launch_trace():
+    rng = np.random.default_rng(12)
+    B, H, D, S, F = 1, 2, 128, 64, 10
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV)]
+    ev = HipEvents()
+    handles = [ev.new() for _ in range(2 * 8)]
+    try:
+        gdn.set_trace(handles)
+        gdn.forward_framewise(*args, schedule="staged")
+        staged = gdn.read_trace()
+        gdn.forward_framewise(*args, schedule="fused")
+        fused = gdn.read_trace()
+        gdn.set_trace(None)
+        torch.cuda.synchronize()
+        assert [k_ for k_, _, _ in staged] == ["products", "scan", "products"]
+        assert [u for _, _, u in staged] == [B * H * F] * 3
+        assert [k_ for k_, _, _ in fused] == ["fused_reset", "fused"]
+        assert fused[1][2] == B * H * F
+        for i in range(len(fused)):
+            assert ev.ms(handles[2 * i], handles[2 * i + 1]) >= 0.0
+    finally:
+        gdn.set_trace(None)
+        ev.close()
 
 
 STEP_SWEEP = [
