@@ -309,6 +309,7 @@ def main():
             "algorithmic_gb_per_launch": round(launch_bytes / 1e9, 4),
             "launch_ms": round(launch_ms, 4),
             "launches_per_step": {k_: a[0] // args.steps for k_, a in per.items()},
+            "plan": plan_key,
             "kernel_ms_per_step": {k_: round(x, 4) for k_, x in kms.items()},
             "schedule": args.schedule,
             "call": {"bytes_alg_gb": round(bytes_alg / 1e9, 3),
