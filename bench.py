@@ -187,12 +187,26 @@ def stream_mode(dev, nframes, ev, stream):
         ev.record(marks[f + 1], stream)
     lat = np.array([ev.ms(marks[f], marks[f + 1]) for f in range(nframes)])
     total = ev.ms(marks[0], marks[-1])
+    # per-kernel split of one pass, from the launch trace, over a few extra frames (untimed above)
+    kus = {}
+    for f in range(min(8, nframes)):
+        sl = slice(f * w.S, (f + 1) * w.S)
+        q, k, v, g, b = passes[0]
+        tr = [ev.new() for _ in range(6)]
+        gdn.set_trace(tr)
+        gdn.step_frame(q[:, :, sl], k[:, :, sl], v[:, :, sl], g[f], b[f], state, commit=False,
+                       out=o, workspace=ws)
+        plan = gdn.read_trace()
+        gdn.set_trace(None)
+        for j, (kname, _, _) in enumerate(plan):
+            kus.setdefault(kname, []).append(ev.ms(tr[2 * j], tr[2 * j + 1]) * 1e3)
     return {"workload": w.name, "frames": nframes, "passes_per_frame": w.passes,
             "frame_latency_ms": {"median": round(float(np.median(lat)), 4),
                                  "p90": round(float(np.percentile(lat, 90)), 4),
                                  "max": round(float(lat.max()), 4)},
             "frames_per_s": round(nframes / (total / 1e3), 1),
-            "pass_us_median": round(float(np.median(lat)) * 1e3 / w.passes, 2)}
+            "pass_us_median": round(float(np.median(lat)) * 1e3 / w.passes, 2),
+            "pass_kernel_us_median": {k_: round(float(np.median(v_)), 2) for k_, v_ in kus.items()}}
 
 
 def main():

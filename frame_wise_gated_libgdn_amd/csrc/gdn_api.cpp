@@ -71,7 +71,10 @@ Plan make_plan(const gdn_problem& p, int step_mode) {
     pl.nsplit = (int)((S + pl.split_tokens - 1) / pl.split_tokens);
 
     const int64_t tiles16 = (S + 15) / 16;
-    int64_t wc = (kTargetGroups + BH * F - 1) / (BH * F);
+    // output chunks: each output workgroup first stages the D x D state, so one frame (step
+    // mode) is cut into fewer, longer chunks
+    const int64_t target_out = step_mode ? kTargetGroups / 4 : kTargetGroups;
+    int64_t wc = (target_out + BH * F - 1) / (BH * F);
     wc = std::max<int64_t>(1, std::min<int64_t>(wc, (tiles16 + 3) / 4));
     pl.chunk_tokens = (int)(((tiles16 + wc - 1) / wc) * 16);
     pl.nchunk = (int)((S + pl.chunk_tokens - 1) / pl.chunk_tokens);

@@ -115,12 +115,12 @@ template <typename T, int D> struct XTile {
 // Global -> registers -> transposed LDS staging of one chunk of K and V. A thread moves
 // VE x VE blocks (VE tokens x VE features, VE = elements per 16 bytes): VE row loads, a register
 // transpose, VE row stores into the LDS tile.
-template <typename T, int D> struct XStage {
+template <typename T, int D, int NTH = NT> struct XStage {
     static constexpr int VE = 16 / (int)sizeof(T);
     static constexpr int FB = 2 * D / VE;              // feature blocks (K then V)
     static constexpr int TB = XTile<T, D>::SC / VE;    // token blocks
     static constexpr int NBLK = FB * TB;
-    static constexpr int PER = (NBLK + NT - 1) / NT;
+    static constexpr int PER = (NBLK + NTH - 1) / NTH;
     u32x4 r[PER][VE];
 
     // tokens [t0, t0 + 64) of the frame; rows at or beyond tend are zero
@@ -128,8 +128,8 @@ template <typename T, int D> struct XStage {
                                          int tid) {
 #pragma unroll
         for (int pi = 0; pi < PER; ++pi) {
-            const int blk = tid + pi * NT;
-            if (NBLK % NT == 0 || blk < NBLK) {
+            const int blk = tid + pi * NTH;
+            if (NBLK % NTH == 0 || blk < NBLK) {
                 const int fb = blk % FB, tb = blk / FB;
                 const T* base = fb < D / VE ? kb + fb * VE : vb + (fb - D / VE) * VE;
 #pragma unroll
@@ -141,11 +141,26 @@ template <typename T, int D> struct XStage {
         }
     }
 
+    // The K blocks as loaded (rows = tokens), to a row-major tile with row length kr elements
+    __device__ __forceinline__ void store_key_rows(T* rows, int kr, int tid) const {
+#pragma unroll
+        for (int pi = 0; pi < PER; ++pi) {
+            const int blk = tid + pi * NTH;
+            if (NBLK % NTH == 0 || blk < NBLK) {
+                const int fb = blk % FB, tb = blk / FB;
+                if (fb < D / VE) {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) st16(rows + (tb * VE + e) * kr + fb * VE, r[pi][e]);
+                }
+            }
+        }
+    }
+
     __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
         for (int pi = 0; pi < PER; ++pi) {
-            const int blk = tid + pi * NT;
-            if (NBLK % NT == 0 || blk < NBLK) {
+            const int blk = tid + pi * NTH;
+            if (NBLK % NTH == 0 || blk < NBLK) {
                 const int fb = blk % FB, tb = blk / FB;
 #pragma unroll
                 for (int f = 0; f < VE; ++f) {
@@ -215,7 +230,7 @@ __device__ __forceinline__ void store_split4(bf16* hi, bf16* lo, f32x4 x) {
 // With one split the kernel writes the scan's per-frame record directly; otherwise fp32
 // partials that combine_kernel sums. Item blk covers frame g0 + (blk / nsplit) % gn.
 template <typename T, int D, bool DELTA>
-__device__ __forceinline__ void gram_body(const Launch& L, int blk) {
+__device__ __forceinline__ void gram_body(const Launch& L, int blk, char* lds) {
     using MM = Mma<T>;
     using X = XTile<T, D>;
     constexpr int NOUT = DELTA ? 2 * D : D;
@@ -223,7 +238,6 @@ __device__ __forceinline__ void gram_body(const Launch& L, int blk) {
     constexpr int WI = TI >= 2 ? 2 : 1;
     constexpr int WJ = (4 / WI) < TJ ? (4 / WI) : TJ;
     constexpr int MI = TI / WI, MJ = TJ / WJ;
-    __shared__ __attribute__((aligned(16))) char lds[X::BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
@@ -470,6 +484,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
 // consecutive output columns of one token (16-byte stores). The A operand rows (output columns
 // j) of 16x16 tile jt are permuted: with bf16 and D >= 32, tiles 2p and 2p+1 cover columns
 // 32p .. 32p+31 such that lane (r, g) receives j = 32p + 8g + 0..7 across the pair.
+// LDS copy of M_f^T for the output items: rows padded by 16 bytes against bank conflicts
+template <typename T, int D> struct OutStage {
+    static constexpr int MR = D + 16 / (int)sizeof(T);
+    static constexpr int BYTES = D * MR * (int)sizeof(T);
+};
+
 template <typename T, int D> __device__ __forceinline__ int out_col(int jt, int m) {
     if constexpr (sizeof(T) == 2 && D >= 32)
         return 32 * (jt >> 1) + 8 * (m >> 2) + 4 * (jt & 1) + (m & 3);
@@ -478,9 +498,10 @@ template <typename T, int D> __device__ __forceinline__ int out_col(int jt, int 
 }
 
 template <typename T, int D>
-__device__ __forceinline__ void output_body(const Launch& L, int blk) {
+__device__ __forceinline__ void output_body(const Launch& L, int blk, char* lds) {
     using MM = Mma<T>;
     constexpr int TJ = D / 16, KSN = (D + MM::KS - 1) / MM::KS;  // contraction padded to KS
+    constexpr int MR = OutStage<T, D>::MR;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
     const int ch = blk % L.nchunk;
@@ -491,26 +512,53 @@ __device__ __forceinline__ void output_body(const Launch& L, int blk) {
     const T* qf = (const T*)L.q + (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * L.S * L.st;
     T* of = (T*)L.o + (int64_t)b * L.ob + (int64_t)h * L.oh + (int64_t)f * L.S * L.ot;
 
+    const int s_beg = ch * L.chunk_tokens;
+    const int s_end = min(L.S, s_beg + L.chunk_tokens);
+    // B operand (Q rows) of one 16-token tile; tiles past the chunk read nothing
+    auto load_q = [&](int s0, typename MM::frag (&bq)[KSN]) {
+        const int s = s0 + r16;
+        const bool ok = s < s_end;
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks)
+            bq[ks] = ok && ks * MM::KS + g * MM::KL < D
+                         ? ld_frag<T>(qf + (int64_t)s * L.st + ks * MM::KS + g * MM::KL)
+                         : zero_frag<T>();
+    };
+    typename MM::frag bq[KSN];
+    load_q(s_beg + wave * 16, bq);  // in flight while the state is staged
+
+    // M_f^T staged once per workgroup (padded rows), then each wave's A fragments from LDS
+    T* ms = (T*)lds;
+    {
+        // all loads in flight before the first LDS store
+        constexpr int VE = 16 / (int)sizeof(T), NE = D * D / VE, PT = (NE + NT - 1) / NT;
+        u32x4 x[PT];
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const int e = min(tid + k * NT, NE - 1);
+            x[k] = ld16(mt + (e / (D / VE)) * D + (e % (D / VE)) * VE);
+        }
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const int e = tid + k * NT;
+            if (NE % NT == 0 || e < NE) st16(ms + (e / (D / VE)) * MR + (e % (D / VE)) * VE, x[k]);
+        }
+    }
+    __syncthreads();
     typename MM::frag am[TJ][KSN];
 #pragma unroll
     for (int jt = 0; jt < TJ; ++jt)
 #pragma unroll
         for (int ks = 0; ks < KSN; ++ks)
             am[jt][ks] = ks * MM::KS + g * MM::KL < D
-                             ? ld_frag<T>(mt + out_col<T, D>(jt, r16) * D + ks * MM::KS + g * MM::KL)
+                             ? ld_frag<T>(ms + out_col<T, D>(jt, r16) * MR + ks * MM::KS + g * MM::KL)
                              : zero_frag<T>();
 
-    const int s_beg = ch * L.chunk_tokens;
-    const int s_end = min(L.S, s_beg + L.chunk_tokens);
     for (int s0 = s_beg + wave * 16; s0 < s_end; s0 += 4 * 16) {
         const int s = s0 + r16;
         const bool ok = s < s_end;
-        typename MM::frag bq[KSN];
-#pragma unroll
-        for (int ks = 0; ks < KSN; ++ks)
-            bq[ks] = ok && ks * MM::KS + g * MM::KL < D
-                         ? ld_frag<T>(qf + (int64_t)s * L.st + ks * MM::KS + g * MM::KL)
-                         : zero_frag<T>();
+        typename MM::frag bn[KSN];
+        load_q(s0 + 4 * 16, bn);  // next tile of this wave, in flight during this one
         f32x4 acc[TJ];
 #pragma unroll
         for (int jt = 0; jt < TJ; ++jt) {
@@ -534,6 +582,8 @@ __device__ __forceinline__ void output_body(const Launch& L, int blk) {
                     store4(orow + 16 * jt + 4 * g, acc[jt][0], acc[jt][1], acc[jt][2], acc[jt][3]);
             }
         }
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks) bq[ks] = bn[ks];
     }
 }
 
@@ -544,11 +594,13 @@ __device__ __forceinline__ void output_body(const Launch& L, int blk) {
 // are ready, and the frame-serial scan of the chunk in between runs beside it.
 template <typename T, int D, bool DELTA>
 __global__ __launch_bounds__(NT, 2) void products_kernel(Launch L) {
+    constexpr int GB = XTile<T, D>::BYTES, OB = OutStage<T, D>::BYTES;
+    __shared__ __attribute__((aligned(16))) char lds[GB > OB ? GB : OB];
     const int ng = L.B * L.H * L.gn * L.nsplit;
     if ((int)blockIdx.x < ng)
-        gram_body<T, D, DELTA>(L, blockIdx.x);
+        gram_body<T, D, DELTA>(L, blockIdx.x, lds);
     else
-        output_body<T, D>(L, blockIdx.x - ng);
+        output_body<T, D>(L, blockIdx.x - ng, lds);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -822,13 +874,20 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
             am[jt][ks] = ld_frag<bf16>(Mt + out_col<bf16, D>(jt, r16) * MR + ks * MM::KS + g * MM::KL);
     const bf16* qf = (const bf16*)L.q + fo;
     bf16* of = (bf16*)L.o + (int64_t)b * L.ob + (int64_t)h * L.oh + (int64_t)f * S * L.ot;
-    for (int s0 = wave * 16; s0 < S; s0 += 4 * 16) {
+    auto load_q = [&](int s0, bf16x8 (&bq)[KSN]) {
         const int s = s0 + r16;
         const bool in = s < S;
-        bf16x8 bq[KSN];
 #pragma unroll
         for (int ks = 0; ks < KSN; ++ks)
             bq[ks] = in ? ld_frag<bf16>(qf + (int64_t)s * L.st + ks * MM::KS + g * MM::KL) : zero_frag<bf16>();
+    };
+    bf16x8 bq[KSN];
+    load_q(wave * 16, bq);
+    for (int s0 = wave * 16; s0 < S; s0 += 4 * 16) {
+        const int s = s0 + r16;
+        const bool in = s < S;
+        bf16x8 bn[KSN];
+        load_q(s0 + 4 * 16, bn);  // next tile of this wave, in flight during this one
         f32x4 acc[TJ];
 #pragma unroll
         for (int jt = 0; jt < TJ; ++jt) {
@@ -846,6 +905,8 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
                            pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])});
             }
         }
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks) bq[ks] = bn[ks];
     }
 }
 
@@ -854,23 +915,34 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
 // R = V - (gamma c) K M (delta) or R = V (no delta). The prediction P = K M runs on MFMA with M
 // (state_in) rounded to the I/O type. For bf16 data U is accumulated as K^T V + K^T (-gamma c P):
 // V is an exact bf16 input and only the small prediction term is rounded to bf16. For fp32
-// data R is formed in fp32. K and V of each 64-token chunk are staged transposed in LDS; the
-// prediction's K rows are read directly.
+// data R is formed in fp32. Each 64-token chunk of K and V is staged in LDS twice: transposed
+// (rows = features; the U product contracts over tokens) and, for K, row-major (the prediction
+// contracts over features). M is staged once per workgroup, transposed, in the I/O type.
 // Token grouping inside a step of the U product: for bf16, a 32-token group is two 16-token
 // tiles; lane group g holds tokens {4g..4g+3} of the first tile and {16+4g..16+4g+3} of the
 // second (exactly the rows of the prediction's C fragments). For fp32, step q of a 16-token
 // tile gives lane group g the token 4g + q.
+// The partial is stored transposed, part[p][j][i] = U_p[i][j], 16 contiguous bytes per lane.
+template <int D> constexpr int step_threads() { return 64 * (D / 16 > 4 ? D / 16 : 4); }
+
 template <typename T, int D, bool DELTA>
-__global__ __launch_bounds__(NT) void step_partial_kernel(Launch L) {
+__global__ __launch_bounds__(step_threads<D>()) void step_partial_kernel(Launch L) {
     using MM = Mma<T>;
     using X = XTile<T, D>;
+    constexpr int SNT = step_threads<D>();   // one wave per 16-column tile (at least 4 waves)
     constexpr int TJ = D / 16;
-    constexpr int NWJ = TJ < 4 ? TJ : 4;      // waves with work
-    constexpr int JW = TJ / NWJ;              // 16-column tiles per wave
+    constexpr int NWJ = TJ;                   // waves with work
+    constexpr int JW = 1;                     // 16-column tiles per wave
     constexpr int KSN = (D + MM::KS - 1) / MM::KS;  // contraction over D, padded to KS
+    constexpr int DP = KSN * MM::KS;          // padded feature count
     constexpr int RT = sizeof(T) == 2 ? 2 : 1; // 16-token tiles per U step group
     constexpr int TG = 16 * RT;               // tokens per group
+    constexpr int KR = DP + 16 / (int)sizeof(T);   // row length (elements) of the row-major K copy
+    constexpr int MR = DP + 16 / (int)sizeof(T);   // row length of the transposed M copy
     __shared__ __attribute__((aligned(16))) char lds[X::BYTES];
+    __shared__ __attribute__((aligned(16))) T krow[DELTA ? X::SC * KR : 1];
+    constexpr bool MT = DELTA && sizeof(T) == 2;   // bf16: M staged transposed; fp32: read directly
+    __shared__ __attribute__((aligned(16))) T mt[MT ? D * MR : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
@@ -883,26 +955,60 @@ __global__ __launch_bounds__(NT) void step_partial_kernel(Launch L) {
     const bool active = wave < NWJ;
     const float gc = L.gamma[bh] * L.c;
 
-    // B operand of the prediction: M[i][j] for this wave's columns, all key rows
+    // two chunks of K and V in flight: chunk c is loaded while chunk c - 2 is computed
+    XStage<T, D, SNT> sa, sb;
+    sa.load(kb, vb, L.st, t0, t1, tid);
+    sb.load(kb, vb, L.st, t0 + X::SC, t1, tid);
+
+    // B operand of the prediction: M[i][j] for this wave's columns, all key rows. bf16: from a
+    // transposed copy mt[j][i] (i past D is zero); fp32: one element per lane, read directly
+    // (lanes of a group read consecutive columns).
     typename MM::frag bm[JW][KSN];
-    if (DELTA && active) {
+    if constexpr (DELTA && !MT) {
+        if (active) {
+            const float* M = L.state_in + (int64_t)bh * D * D;
+#pragma unroll
+            for (int jl = 0; jl < JW; ++jl)
+#pragma unroll
+                for (int ks = 0; ks < KSN; ++ks)
+                    bm[jl][ks] = M[(ks * 4 + g) * D + (wave * JW + jl) * 16 + r16];
+        }
+    }
+    if constexpr (DELTA && DP > D) {
+        for (int e = tid; e < X::SC * (DP - D); e += SNT) krow[(e / (DP - D)) * KR + D + e % (DP - D)] = (T)0.f;
+    }
+    if constexpr (MT) {
         const float* M = L.state_in + (int64_t)bh * D * D;
+        // one 8 x 8 block of M per thread (D/8 x D/8 blocks <= SNT): 16 loads in flight, bf16
+        // conversion and a register transpose, then 8 row stores of 16 bytes into mt
+        constexpr int NBK = D / 8;
+        static_assert(NBK * NBK <= SNT, "one 8x8 block of M per thread");
+        if (tid < NBK * NBK) {
+            const int bi = tid / NBK, bj = tid % NBK;
+            f32x4 x[8][2];
 #pragma unroll
-        for (int jl = 0; jl < JW; ++jl) {
-            const int j = (wave * JW + jl) * 16 + r16;
+            for (int e = 0; e < 8; ++e)
 #pragma unroll
-            for (int ks = 0; ks < KSN; ++ks) {
-                if constexpr (sizeof(T) == 2) {
-                    float m[8];
-                    const bool in = ks * 32 + g * 8 < D;
+                for (int hh = 0; hh < 2; ++hh) x[e][hh] = *(const f32x4*)(M + (8 * bi + e) * D + 8 * bj + 4 * hh);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) m[e] = in ? M[(ks * 32 + g * 8 + e) * D + j] : 0.f;
-                    bm[jl][ks] = __builtin_bit_cast(
-                        bf16x8, u32x4{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]),
-                                      pack_bf16x2(m[4], m[5]), pack_bf16x2(m[6], m[7])});
-                } else {
-                    bm[jl][ks] = M[(ks * 4 + g) * D + j];
-                }
+            for (int cc = 0; cc < 8; ++cc) {
+                const int hh = cc >> 2, q = cc & 3;
+                st16(mt + (8 * bj + cc) * MR + 8 * bi,
+                     u32x4{pack_bf16x2(x[0][hh][q], x[1][hh][q]), pack_bf16x2(x[2][hh][q], x[3][hh][q]),
+                           pack_bf16x2(x[4][hh][q], x[5][hh][q]), pack_bf16x2(x[6][hh][q], x[7][hh][q])});
+            }
+        }
+        if constexpr (DP > D) {
+            for (int e = tid; e < D * (DP - D); e += SNT) mt[(e / (DP - D)) * MR + D + e % (DP - D)] = (T)0.f;
+        }
+        __syncthreads();
+        if (active) {
+#pragma unroll
+            for (int jl = 0; jl < JW; ++jl) {
+                const int j = (wave * JW + jl) * 16 + r16;
+#pragma unroll
+                for (int ks = 0; ks < KSN; ++ks)
+                    bm[jl][ks] = ld_frag<T>(mt + j * MR + ks * MM::KS + g * MM::KL);
             }
         }
     }
@@ -913,15 +1019,14 @@ __global__ __launch_bounds__(NT) void step_partial_kernel(Launch L) {
 #pragma unroll
         for (int jl = 0; jl < JW; ++jl) acc[it][jl] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    XStage<T, D> stg;
-    stg.load(kb, vb, L.st, t0, t1, tid);
-    for (int c0 = t0; c0 < t1; c0 += X::SC) {
+    auto chunk = [&](XStage<T, D, SNT>& stg, int c0) {
         __syncthreads();
         stg.store(lds, tid);
+        if constexpr (DELTA) stg.store_key_rows(krow, KR, tid);  // row-major K copy of the chunk
         __syncthreads();
-        if (c0 + X::SC < t1) stg.load(kb, vb, L.st, c0 + X::SC, t1, tid);
-        if (!active) continue;
-#pragma unroll 1
+        if (c0 + 2 * X::SC < t1) stg.load(kb, vb, L.st, c0 + 2 * X::SC, t1, tid);
+        if (!active) return;
+#pragma unroll
         for (int tg = 0; tg < X::SC; tg += TG) {
             // prediction P = K M (fp32, C layout): rows 4g+q of each 16-token tile, column
             // (wave tile jl, r16)
@@ -930,15 +1035,11 @@ __global__ __launch_bounds__(NT) void step_partial_kernel(Launch L) {
             for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
                 for (int jl = 0; jl < JW; ++jl) pr[rt][jl] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (DELTA) {
-                    const int s = c0 + tg + rt * 16 + r16;
-                    const bool ok = s < t1;
+                if constexpr (DELTA) {
 #pragma unroll
                     for (int ks = 0; ks < KSN; ++ks) {
                         const typename MM::frag ak =
-                            ok && ks * MM::KS + g * MM::KL < D
-                                ? ld_frag<T>(kb + (int64_t)s * L.st + ks * MM::KS + g * MM::KL)
-                                : zero_frag<T>();
+                            ld_frag<T>(krow + (tg + rt * 16 + r16) * KR + ks * MM::KS + g * MM::KL);
 #pragma unroll
                         for (int jl = 0; jl < JW; ++jl) pr[rt][jl] = MM::run(ak, bm[jl][ks], pr[rt][jl]);
                     }
@@ -962,9 +1063,9 @@ __global__ __launch_bounds__(NT) void step_partial_kernel(Launch L) {
                                           pack_bf16x2(-gc * pr[1][jl][2], -gc * pr[1][jl][3])});
 #pragma unroll
                     for (int it = 0; it < TJ; ++it) {
-                        const int krow = it * 16 + r16;
-                        const u32x2 lo = *(const u32x2*)(lds + X::addr(krow, tg + 4 * g));
-                        const u32x2 hi = *(const u32x2*)(lds + X::addr(krow, tg + 16 + 4 * g));
+                        const int krw = it * 16 + r16;
+                        const u32x2 lo = *(const u32x2*)(lds + X::addr(krw, tg + 4 * g));
+                        const u32x2 hi = *(const u32x2*)(lds + X::addr(krw, tg + 16 + 4 * g));
                         const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
                         acc[it][jl] = MM::run(ak, bv, acc[it][jl]);
                         if (DELTA) acc[it][jl] = MM::run(ak, bp, acc[it][jl]);
@@ -989,6 +1090,10 @@ __global__ __launch_bounds__(NT) void step_partial_kernel(Launch L) {
                 }
             }
         }
+    };
+    for (int c0 = t0; c0 < t1; c0 += 2 * X::SC) {
+        chunk(sa, c0);
+        if (c0 + X::SC < t1) chunk(sb, c0 + X::SC);
     }
     if (!active) return;
     float* out = L.part + ((int64_t)bh * L.nsplit + p) * D * D;
@@ -997,31 +1102,41 @@ __global__ __launch_bounds__(NT) void step_partial_kernel(Launch L) {
 #pragma unroll
         for (int jl = 0; jl < JW; ++jl) {
             const int j = (wave * JW + jl) * 16 + r16;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) out[(it * 16 + 4 * g + q) * D + j] = acc[it][jl][q];
+            *(f32x4*)(out + j * D + it * 16 + 4 * g) = acc[it][jl];
         }
 }
 
 // Kernel 5: M' = gamma M + beta c sum_p U_p (fixed order over p); state_out on commit;
-// transposed copy of M' in the I/O type for the output kernel. Thread: 4 key rows x 1 column.
+// transposed copy of M' in the I/O type for the output products. Thread: 4 key rows x 1 column.
+// The partials of a thread are loaded in batches of 16 (indices clamped, extra terms masked) so
+// that their loads are in flight together.
 template <typename T, int D>
 __global__ __launch_bounds__(NT) void step_reduce_kernel(Launch L) {
     constexpr int NQ = D * D / 4;
     constexpr int NB = (NQ + NT - 1) / NT;
+    constexpr int BATCH = 16;
     const int bh = blockIdx.x / NB;
     const int t = (blockIdx.x % NB) * NT + threadIdx.x;
     if (t >= NQ) return;
-    const int j = t % D, i0 = (t / D) * 4;
+    const int i0 = (t % (D / 4)) * 4, j = t / (D / 4);
     const float gm = L.gamma[bh], bc = L.beta[bh] * L.c;
-    const float* part = L.part + (int64_t)bh * L.nsplit * D * D;
+    const float* part = L.part + (int64_t)bh * L.nsplit * D * D + j * D + i0;  // [p][j][i]
+    const float* min_ = L.state_in + (int64_t)bh * D * D;
+    float m0[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m0[q] = min_[(i0 + q) * D + j];  // issued with the first batch
+    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+    const int np = L.nsplit;
+    for (int p0 = 0; p0 < np; p0 += BATCH) {
+        f32x4 x[BATCH];
+#pragma unroll
+        for (int e = 0; e < BATCH; ++e) x[e] = *(const f32x4*)(part + (int64_t)min(p0 + e, np - 1) * D * D);
+#pragma unroll
+        for (int e = 0; e < BATCH; ++e) u += p0 + e < np ? x[e] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     float m[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int idx = (i0 + q) * D + j;
-        float u = 0.f;
-        for (int p = 0; p < L.nsplit; ++p) u += part[(int64_t)p * D * D + idx];
-        m[q] = gm * L.state_in[(int64_t)bh * D * D + idx] + bc * u;
-    }
+    for (int q = 0; q < 4; ++q) m[q] = gm * m0[q] + bc * u[q];
     if (L.state_out) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) L.state_out[(int64_t)bh * D * D + (i0 + q) * D + j] = m[q];
@@ -1069,7 +1184,8 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
         break;
     }
     case K_STEP_PARTIAL:
-        hipLaunchKernelGGL((step_partial_kernel<T, D, DELTA>), dim3(BH * L.nsplit), dim3(NT), 0, s, L);
+        hipLaunchKernelGGL((step_partial_kernel<T, D, DELTA>), dim3(BH * L.nsplit), dim3(step_threads<D>()),
+                           0, s, L);
         break;
     case K_STEP_REDUCE: {
         constexpr int NB = (D * D / 4 + NT - 1) / NT;
