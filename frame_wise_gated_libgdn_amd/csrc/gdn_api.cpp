@@ -88,9 +88,9 @@ Plan make_plan(const gdn_problem& p, int step_mode) {
     pl.canon_bytes = step_mode ? 0 : (size_t)(BH * F * rec);
     pl.part_bytes = (step_mode || pl.nsplit > 1) ? (size_t)(BH * F * pl.nsplit * nout * D * D * 4) : 0;
     pl.mt_bytes = (size_t)(BH * F * D * D * esz);
-    // fused: ticket counter, time-out flag and one frame flag per (b, h); two fp32 state
-    // buffers per (b, h)
-    pl.ctl_bytes = (size_t)(2 + BH) * 4;
+    // fused: ticket counter, time-out flag and one frame flag per (b, h) and column group; two
+    // fp32 state buffers per (b, h)
+    pl.ctl_bytes = (size_t)(2 + BH * gdn::kChainGroups) * 4;
     pl.chain_bytes = (size_t)(2 * BH * D * D * 4);
     return pl;
 }

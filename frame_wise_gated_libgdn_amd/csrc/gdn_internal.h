@@ -25,7 +25,8 @@ struct Launch {
     float* part;         // workspace: per-split fp32 partial products (when nsplit > 1)
     void* mt;            // workspace: materialised per-frame states, transposed, in the I/O type
     int* ctl;            // workspace (fused): [0] ticket counter, [1] wait time-out flag,
-                         //   [2 + bh] last frame of (b, h) whose state is published
+                         //   [2 + bh * kChainGroups + g] last frame of (b, h) whose column
+                         //   group g of the state is published
     float* chain;        // workspace (fused): published states, [2][B*H][D][D] fp32, [c][n] order
     int nsplit;          // S splits of the gram products
     int split_tokens;    // tokens per split (multiple of 64)
@@ -44,6 +45,9 @@ enum Kernel {
     K_PRODUCTS = 0, K_COMBINE = 1, K_SCAN = 2, K_STEP_PARTIAL = 3, K_STEP_REDUCE = 4,
     K_FUSED_RESET = 5, K_FUSED = 6
 };
+
+// Fused forward: value-column groups pipelined through the frame chain (one flag each per (b, h)).
+constexpr int kChainGroups = 4;
 
 // Whether the fused single-pass forward has a kernel for this type / head size.
 bool fused_supported(int bf16, int D);

@@ -743,117 +743,127 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) bacc[nb][cb] *= sB;
 
-    // ---- 2. wait for M_{f-1} of this (b, h)
-    int* flag = L.ctl + 2 + bh;
-    if (tid == 0) {
-        int ok = 1;
-        if (f > 0) {
-            int polls = 0;
-            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < f - 1) {
-                if (++polls > kSpinLimit) {
-                    ok = 0;
-                    __hip_atomic_store(&L.ctl[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(4);
-            }
-        }
-        s_ok = ok;
-    }
-    __syncthreads();  // also: the last chunk's LDS readers are done (planes reuse that space)
-    const bool ok = s_ok != 0;
-
-    // M_{f-1}[n][c] at this lane's C-layout positions: n = nw + 16 nb + 4 g + q, c = 16 cb + r.
-    // All loads are issued before any is used (one uniform branch around the whole batch).
-    f32x4 mp[NB][CB];
-    if (f > 0) {
-        const __amdgpu_buffer_rsrc_t rs =
-            buffer_over(L.chain + ((int64_t)((f - 1) & 1) * BH + bh) * D * D, D * D * 4);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                mp[nb][cb] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               rs, (((wave * NB + nb) * CB + cb) * 64 + lane) * 16, 0, kCoherent));
-    } else {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    mp[nb][cb][q] = L.state_in
-                                        ? L.state_in[((int64_t)bh * D + nw + 16 * nb + 4 * g + q) * D + 16 * cb + r16]
-                                        : 0.f;
-    }
+    // ---- 2. the state step, pipelined over kChainGroups groups of value columns: column c of
+    // M_f only depends on column c of M_{f-1}, so group g of frame f starts as soon as frame f-1
+    // has published its group g, and the frame-to-frame period is one group's latency.
+    constexpr int CG = kChainGroups, CPG = CB / CG;  // groups, 16-column blocks per group
+    static_assert(CB % CG == 0, "column blocks split evenly into groups");
+    int* flags = L.ctl + 2 + bh * CG;
     bf16* Ph = (bf16*)lds;
     bf16* Pl = Ph + PLANE;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_over(L.chain + ((int64_t)((f + 1) & 1) * BH + bh) * D * D, D * D * 4);  // M_{f-1}
+    const __amdgpu_buffer_rsrc_t rd =
+        buffer_over(L.chain + ((int64_t)(f & 1) * BH + bh) * D * D, D * D * 4);        // M_f
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int kb = (nw + 16 * nb) >> 4;
-        const int pos = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int c = 16 * cb + r16;
-            const float nan = __builtin_nanf("");
-            const f32x4 m = ok ? mp[nb][cb] : f32x4{nan, nan, nan, nan};
-            bacc[nb][cb] += gm * m;
-            if constexpr (DELTA) store_split4(Ph + c * MR + pos, Pl + c * MR + pos, m);
-        }
-    }
-    if constexpr (DELTA) {
-        __syncthreads();
-        // three passes (hi.hi, hi.lo, lo.hi) per k step, each over all NB x CB accumulators, so
-        // that consecutive MFMAs never depend on each other
-#pragma unroll
-        for (int ks = 0; ks < KB / 2; ++ks) {
-            bf16x8 ah[NB], al[NB];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                ah[nb] = __builtin_bit_cast(bf16x8, u32x4{gh[2 * ks][nb][0], gh[2 * ks][nb][1],
-                                                         gh[2 * ks + 1][nb][0], gh[2 * ks + 1][nb][1]});
-                al[nb] = __builtin_bit_cast(bf16x8, u32x4{gl[2 * ks][nb][0], gl[2 * ks][nb][1],
-                                                         gl[2 * ks + 1][nb][0], gl[2 * ks + 1][nb][1]});
-            }
-#pragma unroll
-            for (int pass = 0; pass < 3; ++pass) {
-                const bf16* plane = pass == 1 ? Pl : Ph;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    const bf16x8 m = ld_frag<bf16>(plane + (16 * cb + r16) * MR + 32 * ks + 8 * g);
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        bacc[nb][cb] = MM::run(pass == 2 ? al[nb] : ah[nb], m, bacc[nb][cb]);
+    for (int grp = 0; grp < CG; ++grp) {
+        if (tid == 0) {
+            int ok = 1;
+            if (f > 0) {
+                int polls = 0;
+                while (__hip_atomic_load(flags + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < f - 1) {
+                    if (++polls > kSpinLimit) {
+                        ok = 0;
+                        __hip_atomic_store(&L.ctl[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
                 }
             }
+            s_ok = ok;
         }
-    }
+        // also: the LDS readers of the last gram chunk (group 0) and of the previous group's
+        // planes are done
+        __syncthreads();
+        const bool ok = s_ok != 0;
 
-    // ---- publish M_f
-    {
-        const __amdgpu_buffer_rsrc_t rd =
-            buffer_over(L.chain + ((int64_t)(f & 1) * BH + bh) * D * D, D * D * 4);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bacc[nb][cb]), rd,
-                                                       (((wave * NB + nb) * CB + cb) * 64 + lane) * 16, 0,
-                                                       kCoherent);
-        if (f == F - 1 && L.state_out) {
-            float* so = L.state_out + (int64_t)bh * D * D;
+        // M_{f-1}[n][c] at this lane's C-layout positions: n = nw + 16 nb + 4 g + q,
+        // c = 16 cb + r, for the group's column blocks; all loads issued before any is used
+        f32x4 mp[NB][CPG];
+        if (f > 0) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
+                for (int j = 0; j < CPG; ++j)
+                    mp[nb][j] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   rs, (((wave * NB + nb) * CB + grp * CPG + j) * 64 + lane) * 16, 0, kCoherent));
+        } else {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) so[(nw + 16 * nb + 4 * g + q) * D + 16 * cb + r16] = bacc[nb][cb][q];
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int j = 0; j < CPG; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        mp[nb][j][q] = L.state_in ? L.state_in[((int64_t)bh * D + nw + 16 * nb + 4 * g + q) * D +
+                                                               16 * (grp * CPG + j) + r16]
+                                                  : 0.f;
         }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int kb = (nw + 16 * nb) >> 4;
+            const int pos = 32 * (kb >> 1) + 8 * g + 4 * (kb & 1);
+#pragma unroll
+            for (int j = 0; j < CPG; ++j) {
+                const int cb = grp * CPG + j;
+                const int c = 16 * cb + r16;
+                const float nan = __builtin_nanf("");
+                const f32x4 m = ok ? mp[nb][j] : f32x4{nan, nan, nan, nan};
+                bacc[nb][cb] += gm * m;
+                if constexpr (DELTA) store_split4(Ph + c * MR + pos, Pl + c * MR + pos, m);
+            }
+        }
+        if constexpr (DELTA) {
+            __syncthreads();
+            // three passes (hi.hi, hi.lo, lo.hi) per k step, each over all of the group's
+            // accumulators, so that consecutive MFMAs never depend on each other
+#pragma unroll
+            for (int ks = 0; ks < KB / 2; ++ks) {
+                bf16x8 ah[NB], al[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    ah[nb] = __builtin_bit_cast(bf16x8, u32x4{gh[2 * ks][nb][0], gh[2 * ks][nb][1],
+                                                             gh[2 * ks + 1][nb][0], gh[2 * ks + 1][nb][1]});
+                    al[nb] = __builtin_bit_cast(bf16x8, u32x4{gl[2 * ks][nb][0], gl[2 * ks][nb][1],
+                                                             gl[2 * ks + 1][nb][0], gl[2 * ks + 1][nb][1]});
+                }
+#pragma unroll
+                for (int pass = 0; pass < 3; ++pass) {
+                    const bf16* plane = pass == 1 ? Pl : Ph;
+#pragma unroll
+                    for (int j = 0; j < CPG; ++j) {
+                        const int cb = grp * CPG + j;
+                        const bf16x8 m = ld_frag<bf16>(plane + (16 * cb + r16) * MR + 32 * ks + 8 * g);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            bacc[nb][cb] = MM::run(pass == 2 ? al[nb] : ah[nb], m, bacc[nb][cb]);
+                    }
+                }
+            }
+        }
+        // publish group grp of M_f
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int j = 0; j < CPG; ++j) {
+                const int cb = grp * CPG + j;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, bacc[nb][cb]), rd,
+                                                       (((wave * NB + nb) * CB + cb) * 64 + lane) * 16, 0,
+                                                       kCoherent);
+            }
+        __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's state stores are done
+        __syncthreads();  // ... and every wave's; also: the group's planes are no longer read
+        if (tid == 0) __hip_atomic_store(flags + grp, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's state stores are done
-    __syncthreads();  // ... and every wave's; also: the planes are no longer read
-    if (tid == 0) __hip_atomic_store(flag, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (f == F - 1 && L.state_out) {
+        float* so = L.state_out + (int64_t)bh * D * D;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) so[(nw + 16 * nb + 4 * g + q) * D + 16 * cb + r16] = bacc[nb][cb][q];
+    }
 
     // ---- 3. O_f = Q_f M_f (as output_body, with bf16(M_f)^T from LDS)
     bf16* Mt = (bf16*)lds;  // [c][n]
@@ -1171,7 +1181,7 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
         break;
     }
     case K_FUSED_RESET: {
-        const int n = 2 + BH;
+        const int n = 2 + BH * kChainGroups;
         hipLaunchKernelGGL(fused_reset_kernel, dim3((n + NT - 1) / NT), dim3(NT), 0, s, L.ctl, n);
         break;
     }
