@@ -47,6 +47,10 @@ def _bind(path):
                                     + [ctypes.c_int])
     lib.gdn_oracle_step.restype = ctypes.c_int
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
+    if hasattr(lib, "gdn_oracle_backward"):
+        lib.gdn_oracle_backward.argtypes = ([ctypes.c_int] * 6 + [ctypes.c_double] + [_dp] * 14
+                                            + [ctypes.c_int])
+        lib.gdn_oracle_backward.restype = ctypes.c_int
     return lib
 
 
@@ -140,3 +144,32 @@ def step(q, k, v, gamma, beta, state_in, *, commit=True, use_delta=True, key_sca
     if rc != 0:
         raise RuntimeError("gdn_oracle_step failed with code %d" % rc)
     return o, so
+
+
+def backward(q, k, v, gamma, beta, state_in, d_o, d_state_out=None, *, use_delta=True,
+             key_scale=None, nthreads=0, lib=None):
+    """Gradients of the forward for upstream gradients d_o = dL/dO [B, H, F*S, D] and
+    d_state_out = dL/dstate_out [B, H, D, D] (None: zero).
+
+    Returns (dq, dk, dv [B, H, F*S, D], dgamma, dbeta [B, H, F], d_state_in [B, H, D, D]) as
+    fp64 arrays; d_state_in is the gradient with respect to state_in (a zero initial state when
+    state_in is None).
+    """
+    q, k, v, gamma, beta, d_o = map(_f64, (q, k, v, gamma, beta, d_o))
+    B, H, T, D = q.shape
+    F = gamma.shape[2]
+    assert T % F == 0, "token count must be a whole number of frames"
+    S = T // F
+    st = None if state_in is None else _f64(state_in)
+    dso = None if d_state_out is None else _f64(d_state_out)
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    dg, db = np.empty_like(gamma), np.empty_like(gamma)
+    dsi = np.empty((B, H, D, D), dtype=np.float64)
+    c = 0.0 if key_scale is None else float(key_scale)
+    rc = (lib or _load()).gdn_oracle_backward(
+        B, H, D, S, F, int(bool(use_delta)), c, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+        _ptr(beta), _ptr(st), _ptr(d_o), _ptr(dso), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+        _ptr(db), _ptr(dsi), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_backward failed with code %d" % rc)
+    return dq, dk, dv, dg, db, dsi

@@ -169,6 +169,191 @@ int gdn_oracle_step(int B, int H, int D, int S, int use_delta, double key_scale,
                               state_in, o, state_out, nthreads);
 }
 
+/*
+ * Backward (gradients) of the forward above for a scalar loss L whose gradients with respect
+ * to the outputs are given: d_o = dL/dO [B][H][F*S][D] and d_state_out = dL/dstate_out
+ * [B][H][D][D] (NULL: zero). Returns dq, dk, dv [B][H][F*S][D], dgamma, dbeta [B][H][F] and,
+ * when d_state_in is not NULL, dL/dstate_in [B][H][D][D]. key_scale is a constant (no gradient).
+ *
+ * The pages define only the forward; this is its reverse-mode derivative, written as the adjoint
+ * of each forward line, visited in reverse order. For frame f, with G = dL/dM_f accumulated from
+ * later frames and from state_out:
+ *     O_f = Q_f M_f              ->  dQ_f = dO_f M_f^T ;  G += Q_f^T dO_f
+ *     M_f = gamma M + beta U     ->  dU = beta G ;  dgamma_f = <G, M> ;  dbeta_f = <G, U> ;
+ *                                    G_prev = gamma G
+ *     U = Kt^T R                 ->  dKt = R dU^T ;  dR = Kt dU
+ *     R = V - gamma P            ->  dV_f = dR ;  dP = -gamma dR ;  dgamma_f -= <dR, P>
+ *                                    (R = V without the delta term: dV_f = dR, no dP)
+ *     P = Kt M                   ->  dKt += dP M^T ;  G_prev += Kt^T dP
+ *     Kt = c K_f                 ->  dK_f = c dKt
+ * where M is the state before frame f. The forward states are recomputed first and kept.
+ */
+static void gdn_head_backward(int D, int S, int F, int use_delta, double c,
+                              const double* q, const double* k, const double* v,
+                              const double* gamma, const double* beta, const double* d_o,
+                              double* Ms, double* G, double* dq, double* dk, double* dv,
+                              double* dgamma, double* dbeta,
+                              double* Kt, double* P, double* R, double* U, double* dU,
+                              double* dR, double* dKt, double* Gp)
+{
+    const size_t DD = (size_t)D * D;
+    /* forward states: Ms[0] = state before frame 0, Ms[f + 1] = state after frame f */
+    for (int f = 0; f < F; ++f) {
+        const double* Kf = k + (size_t)f * S * D;
+        const double* Vf = v + (size_t)f * S * D;
+        const double* M = Ms + (size_t)f * DD;
+        double* Mn = Ms + (size_t)(f + 1) * DD;
+        for (size_t e = 0; e < (size_t)S * D; ++e) Kt[e] = c * Kf[e];
+        for (int s = 0; s < S; ++s)
+            for (int j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < D; ++i) acc += Kt[(size_t)s * D + i] * M[(size_t)i * D + j];
+                R[(size_t)s * D + j] = use_delta ? Vf[(size_t)s * D + j] - gamma[f] * acc
+                                                 : Vf[(size_t)s * D + j];
+            }
+        for (int i = 0; i < D; ++i)
+            for (int j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int s = 0; s < S; ++s) acc += Kt[(size_t)s * D + i] * R[(size_t)s * D + j];
+                Mn[(size_t)i * D + j] = gamma[f] * M[(size_t)i * D + j] + beta[f] * acc;
+            }
+    }
+
+    for (int f = F - 1; f >= 0; --f) {
+        const double* Qf = q + (size_t)f * S * D;
+        const double* Kf = k + (size_t)f * S * D;
+        const double* Vf = v + (size_t)f * S * D;
+        const double* dOf = d_o + (size_t)f * S * D;
+        const double* M = Ms + (size_t)f * DD;         /* state before frame f */
+        const double* Mf = Ms + (size_t)(f + 1) * DD;  /* state after frame f */
+        const double g = gamma[f], bt = beta[f];
+
+        /* O_f = Q_f M_f */
+        for (int s = 0; s < S; ++s)
+            for (int i = 0; i < D; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < D; ++j) acc += dOf[(size_t)s * D + j] * Mf[(size_t)i * D + j];
+                dq[(size_t)f * S * D + (size_t)s * D + i] = acc;
+            }
+        for (int i = 0; i < D; ++i)
+            for (int j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int s = 0; s < S; ++s) acc += Qf[(size_t)s * D + i] * dOf[(size_t)s * D + j];
+                G[(size_t)i * D + j] += acc;
+            }
+
+        /* recompute the frame's intermediates: Kt, P, R, U */
+        for (size_t e = 0; e < (size_t)S * D; ++e) Kt[e] = c * Kf[e];
+        for (int s = 0; s < S; ++s)
+            for (int j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < D; ++i) acc += Kt[(size_t)s * D + i] * M[(size_t)i * D + j];
+                P[(size_t)s * D + j] = acc;
+                R[(size_t)s * D + j] = use_delta ? Vf[(size_t)s * D + j] - g * acc : Vf[(size_t)s * D + j];
+            }
+        for (int i = 0; i < D; ++i)
+            for (int j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int s = 0; s < S; ++s) acc += Kt[(size_t)s * D + i] * R[(size_t)s * D + j];
+                U[(size_t)i * D + j] = acc;
+            }
+
+        /* M_f = gamma M + beta U */
+        double dg = 0.0, db = 0.0;
+        for (size_t e = 0; e < DD; ++e) {
+            dU[e] = bt * G[e];
+            dg += G[e] * M[e];
+            db += G[e] * U[e];
+            Gp[e] = g * G[e];
+        }
+
+        /* U = Kt^T R */
+        for (int s = 0; s < S; ++s)
+            for (int i = 0; i < D; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < D; ++j) acc += R[(size_t)s * D + j] * dU[(size_t)i * D + j];
+                dKt[(size_t)s * D + i] = acc;
+            }
+        for (int s = 0; s < S; ++s)
+            for (int j = 0; j < D; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < D; ++i) acc += Kt[(size_t)s * D + i] * dU[(size_t)i * D + j];
+                dR[(size_t)s * D + j] = acc;
+            }
+
+        /* R = V - gamma P */
+        for (size_t e = 0; e < (size_t)S * D; ++e) dv[(size_t)f * S * D + e] = dR[e];
+        if (use_delta) {
+            for (size_t e = 0; e < (size_t)S * D; ++e) dg -= dR[e] * P[e];
+            /* P = Kt M with dP = -gamma dR */
+            for (int s = 0; s < S; ++s)
+                for (int i = 0; i < D; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < D; ++j) acc += -g * dR[(size_t)s * D + j] * M[(size_t)i * D + j];
+                    dKt[(size_t)s * D + i] += acc;
+                }
+            for (int i = 0; i < D; ++i)
+                for (int j = 0; j < D; ++j) {
+                    double acc = 0.0;
+                    for (int s = 0; s < S; ++s) acc += Kt[(size_t)s * D + i] * (-g * dR[(size_t)s * D + j]);
+                    Gp[(size_t)i * D + j] += acc;
+                }
+        }
+
+        /* Kt = c K_f */
+        for (size_t e = 0; e < (size_t)S * D; ++e) dk[(size_t)f * S * D + e] = c * dKt[e];
+        dgamma[f] = dg;
+        dbeta[f] = db;
+        memcpy(G, Gp, DD * sizeof(double));
+    }
+}
+
+int gdn_oracle_backward(int B, int H, int D, int S, int F, int use_delta, double key_scale,
+                        const double* q, const double* k, const double* v,
+                        const double* gamma, const double* beta, const double* state_in,
+                        const double* d_o, const double* d_state_out,
+                        double* dq, double* dk, double* dv, double* dgamma, double* dbeta,
+                        double* d_state_in, int nthreads)
+{
+    if (B < 1 || H < 1 || D < 1 || S < 1 || F < 1) return 1;
+    if (!q || !k || !v || !gamma || !beta || !d_o || !dq || !dk || !dv || !dgamma || !dbeta)
+        return 2;
+    const double c = key_scale > 0.0 ? key_scale : 1.0 / sqrt((double)D * (double)S);
+    const int nbh = B * H;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1) reduction(| : failed)
+#endif
+    for (int bh = 0; bh < nbh; ++bh) {
+        const size_t tok = (size_t)F * S * D, DD = (size_t)D * D, SD = (size_t)S * D;
+        double* Ms = (double*)calloc((size_t)(F + 1) * DD, sizeof(double));
+        double* G = (double*)calloc(DD, sizeof(double));
+        double* U = (double*)malloc(DD * sizeof(double));
+        double* dU = (double*)malloc(DD * sizeof(double));
+        double* Gp = (double*)malloc(DD * sizeof(double));
+        double* Kt = (double*)malloc(SD * sizeof(double));
+        double* P = (double*)malloc(SD * sizeof(double));
+        double* R = (double*)malloc(SD * sizeof(double));
+        double* dR = (double*)malloc(SD * sizeof(double));
+        double* dKt = (double*)malloc(SD * sizeof(double));
+        if (!Ms || !G || !U || !dU || !Gp || !Kt || !P || !R || !dR || !dKt) {
+            failed |= 1;
+        } else {
+            if (state_in) memcpy(Ms, state_in + (size_t)bh * DD, DD * sizeof(double));
+            if (d_state_out) memcpy(G, d_state_out + (size_t)bh * DD, DD * sizeof(double));
+            gdn_head_backward(D, S, F, use_delta, c, q + bh * tok, k + bh * tok, v + bh * tok,
+                              gamma + (size_t)bh * F, beta + (size_t)bh * F, d_o + bh * tok, Ms, G,
+                              dq + bh * tok, dk + bh * tok, dv + bh * tok, dgamma + (size_t)bh * F,
+                              dbeta + (size_t)bh * F, Kt, P, R, U, dU, dR, dKt, Gp);
+            if (d_state_in) memcpy(d_state_in + (size_t)bh * DD, G, DD * sizeof(double));
+        }
+        free(Ms); free(G); free(U); free(dU); free(Gp); free(Kt); free(P); free(R); free(dR); free(dKt);
+    }
+    (void)nthreads;
+    return failed ? 3 : 0;
+}
+
 int gdn_oracle_max_threads(void)
 {
 #ifdef _OPENMP
