@@ -84,9 +84,12 @@ MUTANTS = [
 def test_pins_catch_planted_mistake(mutant):
     _, old, new = mutant
     src = oracle.source_text()
-    assert src.count(old) == 1, "mutation anchor not found exactly once: %r" % old
+    # plant the mistake in the forward code only (the backward section repeats some lines)
+    cut = src.index("/*\n * Backward (gradients) of the forward")
+    fwd, rest = src[:cut], src[cut:]
+    assert fwd.count(old) == 1, "mutation anchor not found exactly once: %r" % old
     with tempfile.TemporaryDirectory() as tmp:
-        lib = oracle.load_variant(src.replace(old, new), tmp)
+        lib = oracle.load_variant(fwd.replace(old, new) + rest, tmp)
         caught = []
         for pin in pins.ALL_PINS:
             try:
