@@ -83,6 +83,8 @@ def parse():
                     help="target CPU time (wall x threads) of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--stream-frames", type=int, default=240)
     ap.add_argument("--schedule", default="auto", choices=["auto", "staged", "fused"],
                     help="forward schedule (auto: the library's choice)")
@@ -207,6 +209,69 @@ def stream_mode(dev, nframes, ev, stream):
             "frames_per_s": round(nframes / (total / 1e3), 1),
             "pass_us_median": round(float(np.median(lat)) * 1e3 / w.passes, 2),
             "pass_kernel_us_median": {k_: round(float(np.median(v_)), 2) for k_, v_ in kus.items()}}
+
+
+def backward_mode(w, dev, steps, ev, stream):
+    """Training direction: one gdn_backward_framewise call over the whole workload (forward
+    states recomputed inside), for upstream gradients dO of the output's shape."""
+    import torch
+    import frame_wise_gated_libgdn_amd as gdn
+    import gdn_synth
+    gen = gdn_synth.TorchGen(dev)
+    q, k, v = gdn_synth.qkv_torch(w, dev, gen=gen)
+    g, b = gdn_synth.gates_torch(w, dev)
+    d_o = torch.empty_like(q)
+    for bb in range(w.B):
+        for hh in range(w.H):   # seeded like Q, from another seed
+            gen.fill_normal(d_o[bb, hh], w.seed + 1000, gdn_synth.TID_Q, bb, hh, 0, w.S, w.D)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    p = gdn.Problem(w.B, w.H, w.D, w.S, w.F, gdn.GDN_BF16, int(w.use_delta), 0.0, *q.stride()[:3],
+                    *d_o.stride()[:3])
+    ws = torch.empty(gdn.workspace_size(p, 2), dtype=torch.uint8, device=dev)
+
+    def call():
+        return gdn.backward_framewise(q, k, v, g, b, d_o, use_delta=w.use_delta, dq=dq, dk=dk,
+                                      dv=dv, workspace=ws, stream=stream)
+
+    probe = [ev.new() for _ in range(2 * 16)]
+    gdn.set_trace(probe)
+    call()
+    plan = gdn.read_trace()
+    gdn.set_trace(None)
+    call()
+    torch.cuda.synchronize()
+    nl = len(plan)
+    trace = [[ev.new() for _ in range(2 * nl)] for _ in range(steps)]
+    t0, t1 = ev.new(), ev.new()
+    sh = stream.cuda_stream
+    ev.record(t0, sh)
+    for i in range(steps):
+        gdn.set_trace(trace[i])
+        call()
+    gdn.set_trace(None)
+    ev.record(t1, sh)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    kms = {}
+    for i in range(steps):
+        for j, (kname, _, _) in enumerate(plan):
+            kms[kname] = kms.get(kname, 0.0) + ev.ms(trace[i][2 * j], trace[i][2 * j + 1]) / steps
+    esz = w.elem_bytes()
+    bytes_alg = 7 * w.B * w.H * w.F * w.S * w.D * esz   # Q, K, V, dO read; dQ, dK, dV written
+    flops_alg = (10 if w.use_delta else 6) * w.B * w.H * w.F * w.S * w.D * w.D
+    t_roof = max(bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    bwd_ms = kms.get("bwd", 0.0)
+    bwd_bytes = 6 * w.B * w.H * w.F * w.S * w.D * esz   # per-frame gradient kernel: K, V, dO, dQ, dK, dV
+    del q, k, v, d_o, dq, dk, dv, ws
+    return {"workload": w.name, "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(w.B * w.F * w.S / (ms * 1e-3), 1),
+            "launches": [k_ for k_, _, _ in plan],
+            "kernel_ms_per_call": {k_: round(x, 4) for k_, x in kms.items()},
+            "call": {"bytes_alg_gb": round(bytes_alg / 1e9, 3), "t_roof_ms": round(t_roof, 4),
+                     "frac_of_roofline": round(t_roof / ms, 4),
+                     "achieved_gb_s": round(bytes_alg / (ms * 1e-3) / 1e9, 1)},
+            "bwd_kernel": {"achieved_gb_s": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1) if bwd_ms else None,
+                           "frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if bwd_ms else None}}
 
 
 def main():
@@ -343,6 +408,13 @@ def main():
         result["stream"] = stream_mode(dev, args.stream_frames, ev2, sh)
         ev2.close()
         log("stream done: %s" % result["stream"]["frame_latency_ms"])
+    if not args.no_backward and w.dtype == "bf16" and w.D in (64, 128):
+        ev3 = HipEvents()
+        log("backward: %d calls" % args.backward_steps)
+        result["backward"] = backward_mode(w, dev, args.backward_steps, ev3, torch.cuda.current_stream())
+        ev3.close()
+        torch.cuda.empty_cache()
+        log("backward done: %.3f ms/call" % result["backward"]["ms_per_call"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

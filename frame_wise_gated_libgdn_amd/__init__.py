@@ -16,7 +16,7 @@ import os
 import threading
 
 __all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "forward_framewise",
-           "step_frame", "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES",
+           "step_frame", "backward_framewise", "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES",
            "GDN_F32", "GDN_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +27,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
           4: "GDN_ERR_STRIDE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
           8: "GDN_ERR_HIP"}
 KERNEL_NAMES = {0: "products", 1: "combine", 2: "scan", 3: "step_partial", 4: "step_reduce",
-                5: "fused_reset", 6: "fused"}
+                5: "fused_reset", 6: "fused", 7: "scan_bwd", 8: "bwd"}
 SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
 
 
@@ -83,6 +83,8 @@ def load():
             for fn in (lib.gdn_forward_framewise, lib.gdn_step_frame):
                 fn.argtypes = [P] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
                 fn.restype = ctypes.c_int
+            lib.gdn_backward_framewise.argtypes = [P] + [_vp] * 14 + [_vp, ctypes.c_size_t, _vp]
+            lib.gdn_backward_framewise.restype = ctypes.c_int
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_last_error_message.restype = ctypes.c_char_p
@@ -131,9 +133,10 @@ def _check(code):
         raise GdnError(code, load().gdn_last_error_message().decode(errors="replace"))
 
 
-def workspace_size(p: Problem, step_mode: bool) -> int:
+def workspace_size(p: Problem, mode) -> int:
+    """mode: 0 / False forward, 1 / True step, 2 backward."""
     n = ctypes.c_size_t(0)
-    _check(load().gdn_workspace_size(ctypes.byref(p), int(bool(step_mode)), ctypes.byref(n)))
+    _check(load().gdn_workspace_size(ctypes.byref(p), int(mode), ctypes.byref(n)))
     return int(n.value)
 
 
@@ -251,3 +254,45 @@ def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_
                                  _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out), _ptr(ws),
                                  nbytes, _stream(stream)))
     return out, state_out
+
+
+def backward_framewise(q, k, v, gamma, beta, d_o, state=None, d_state_out=None, *,
+                       use_delta=True, key_scale=None, dq=None, dk=None, dv=None,
+                       return_state_grad=True, workspace=None, stream=None):
+    """Gradients of forward_framewise. q, k, v [B, H, F*S, D] (bf16, D = 64 or 128, same
+    strides); d_o: dL/dO with o's shape (any strides with D contiguous); gamma, beta fp32
+    [B, H, F]; state, d_state_out fp32 [B, H, D, D] or None.
+    Returns (dq, dk, dv, dgamma, dbeta, d_state_in); d_state_in is None when
+    return_state_grad is False."""
+    import torch
+    B, H, T, D = q.shape
+    F = gamma.shape[2]
+    if k.stride() != q.stride() or v.stride() != q.stride() or k.shape != q.shape \
+            or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype \
+            or d_o.shape != q.shape or d_o.dtype != q.dtype:
+        raise GdnError(4, "q, k and v must share shape, dtype and strides; d_o must match their "
+                          "shape and dtype")
+    if d_o.stride(3) != 1:
+        raise GdnError(4, "the head dimension of d_o must be contiguous")
+
+    def like_q(t):
+        if t is not None:
+            return t
+        return torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+
+    dq, dk, dv = like_q(dq), like_q(dk), like_q(dv)
+    dg = torch.empty((B, H, F), dtype=torch.float32, device=q.device)
+    db = torch.empty((B, H, F), dtype=torch.float32, device=q.device)
+    dsi = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device) \
+        if return_state_grad else None
+    _check_f32("gamma", gamma, (B, H, F))
+    _check_f32("beta", beta, (B, H, F))
+    _check_f32("state", state, (B, H, D, D))
+    _check_f32("d_state_out", d_state_out, (B, H, D, D))
+    p = _problem(q, d_o, F, use_delta, key_scale)
+    ws, nbytes = _workspace(p, 2, workspace, q.device)
+    _check(load().gdn_backward_framewise(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(state),
+        _ptr(d_o), _ptr(d_state_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db),
+        _ptr(dsi), _ptr(ws), nbytes, _stream(stream)))
+    return dq, dk, dv, dg, db, dsi

@@ -28,12 +28,17 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Schedule and splits chosen from the problem only, so that the workspace size is a pure
 // function of it.
 struct Plan {
+    int mode;                   // 0 forward, 1 step, 2 backward
     bool fused;                 // forward: fused single pass (else staged)
     int nsplit, split_tokens;   // partial-product kernel
     int nchunk, chunk_tokens;   // output kernel
     size_t canon_bytes, part_bytes, mt_bytes;   // staged forward and step
     size_t ctl_bytes, chain_bytes;              // fused forward
+    size_t crec_bytes, gt_bytes;                // backward
     size_t total() const {
+        if (mode == 2)
+            return align256(canon_bytes) + align256(part_bytes) + align256(mt_bytes) +
+                   align256(crec_bytes) + gt_bytes;
         return fused ? align256(ctl_bytes) + chain_bytes
                      : align256(canon_bytes) + align256(part_bytes) + mt_bytes;
     }
@@ -51,9 +56,12 @@ bool choose_fused(const gdn_problem& p, int step_mode) {
 
 constexpr int kTargetGroups = 2048;  // workgroups wanted per parallel launch (256 CUs x 8)
 
-Plan make_plan(const gdn_problem& p, int step_mode) {
+// mode: 0 forward, 1 step, 2 backward
+Plan make_plan(const gdn_problem& p, int mode) {
+    const int step_mode = mode == 1;
     Plan pl{};
-    pl.fused = choose_fused(p, step_mode);
+    pl.mode = mode;
+    pl.fused = mode == 0 && choose_fused(p, 0);
     const int64_t D = p.head_dim, S = p.tokens_per_frame;
     const int64_t BH = (int64_t)p.batch * p.heads;
     const int64_t F = step_mode ? 1 : p.frames;
@@ -92,10 +100,18 @@ Plan make_plan(const gdn_problem& p, int step_mode) {
     // fp32 state buffers per (b, h)
     pl.ctl_bytes = (size_t)(2 + BH * gdn::kChainGroups) * 4;
     pl.chain_bytes = (size_t)(2 * BH * D * D * 4);
+    if (mode == 2) {
+        // forward states and state gradients get F + 1 slots (slot 0: initial state / its
+        // gradient); the C_f records hold one fp32 D x D matrix each
+        pl.mt_bytes = (size_t)(BH * (F + 1) * D * D * esz);
+        pl.crec_bytes = (size_t)(BH * F * D * D * 4);
+        pl.gt_bytes = pl.mt_bytes;
+    }
     return pl;
 }
 
-gdn_status check_sizes(const gdn_problem* p, int step_mode) {
+gdn_status check_sizes(const gdn_problem* p, int mode) {
+    const int step_mode = mode == 1;
     if (!p) return fail(GDN_ERR_NULL, "problem descriptor is NULL");
     if (p->batch < 1 || p->heads < 1 || p->tokens_per_frame < 1 || (!step_mode && p->frames < 1))
         return fail(GDN_ERR_SHAPE, "sizes must be >= 1 (B=%d H=%d S=%d F=%d)", p->batch, p->heads,
@@ -107,9 +123,11 @@ gdn_status check_sizes(const gdn_problem* p, int step_mode) {
         return fail(GDN_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
     if (p->schedule < GDN_SCHEDULE_AUTO || p->schedule > GDN_SCHEDULE_FUSED)
         return fail(GDN_ERR_SHAPE, "schedule must be 0, 1 or 2, got %d", p->schedule);
-    if (!step_mode && p->schedule == GDN_SCHEDULE_FUSED &&
+    if (mode == 0 && p->schedule == GDN_SCHEDULE_FUSED &&
         !gdn::fused_supported(p->dtype == GDN_BF16, D))
         return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs bf16 data and D = 64 or 128");
+    if (mode == 2 && !gdn::backward_supported(p->dtype == GDN_BF16, D))
+        return fail(GDN_ERR_UNSUPPORTED, "the backward needs bf16 data and D = 64 or 128");
     const int64_t F = step_mode ? 1 : p->frames;
     const int64_t BH = (int64_t)p->batch * p->heads;
     // grid sizes: BH * F * splits must fit a 1-D grid; token indices f*S+s must fit int32 math
@@ -215,6 +233,7 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     L.q = q; L.k = k; L.v = v; L.o = o;
     L.sb = p->qkv_stride_b; L.sh = p->qkv_stride_h; L.st = p->qkv_stride_t;
     L.ob = p->o_stride_b; L.oh = p->o_stride_h; L.ot = p->o_stride_t;
+    L.xsb = L.sb; L.xsh = L.sh; L.xst = L.st;
     L.gamma = gamma; L.beta = beta; L.state_in = state_in; L.state_out = state_out;
     if (pl.fused) {
         L.ctl = (int*)ws;
@@ -237,16 +256,104 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     return GDN_OK;
 }
 
+gdn_status run_bwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                   const float* gamma, const float* beta, const float* state_in, const void* d_o,
+                   const float* d_state_out, void* dq, void* dk, void* dv, float* dgamma,
+                   float* dbeta, float* d_state_in, void* ws, size_t ws_bytes, void* stream) {
+    g_msg[0] = '\0';
+    gdn_status s = check_sizes(p, 2);
+    if (s != GDN_OK) return s;
+    const int64_t B = p->batch, H = p->heads, D = p->head_dim, S = p->tokens_per_frame;
+    const int64_t F = p->frames, T = F * S;
+    const int64_t esz = p->dtype == GDN_BF16 ? 2 : 4;
+    if (!q || !k || !v || !gamma || !beta || !d_o || !dq || !dk || !dv || !dgamma || !dbeta)
+        return fail(GDN_ERR_NULL, "q, k, v, gamma, beta, d_o and every gradient but d_state_in are required");
+    if (!layout_ok(B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t))
+        return fail(GDN_ERR_STRIDE, "q/k/v strides (%lld, %lld, %lld) overlap rows or are negative",
+                    (long long)p->qkv_stride_b, (long long)p->qkv_stride_h, (long long)p->qkv_stride_t);
+    if (!layout_ok(B, H, T, D, p->o_stride_b, p->o_stride_h, p->o_stride_t))
+        return fail(GDN_ERR_STRIDE, "o strides (%lld, %lld, %lld) overlap rows or are negative",
+                    (long long)p->o_stride_b, (long long)p->o_stride_h, (long long)p->o_stride_t);
+    for (const void* ptr : {q, k, v, d_o, (const void*)dq, (const void*)dk, (const void*)dv})
+        if (!aligned(ptr, 16)) return fail(GDN_ERR_ALIGN, "q, k, v, d_o and dq, dk, dv must be 16-byte aligned");
+    const int64_t strides[6] = {p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t,
+                                p->o_stride_b,   p->o_stride_h,   p->o_stride_t};
+    for (int64_t st : strides)
+        if (st % 8) return fail(GDN_ERR_ALIGN, "strides must be multiples of 8 elements");
+    for (const void* ptr : {(const void*)gamma, (const void*)beta, (const void*)state_in,
+                            (const void*)d_state_out, (const void*)dgamma, (const void*)dbeta,
+                            (const void*)d_state_in})
+        if (ptr && !aligned(ptr, 4)) return fail(GDN_ERR_ALIGN, "gates, states and their gradients must be 4-byte aligned");
+
+    const Plan pl = make_plan(*p, 2);
+    const size_t need = pl.total();
+    auto qkv_span = [&](const void* x) {
+        return span_of(x, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
+    };
+    const Span none = {nullptr, nullptr};
+    const Span in[] = {qkv_span(q), qkv_span(k), qkv_span(v),
+                       {(const char*)gamma, (const char*)(gamma + B * H * F)},
+                       {(const char*)beta, (const char*)(beta + B * H * F)},
+                       state_in ? Span{(const char*)state_in, (const char*)(state_in + B * H * D * D)} : none,
+                       span_of(d_o, B, H, T, D, p->o_stride_b, p->o_stride_h, p->o_stride_t, esz),
+                       d_state_out ? Span{(const char*)d_state_out, (const char*)(d_state_out + B * H * D * D)} : none,
+                       ws ? Span{(const char*)ws, (const char*)ws + need} : none};
+    const Span dsi = d_state_in ? Span{(const char*)d_state_in, (const char*)(d_state_in + B * H * D * D)} : none;
+    const Span out[] = {qkv_span(dq), qkv_span(dk), qkv_span(dv),
+                        {(const char*)dgamma, (const char*)(dgamma + B * H * F)},
+                        {(const char*)dbeta, (const char*)(dbeta + B * H * F)}, dsi};
+    const int nin = sizeof(in) / sizeof(in[0]), nout = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j) {
+            // the state gradient may be computed in place (d_state_in == d_state_out)
+            if (i == nout - 1 && j == 7 && d_state_in && (const void*)d_state_in == (const void*)d_state_out)
+                continue;
+            if (overlap(out[i], in[j])) return fail(GDN_ERR_ALIAS, "a gradient output overlaps an input or the workspace");
+        }
+        for (int j = 0; j < i; ++j)
+            if (overlap(out[i], out[j])) return fail(GDN_ERR_ALIAS, "two gradient outputs overlap");
+    }
+    if (!ws || ws_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    ws ? ws_bytes : (size_t)0);
+    if (!aligned(ws, 256)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+    gdn::Launch L{};
+    L.B = (int)B; L.H = (int)H; L.D = (int)D; L.S = (int)S; L.F = (int)F;
+    L.bf16 = p->dtype == GDN_BF16;
+    L.use_delta = p->use_delta != 0;
+    L.c = p->key_scale > 0.f ? p->key_scale : (float)(1.0 / std::sqrt((double)D * (double)S));
+    L.q = q; L.k = k; L.v = v;
+    L.sb = p->qkv_stride_b; L.sh = p->qkv_stride_h; L.st = p->qkv_stride_t;
+    L.ob = p->o_stride_b; L.oh = p->o_stride_h; L.ot = p->o_stride_t;
+    L.xsb = L.sb; L.xsh = L.sh; L.xst = L.st;
+    L.gamma = gamma; L.beta = beta; L.state_in = state_in;
+    L.d_o = d_o; L.d_state_out = d_state_out; L.d_state_in = d_state_in;
+    L.dq = dq; L.dk = dk; L.dv = dv; L.dgamma = dgamma; L.dbeta = dbeta;
+    char* w = (char*)ws;
+    L.canon = w;                       w += align256(pl.canon_bytes);
+    L.part = (float*)w;                w += align256(pl.part_bytes);
+    L.mt = w;                          w += align256(pl.mt_bytes);
+    L.crec = w;                        w += align256(pl.crec_bytes);
+    L.gt = w;
+    L.nsplit = pl.nsplit; L.split_tokens = pl.split_tokens;
+    L.nchunk = pl.nchunk; L.chunk_tokens = pl.chunk_tokens;
+    const hipError_t e = gdn::run_backward(L, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-gdn_status gdn_workspace_size(const gdn_problem* p, int step_mode, size_t* bytes_out) {
+gdn_status gdn_workspace_size(const gdn_problem* p, int mode, size_t* bytes_out) {
     g_msg[0] = '\0';
     if (!bytes_out) return fail(GDN_ERR_NULL, "bytes_out is NULL");
-    gdn_status s = check_sizes(p, step_mode);
+    if (mode < 0 || mode > 2) return fail(GDN_ERR_SHAPE, "mode must be 0, 1 or 2, got %d", mode);
+    gdn_status s = check_sizes(p, mode);
     if (s != GDN_OK) return s;
-    const Plan pl = make_plan(*p, step_mode);
+    const Plan pl = make_plan(*p, mode);
     *bytes_out = pl.total();
     return GDN_OK;
 }
@@ -265,6 +372,16 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                           void* hip_stream) {
     return run(1, p, q, k, v, gamma, beta, state_in, o, state_out, workspace, workspace_bytes,
                hip_stream);
+}
+
+gdn_status gdn_backward_framewise(const gdn_problem* p, const void* q, const void* k,
+                                  const void* v, const float* gamma, const float* beta,
+                                  const float* state_in, const void* d_o,
+                                  const float* d_state_out, void* dq, void* dk, void* dv,
+                                  float* dgamma, float* dbeta, float* d_state_in,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return run_bwd(p, q, k, v, gamma, beta, state_in, d_o, d_state_out, dq, dk, dv, dgamma, dbeta,
+                   d_state_in, workspace, workspace_bytes, hip_stream);
 }
 
 gdn_status gdn_set_trace(void* const* events, int pairs) {

@@ -19,6 +19,8 @@ struct Launch {
     void* o;
     int64_t sb, sh, st;  // Q/K/V strides
     int64_t ob, oh, ot;  // O strides
+    int64_t xsb, xsh, xst;  // strides of the gram products' second operand (V; dO in the backward)
+    int unit_scale;      // gram products without the beta c / gamma beta c^2 factors (backward)
     const float *gamma, *beta, *state_in;
     float* state_out;
     void* canon;         // workspace: per-frame record handed from the products kernel to the scan
@@ -35,7 +37,16 @@ struct Launch {
     // frame ranges of one launch
     int g0, gn;          // gram products (and combine) over frames [g0, g0 + gn)
     int o0, on;          // output products over frames [o0, o0 + on)
-    int s0, s1;          // scan over frames [s0, s1)
+    int s0, s1;          // scan over frames [s0, s1) (backward scan: steps)
+    int mt_lead;         // per-step scan outputs have F + mt_lead slots per (b, h); forward: the
+                         //   initial state goes to slot 0 and M_f to slot f + 1 when set
+    void* crec;          // workspace (backward): per-frame records of C_f = Q_f^T dO_f
+    void* gt;            // workspace (backward): G_f = dL/dM_f (transposed, I/O type), slot f + 1
+    const void* d_o;     // backward: dL/dO (O strides)
+    const float* d_state_out;  // backward: dL/dstate_out (NULL: zero)
+    float* d_state_in;   // backward: dL/dstate_in (NULL: not returned)
+    void *dq, *dk, *dv;  // backward: gradients of Q, K, V (Q/K/V strides)
+    float *dgamma, *dbeta;  // backward: [B][H][F]
     const float* scan_in;  // state before frame s0 (NULL: zero)
     float* scan_out;       // state after frame s1 - 1 (NULL: not stored)
 };
@@ -43,7 +54,7 @@ struct Launch {
 // Kernels the runtime can launch (also the trace kinds of the C ABI).
 enum Kernel {
     K_PRODUCTS = 0, K_COMBINE = 1, K_SCAN = 2, K_STEP_PARTIAL = 3, K_STEP_REDUCE = 4,
-    K_FUSED_RESET = 5, K_FUSED = 6
+    K_FUSED_RESET = 5, K_FUSED = 6, K_SCAN_BWD = 7, K_BWD = 8
 };
 
 // Fused forward: value-column groups pipelined through the frame chain (one flag each per (b, h)).
@@ -51,6 +62,8 @@ constexpr int kChainGroups = 4;
 
 // Whether the fused single-pass forward has a kernel for this type / head size.
 bool fused_supported(int bf16, int D);
+// Whether the backward has kernels for this type / head size.
+bool backward_supported(int bf16, int D);
 
 // Enqueue one kernel on `s`. Returns the HIP error of the launch.
 hipError_t launch_kernel(Kernel k, const Launch& L, hipStream_t s);
@@ -59,6 +72,7 @@ hipError_t launch_kernel(Kernel k, const Launch& L, hipStream_t s);
 // and of a step, all on stream `s`.
 hipError_t run_forward(const Launch& L, bool fused, hipStream_t s);
 hipError_t run_step(const Launch& L, hipStream_t s);
+hipError_t run_backward(const Launch& L, hipStream_t s);
 void set_trace(void* const* events, int pairs);
 int read_trace(gdn_trace_entry* out, int capacity);
 

@@ -124,14 +124,17 @@ template <typename T, int D, int NTH = NT> struct XStage {
     u32x4 r[PER][VE];
 
     // tokens [t0, t0 + 64) of the frame; rows at or beyond tend are zero
-    __device__ __forceinline__ void load(const T* kb, const T* vb, int64_t st, int t0, int tend,
-                                         int tid) {
+    // kb, vb: token 0 of the first and second operand; kst, vst: their token strides
+    __device__ __forceinline__ void load(const T* kb, const T* vb, int64_t kst, int64_t vst, int t0,
+                                         int tend, int tid) {
 #pragma unroll
         for (int pi = 0; pi < PER; ++pi) {
             const int blk = tid + pi * NTH;
             if (NBLK % NTH == 0 || blk < NBLK) {
                 const int fb = blk % FB, tb = blk / FB;
-                const T* base = fb < D / VE ? kb + fb * VE : vb + (fb - D / VE) * VE;
+                const bool first = fb < D / VE;
+                const T* base = first ? kb + fb * VE : vb + (fb - D / VE) * VE;
+                const int64_t st = first ? kst : vst;
 #pragma unroll
                 for (int e = 0; e < VE; ++e) {
                     const int tok = t0 + tb * VE + e;
@@ -245,9 +248,8 @@ __device__ __forceinline__ void gram_body(const Launch& L, int blk, char* lds) {
     blk /= L.nsplit;
     const int f = L.g0 + blk % L.gn, bh = blk / L.gn;
     const int b = bh / L.H, h = bh % L.H;
-    const int64_t fo = (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * L.S * L.st;
-    const T* kb = (const T*)L.k + fo;
-    const T* vb = (const T*)L.v + fo;
+    const T* kb = (const T*)L.k + (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * L.S * L.st;
+    const T* vb = (const T*)L.v + (int64_t)b * L.xsb + (int64_t)h * L.xsh + (int64_t)f * L.S * L.xst;
     const int t0 = p * L.split_tokens;
     const int t1 = min(L.S, t0 + L.split_tokens);
     const bool active = wave < WI * WJ;
@@ -260,12 +262,12 @@ __device__ __forceinline__ void gram_body(const Launch& L, int blk, char* lds) {
         for (int mj = 0; mj < MJ; ++mj) acc[mi][mj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     XStage<T, D> stg;
-    stg.load(kb, vb, L.st, t0, t1, tid);
+    stg.load(kb, vb, L.st, L.xst, t0, t1, tid);
     for (int c0 = t0; c0 < t1; c0 += X::SC) {
         __syncthreads();  // readers of the previous chunk are done
         stg.store(lds, tid);
         __syncthreads();
-        if (c0 + X::SC < t1) stg.load(kb, vb, L.st, c0 + X::SC, t1, tid);
+        if (c0 + X::SC < t1) stg.load(kb, vb, L.st, L.xst, c0 + X::SC, t1, tid);
         if (active) {
 #pragma unroll
             for (int ks = 0; ks < X::SC / MM::KS; ++ks) {
@@ -289,7 +291,7 @@ __device__ __forceinline__ void gram_body(const Launch& L, int blk, char* lds) {
     if (!active) return;
     const int gi = bh * L.F + f;
     const float gm = L.gamma[gi], bt = L.beta[gi];
-    const float sG = gm * bt * L.c * L.c, sB = bt * L.c;
+    const float sG = gm * bt * L.c * L.c, sB = L.unit_scale ? 1.f : bt * L.c;
     // Lane (r16, g) holds out[i0 + q][col], q = 0..3. It is stored transposed, [col][i0 .. i0+3]
     // (16 contiguous bytes): for Bhat this is Bhat^T; Ghat is symmetric, so its transposed
     // store is Ghat itself.
@@ -373,17 +375,18 @@ template <int D, bool DELTA> struct ScanSlot {
 };
 constexpr int kGammaSeg = 4000;  // frames per gamma staging (a multiple of the scan ring size)
 
-template <typename T, int D, bool DELTA, int P>
+template <typename T, int D, bool DELTA, int P, bool BWD>
 __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
     constexpr int NC = 16;              // value columns per workgroup
     constexpr int NCB = D / NC;         // column blocks per head
     constexpr int KSN = (D + 31) / 32;  // bf16 k steps (padded past D with zeros)
     constexpr int MR = D + 8;           // row length (bf16) of the transposed state planes
     constexpr int REC = canon_bytes<D, DELTA>();
+    constexpr int CREC = canon_bytes<D, false>();  // backward: record of C_t = Q_t^T dO_t
     __shared__ __attribute__((aligned(16))) bf16 Ms[2][2][NC * MR];  // [buffer][hi, lo][col][k]
-    // gamma_f of the current chunk of frames. Gammas come through LDS rather than scalar loads:
-    // a scalar load in the frame loop would share the LDS wait counter and expose a full memory
-    // round trip in every frame.
+    // gamma of the current chunk of steps. Gammas come through LDS rather than scalar loads:
+    // a scalar load in the step loop would share the LDS wait counter and expose a full memory
+    // round trip in every step.
     __shared__ float Gam[kGammaSeg];
 
     const int w = blockIdx.x, xcd = w & 7, slot = w >> 3;
@@ -394,35 +397,52 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
     const int col = cb * NC + r16;
     const int row0 = wave * 16 + 4 * g;  // this lane's 4 state rows
     const int F = L.F, s0 = L.s0, s1 = L.s1;
+    const int lead = L.mt_lead;         // per-step outputs have F + lead slots per (b, h)
     const char* rec_bh = (const char*)L.canon + (int64_t)bh * F * REC;
-    T* mt_bh = (T*)L.mt + (int64_t)bh * F * D * D;
+    const char* crec_bh = (const char*)L.crec + (int64_t)bh * F * CREC;
+    T* mt_bh = (T*)L.mt + (int64_t)bh * (F + lead) * D * D;
 
     float Mc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         Mc[q] = L.scan_in ? L.scan_in[((int64_t)bh * D + row0 + q) * D + col] : 0.f;
     store_split4(&Ms[0][0][r16 * MR + row0], &Ms[0][1][r16 * MR + row0], f32x4{Mc[0], Mc[1], Mc[2], Mc[3]});
+    if (!BWD && lead) store4(mt_bh + (int64_t)col * D + row0, Mc[0], Mc[1], Mc[2], Mc[3]);
 
-    // The ring has P + 1 slots: right after a frame's barrier the slot freed by the previous
-    // frame is refilled with frame f + P, so the loads stream while this frame's MFMAs run.
-    // The frame loop body is branch-free so that the compiler keeps the ring's loads in flight
-    // across iterations: loads past the last frame s1-1 re-read it, and a frame past the end
-    // leaves M unchanged and rewrites M_{s1-1} into its own slot.
+    // Forward: step f applies frame f (Ghat_f, Bhat_f, gamma_f) and its result M_f goes to
+    // slot f + lead. Backward (BWD, steps 0 .. F): step u with t = F - 1 - u computes
+    //     G_t = gamma_{t+1} G_{t+1} - Ghat_{t+1} G_{t+1} + C_t
+    // (Ghat_F = 0 and gamma_F = 1, so G_{F-1} = dstate_out + C_{F-1}; C_{-1} = 0, so the last
+    // step gives the gradient of the initial state) and writes it to slot t + 1.
+    // The ring has P + 1 slots: right after a step's barrier the slot freed by the previous
+    // step is refilled with step f + P, so the loads stream while this step's MFMAs run.
+    // The step loop body is branch-free so that the compiler keeps the ring's loads in flight
+    // across iterations: loads past the last step s1-1 re-read it, and a step past the end
+    // leaves the state unchanged and rewrites the last result into its own slot.
     constexpr int R = P + 1;
     ScanSlot<D, DELTA> ring[R];
     auto issue = [&](ScanSlot<D, DELTA>& r, int f) {
         f = min(f, s1 - 1);
-        const char* rec = rec_bh + (int64_t)f * REC;
+        const int gf = BWD ? F - f : f;                  // frame of Ghat
+        const bool gzero = BWD && gf >= F;               // uniform
+        const char* rec = rec_bh + (int64_t)min(gf, F - 1) * REC;
         if constexpr (DELTA) {
 #pragma unroll
             for (int ks = 0; ks < KSN; ++ks) {
-                const bool in = ks * 32 + g * 8 < D;
+                const bool in = ks * 32 + g * 8 < D && !gzero;
                 const char* fr = rec + ((wave * 2) * KSN + ks) * 1024 + lane * 16;
                 r.a[0][ks] = in ? ld_frag<bf16>((const bf16*)fr) : zero_frag<bf16>();
                 r.a[1][ks] = in ? ld_frag<bf16>((const bf16*)(fr + KSN * 1024)) : zero_frag<bf16>();
             }
         }
-        r.bh = *(const f32x4*)(rec + rec_g_bytes<D, DELTA>() + ((cb * (D / 16) + wave) * 64 + lane) * 16);
+        const int boff = ((cb * (D / 16) + wave) * 64 + lane) * 16;
+        if constexpr (BWD) {
+            const int t = F - 1 - f;                     // frame of C
+            const f32x4 cv = *(const f32x4*)(crec_bh + (int64_t)max(t, 0) * CREC + boff);
+            r.bh = t >= 0 ? cv : f32x4{0.f, 0.f, 0.f, 0.f};
+        } else {
+            r.bh = *(const f32x4*)(rec + rec_g_bytes<D, DELTA>() + boff);
+        }
     };
 #pragma unroll
     for (int u = 0; u < P; ++u) issue(ring[u], s0 + u);
@@ -432,15 +452,19 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
     int cur = 0;
     for (int sb = s0; sb < s1; sb += kGammaSeg) {
         __syncthreads();  // the previous segment's gammas are no longer read
-        for (int t = threadIdx.x; t < kGammaSeg; t += blockDim.x) Gam[t] = gam_bh[min(sb + t, s1 - 1)];
+        for (int t = threadIdx.x; t < kGammaSeg; t += blockDim.x) {
+            const int f = min(sb + t, s1 - 1);
+            if constexpr (BWD) Gam[t] = F - f < F ? gam_bh[F - f] : 1.f;
+            else Gam[t] = gam_bh[f];
+        }
       for (int f0 = sb; f0 < sb + kGammaSeg && f0 < s1; f0 += R) {
 #pragma unroll
         for (int u = 0; u < R; ++u) {
             const int f = f0 + u;
             const bool valid = f < s1;  // uniform
             {
-                __syncthreads();  // planes of M_{f-1} complete; readers of the other buffer done
-                issue(ring[(u + P) % R], f + P);  // the slot of frame f - 1
+                __syncthreads();  // planes of the last state complete; readers of the other buffer done
+                issue(ring[(u + P) % R], f + P);  // the slot of step f - 1
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (DELTA) {
                     f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
@@ -465,7 +489,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
                 if constexpr (DELTA)
                     store_split4(&Ms[cur ^ 1][0][r16 * MR + row0], &Ms[cur ^ 1][1][r16 * MR + row0], mv);
                 const int fs = min(f, s1 - 1);
-                store4(mt_bh + ((int64_t)fs * D + col) * D + row0, Mc[0], Mc[1], Mc[2], Mc[3]);
+                const int os = BWD ? F - fs : fs + lead;  // output slot
+                store4(mt_bh + ((int64_t)os * D + col) * D + row0, Mc[0], Mc[1], Mc[2], Mc[3]);
                 cur ^= 1;
             }
         }
@@ -689,12 +714,12 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
         const bf16* kp = (const bf16*)L.k + fo;
         const bf16* vp = (const bf16*)L.v + fo;
         XStage<bf16, D> stg;
-        stg.load(kp, vp, L.st, 0, S, tid);
+        stg.load(kp, vp, L.st, L.st, 0, S, tid);
         for (int c0 = 0; c0 < S; c0 += X::SC) {
             __syncthreads();  // readers of the previous chunk are done
             stg.store(lds, tid);
             __syncthreads();
-            if (c0 + X::SC < S) stg.load(kp, vp, L.st, c0 + X::SC, S, tid);
+            if (c0 + X::SC < S) stg.load(kp, vp, L.st, L.st, c0 + X::SC, S, tid);
 #pragma unroll
             for (int ks = 0; ks < X::SC / MM::KS; ++ks) {
                 const int tok = ks * MM::KS + g * MM::KL;
@@ -921,6 +946,208 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Backward, per (b, h, f): the gradients of the frame's inputs from G_f = dL/dM_f, the states
+// before and after the frame (M_{f-1}, M_f) and the frame's K, V, dO. With Kt = c K and
+// P = Kt M_{f-1} (the reverse-mode derivative of the forward update):
+//     dQ = dO M_f^T                       dV = beta Kt G
+//     dKt = beta R G^T - gamma beta (Kt G) M_{f-1}^T,   R = V - gamma P,   dK = c dKt
+//     dgamma = <G, M_{f-1}> - beta <Kt G, P>            dbeta = <Kt G, R>
+// (no delta term: R = V and only the first term of dKt and of dgamma). The states and G_f
+// come from the workspace in the I/O type, transposed ([c][n]), and are staged in LDS. Every
+// product runs transposed on MFMA, so that each lane ends up with 4 consecutive feature rows
+// of one token: P^T and (Kt G)^T from A = M_{f-1}^T / G^T rows and B = K rows; their C tiles
+// are then the B operand of dKt^T = G (beta R^T) + M_{f-1} (-gamma beta (Kt G)^T), with the
+// k order of a 32-long step taken from two C tiles (slots 0-3 and 4-7) and the A operand read
+// transposed from the same LDS copies (ds_read_tr16_b64); dQ^T = M_f dO^T likewise.
+// dgamma and dbeta are summed over the frame inside the workgroup in a fixed order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// A operand slice of Y = X^T from a [k][n] LDS matrix X (row length MR): lane (r, g) of a
+// 16-lane group receives Y[n0 + r][k0 + 4 g + j] = X[k0 + 4 g + j][n0 + r], j = 0..3.
+template <int MR> __device__ __forceinline__ u32x2 read_tr4(const bf16* X, int k0, int n0, int r16, int g) {
+    const bf16* a = X + (k0 + 4 * g + (r16 >> 2)) * MR + n0 + 4 * (r16 & 3);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a));
+}
+
+constexpr int kBwdThreads = 256;
+
+template <int D, bool DELTA>
+__global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
+    using MM = Mma<bf16>;
+    constexpr int NW = kBwdThreads / 64;
+    constexpr int CT = D / 16;        // 16-row tiles of a feature dimension
+    constexpr int KS = D / 32;        // 32-long k steps over a feature dimension
+    constexpr int MR = D + 8;         // LDS row length (bf16)
+    constexpr int PLANE = D * MR;
+    __shared__ __attribute__((aligned(16))) bf16 sm[3 * PLANE];  // M_{f-1}^T, G_f^T, M_f^T
+    __shared__ float red[2][NW];
+    static_assert(D == 64 || D == 128, "backward: D = 64 or 128");
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int F = L.F, S = L.S;
+    const int f = blockIdx.x % F, bh = blockIdx.x / F;
+    const int b = bh / L.H, h = bh % L.H;
+    const int gi = bh * F + f;
+    const float gm = L.gamma[gi], bt = L.beta[gi], c = L.c;
+    bf16* Mp = sm;              // M_{f-1}^T [c][n]
+    bf16* Gs = sm + PLANE;      // G_f^T
+    bf16* Mn = sm + 2 * PLANE;  // M_f^T
+
+    // stage the three matrices (slots f and f + 1 of the states, f + 1 of G) and form the frame
+    // term <G_f, M_{f-1}> of dgamma on the way
+    float dg = 0.f, db = 0.f;
+    {
+        const bf16* mt = (const bf16*)L.mt + ((int64_t)bh * (F + 1) + f) * D * D;
+        const bf16* gt = (const bf16*)L.gt + ((int64_t)bh * (F + 1) + f + 1) * D * D;
+        constexpr int NE = D * D / 8, PT = (NE + kBwdThreads - 1) / kBwdThreads;
+        u32x4 xm[PT], xg[PT], xn[PT];
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const int e = min(tid + k * kBwdThreads, NE - 1);
+            xm[k] = ld16(mt + e * 8);
+            xg[k] = ld16(gt + e * 8);
+            xn[k] = ld16(mt + D * D + e * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const int e = tid + k * kBwdThreads;
+            if (NE % kBwdThreads == 0 || e < NE) {
+                const int row = e / (D / 8), cb8 = e % (D / 8);
+                st16(Mp + row * MR + cb8 * 8, xm[k]);
+                st16(Gs + row * MR + cb8 * 8, xg[k]);
+                st16(Mn + row * MR + cb8 * 8, xn[k]);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t a = xm[k][d], q = xg[k][d];
+                    dg += __builtin_bit_cast(float, a << 16) * __builtin_bit_cast(float, q << 16) +
+                          __builtin_bit_cast(float, a & 0xFFFF0000u) * __builtin_bit_cast(float, q & 0xFFFF0000u);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const int64_t io = (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * S * L.st;
+    const int64_t oo = (int64_t)b * L.ob + (int64_t)h * L.oh + (int64_t)f * S * L.ot;
+    const bf16* kf = (const bf16*)L.k + io;
+    const bf16* vf = (const bf16*)L.v + io;
+    const bf16* dof = (const bf16*)L.d_o + oo;   // dO (o strides)
+    bf16* dqf = (bf16*)L.dq + io;
+    bf16* dkf = (bf16*)L.dk + io;
+    bf16* dvf = (bf16*)L.dv + io;
+
+    for (int s0 = wave * 16; s0 < S; s0 += NW * 16) {
+        const int s = s0 + r16;
+        const bool in = s < S;
+        bf16x8 bk[KS], bo[KS];
+        u32x2 vv[CT];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bk[ks] = in ? ld_frag<bf16>(kf + (int64_t)s * L.st + ks * 32 + 8 * g) : zero_frag<bf16>();
+            bo[ks] = in ? ld_frag<bf16>(dof + (int64_t)s * L.ot + ks * 32 + 8 * g) : zero_frag<bf16>();
+        }
+#pragma unroll
+        for (int cb = 0; cb < CT; ++cb)
+            vv[cb] = in ? *(const u32x2*)(vf + (int64_t)s * L.st + 16 * cb + 4 * g) : u32x2{0u, 0u};
+
+        // P^T and (Kt G)^T: C tiles [c = 16 cb + 4 g + q][token r]
+        f32x4 pt[CT], kg[CT];
+#pragma unroll
+        for (int cb = 0; cb < CT; ++cb) {
+            pt[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            kg[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off = (16 * cb + r16) * MR + ks * 32 + 8 * g;
+                if constexpr (DELTA) pt[cb] = MM::run(ld_frag<bf16>(Mp + off), bk[ks], pt[cb]);
+                kg[cb] = MM::run(ld_frag<bf16>(Gs + off), bk[ks], kg[cb]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep each tile's LDS reads next to its MFMAs
+        }
+        // residual, dV, dgamma / dbeta terms; B operands of dKt^T as bf16 pairs
+        uint32_t b1[CT][2], b2[CT][2];
+#pragma unroll
+        for (int cb = 0; cb < CT; ++cb) {
+            float rr[4], kk[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w2 = vv[cb][q >> 1];
+                const float v = __builtin_bit_cast(float, (q & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
+                const float p = c * pt[cb][q];
+                kk[q] = c * kg[cb][q];
+                rr[q] = DELTA ? v - gm * p : v;
+                db += kk[q] * rr[q];
+                if (DELTA) dg -= bt * kk[q] * p;
+            }
+            if (in) *(u32x2*)(dvf + (int64_t)s * L.st + 16 * cb + 4 * g) =
+                u32x2{pack_bf16x2(bt * kk[0], bt * kk[1]), pack_bf16x2(bt * kk[2], bt * kk[3])};
+            b1[cb][0] = pack_bf16x2(bt * rr[0], bt * rr[1]);
+            b1[cb][1] = pack_bf16x2(bt * rr[2], bt * rr[3]);
+            const float sc = -gm * bt;
+            b2[cb][0] = pack_bf16x2(sc * kk[0], sc * kk[1]);
+            b2[cb][1] = pack_bf16x2(sc * kk[2], sc * kk[3]);
+        }
+        // dKt^T [n = 16 nt + 4 g + q][token] and dQ^T (not unrolled: it indexes no register
+        // array, and unrolling lets the compiler hoist every LDS read of the loop)
+#pragma unroll 1
+        for (int nt = 0; nt < CT; ++nt) {
+            f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                // k order of this step: slots 0-3 -> c = 32 ks + 4 g + j (tile 2 ks), slots 4-7 ->
+                // c = 32 ks + 16 + 4 g + j (tile 2 ks + 1)
+                const bf16x8 B1 = __builtin_bit_cast(bf16x8, u32x4{b1[2 * ks][0], b1[2 * ks][1],
+                                                                  b1[2 * ks + 1][0], b1[2 * ks + 1][1]});
+                const u32x2 g0 = read_tr4<MR>(Gs, 32 * ks, 16 * nt, r16, g);
+                const u32x2 g1 = read_tr4<MR>(Gs, 32 * ks + 16, 16 * nt, r16, g);
+                ak = MM::run(__builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]}), B1, ak);
+                if constexpr (DELTA) {
+                    const bf16x8 B2 = __builtin_bit_cast(bf16x8, u32x4{b2[2 * ks][0], b2[2 * ks][1],
+                                                                      b2[2 * ks + 1][0], b2[2 * ks + 1][1]});
+                    const u32x2 m0 = read_tr4<MR>(Mp, 32 * ks, 16 * nt, r16, g);
+                    const u32x2 m1 = read_tr4<MR>(Mp, 32 * ks + 16, 16 * nt, r16, g);
+                    ak = MM::run(__builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]}), B2, ak);
+                }
+                // dQ^T: natural k order c = 32 ks + 8 g + j, matching the dO row fragment
+                const u32x2 n0 = read_tr4<MR>(Mn, 32 * ks, 16 * nt, r16, 2 * g);      // c = 32 ks + 8 g + j
+                const u32x2 n1 = read_tr4<MR>(Mn, 32 * ks + 4, 16 * nt, r16, 2 * g);  // c = 32 ks + 8 g + 4 + j
+                aq = MM::run(__builtin_bit_cast(bf16x8, u32x4{n0[0], n0[1], n1[0], n1[1]}), bo[ks], aq);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (in) {
+                *(u32x2*)(dkf + (int64_t)s * L.st + 16 * nt + 4 * g) =
+                    u32x2{pack_bf16x2(c * ak[0], c * ak[1]), pack_bf16x2(c * ak[2], c * ak[3])};
+                *(u32x2*)(dqf + (int64_t)s * L.st + 16 * nt + 4 * g) =
+                    u32x2{pack_bf16x2(aq[0], aq[1]), pack_bf16x2(aq[2], aq[3])};
+            }
+        }
+    }
+
+    // dgamma, dbeta: wave sums, then a fixed-order sum over waves
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        dg += __shfl_xor(dg, o);
+        db += __shfl_xor(db, o);
+    }
+    if (lane == 0) {
+        red[0][wave] = dg;
+        red[1][wave] = db;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float sg = 0.f, sbt = 0.f;
+        for (int w = 0; w < NW; ++w) {
+            sg += red[0][w];
+            sbt += red[1][w];
+        }
+        L.dgamma[gi] = sg;
+        L.dbeta[gi] = sbt;
+    }
+}
+
+// ----------------------------------------------------------------------------------------
 // Kernel 4: one frame, partial sums over the split's tokens of U = K^T R, with
 // R = V - (gamma c) K M (delta) or R = V (no delta). The prediction P = K M runs on MFMA with M
 // (state_in) rounded to the I/O type. For bf16 data U is accumulated as K^T V + K^T (-gamma c P):
@@ -967,8 +1194,8 @@ __global__ __launch_bounds__(step_threads<D>()) void step_partial_kernel(Launch 
 
     // two chunks of K and V in flight: chunk c is loaded while chunk c - 2 is computed
     XStage<T, D, SNT> sa, sb;
-    sa.load(kb, vb, L.st, t0, t1, tid);
-    sb.load(kb, vb, L.st, t0 + X::SC, t1, tid);
+    sa.load(kb, vb, L.st, L.st, t0, t1, tid);
+    sb.load(kb, vb, L.st, L.st, t0 + X::SC, t1, tid);
 
     // B operand of the prediction: M[i][j] for this wave's columns, all key rows. bf16: from a
     // transposed copy mt[j][i] (i past D is zero); fp32: one element per lane, read directly
@@ -1034,7 +1261,7 @@ __global__ __launch_bounds__(step_threads<D>()) void step_partial_kernel(Launch 
         stg.store(lds, tid);
         if constexpr (DELTA) stg.store_key_rows(krow, KR, tid);  // row-major K copy of the chunk
         __syncthreads();
-        if (c0 + 2 * X::SC < t1) stg.load(kb, vb, L.st, c0 + 2 * X::SC, t1, tid);
+        if (c0 + 2 * X::SC < t1) stg.load(kb, vb, L.st, L.st, c0 + 2 * X::SC, t1, tid);
         if (!active) return;
 #pragma unroll
         for (int tg = 0; tg < X::SC; tg += TG) {
@@ -1176,7 +1403,7 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
     case K_SCAN: {
         if (L.s1 <= L.s0) return hipSuccess;
         const int units = (BH + 7) / 8 * 8 * (D / 16);
-        hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead>), dim3(units), dim3(64 * (D / 16)),
+        hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead, false>), dim3(units), dim3(64 * (D / 16)),
                            0, s, L);
         break;
     }
@@ -1188,6 +1415,21 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
     case K_FUSED: {
         if constexpr (std::is_same<T, bf16>::value && (D == 64 || D == 128)) {
             hipLaunchKernelGGL((fused_kernel<D, DELTA>), dim3(BH * L.F), dim3(NT), 0, s, L);
+        } else {
+            return hipErrorInvalidValue;
+        }
+        break;
+    }
+    case K_SCAN_BWD: {
+        if (L.s1 <= L.s0) return hipSuccess;
+        const int units = (BH + 7) / 8 * 8 * (D / 16);
+        hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead, true>), dim3(units), dim3(64 * (D / 16)),
+                           0, s, L);
+        break;
+    }
+    case K_BWD: {
+        if constexpr (std::is_same<T, bf16>::value && (D == 64 || D == 128)) {
+            hipLaunchKernelGGL((bwd_kernel<D, DELTA>), dim3(BH * L.F), dim3(kBwdThreads), 0, s, L);
         } else {
             return hipErrorInvalidValue;
         }
@@ -1209,6 +1451,7 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
 }
 
 bool fused_supported(int bf16_data, int D) { return bf16_data && (D == 64 || D == 128); }
+bool backward_supported(int bf16_data, int D) { return bf16_data && (D == 64 || D == 128); }
 
 hipError_t launch_kernel(Kernel k, const Launch& L, hipStream_t s) {
     const bool dl = L.use_delta != 0;

@@ -5,6 +5,8 @@
 //                   (output items of every frame).
 // Forward, fused:   reset of the ticket counter and frame flags -> fused kernel.
 // Step:             step_partial -> step_reduce -> products (output items of the one frame).
+// Backward:         products + [combine] + scan (forward states), products + [combine] of
+//                   C_f = Q_f^T dO_f, reverse scan (state gradients), per-frame gradients.
 #include <vector>
 
 #include "../../include/libgdn.h"
@@ -74,6 +76,46 @@ hipError_t run_step(const Launch& L0, hipStream_t s) {
     A.o0 = 0;
     A.on = 1;
     return run.go(K_PRODUCTS, A, s, BH);
+}
+
+hipError_t run_backward(const Launch& L0, hipStream_t s) {
+    t_trace_log.clear();
+    Launcher run{L0, s};
+    const int64_t BH = (int64_t)L0.B * L0.H;
+    const int F = L0.F;
+    // 1. forward states: products of every frame, then the scan, M_f to slot f + 1 (slot 0:
+    //    the initial state)
+    Launch A = L0;
+    A.g0 = 0; A.gn = F; A.o0 = 0; A.on = 0;
+    GDN_TRY(run.go(K_PRODUCTS, A, s, BH * F));
+    if (L0.nsplit > 1) GDN_TRY(run.go(K_COMBINE, A, s, BH * F));
+    A.s0 = 0; A.s1 = F;
+    A.scan_in = L0.state_in;
+    A.scan_out = nullptr;
+    A.mt_lead = 1;
+    GDN_TRY(run.go(K_SCAN, A, s, BH * F));
+    // 2. C_f = Q_f^T dO_f of every frame: the gram products without the delta term and the
+    //    gates, first operand Q (Q/K/V strides), second dO (O strides)
+    Launch C = L0;
+    C.use_delta = 0;
+    C.unit_scale = 1;
+    C.k = L0.q;
+    C.v = L0.d_o;
+    C.xsb = L0.ob; C.xsh = L0.oh; C.xst = L0.ot;
+    C.canon = L0.crec;
+    C.g0 = 0; C.gn = F; C.o0 = 0; C.on = 0;
+    GDN_TRY(run.go(K_PRODUCTS, C, s, BH * F));
+    if (L0.nsplit > 1) GDN_TRY(run.go(K_COMBINE, C, s, BH * F));
+    // 3. reverse scan: G_f for every frame (slot f + 1) and the gradient of the initial state
+    Launch R = L0;
+    R.s0 = 0; R.s1 = F + 1;
+    R.scan_in = L0.d_state_out;
+    R.scan_out = L0.d_state_in;
+    R.mt = L0.gt;
+    R.mt_lead = 1;
+    GDN_TRY(run.go(K_SCAN_BWD, R, s, BH * (F + 1)));
+    // 4. per-frame gradients
+    return run.go(K_BWD, L0, s, BH * F);
 }
 
 void set_trace(void* const* events, int pairs) {

@@ -108,11 +108,12 @@ typedef struct {
 } gdn_problem;
 
 /*
- * Workspace bytes needed by gdn_forward_framewise (step_mode = 0) or gdn_step_frame
- * (step_mode = 1) for this problem. The step-mode size does not depend on `frames`.
- * Validates the sizes in `p` (not the pointers or strides).
+ * Workspace bytes needed by gdn_forward_framewise (mode = 0), gdn_step_frame (mode = 1) or
+ * gdn_backward_framewise (mode = 2) for this problem. The step-mode size does not depend on
+ * `frames`. Validates the sizes in `p` (not the pointers or strides); other modes are
+ * GDN_ERR_SHAPE.
  */
-gdn_status gdn_workspace_size(const gdn_problem* p, int step_mode, size_t* bytes_out);
+gdn_status gdn_workspace_size(const gdn_problem* p, int mode, size_t* bytes_out);
 
 /*
  * All F frames of every (b, h) in one call (the recurrence above).
@@ -148,6 +149,37 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                           void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Gradients of gdn_forward_framewise for training: given dL/dO and dL/dstate_out of a scalar
+ * loss L, returns dL/dQ, dL/dK, dL/dV, dL/dgamma, dL/dbeta and dL/dstate_in (key_scale is a
+ * constant). The pages define the forward only; this is its reverse-mode derivative. With
+ * G_f = dL/dM_f, Kt = c K_f, M the state before frame f and P = Kt M, R = V_f - gamma_f P:
+ *     G_f      = Q_f^T dO_f + (gamma_{f+1} I - gamma_{f+1} beta_{f+1} Kt_{f+1}^T Kt_{f+1}) G_{f+1}
+ *                (G_{F-1} also receives dstate_out)
+ *     dQ_f     = dO_f M_f^T
+ *     dV_f     = beta_f Kt G_f
+ *     dK_f     = c (beta_f R G_f^T - gamma_f beta_f (Kt G_f) M^T)
+ *     dgamma_f = <G_f, M> - beta_f <Kt G_f, P>,    dbeta_f = <Kt G_f, R>
+ *     dstate_in = (gamma_0 I - gamma_0 beta_0 Kt_0^T Kt_0) G_0
+ * (without the delta term: R = V_f, dK_f = c beta_f V_f G_f^T, dgamma_f = <G_f, M>, and the
+ * chain uses gamma I). The forward states are recomputed inside the call.
+ *   q, k, v, gamma, beta, state_in   the forward's inputs (state_in NULL: zero)
+ *   d_o          dL/dO, layout of o (o_stride_*)
+ *   d_state_out  dL/dstate_out fp32 [B][H][D][D], or NULL for zero
+ *   dq, dk, dv   outputs, layout of q/k/v (qkv_stride_*), type of q
+ *   dgamma, dbeta  outputs, fp32 [B][H][F]
+ *   d_state_in   output fp32 [B][H][D][D], or NULL; may equal d_state_out exactly
+ *   workspace    at least gdn_workspace_size(p, 2) bytes, 256-byte aligned
+ * Supported: bf16 data with D = 64 or 128 (GDN_ERR_UNSUPPORTED otherwise). No output may
+ * overlap an input, the workspace or another output.
+ */
+gdn_status gdn_backward_framewise(const gdn_problem* p, const void* q, const void* k,
+                                  const void* v, const float* gamma, const float* beta,
+                                  const float* state_in, const void* d_o,
+                                  const float* d_state_out, void* dq, void* dk, void* dv,
+                                  float* dgamma, float* dbeta, float* d_state_in,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * Instrumentation (launch trace). gdn_set_trace arms `pairs` pairs of caller-created,
  * timing-enabled hipEvent_t handles on the calling host thread: in every later
  * gdn_forward_framewise / gdn_step_frame call on this thread, kernel launch i (i < pairs) is
@@ -165,7 +197,9 @@ typedef enum {
     GDN_KERNEL_STEP_PARTIAL = 3,  /* step: per-split K^T R */
     GDN_KERNEL_STEP_REDUCE = 4,   /* step: state update */
     GDN_KERNEL_FUSED_RESET = 5,   /* fused: clears the ticket counter and frame flags */
-    GDN_KERNEL_FUSED = 6          /* fused: products, state step and outputs of every frame */
+    GDN_KERNEL_FUSED = 6,         /* fused: products, state step and outputs of every frame */
+    GDN_KERNEL_SCAN_BWD = 7,      /* backward: reverse scan of the state gradients */
+    GDN_KERNEL_BWD = 8            /* backward: per-frame gradients of Q, K, V, gamma, beta */
 } gdn_kernel_kind;
 
 typedef struct {
@@ -173,7 +207,8 @@ typedef struct {
     int32_t stream;   /* stream of the launch: 0 = the caller's (the only one used) */
     int64_t units;    /* (b, h, frame) items. A PRODUCTS item moves 2*S*D elements of Q/K/V/O
                          (K and V read, or Q read and O written); a FUSED item moves 4*S*D
-                         (K, V, Q read, O written) */
+                         (K, V, Q read, O written); a BWD item 6*S*D (K, V, dO read; dQ, dK,
+                         dV written) */
 } gdn_trace_entry;
 
 gdn_status gdn_set_trace(void* const* events, int pairs);

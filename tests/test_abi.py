@@ -206,3 +206,36 @@ def test_in_place_state_passes_alias_checks():
     # exact in-place commit is allowed: the call only fails later, at the workspace check
     p = prob()
     assert call(p, si=7 * A, so=7 * A, wsb=16) == 7
+
+
+def call_bwd(p, q=A, k=2 * A, v=3 * A, g=4 * A, b=5 * A, si=None, do=6 * A, dso=None, dq=9 * A,
+             dk=10 * A, dv=11 * A, dg=12 * A, db=13 * A, dsi=None, ws=14 * A, wsb=1 << 40):
+    lib = gdn.load()
+    pp = None if p is None else ctypes.byref(p)
+    return lib.gdn_backward_framewise(pp, q, k, v, g, b, si, do, dso, dq, dk, dv, dg, db, dsi, ws,
+                                      wsb, None)
+
+
+def test_backward_validation():
+    assert call_bwd(None) == 1
+    assert call_bwd(prob(), do=None) == 1
+    assert call_bwd(prob(), dg=None) == 1
+    assert call_bwd(prob(dtype=gdn.GDN_F32)) == 3          # bf16 only
+    assert call_bwd(prob(D=32)) == 3                        # D = 64 or 128
+    assert "backward" in msg()
+    assert call_bwd(prob(), dq=A) == 6                      # dq == q
+    assert call_bwd(prob(), dk=9 * A + 1024) == 6           # dk overlaps dq
+    assert call_bwd(prob(), dsi=7 * A, dso=7 * A, wsb=16) == 7   # in-place state gradient is fine
+    assert call_bwd(prob(), dsi=7 * A, dso=7 * A + 4096) == 6    # partial overlap is not
+    assert call_bwd(prob(), wsb=16) == 7
+    assert call_bwd(prob(), ws=14 * A + 16) == 5
+
+
+def test_backward_workspace():
+    p = prob(F=30)
+    n = gdn.workspace_size(p, 2)
+    # forward states and state gradients (F + 1 slots), the forward records and C_f records
+    assert n >= 2 * (31 * 2 * 64 * 64 * 2) + 30 * 2 * 64 * 64 * 4
+    assert gdn.workspace_size(prob(F=60), 2) > n
+    n3 = ctypes.c_size_t(0)
+    assert gdn.load().gdn_workspace_size(ctypes.byref(p), 3, ctypes.byref(n3)) == 2

@@ -1,0 +1,133 @@
+"""Backward (gradients) on the GPU, through the C ABI, against the fp64 backward oracle.
+
+Tolerance: max|d| / max|ref| <= 1e-2 per gradient (bf16 data; the forward states and the state
+gradients enter the per-frame products rounded to bf16).
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import frame_wise_gated_libgdn_amd as gdn  # noqa: E402
+import gdn_synth  # noqa: E402
+import oracle  # noqa: E402
+from gpu_util import TOL, rel_err, random_qkv, to_dev, to_np  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NAMES = ["dq", "dk", "dv", "dgamma", "dbeta", "dstate_in"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_round(x):
+    return gdn_synth.bf16_bits_to_f32(gdn_synth.f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+
+def run_case(B, H, D, S, F, delta, with_state, with_dm, layout, seed):
+    rng = np.random.default_rng(seed)
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    d_o = bf16_round(rng.standard_normal((B, H, F * S, D)))
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    s0 = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32) if with_state else None
+    dm = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32) if with_dm else None
+    dev = [to_dev(x, "bf16", DEV, layout) for x in (q, k, v)]
+    ddo = to_dev(d_o, "bf16", DEV, layout)
+    tg, tb = torch.from_numpy(g).to(DEV), torch.from_numpy(b).to(DEV)
+    ts0 = None if s0 is None else torch.from_numpy(s0).to(DEV)
+    tdm = None if dm is None else torch.from_numpy(dm).to(DEV)
+    got = gdn.backward_framewise(*dev, tg, tb, ddo, ts0, tdm, use_delta=delta)
+    torch.cuda.synchronize()
+    ref = oracle.backward(q, k, v, g, b, s0, d_o, dm, use_delta=delta)
+    return got, ref
+
+
+CASES = [
+    # B, H, D, S, F, delta, initial state, dstate_out, layout
+    (1, 2, 128, 200, 5, True, True, True, "head"),
+    (1, 1, 64, 64, 7, True, False, False, "head"),
+    (2, 2, 64, 130, 4, True, True, True, "token"),
+    (1, 2, 128, 96, 6, False, True, True, "head"),
+    (1, 3, 64, 33, 3, False, False, True, "head"),
+    (1, 1, 128, 1, 9, True, True, True, "head"),      # one token per frame
+    (1, 2, 128, 300, 1, True, True, False, "head"),   # one frame
+    (1, 16, 128, 3520, 2, True, True, True, "head"),  # the 720p frame size
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c)) for c in CASES])
+def test_backward_matches_oracle(case):
+    say("backward", case)
+    got, ref = run_case(*case, seed=zlib.crc32(repr(case).encode()))
+    errs = {}
+    for name, x, r in zip(NAMES, got, ref):
+        errs[name] = rel_err(to_np(x), r)
+    say("  " + " ".join("%s %.2e" % kv for kv in errs.items()))
+    assert max(errs.values()) <= TOL["bf16"], errs
+
+
+def test_backward_in_place_state_gradient_and_determinism():
+    B, H, D, S, F = 1, 2, 128, 70, 5
+    rng = np.random.default_rng(31)
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    d_o = bf16_round(rng.standard_normal((B, H, F * S, D)))
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    dm = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV),
+                                                          to_dev(d_o, "bf16", DEV)]
+    tdm = torch.from_numpy(dm).to(DEV)
+    r1 = gdn.backward_framewise(*args, None, tdm.clone())
+    r2 = gdn.backward_framewise(*args, None, tdm.clone())
+    # in place: the state gradient overwrites dstate_out
+    lib = gdn.load()
+    import ctypes
+    p = gdn._problem(args[0], args[5], F, True, None)
+    ws, nb = gdn._workspace(p, 2, None, args[0].device)
+    outs = [torch.empty_like(args[0]) for _ in range(3)]
+    dg = torch.empty((B, H, F), dtype=torch.float32, device=DEV)
+    db = torch.empty((B, H, F), dtype=torch.float32, device=DEV)
+    inplace = tdm.clone()
+    code = lib.gdn_backward_framewise(
+        ctypes.byref(p), *[ctypes.c_void_p(t.data_ptr()) for t in args[:5]], None,
+        ctypes.c_void_p(args[5].data_ptr()), ctypes.c_void_p(inplace.data_ptr()),
+        *[ctypes.c_void_p(t.data_ptr()) for t in outs], ctypes.c_void_p(dg.data_ptr()),
+        ctypes.c_void_p(db.data_ptr()), ctypes.c_void_p(inplace.data_ptr()),
+        ctypes.c_void_p(ws.data_ptr()), nb, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert code == 0
+    for a, c in zip(r1, r2):
+        assert torch.equal(a, c), "backward is not bitwise repeatable"
+    assert torch.equal(inplace, r1[5])
+    for a, c in zip(outs, r1[:3]):
+        assert torch.equal(a, c)
+
+
+def test_backward_880x81_sampled_heads():
+    w = gdn_synth.WORKLOADS["gdn_880x81_bf16"]
+    say("backward on the 880x81 workload, oracle on head 7 of batch 1")
+    q, k, v = gdn_synth.qkv_torch(w, DEV)
+    g, b = gdn_synth.gates_torch(w, DEV)
+    gen = np.random.default_rng(41)
+    d_o_np = bf16_round(gen.standard_normal((w.B, w.H, w.F * w.S, w.D)).astype(np.float32))
+    d_o = torch.from_numpy(d_o_np).to(torch.bfloat16).to(DEV)
+    got = gdn.backward_framewise(q, k, v, g, b, d_o)
+    torch.cuda.synchronize()
+    heads = [7]
+    (qc, kc, vc), _ = gdn_synth.qkv_cpu(w, heads=heads)
+    gc, bc = gdn_synth.gates_cpu(w, heads=heads)
+    ref = oracle.backward(qc[1:2], kc[1:2], vc[1:2], gc[1:2], bc[1:2], None,
+                          d_o_np[1:2, heads])
+    errs = {}
+    for name, x, r in zip(NAMES, got, ref):
+        errs[name] = rel_err(to_np(x[1:2, heads]), r)
+    say("  " + " ".join("%s %.2e" % kv for kv in errs.items()))
+    assert max(errs.values()) <= TOL["bf16"], errs
