@@ -963,20 +963,26 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// A operand slice of Y = X^T from a [k][n] LDS matrix X (row length MR): lane (r, g) of a
-// 16-lane group receives Y[n0 + r][k0 + 4 g + j] = X[k0 + 4 g + j][n0 + r], j = 0..3.
-template <int MR> __device__ __forceinline__ u32x2 read_tr4(const bf16* X, int k0, int n0, int r16, int g) {
-    const bf16* a = X + (k0 + 4 * g + (r16 >> 2)) * MR + n0 + 4 * (r16 & 3);
+// A operand slice of Y = X^T from a [k][n] LDS matrix X (row length MR), with the rows of the
+// 16-row tile jt permuted as in out_col (tiles 2p and 2p + 1 together cover 32 p .. 32 p + 31
+// so that lane (r, g) of their C tiles holds 8 consecutive rows): lane (r, g) of a 16-lane
+// group receives Y[out_col(jt, r)][k0 + 4 g + j] = X[k0 + 4 g + j][out_col(jt, r)], j = 0..3.
+// (ds_read_tr16_b64: in each 16-lane group, destination lane i takes element i mod 4 of the four
+// b16 values at the address of source lane 4 j + i / 4; source lane 4 j + a points at row
+// k0 + 4 g + j, columns out_col(jt, 4 a) .. + 3.)
+template <int MR> __device__ __forceinline__ u32x2 read_tr4(const bf16* X, int k0, int jt, int r16, int g) {
+    const bf16* a = X + (k0 + 4 * g + (r16 >> 2)) * MR + 32 * (jt >> 1) + 8 * (r16 & 3) + 4 * (jt & 1);
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a));
 }
 
-constexpr int kBwdThreads = 256;
+constexpr int kBwdThreads = 512;
 
 template <int D, bool DELTA>
 __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
     using MM = Mma<bf16>;
     constexpr int NW = kBwdThreads / 64;
     constexpr int CT = D / 16;        // 16-row tiles of a feature dimension
+    constexpr int CP = CT / 2;        // tile pairs (32 features)
     constexpr int KS = D / 32;        // 32-long k steps over a feature dimension
     constexpr int MR = D + 8;         // LDS row length (bf16)
     constexpr int PLANE = D * MR;
@@ -1041,86 +1047,104 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
     for (int s0 = wave * 16; s0 < S; s0 += NW * 16) {
         const int s = s0 + r16;
         const bool in = s < S;
+        // operands are loaded where their use begins, to keep live ranges short
         bf16x8 bk[KS], bo[KS];
-        u32x2 vv[CT];
+        u32x4 vv[CP];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
             bk[ks] = in ? ld_frag<bf16>(kf + (int64_t)s * L.st + ks * 32 + 8 * g) : zero_frag<bf16>();
-            bo[ks] = in ? ld_frag<bf16>(dof + (int64_t)s * L.ot + ks * 32 + 8 * g) : zero_frag<bf16>();
-        }
 #pragma unroll
-        for (int cb = 0; cb < CT; ++cb)
-            vv[cb] = in ? *(const u32x2*)(vf + (int64_t)s * L.st + 16 * cb + 4 * g) : u32x2{0u, 0u};
+        for (int p = 0; p < CP; ++p)
+            vv[p] = in ? ld16(vf + (int64_t)s * L.st + 32 * p + 8 * g) : u32x4{0u, 0u, 0u, 0u};
 
-        // P^T and (Kt G)^T: C tiles [c = 16 cb + 4 g + q][token r]
+        // P^T and (Kt G)^T: C tiles whose rows are the features out_col(cb, 4 g + q), i.e. for
+        // tile pair p, lane (r, g) holds features 32 p + 8 g + (0..7) of token r
         f32x4 pt[CT], kg[CT];
 #pragma unroll
         for (int cb = 0; cb < CT; ++cb) {
             pt[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
             kg[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int row = out_col<bf16, D>(cb, r16);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int off = (16 * cb + r16) * MR + ks * 32 + 8 * g;
+                const int off = row * MR + ks * 32 + 8 * g;
                 if constexpr (DELTA) pt[cb] = MM::run(ld_frag<bf16>(Mp + off), bk[ks], pt[cb]);
                 kg[cb] = MM::run(ld_frag<bf16>(Gs + off), bk[ks], kg[cb]);
             }
             __builtin_amdgcn_sched_barrier(0);  // keep each tile's LDS reads next to its MFMAs
         }
-        // residual, dV, dgamma / dbeta terms; B operands of dKt^T as bf16 pairs
+        // residual, dV, dgamma / dbeta terms; B operands of dKt^T as bf16 pairs (natural k
+        // order: slots 0-7 of step ks are features 32 ks + 8 g + 0..7)
         uint32_t b1[CT][2], b2[CT][2];
 #pragma unroll
-        for (int cb = 0; cb < CT; ++cb) {
-            float rr[4], kk[4];
+        for (int p = 0; p < CP; ++p) {
+            uint32_t dvw[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t w2 = vv[cb][q >> 1];
-                const float v = __builtin_bit_cast(float, (q & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
-                const float p = c * pt[cb][q];
-                kk[q] = c * kg[cb][q];
-                rr[q] = DELTA ? v - gm * p : v;
-                db += kk[q] * rr[q];
-                if (DELTA) dg -= bt * kk[q] * p;
+            for (int hh = 0; hh < 2; ++hh) {
+                const int cb = 2 * p + hh;
+                float rr[4], kk[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w2 = vv[p][2 * hh + (q >> 1)];
+                    const float v = __builtin_bit_cast(float, (q & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
+                    const float pp = c * pt[cb][q];
+                    kk[q] = c * kg[cb][q];
+                    rr[q] = DELTA ? v - gm * pp : v;
+                    db += kk[q] * rr[q];
+                    if (DELTA) dg -= bt * kk[q] * pp;
+                }
+                dvw[2 * hh] = pack_bf16x2(bt * kk[0], bt * kk[1]);
+                dvw[2 * hh + 1] = pack_bf16x2(bt * kk[2], bt * kk[3]);
+                b1[cb][0] = pack_bf16x2(bt * rr[0], bt * rr[1]);
+                b1[cb][1] = pack_bf16x2(bt * rr[2], bt * rr[3]);
+                const float sc = -gm * bt;
+                b2[cb][0] = pack_bf16x2(sc * kk[0], sc * kk[1]);
+                b2[cb][1] = pack_bf16x2(sc * kk[2], sc * kk[3]);
             }
-            if (in) *(u32x2*)(dvf + (int64_t)s * L.st + 16 * cb + 4 * g) =
-                u32x2{pack_bf16x2(bt * kk[0], bt * kk[1]), pack_bf16x2(bt * kk[2], bt * kk[3])};
-            b1[cb][0] = pack_bf16x2(bt * rr[0], bt * rr[1]);
-            b1[cb][1] = pack_bf16x2(bt * rr[2], bt * rr[3]);
-            const float sc = -gm * bt;
-            b2[cb][0] = pack_bf16x2(sc * kk[0], sc * kk[1]);
-            b2[cb][1] = pack_bf16x2(sc * kk[2], sc * kk[3]);
+            if (in) st16(dvf + (int64_t)s * L.st + 32 * p + 8 * g, u32x4{dvw[0], dvw[1], dvw[2], dvw[3]});
         }
-        // dKt^T [n = 16 nt + 4 g + q][token] and dQ^T (not unrolled: it indexes no register
-        // array, and unrolling lets the compiler hoist every LDS read of the loop)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            bo[ks] = in ? ld_frag<bf16>(dof + (int64_t)s * L.ot + ks * 32 + 8 * g) : zero_frag<bf16>();
+        // dKt^T and dQ^T, a pair of 16-row tiles (32 features) at a time (not unrolled: it
+        // indexes no register array, and unrolling lets the compiler hoist every LDS read)
 #pragma unroll 1
-        for (int nt = 0; nt < CT; ++nt) {
-            f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < CP; ++p) {
+            f32x4 ak[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            f32x4 aq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                // k order of this step: slots 0-3 -> c = 32 ks + 4 g + j (tile 2 ks), slots 4-7 ->
-                // c = 32 ks + 16 + 4 g + j (tile 2 ks + 1)
                 const bf16x8 B1 = __builtin_bit_cast(bf16x8, u32x4{b1[2 * ks][0], b1[2 * ks][1],
                                                                   b1[2 * ks + 1][0], b1[2 * ks + 1][1]});
-                const u32x2 g0 = read_tr4<MR>(Gs, 32 * ks, 16 * nt, r16, g);
-                const u32x2 g1 = read_tr4<MR>(Gs, 32 * ks + 16, 16 * nt, r16, g);
-                ak = MM::run(__builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]}), B1, ak);
-                if constexpr (DELTA) {
-                    const bf16x8 B2 = __builtin_bit_cast(bf16x8, u32x4{b2[2 * ks][0], b2[2 * ks][1],
-                                                                      b2[2 * ks + 1][0], b2[2 * ks + 1][1]});
-                    const u32x2 m0 = read_tr4<MR>(Mp, 32 * ks, 16 * nt, r16, g);
-                    const u32x2 m1 = read_tr4<MR>(Mp, 32 * ks + 16, 16 * nt, r16, g);
-                    ak = MM::run(__builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]}), B2, ak);
+                bf16x8 B2;
+                if constexpr (DELTA)
+                    B2 = __builtin_bit_cast(bf16x8, u32x4{b2[2 * ks][0], b2[2 * ks][1],
+                                                         b2[2 * ks + 1][0], b2[2 * ks + 1][1]});
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int jt = 2 * p + hh;
+                    // slots 0-3: features 32 ks + 8 g + j; slots 4-7: 32 ks + 8 g + 4 + j
+                    const u32x2 g0 = read_tr4<MR>(Gs, 32 * ks, jt, r16, 2 * g);
+                    const u32x2 g1 = read_tr4<MR>(Gs, 32 * ks + 4, jt, r16, 2 * g);
+                    ak[hh] = MM::run(__builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]}), B1, ak[hh]);
+                    if constexpr (DELTA) {
+                        const u32x2 m0 = read_tr4<MR>(Mp, 32 * ks, jt, r16, 2 * g);
+                        const u32x2 m1 = read_tr4<MR>(Mp, 32 * ks + 4, jt, r16, 2 * g);
+                        ak[hh] = MM::run(__builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]}), B2, ak[hh]);
+                    }
+                    const u32x2 n0 = read_tr4<MR>(Mn, 32 * ks, jt, r16, 2 * g);
+                    const u32x2 n1 = read_tr4<MR>(Mn, 32 * ks + 4, jt, r16, 2 * g);
+                    aq[hh] = MM::run(__builtin_bit_cast(bf16x8, u32x4{n0[0], n0[1], n1[0], n1[1]}), bo[ks], aq[hh]);
                 }
-                // dQ^T: natural k order c = 32 ks + 8 g + j, matching the dO row fragment
-                const u32x2 n0 = read_tr4<MR>(Mn, 32 * ks, 16 * nt, r16, 2 * g);      // c = 32 ks + 8 g + j
-                const u32x2 n1 = read_tr4<MR>(Mn, 32 * ks + 4, 16 * nt, r16, 2 * g);  // c = 32 ks + 8 g + 4 + j
-                aq = MM::run(__builtin_bit_cast(bf16x8, u32x4{n0[0], n0[1], n1[0], n1[1]}), bo[ks], aq);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (in) {
-                *(u32x2*)(dkf + (int64_t)s * L.st + 16 * nt + 4 * g) =
-                    u32x2{pack_bf16x2(c * ak[0], c * ak[1]), pack_bf16x2(c * ak[2], c * ak[3])};
-                *(u32x2*)(dqf + (int64_t)s * L.st + 16 * nt + 4 * g) =
-                    u32x2{pack_bf16x2(aq[0], aq[1]), pack_bf16x2(aq[2], aq[3])};
+                st16(dkf + (int64_t)s * L.st + 32 * p + 8 * g,
+                     u32x4{pack_bf16x2(c * ak[0][0], c * ak[0][1]), pack_bf16x2(c * ak[0][2], c * ak[0][3]),
+                           pack_bf16x2(c * ak[1][0], c * ak[1][1]), pack_bf16x2(c * ak[1][2], c * ak[1][3])});
+                st16(dqf + (int64_t)s * L.st + 32 * p + 8 * g,
+                     u32x4{pack_bf16x2(aq[0][0], aq[0][1]), pack_bf16x2(aq[0][2], aq[0][3]),
+                           pack_bf16x2(aq[1][0], aq[1][1]), pack_bf16x2(aq[1][2], aq[1][3])});
             }
         }
     }
