@@ -101,9 +101,9 @@ Plan make_plan(const gdn_problem& p, int mode) {
     pl.ctl_bytes = (size_t)(2 + BH * gdn::kChainGroups) * 4;
     pl.chain_bytes = (size_t)(2 * BH * D * D * 4);
     if (mode == 2) {
-        // forward states and state gradients get F + 1 slots (slot 0: initial state / its
+        // fp32 forward states and state gradients get F + 1 slots (slot 0: initial state / its
         // gradient); the C_f records hold one fp32 D x D matrix each
-        pl.mt_bytes = (size_t)(BH * (F + 1) * D * D * esz);
+        pl.mt_bytes = (size_t)(BH * (F + 1) * D * D * 4);
         pl.crec_bytes = (size_t)(BH * F * D * D * 4);
         pl.gt_bytes = pl.mt_bytes;
     }

@@ -41,7 +41,7 @@ struct Launch {
     int mt_lead;         // per-step scan outputs have F + mt_lead slots per (b, h); forward: the
                          //   initial state goes to slot 0 and M_f to slot f + 1 when set
     void* crec;          // workspace (backward): per-frame records of C_f = Q_f^T dO_f
-    void* gt;            // workspace (backward): G_f = dL/dM_f (transposed, I/O type), slot f + 1
+    void* gt;            // workspace (backward): G_f = dL/dM_f (transposed, fp32), slot f + 1
     const void* d_o;     // backward: dL/dO (O strides)
     const float* d_state_out;  // backward: dL/dstate_out (NULL: zero)
     float* d_state_in;   // backward: dL/dstate_in (NULL: not returned)
@@ -54,7 +54,8 @@ struct Launch {
 // Kernels the runtime can launch (also the trace kinds of the C ABI).
 enum Kernel {
     K_PRODUCTS = 0, K_COMBINE = 1, K_SCAN = 2, K_STEP_PARTIAL = 3, K_STEP_REDUCE = 4,
-    K_FUSED_RESET = 5, K_FUSED = 6, K_SCAN_BWD = 7, K_BWD = 8
+    K_FUSED_RESET = 5, K_FUSED = 6, K_SCAN_BWD = 7, K_BWD = 8,
+    K_SCAN_STATES = 9    // the forward scan with fp32 per-frame states (backward's recompute)
 };
 
 // Fused forward: value-column groups pipelined through the frame chain (one flag each per (b, h)).

@@ -375,7 +375,9 @@ template <int D, bool DELTA> struct ScanSlot {
 };
 constexpr int kGammaSeg = 4000;  // frames per gamma staging (a multiple of the scan ring size)
 
-template <typename T, int D, bool DELTA, int P, bool BWD>
+// OT: type of the per-step outputs (the I/O type for the forward's output products; fp32 for
+// the backward, whose dgamma needs the states and their gradients unrounded).
+template <typename T, int D, bool DELTA, int P, bool BWD, typename OT>
 __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
     constexpr int NC = 16;              // value columns per workgroup
     constexpr int NCB = D / NC;         // column blocks per head
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
     const int lead = L.mt_lead;         // per-step outputs have F + lead slots per (b, h)
     const char* rec_bh = (const char*)L.canon + (int64_t)bh * F * REC;
     const char* crec_bh = (const char*)L.crec + (int64_t)bh * F * CREC;
-    T* mt_bh = (T*)L.mt + (int64_t)bh * (F + lead) * D * D;
+    OT* mt_bh = (OT*)L.mt + (int64_t)bh * (F + lead) * D * D;
 
     float Mc[4];
 #pragma unroll
@@ -953,7 +955,7 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
 //     dKt = beta R G^T - gamma beta (Kt G) M_{f-1}^T,   R = V - gamma P,   dK = c dKt
 //     dgamma = <G, M_{f-1}> - beta <Kt G, P>            dbeta = <Kt G, R>
 // (no delta term: R = V and only the first term of dKt and of dgamma). The states and G_f
-// come from the workspace in the I/O type, transposed ([c][n]), and are staged in LDS. Every
+// come from the workspace in fp32, transposed ([c][n]), and are staged in LDS as bf16. Every
 // product runs transposed on MFMA, so that each lane ends up with 4 consecutive feature rows
 // of one token: P^T and (Kt G)^T from A = M_{f-1}^T / G^T rows and B = K rows; their C tiles
 // are then the B operand of dKt^T = G (beta R^T) + M_{f-1} (-gamma beta (Kt G)^T), with the
@@ -1001,35 +1003,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
     bf16* Gs = sm + PLANE;      // G_f^T
     bf16* Mn = sm + 2 * PLANE;  // M_f^T
 
-    // stage the three matrices (slots f and f + 1 of the states, f + 1 of G) and form the frame
-    // term <G_f, M_{f-1}> of dgamma on the way
+    // stage the three matrices (fp32 slots f and f + 1 of the states, f + 1 of G) as bf16 and
+    // form the frame term <G_f, M_{f-1}> of dgamma from the fp32 values on the way
     float dg = 0.f, db = 0.f;
     {
-        const bf16* mt = (const bf16*)L.mt + ((int64_t)bh * (F + 1) + f) * D * D;
-        const bf16* gt = (const bf16*)L.gt + ((int64_t)bh * (F + 1) + f + 1) * D * D;
+        const float* mt = (const float*)L.mt + ((int64_t)bh * (F + 1) + f) * D * D;
+        const float* gt = (const float*)L.gt + ((int64_t)bh * (F + 1) + f + 1) * D * D;
         constexpr int NE = D * D / 8, PT = (NE + kBwdThreads - 1) / kBwdThreads;
-        u32x4 xm[PT], xg[PT], xn[PT];
+        f32x4 xm[PT][2], xg[PT][2], xn[PT][2];
 #pragma unroll
         for (int k = 0; k < PT; ++k) {
             const int e = min(tid + k * kBwdThreads, NE - 1);
-            xm[k] = ld16(mt + e * 8);
-            xg[k] = ld16(gt + e * 8);
-            xn[k] = ld16(mt + D * D + e * 8);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                xm[k][hh] = *(const f32x4*)(mt + e * 8 + 4 * hh);
+                xg[k][hh] = *(const f32x4*)(gt + e * 8 + 4 * hh);
+                xn[k][hh] = *(const f32x4*)(mt + D * D + e * 8 + 4 * hh);
+            }
         }
+        auto pack8 = [](const f32x4 (&x)[2]) {
+            return u32x4{pack_bf16x2(x[0][0], x[0][1]), pack_bf16x2(x[0][2], x[0][3]),
+                         pack_bf16x2(x[1][0], x[1][1]), pack_bf16x2(x[1][2], x[1][3])};
+        };
 #pragma unroll
         for (int k = 0; k < PT; ++k) {
             const int e = tid + k * kBwdThreads;
             if (NE % kBwdThreads == 0 || e < NE) {
                 const int row = e / (D / 8), cb8 = e % (D / 8);
-                st16(Mp + row * MR + cb8 * 8, xm[k]);
-                st16(Gs + row * MR + cb8 * 8, xg[k]);
-                st16(Mn + row * MR + cb8 * 8, xn[k]);
+                st16(Mp + row * MR + cb8 * 8, pack8(xm[k]));
+                st16(Gs + row * MR + cb8 * 8, pack8(xg[k]));
+                st16(Mn + row * MR + cb8 * 8, pack8(xn[k]));
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t a = xm[k][d], q = xg[k][d];
-                    dg += __builtin_bit_cast(float, a << 16) * __builtin_bit_cast(float, q << 16) +
-                          __builtin_bit_cast(float, a & 0xFFFF0000u) * __builtin_bit_cast(float, q & 0xFFFF0000u);
-                }
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) dg += xm[k][hh][q] * xg[k][hh][q];
             }
         }
     }
@@ -1427,8 +1434,15 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
     case K_SCAN: {
         if (L.s1 <= L.s0) return hipSuccess;
         const int units = (BH + 7) / 8 * 8 * (D / 16);
-        hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead, false>), dim3(units), dim3(64 * (D / 16)),
+        hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead, false, T>), dim3(units), dim3(64 * (D / 16)),
                            0, s, L);
+        break;
+    }
+    case K_SCAN_STATES: {
+        if (L.s1 <= L.s0) return hipSuccess;
+        const int units = (BH + 7) / 8 * 8 * (D / 16);
+        hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead, false, float>), dim3(units),
+                           dim3(64 * (D / 16)), 0, s, L);
         break;
     }
     case K_FUSED_RESET: {
@@ -1447,8 +1461,8 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
     case K_SCAN_BWD: {
         if (L.s1 <= L.s0) return hipSuccess;
         const int units = (BH + 7) / 8 * 8 * (D / 16);
-        hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead, true>), dim3(units), dim3(64 * (D / 16)),
-                           0, s, L);
+        hipLaunchKernelGGL((scan_kernel<T, D, DELTA, kScanAhead, true, float>), dim3(units),
+                           dim3(64 * (D / 16)), 0, s, L);
         break;
     }
     case K_BWD: {

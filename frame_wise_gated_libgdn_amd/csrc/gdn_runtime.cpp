@@ -6,7 +6,8 @@
 // Forward, fused:   reset of the ticket counter and frame flags -> fused kernel.
 // Step:             step_partial -> step_reduce -> products (output items of the one frame).
 // Backward:         products + [combine] + scan (forward states), products + [combine] of
-//                   C_f = Q_f^T dO_f, reverse scan (state gradients), per-frame gradients.
+//                   C_f = Q_f^T dO_f, reverse scan (state gradients), per-frame gradients;
+//                   the states and state gradients are kept in fp32.
 #include <vector>
 
 #include "../../include/libgdn.h"
@@ -93,7 +94,7 @@ hipError_t run_backward(const Launch& L0, hipStream_t s) {
     A.scan_in = L0.state_in;
     A.scan_out = nullptr;
     A.mt_lead = 1;
-    GDN_TRY(run.go(K_SCAN, A, s, BH * F));
+    GDN_TRY(run.go(K_SCAN_STATES, A, s, BH * F));
     // 2. C_f = Q_f^T dO_f of every frame: the gram products without the delta term and the
     //    gates, first operand Q (Q/K/V strides), second dO (O strides)
     Launch C = L0;

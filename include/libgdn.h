@@ -199,7 +199,8 @@ typedef enum {
     GDN_KERNEL_FUSED_RESET = 5,   /* fused: clears the ticket counter and frame flags */
     GDN_KERNEL_FUSED = 6,         /* fused: products, state step and outputs of every frame */
     GDN_KERNEL_SCAN_BWD = 7,      /* backward: reverse scan of the state gradients */
-    GDN_KERNEL_BWD = 8            /* backward: per-frame gradients of Q, K, V, gamma, beta */
+    GDN_KERNEL_BWD = 8,           /* backward: per-frame gradients of Q, K, V, gamma, beta */
+    GDN_KERNEL_SCAN_STATES = 9    /* backward: forward scan keeping every state in fp32 */
 } gdn_kernel_kind;
 
 typedef struct {

@@ -234,8 +234,8 @@ def test_backward_validation():
 def test_backward_workspace():
     p = prob(F=30)
     n = gdn.workspace_size(p, 2)
-    # forward states and state gradients (F + 1 slots), the forward records and C_f records
-    assert n >= 2 * (31 * 2 * 64 * 64 * 2) + 30 * 2 * 64 * 64 * 4
+    # fp32 forward states and state gradients (F + 1 slots), the forward records and C_f records
+    assert n >= 2 * (31 * 2 * 64 * 64 * 4) + 30 * 2 * 64 * 64 * 4
     assert gdn.workspace_size(prob(F=60), 2) > n
     n3 = ctypes.c_size_t(0)
     assert gdn.load().gdn_workspace_size(ctypes.byref(p), 3, ctypes.byref(n3)) == 2
