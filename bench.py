@@ -15,6 +15,11 @@ Prints one JSON line. Extra objects:
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
   stream        streaming step mode (gdn_step_frame): 4 denoising passes per frame, state
                 committed after the last; per-frame latency and frames/s.
+  fp8           the same forward from E4M3 Q, K, V with per-frame scales
+                (gdn_forward_framewise_fp8): ms per call and its own roofline (Q, K, V at one
+                byte per element, O at two).
+  backward      gdn_backward_framewise over the workload: ms per call, per-kernel ms and the
+                call's roofline (Q, K, V, dO read; dQ, dK, dV written).
 """
 from __future__ import annotations
 
@@ -84,6 +89,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--stream-frames", type=int, default=240)
     ap.add_argument("--schedule", default="auto", choices=["auto", "staged", "fused"],
@@ -274,6 +280,65 @@ def backward_mode(w, dev, steps, ev, stream):
                            "frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if bwd_ms else None}}
 
 
+def fp8_mode(dev, steps, warmup, ev, stream):
+    """The 720p forward from E4M3 Q, K, V (one scale per (b, h, f) and tensor), bf16 output."""
+    import torch
+    import frame_wise_gated_libgdn_amd as gdn
+    import gdn_synth
+    w = gdn_synth.WORKLOADS["gdn_720p_60s_fp8"]
+    (q, k, v), (sq, sk, sv) = gdn_synth.qkv_fp8_torch(w, dev)
+    g, b = gdn_synth.gates_torch(w, dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    p = gdn.Problem(w.B, w.H, w.D, w.S, w.F, gdn.GDN_FP8_E4M3, int(w.use_delta), 0.0,
+                    *q.stride()[:3], *o.stride()[:3])
+    ws = torch.empty(gdn.workspace_size(p, False), dtype=torch.uint8, device=dev)
+
+    def call():
+        gdn.forward_framewise_fp8(q, k, v, sq, sk, sv, g, b, use_delta=w.use_delta, out=o,
+                                  state_out=st, workspace=ws, stream=stream)
+
+    probe = [ev.new() for _ in range(2 * 16)]
+    gdn.set_trace(probe)
+    call()
+    plan = gdn.read_trace()
+    gdn.set_trace(None)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    nl = len(plan)
+    trace = [[ev.new() for _ in range(2 * nl)] for _ in range(steps)]
+    t0, t1 = ev.new(), ev.new()
+    sh = stream.cuda_stream
+    ev.record(t0, sh)
+    for i in range(steps):
+        gdn.set_trace(trace[i])
+        call()
+    gdn.set_trace(None)
+    ev.record(t1, sh)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    kms = {}
+    for i in range(steps):
+        for j, (kname, _, _) in enumerate(plan):
+            kms[kname] = kms.get(kname, 0.0) + ev.ms(trace[i][2 * j], trace[i][2 * j + 1]) / steps
+    n = w.B * w.H * w.F * w.S * w.D
+    bytes_alg = 3 * n * 1 + n * 2      # E4M3 Q, K, V read; bf16 O written (scales, gates ~0)
+    flops_alg = (6 if w.use_delta else 4) * n * w.D
+    t_roof = max(bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    fms = kms.get("fused", 0.0)
+    del q, k, v, o, ws
+    return {"workload": w.name, "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(w.B * w.F * w.S / (ms * 1e-3), 1),
+            "launches": [k_ for k_, _, _ in plan],
+            "kernel_ms_per_call": {k_: round(x, 4) for k_, x in kms.items()},
+            "call": {"bytes_alg_gb": round(bytes_alg / 1e9, 3), "t_roof_ms": round(t_roof, 4),
+                     "frac_of_roofline": round(t_roof / ms, 4),
+                     "achieved_gb_s": round(bytes_alg / (ms * 1e-3) / 1e9, 1)},
+            "fused_kernel": {"achieved_gb_s": round(bytes_alg / (fms * 1e-3) / 1e9, 1) if fms else None,
+                             "frac": round(bytes_alg / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if fms else None}}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -408,6 +473,13 @@ def main():
         result["stream"] = stream_mode(dev, args.stream_frames, ev2, sh)
         ev2.close()
         log("stream done: %s" % result["stream"]["frame_latency_ms"])
+    if not args.no_fp8 and w.name == "gdn_720p_60s_bf16":
+        ev4 = HipEvents()
+        log("fp8 inputs: %d calls" % args.steps)
+        result["fp8"] = fp8_mode(dev, args.steps, args.warmup, ev4, torch.cuda.current_stream())
+        ev4.close()
+        torch.cuda.empty_cache()
+        log("fp8 done: %.3f ms/call" % result["fp8"]["ms_per_call"])
     if not args.no_backward and w.dtype == "bf16" and w.D in (64, 128):
         ev3 = HipEvents()
         log("backward: %d calls" % args.backward_steps)

@@ -22,7 +22,7 @@ __all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "for
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
-GDN_F32, GDN_BF16 = 0, 1
+GDN_F32, GDN_BF16, GDN_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_STRIDE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
           8: "GDN_ERR_HIP"}
@@ -83,6 +83,8 @@ def load():
             for fn in (lib.gdn_forward_framewise, lib.gdn_step_frame):
                 fn.argtypes = [P] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
                 fn.restype = ctypes.c_int
+            lib.gdn_forward_framewise_fp8.argtypes = [P] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
+            lib.gdn_forward_framewise_fp8.restype = ctypes.c_int
             lib.gdn_backward_framewise.argtypes = [P] + [_vp] * 14 + [_vp, ctypes.c_size_t, _vp]
             lib.gdn_backward_framewise.restype = ctypes.c_int
             lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -146,7 +148,10 @@ def _dtype_code(t):
         return GDN_BF16
     if t.dtype == torch.float32:
         return GDN_F32
-    raise GdnError(3, "Q/K/V must be bfloat16 or float32, got %s" % t.dtype)
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return GDN_FP8_E4M3
+    raise GdnError(3, "Q/K/V must be bfloat16, float32, or E4M3 codes (uint8 / float8_e4m3fn), "
+                      "got %s" % t.dtype)
 
 
 def _ptr(t):
@@ -226,6 +231,41 @@ def forward_framewise(q, k, v, gamma, beta, state=None, *, use_delta=True, key_s
     _check(load().gdn_forward_framewise(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                         _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),
                                         _ptr(ws), nbytes, _stream(stream)))
+    return out, state_out
+
+
+def forward_framewise_fp8(q, k, v, q_scale, k_scale, v_scale, gamma, beta, state=None, *,
+                          use_delta=True, key_scale=None, out=None, state_out=None,
+                          return_state=True, workspace=None, stream=None, schedule="auto"):
+    """All frames from E4M3 inputs: q, k, v [B, H, F*S, D] of OCP FP8 E4M3 codes (torch.uint8
+    or torch.float8_e4m3fn, D contiguous, same strides); q_scale, k_scale, v_scale, gamma, beta
+    fp32 [B, H, F]; an element's value is its frame's scale times the code's value.
+    Returns (o, state_out) with o bf16 [B, H, F*S, D]."""
+    import torch
+    B, H, T, D = q.shape
+    F = gamma.shape[2]
+    if k.stride() != q.stride() or v.stride() != q.stride() or k.shape != q.shape \
+            or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise GdnError(4, "q, k and v must share shape, dtype and strides")
+    if _dtype_code(q) != GDN_FP8_E4M3:
+        raise GdnError(3, "forward_framewise_fp8 takes E4M3 codes (uint8 or float8_e4m3fn)")
+    if out is None:
+        out = torch.empty((B, H, T, D), dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16:
+        raise GdnError(3, "the output of the E4M3 forward is bfloat16")
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    for name, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale),
+                    ("gamma", gamma), ("beta", beta)):
+        _check_f32(name, t, (B, H, F))
+    _check_f32("state", state, (B, H, D, D))
+    _check_f32("state_out", state_out, (B, H, D, D))
+    p = _problem(q, out, F, use_delta, key_scale, schedule)
+    ws, nbytes = _workspace(p, False, workspace, q.device)
+    _check(load().gdn_forward_framewise_fp8(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+        _ptr(gamma), _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out), _ptr(ws), nbytes,
+        _stream(stream)))
     return out, state_out
 
 

@@ -47,8 +47,18 @@ struct Plan {
 // The fused forward pays off once there are enough (b, h, f) items to fill the chip.
 constexpr int64_t kFusedMinItems = 1024;
 
+// The fused kernel reads a frame's K and V rows through 32-bit buffer offsets: the bytes from
+// a frame's first row to the end of its last must stay below 2 GiB.
+bool fused_rows_fit(const gdn_problem& p) {
+    const int64_t esz = p.dtype == GDN_FP8_E4M3 ? 1 : 2;
+    const int64_t span = ((int64_t)(p.tokens_per_frame - 1) * p.qkv_stride_t + p.head_dim) * esz;
+    return p.qkv_stride_t >= 0 && span < ((int64_t)1 << 31);
+}
+
 bool choose_fused(const gdn_problem& p, int step_mode) {
+    if (!step_mode && p.dtype == GDN_FP8_E4M3) return true;  // E4M3 runs only fused
     if (step_mode || !gdn::fused_supported(p.dtype == GDN_BF16, p.head_dim)) return false;
+    if (!fused_rows_fit(p)) return false;
     if (p.schedule == GDN_SCHEDULE_FUSED) return true;
     if (p.schedule == GDN_SCHEDULE_STAGED) return false;
     return (int64_t)p.batch * p.heads * p.frames >= kFusedMinItems;
@@ -65,7 +75,7 @@ Plan make_plan(const gdn_problem& p, int mode) {
     const int64_t D = p.head_dim, S = p.tokens_per_frame;
     const int64_t BH = (int64_t)p.batch * p.heads;
     const int64_t F = step_mode ? 1 : p.frames;
-    const int64_t esz = p.dtype == GDN_BF16 ? 2 : 4;
+    const int64_t esz = p.dtype == GDN_F32 ? 4 : 2;
     const int64_t tiles64 = (S + 63) / 64;
     int64_t want;
     if (step_mode) {
@@ -119,13 +129,24 @@ gdn_status check_sizes(const gdn_problem* p, int mode) {
     const int D = p->head_dim;
     if (D != 16 && D != 32 && D != 64 && D != 128)
         return fail(GDN_ERR_UNSUPPORTED, "head_dim %d not supported (16, 32, 64, 128)", D);
-    if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+    if (p->dtype != GDN_F32 && p->dtype != GDN_BF16 && p->dtype != GDN_FP8_E4M3)
         return fail(GDN_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
+    if (p->dtype == GDN_FP8_E4M3) {
+        if (mode != 0)
+            return fail(GDN_ERR_UNSUPPORTED, "E4M3 inputs: the forward over all frames only");
+        if (D != 64 && D != 128)
+            return fail(GDN_ERR_UNSUPPORTED, "E4M3 inputs need D = 64 or 128");
+        if (p->schedule == GDN_SCHEDULE_STAGED)
+            return fail(GDN_ERR_UNSUPPORTED, "E4M3 inputs run on the fused schedule only");
+    }
     if (p->schedule < GDN_SCHEDULE_AUTO || p->schedule > GDN_SCHEDULE_FUSED)
         return fail(GDN_ERR_SHAPE, "schedule must be 0, 1 or 2, got %d", p->schedule);
     if (mode == 0 && p->schedule == GDN_SCHEDULE_FUSED &&
-        !gdn::fused_supported(p->dtype == GDN_BF16, D))
+        !gdn::fused_supported(p->dtype != GDN_F32, D))
         return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs bf16 data and D = 64 or 128");
+    if (mode == 0 && (p->schedule == GDN_SCHEDULE_FUSED || p->dtype == GDN_FP8_E4M3) &&
+        !fused_rows_fit(*p))
+        return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs a frame's q/k/v rows within 2 GiB");
     if (mode == 2 && !gdn::backward_supported(p->dtype == GDN_BF16, D))
         return fail(GDN_ERR_UNSUPPORTED, "the backward needs bf16 data and D = 64 or 128");
     const int64_t F = step_mode ? 1 : p->frames;
@@ -168,18 +189,28 @@ bool layout_ok(int64_t B, int64_t H, int64_t T, int64_t D, int64_t sb, int64_t s
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// scales: the three E4M3 scale arrays (gdn_forward_framewise_fp8), or NULL
 gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k, const void* v,
-               const float* gamma, const float* beta, const float* state_in, void* o,
-               float* state_out, void* ws, size_t ws_bytes, void* stream) {
+               const float* const* scales, const float* gamma, const float* beta,
+               const float* state_in, void* o, float* state_out, void* ws, size_t ws_bytes,
+               void* stream) {
     g_msg[0] = '\0';
     gdn_status s = check_sizes(p, step_mode);
     if (s != GDN_OK) return s;
+    const bool fp8 = p->dtype == GDN_FP8_E4M3;
+    if (fp8 && !scales)
+        return fail(GDN_ERR_UNSUPPORTED, "E4M3 inputs go through gdn_forward_framewise_fp8");
+    if (!fp8 && scales)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_forward_framewise_fp8 needs dtype GDN_FP8_E4M3");
     const int64_t B = p->batch, H = p->heads, D = p->head_dim, S = p->tokens_per_frame;
     const int64_t F = step_mode ? 1 : p->frames;
     const int64_t T = F * S;
-    const int64_t esz = p->dtype == GDN_BF16 ? 2 : 4;
+    const int64_t esz = fp8 ? 1 : p->dtype == GDN_BF16 ? 2 : 4;   // Q, K, V
+    const int64_t oesz = fp8 ? 2 : esz;                             // O
     if (!q || !k || !v || !o || !gamma || !beta)
         return fail(GDN_ERR_NULL, "q, k, v, o, gamma and beta are required");
+    if (fp8 && (!scales[0] || !scales[1] || !scales[2]))
+        return fail(GDN_ERR_NULL, "q_scale, k_scale and v_scale are required");
     if (step_mode && !state_in) return fail(GDN_ERR_NULL, "state_in is required in step mode");
     if (!layout_ok(B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t))
         return fail(GDN_ERR_STRIDE, "q/k/v strides (%lld, %lld, %lld) overlap rows or are negative",
@@ -196,6 +227,9 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     for (const void* ptr : {(const void*)gamma, (const void*)beta, (const void*)state_in,
                             (const void*)state_out})
         if (ptr && !aligned(ptr, 4)) return fail(GDN_ERR_ALIGN, "gates and states must be 4-byte aligned");
+    if (fp8)
+        for (int i = 0; i < 3; ++i)
+            if (!aligned(scales[i], 4)) return fail(GDN_ERR_ALIGN, "scales must be 4-byte aligned");
 
     const Plan pl = make_plan(*p, step_mode);
     const size_t need = pl.total();
@@ -203,7 +237,7 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     const Span sq = span_of(q, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
     const Span sk = span_of(k, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
     const Span sv = span_of(v, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
-    const Span so = span_of(o, B, H, T, D, p->o_stride_b, p->o_stride_h, p->o_stride_t, esz);
+    const Span so = span_of(o, B, H, T, D, p->o_stride_b, p->o_stride_h, p->o_stride_t, oesz);
     const Span sg = {(const char*)gamma, (const char*)(gamma + B * H * F)};
     const Span sbt = {(const char*)beta, (const char*)(beta + B * H * F)};
     const Span none = {nullptr, nullptr};
@@ -212,6 +246,12 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     const Span sso = state_out ? Span{(const char*)state_out, (const char*)(state_out + B * H * D * D)} : none;
     for (Span in : {sq, sk, sv, sg, sbt, si, sw})
         if (overlap(so, in)) return fail(GDN_ERR_ALIAS, "o overlaps an input or the workspace");
+    if (fp8)
+        for (int i = 0; i < 3; ++i) {
+            const Span sc = {(const char*)scales[i], (const char*)(scales[i] + B * H * F)};
+            if (overlap(so, sc) || overlap(sw, sc) || (state_out && overlap(sso, sc)))
+                return fail(GDN_ERR_ALIAS, "an output or the workspace overlaps a scale array");
+        }
     for (Span in : {sq, sk, sv, sg, sbt, so, si})
         if (overlap(sw, in)) return fail(GDN_ERR_ALIAS, "workspace overlaps an input or output");
     if (state_out) {
@@ -228,6 +268,10 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     gdn::Launch L{};
     L.B = (int)B; L.H = (int)H; L.D = (int)D; L.S = (int)S; L.F = (int)F;
     L.bf16 = p->dtype == GDN_BF16;
+    L.fp8 = fp8;
+    if (fp8) {
+        L.q_scale = scales[0]; L.k_scale = scales[1]; L.v_scale = scales[2];
+    }
     L.use_delta = p->use_delta != 0;
     L.c = p->key_scale > 0.f ? p->key_scale : (float)(1.0 / std::sqrt((double)D * (double)S));
     L.q = q; L.k = k; L.v = v; L.o = o;
@@ -238,6 +282,13 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     if (pl.fused) {
         L.ctl = (int*)ws;
         L.chain = (float*)((char*)ws + align256(pl.ctl_bytes));
+        // the fused kernel finds the end of a frame's rows from the token stride (rows past
+        // the frame read as zero); a single-token tensor may carry any token stride, which
+        // addresses nothing else, so give it one row's length
+        if (T == 1) {
+            L.st = std::max<int64_t>(L.st, D);
+            L.ot = std::max<int64_t>(L.ot, D);
+        }
     } else {
         L.canon = ws;
         L.part = (float*)((char*)ws + align256(pl.canon_bytes));
@@ -362,16 +413,26 @@ gdn_status gdn_forward_framewise(const gdn_problem* p, const void* q, const void
                                  const float* gamma, const float* beta, const float* state_in,
                                  void* o, float* state_out, void* workspace, size_t workspace_bytes,
                                  void* hip_stream) {
-    return run(0, p, q, k, v, gamma, beta, state_in, o, state_out, workspace, workspace_bytes,
-               hip_stream);
+    return run(0, p, q, k, v, nullptr, gamma, beta, state_in, o, state_out, workspace,
+               workspace_bytes, hip_stream);
+}
+
+gdn_status gdn_forward_framewise_fp8(const gdn_problem* p, const void* q, const void* k,
+                                     const void* v, const float* q_scale, const float* k_scale,
+                                     const float* v_scale, const float* gamma, const float* beta,
+                                     const float* state_in, void* o, float* state_out,
+                                     void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const float* scales[3] = {q_scale, k_scale, v_scale};
+    return run(0, p, q, k, v, scales, gamma, beta, state_in, o, state_out, workspace,
+               workspace_bytes, hip_stream);
 }
 
 gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, const void* v,
                           const float* gamma, const float* beta, const float* state_in, void* o,
                           float* state_out, void* workspace, size_t workspace_bytes,
                           void* hip_stream) {
-    return run(1, p, q, k, v, gamma, beta, state_in, o, state_out, workspace, workspace_bytes,
-               hip_stream);
+    return run(1, p, q, k, v, nullptr, gamma, beta, state_in, o, state_out, workspace,
+               workspace_bytes, hip_stream);
 }
 
 gdn_status gdn_backward_framewise(const gdn_problem* p, const void* q, const void* k,
@@ -401,7 +462,7 @@ const char* gdn_status_string(gdn_status s) {
     case GDN_OK: return "ok";
     case GDN_ERR_NULL: return "null pointer";
     case GDN_ERR_SHAPE: return "bad shape";
-    case GDN_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case GDN_ERR_UNSUPPORTED: return "unsupported head_dim, dtype or mode";
     case GDN_ERR_STRIDE: return "bad strides";
     case GDN_ERR_ALIGN: return "misaligned pointer or stride";
     case GDN_ERR_ALIAS: return "overlapping buffers";

@@ -13,6 +13,8 @@ namespace gdn {
 struct Launch {
     int B, H, D, S, F;
     int bf16;            // 1: Q/K/V/O are bf16; 0: fp32
+    int fp8;             // 1: Q/K/V are OCP FP8 E4M3 codes with per-frame scales, O is bf16
+    const float *q_scale, *k_scale, *v_scale;  // fp8: [B][H][F] scales of Q, K, V
     int use_delta;
     float c;             // key scale
     const void *q, *k, *v;

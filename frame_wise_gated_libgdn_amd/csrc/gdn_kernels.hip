@@ -62,6 +62,21 @@ template <> struct Mma<float> {
 };
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *(const u32x2*)p; }
+
+// Buffer resource over `bytes` bytes at p (raw dword access; accesses past the end read zero)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// Eight OCP FP8 E4M3 codes (byte i = element i) to eight bf16 values (exact: every E4M3 value,
+// subnormals included, is a bf16 value); gfx950's scaled conversion with a unit scale.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 w) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true))};
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 
 template <typename T> __device__ __forceinline__ typename Mma<T>::frag ld_frag(const T* p);
@@ -95,12 +110,13 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 // LDS tile holding 64 tokens of K and V transposed: row = feature (K features 0..D-1, V
 // features D..2D-1), tokens contiguous along the row. The 16-byte column blocks of each row are
 // XOR-swizzled so that the transposing writes and the MFMA fragment reads spread over banks.
-template <typename T, int D> struct XTile {
-    static constexpr int SC = 64;                      // tokens per chunk
+template <typename T, int D, int SC_ = 64> struct XTile {
+    static constexpr int SC = SC_;                     // tokens per chunk
     static constexpr int RB = SC * (int)sizeof(T);     // bytes per row
     static constexpr int NCB = RB / 16;                // column blocks per row
     static constexpr int ROWS = 2 * D;
     static constexpr int BYTES = ROWS * RB;
+    // XOR swizzle of the 16-byte column blocks of a row
     static __device__ __forceinline__ int swz(int row) {
         if constexpr (NCB == 8) return ((row >> 1) ^ (row >> 3)) & 7;
         else return row & (NCB - 1);
@@ -115,10 +131,11 @@ template <typename T, int D> struct XTile {
 // Global -> registers -> transposed LDS staging of one chunk of K and V. A thread moves
 // VE x VE blocks (VE tokens x VE features, VE = elements per 16 bytes): VE row loads, a register
 // transpose, VE row stores into the LDS tile.
-template <typename T, int D, int NTH = NT> struct XStage {
+template <typename T, int D, int NTH = NT, int SC = 64> struct XStage {
+    using Tile = XTile<T, D, SC>;
     static constexpr int VE = 16 / (int)sizeof(T);
     static constexpr int FB = 2 * D / VE;              // feature blocks (K then V)
-    static constexpr int TB = XTile<T, D>::SC / VE;    // token blocks
+    static constexpr int TB = SC / VE;                 // token blocks
     static constexpr int NBLK = FB * TB;
     static constexpr int PER = (NBLK + NTH - 1) / NTH;
     u32x4 r[PER][VE];
@@ -159,28 +176,143 @@ template <typename T, int D, int NTH = NT> struct XStage {
         }
     }
 
+    // block blk (VE tokens x VE features, rows as loaded) to the LDS tile, transposed
+    static __device__ __forceinline__ void store_block(const u32x4 (&rb)[VE], int blk, char* lds) {
+        const int fb = blk % FB, tb = blk / FB;
+#pragma unroll
+        for (int f = 0; f < VE; ++f) {
+            u32x4 w;
+            if constexpr (VE == 8) {
+                // feature f of tokens 2c, 2c+1 -> dword c
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t a = rb[2 * c][f >> 1], b = rb[2 * c + 1][f >> 1];
+                    w[c] = (f & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) w[c] = rb[c][f];
+            }
+            st16(lds + Tile::addr(fb * VE + f, tb * VE), w);
+        }
+    }
+
     __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+        for (int pi = 0; pi < PER; ++pi) {
+            const int blk = tid + pi * NTH;
+            if (NBLK % NTH == 0 || blk < NBLK) store_block(r[pi], blk, lds);
+        }
+    }
+
+    // Split-operand order: the first half of the threads (whole waves) moves K's blocks, the
+    // second half V's, so each wave reads through one buffer resource. Block blk1 of an operand
+    // is feature block blk1 % (D / VE), token block blk1 / (D / VE).
+    static constexpr int HALF = NTH / 2;
+    static_assert(HALF % 64 == 0, "each operand gets whole waves");
+    static constexpr int NB1 = (D / VE) * TB;
+    static constexpr int PER1 = (NB1 + HALF - 1) / HALF;
+    static_assert(PER1 <= PER, "split order fits the register blocks");
+    static __device__ __forceinline__ int split_block(int tid, int pi) {   // -> blk, or -1
+        const int op = tid / HALF, b1 = tid % HALF + pi * HALF;
+        if (NB1 % HALF != 0 && b1 >= NB1) return -1;
+        return (b1 / (D / VE)) * FB + op * (D / VE) + b1 % (D / VE);
+    }
+
+    // tokens [t0, t0 + SC) from buffers over the frame's rows of K (rk) and V (rv), token
+    // stride stb bytes; rows past the end of a buffer read as zero
+    __device__ __forceinline__ void load_rs(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int stb,
+                                            int t0, int tid) {
+        // the operand is a per-wave choice; readfirstlane lets the compiler keep it scalar
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_readfirstlane(tid >> 6) < HALF / 64 ? rk : rv;
+#pragma unroll
+        for (int pi = 0; pi < PER1; ++pi) {
+            const int blk = split_block(tid, pi);
+            if (blk >= 0) {
+                const int fb = blk % FB % (D / VE), tb = blk / FB;
+                const int vo = (t0 + tb * VE) * stb + fb * 16;
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    r[pi][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo + e * stb, 0, 0));
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store_rs(char* lds, int tid) const {
+#pragma unroll
+        for (int pi = 0; pi < PER1; ++pi) {
+            const int blk = split_block(tid, pi);
+            if (blk >= 0) store_block(r[pi], blk, lds);
+        }
+    }
+};
+
+// XStage for 8-bit (E4M3) K and V: the same blocks of 8 tokens x 8 features, loaded as 8 bytes
+// per row and kept as codes while in flight; decoded to bf16 when staged into LDS.
+template <int D, int NTH = NT, int SC = 64> struct XStage8 {
+    using Wide = XStage<bf16, D, NTH, SC>;
+    static constexpr int VE = Wide::VE, FB = Wide::FB, NBLK = Wide::NBLK, PER = Wide::PER;
+    u32x2 r[PER][VE];
+
+    __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, int64_t kst, int64_t vst,
+                                         int t0, int tend, int tid) {
 #pragma unroll
         for (int pi = 0; pi < PER; ++pi) {
             const int blk = tid + pi * NTH;
             if (NBLK % NTH == 0 || blk < NBLK) {
                 const int fb = blk % FB, tb = blk / FB;
+                const bool first = fb < D / VE;
+                const uint8_t* base = first ? kb + fb * VE : vb + (fb - D / VE) * VE;
+                const int64_t st = first ? kst : vst;
 #pragma unroll
-                for (int f = 0; f < VE; ++f) {
-                    u32x4 w;
-                    if constexpr (VE == 8) {
-                        // feature f of tokens 2c, 2c+1 -> dword c
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const uint32_t a = r[pi][2 * c][f >> 1], b = r[pi][2 * c + 1][f >> 1];
-                            w[c] = (f & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-                        }
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) w[c] = r[pi][c][f];
-                    }
-                    st16(lds + XTile<T, D>::addr(fb * VE + f, tb * VE), w);
+                for (int e = 0; e < VE; ++e) {
+                    const int tok = t0 + tb * VE + e;
+                    r[pi][e] = tok < tend ? ld8(base + (int64_t)tok * st) : u32x2{0u, 0u};
                 }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+        for (int pi = 0; pi < PER; ++pi) {
+            const int blk = tid + pi * NTH;
+            if (NBLK % NTH == 0 || blk < NBLK) {
+                u32x4 rb[VE];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) rb[e] = e4m3x8_to_bf16x8(r[pi][e]);
+                Wide::store_block(rb, blk, lds);
+            }
+        }
+    }
+
+    // split-operand order of XStage (load_rs / store_rs), 8 bytes per row
+    static constexpr int PER1 = Wide::PER1;
+    __device__ __forceinline__ void load_rs(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int stb,
+                                            int t0, int tid) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_readfirstlane(tid >> 6) < Wide::HALF / 64 ? rk : rv;
+#pragma unroll
+        for (int pi = 0; pi < PER1; ++pi) {
+            const int blk = Wide::split_block(tid, pi);
+            if (blk >= 0) {
+                const int fb = blk % FB % (D / VE), tb = blk / FB;
+                const int vo = (t0 + tb * VE) * stb + fb * 8;
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    r[pi][e] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, vo + e * stb, 0, 0));
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store_rs(char* lds, int tid) const {
+#pragma unroll
+        for (int pi = 0; pi < PER1; ++pi) {
+            const int blk = Wide::split_block(tid, pi);
+            if (blk >= 0) {
+                u32x4 rb[VE];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) rb[e] = e4m3x8_to_bf16x8(r[pi][e]);
+                Wide::store_block(rb, blk, lds);
             }
         }
     }
@@ -631,7 +763,7 @@ __global__ __launch_bounds__(NT, 2) void products_kernel(Launch L) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Fused forward (bf16 data, D = 64 or 128): one workgroup per (b, h, f) computes
+// Fused forward (bf16 or E4M3 data, D = 64 or 128): one workgroup per (b, h, f) computes
 //   1. the frame's products Ghat_f, Bhat_f (as gram_body, all S tokens, K and V staged in LDS),
 //   2. the state step M_f = gamma_f M_{f-1} + Bhat_f - Ghat_f M_{f-1} on MFMA, once M_{f-1} of
 //      the same (b, h) is published, then publishes M_f,
@@ -665,23 +797,25 @@ __global__ __launch_bounds__(NT, 2) void products_kernel(Launch L) {
 // n0 + 16 nb + r and k = 16 kb + 4 g + q, so the step's A operand needs no data movement: a
 // 32-long MFMA k step ks takes tiles 2 ks and 2 ks + 1 in its lane slots 0-3 and 4-7. The B
 // operand (M_{f-1} split into bf16 hi + lo) is laid out in LDS with the same k order.
+//
+// E4M3 inputs (FP8): Q, K and V arrive as 8-bit codes with one scale per (b, h, f) and tensor.
+// The codes are decoded exactly to bf16 on the way into LDS or into MFMA operands, the
+// products run on the codes, and the scales enter as scalars: Ghat takes k_scale^2, Bhat
+// k_scale v_scale, and the output tile q_scale before rounding to bf16.
 constexpr int kSpinLimit = 1 << 20;  // polls of about a microsecond each
 constexpr int kCoherent = 16;        // cache-policy operand of the buffer intrinsics: sc1
 
-// Buffer resource over `bytes` bytes at p (raw dword access; accesses past the end read zero)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
-}
 
 __global__ void fused_reset_kernel(int* ctl, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) ctl[i] = i < 2 ? 0 : -1;
 }
 
-template <int D, bool DELTA>
+template <int D, bool DELTA, bool FP8>
 __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
     using MM = Mma<bf16>;
-    using X = XTile<bf16, D>;
+    constexpr int SC = 64;          // tokens per staged chunk (128 measured slower for E4M3)
+    using X = XTile<bf16, D, SC>;
     static_assert(D == 64 || D == 128, "fused path: D = 64 or 128");
     constexpr int NR = D / 4;       // key rows per wave
     constexpr int NB = NR / 16;     // 16-row blocks per wave
@@ -713,15 +847,21 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
         for (int cb = 0; cb < CB; ++cb) bacc[nb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     {
-        const bf16* kp = (const bf16*)L.k + fo;
-        const bf16* vp = (const bf16*)L.v + fo;
-        XStage<bf16, D> stg;
-        stg.load(kp, vp, L.st, L.st, 0, S, tid);
+        // K and V rows of the frame through buffer resources that end with the frame's last
+        // row, so the ragged last chunk reads zeros without a branch per row (the host keeps
+        // a frame's rows within 2 GiB for the fused schedule)
+        constexpr int ESZ = FP8 ? 1 : 2;
+        const int stb = (int)L.st * ESZ;
+        const int fbytes = ((S - 1) * (int)L.st + D) * ESZ;
+        const __amdgpu_buffer_rsrc_t rk = buffer_over((const char*)L.k + fo * ESZ, fbytes);
+        const __amdgpu_buffer_rsrc_t rv = buffer_over((const char*)L.v + fo * ESZ, fbytes);
+        typename std::conditional<FP8, XStage8<D, NT, SC>, XStage<bf16, D, NT, SC>>::type stg;
+        stg.load_rs(rk, rv, stb, 0, tid);
         for (int c0 = 0; c0 < S; c0 += X::SC) {
             __syncthreads();  // readers of the previous chunk are done
-            stg.store(lds, tid);
+            stg.store_rs(lds, tid);
             __syncthreads();
-            if (c0 + X::SC < S) stg.load(kp, vp, L.st, L.st, c0 + X::SC, S, tid);
+            if (c0 + X::SC < S) stg.load_rs(rk, rv, stb, c0 + X::SC, tid);
 #pragma unroll
             for (int ks = 0; ks < X::SC / MM::KS; ++ks) {
                 const int tok = ks * MM::KS + g * MM::KL;
@@ -748,7 +888,12 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
     }
     const int gi = bh * F + f;
     const float gm = L.gamma[gi], bt = L.beta[gi];
-    const float sG = gm * bt * L.c * L.c, sB = bt * L.c;
+    float sG = gm * bt * L.c * L.c, sB = bt * L.c;
+    if constexpr (FP8) {
+        const float sk = L.k_scale[gi];
+        sG *= sk * sk;
+        sB *= sk * L.v_scale[gi];
+    }
     // -Ghat as bf16 hi + lo (A operand of the step), Bhat scaled in place
     uint32_t gh[DELTA ? KB : 1][NB][2], gl[DELTA ? KB : 1][NB][2];
     if constexpr (DELTA) {
@@ -909,41 +1054,64 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
 #pragma unroll
         for (int ks = 0; ks < KSN; ++ks)
             am[jt][ks] = ld_frag<bf16>(Mt + out_col<bf16, D>(jt, r16) * MR + ks * MM::KS + g * MM::KL);
-    const bf16* qf = (const bf16*)L.q + fo;
-    bf16* of = (bf16*)L.o + (int64_t)b * L.ob + (int64_t)h * L.oh + (int64_t)f * S * L.ot;
-    auto load_q = [&](int s0, bf16x8 (&bq)[KSN]) {
-        const int s = s0 + r16;
-        const bool in = s < S;
+    // Q tiles read and O tiles written through buffer resources that end with the frame's
+    // last row, so tiles past S read zeros and drop their stores without branches; each wave
+    // keeps QD tiles of Q in flight (a ring, unrolled so that every slot is a register)
+    constexpr int ESZ = FP8 ? 1 : 2;
+    constexpr int QD = 4;
+    const __amdgpu_buffer_rsrc_t rq =
+        buffer_over((const char*)L.q + fo * ESZ, ((S - 1) * (int)L.st + D) * ESZ);
+    const __amdgpu_buffer_rsrc_t ro = buffer_over(
+        (char*)L.o + ((int64_t)b * L.ob + (int64_t)h * L.oh + (int64_t)f * S * L.ot) * 2,
+        ((S - 1) * (int)L.ot + D) * 2);
+    const int qstb = (int)L.st * ESZ, ostb = (int)L.ot * 2;
+    const float oscale = FP8 ? L.q_scale[gi] : 1.f;
+    // Q fragments as loaded: 8 bf16 values, or 8 E4M3 codes decoded when used
+    using QRaw = typename std::conditional<FP8, u32x2, u32x4>::type;
+    auto load_q = [&](int s0, QRaw (&bq)[KSN]) {
+        const int vo = (s0 + r16) * qstb + (g * MM::KL) * ESZ;
 #pragma unroll
-        for (int ks = 0; ks < KSN; ++ks)
-            bq[ks] = in ? ld_frag<bf16>(qf + (int64_t)s * L.st + ks * MM::KS + g * MM::KL) : zero_frag<bf16>();
-    };
-    bf16x8 bq[KSN];
-    load_q(wave * 16, bq);
-    for (int s0 = wave * 16; s0 < S; s0 += 4 * 16) {
-        const int s = s0 + r16;
-        const bool in = s < S;
-        bf16x8 bn[KSN];
-        load_q(s0 + 4 * 16, bn);  // next tile of this wave, in flight during this one
-        f32x4 acc[TJ];
-#pragma unroll
-        for (int jt = 0; jt < TJ; ++jt) {
-            acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KSN; ++ks) acc[jt] = MM::run(am[jt][ks], bq[ks], acc[jt]);
+        for (int ks = 0; ks < KSN; ++ks) {
+            if constexpr (FP8)
+                bq[ks] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, vo + ks * MM::KS, 0, 0));
+            else
+                bq[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vo + ks * MM::KS * 2, 0, 0));
         }
-        if (in) {
-            bf16* orow = of + (int64_t)s * L.ot;
+    };
+    QRaw bq[QD][KSN];
+#pragma unroll
+    for (int d = 0; d < QD; ++d) load_q(wave * 16 + d * 64, bq[d]);
+    for (int s0 = wave * 16; s0 < S; s0 += QD * 64) {
+#pragma unroll
+        for (int d = 0; d < QD; ++d) {
+            const int st = s0 + d * 64;   // this tile; all lanes past S when st >= S
+            bf16x8 bw[KSN];
+#pragma unroll
+            for (int ks = 0; ks < KSN; ++ks) {
+                if constexpr (FP8)
+                    bw[ks] = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(bq[d][ks]));
+                else
+                    bw[ks] = __builtin_bit_cast(bf16x8, bq[d][ks]);
+            }
+            load_q(st + QD * 64, bq[d]);  // the tile QD steps ahead, into the freed slot
+            f32x4 acc[TJ];
+#pragma unroll
+            for (int jt = 0; jt < TJ; ++jt) {
+                acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSN; ++ks) acc[jt] = MM::run(am[jt][ks], bw[ks], acc[jt]);
+                if constexpr (FP8) acc[jt] *= oscale;
+            }
+            const int oo = (st + r16) * ostb;
 #pragma unroll
             for (int p = 0; p < TJ / 2; ++p) {
                 const f32x4 x = acc[2 * p], y = acc[2 * p + 1];
-                st16(orow + 32 * p + 8 * g,
-                     u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                           pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])});
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
+                          pack_bf16x2(y[2], y[3])},
+                    ro, oo + (32 * p + 8 * g) * 2, 0, 0);
             }
         }
-#pragma unroll
-        for (int ks = 0; ks < KSN; ++ks) bq[ks] = bn[ks];
     }
 }
 
@@ -1452,7 +1620,10 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
     }
     case K_FUSED: {
         if constexpr (std::is_same<T, bf16>::value && (D == 64 || D == 128)) {
-            hipLaunchKernelGGL((fused_kernel<D, DELTA>), dim3(BH * L.F), dim3(NT), 0, s, L);
+            if (L.fp8)
+                hipLaunchKernelGGL((fused_kernel<D, DELTA, true>), dim3(BH * L.F), dim3(NT), 0, s, L);
+            else
+                hipLaunchKernelGGL((fused_kernel<D, DELTA, false>), dim3(BH * L.F), dim3(NT), 0, s, L);
         } else {
             return hipErrorInvalidValue;
         }
@@ -1488,6 +1659,7 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
     return hipGetLastError();
 }
 
+// bf16_data: bf16 or E4M3 inputs (E4M3 runs only on the fused kernel)
 bool fused_supported(int bf16_data, int D) { return bf16_data && (D == 64 || D == 128); }
 bool backward_supported(int bf16_data, int D) { return bf16_data && (D == 64 || D == 128); }
 
@@ -1495,7 +1667,7 @@ hipError_t launch_kernel(Kernel k, const Launch& L, hipStream_t s) {
     const bool dl = L.use_delta != 0;
 #define GDN_CASE(T, D) \
     case D: return dl ? launch<T, D, true>(k, L, s) : launch<T, D, false>(k, L, s);
-    if (L.bf16) {
+    if (L.bf16 || L.fp8) {
         switch (L.D) { GDN_CASE(bf16, 16) GDN_CASE(bf16, 32) GDN_CASE(bf16, 64) GDN_CASE(bf16, 128) }
     } else {
         switch (L.D) { GDN_CASE(float, 16) GDN_CASE(float, 32) GDN_CASE(float, 64) GDN_CASE(float, 128) }

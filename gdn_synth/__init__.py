@@ -15,6 +15,11 @@ Generator (counter-based, so any (tensor, b, h, f, pass) slice can be made on it
   quantile rounded to fp32 (scipy.special.ndtri), i.e. an exact-quantile N(0, 1) with 2**24
   levels. bf16 tensors take round-to-nearest-even of that fp32 value.
 * Uniform gates: lo + (hi - lo) * ((w >> 8) + 0.5) / 2**24 in fp64, rounded to fp32.
+* E4M3 workloads (8-bit Q, K, V with one scale per (tensor, b, h, f)): the frame's fp32 normal
+  values x get the power-of-two scale s = 2**(E - 8), E the binary exponent of max|x| (max|x| =
+  m 2**E with m in [0.5, 1)), so that |x| / s < 256 stays inside E4M3's finite range (448);
+  x / s is then exact, and the codes are torch's round-to-nearest-even conversion to
+  float8_e4m3fn. Both the scale and the division are exact, so host and device codes agree.
 
 The host path uses numpy uint32 arithmetic; the device path uses torch int64 arithmetic whose
 intermediates stay below 2**49, so both are exact and produce identical bits.
@@ -130,7 +135,7 @@ class Workload:
     D: int
     S: int
     F: int                      # frames (forward) or frames streamed (step mode)
-    dtype: str                  # "f32" or "bf16" for Q, K, V, O
+    dtype: str                  # "f32" or "bf16" for Q, K, V, O; "fp8": E4M3 Q, K, V, bf16 O
     use_delta: bool
     gamma: tuple                # (lo, hi) of U(lo, hi); lo == hi means a constant
     beta: tuple
@@ -143,7 +148,8 @@ class Workload:
         return self.B * self.F * self.S
 
     def elem_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        """Bytes per element of Q, K and V."""
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
 
 
 WORKLOADS = {
@@ -157,10 +163,12 @@ WORKLOADS = {
                  (0.1, 0.9)),
         Workload("stream_720p_bf16", 4, 1, 16, 128, 3520, 240, "bf16", True, (0.9, 1.0),
                  (0.1, 0.9), passes=4, step_mode=True),
+        Workload("gdn_720p_60s_fp8", 5, 1, 16, 128, 3520, 961, "fp8", True, (0.9, 1.0),
+                 (0.1, 0.9)),
     ]
 }
 WORKLOAD_ORDER = ["tiny_f32", "block_causal_bf16", "gdn_880x81_bf16", "gdn_720p_60s_bf16",
-                  "stream_720p_bf16"]
+                  "stream_720p_bf16", "gdn_720p_60s_fp8"]
 
 
 def gates_cpu(w: Workload, heads=None, frames=None, pass_=0):
@@ -200,6 +208,45 @@ def qkv_cpu(w: Workload, heads=None, frames=None, pass_=0):
         out_vals.append(vals)
         out_raw.append(raw)
     return out_vals, out_raw
+
+
+def e4m3_codes(x, S, D):
+    """Quantise frames of fp32 values to E4M3 with one power-of-two scale per frame.
+
+    x: torch float32 [nf*S, D] (host or device). Returns (codes uint8 [nf*S, D], scales
+    float32 [nf]) on x's device."""
+    import torch
+    nf = x.shape[0] // S
+    xf = x.reshape(nf, S * D)
+    _, e = torch.frexp(xf.abs().amax(dim=1))
+    e = e.to(torch.int32)
+    # 2**(E - 8) and its inverse built from their bit patterns (exact, no libm)
+    scale = ((e - 8 + 127) << 23).view(torch.float32)
+    inv = ((8 - e + 127) << 23).view(torch.float32)
+    codes = (xf * inv[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.reshape(nf * S, D), scale
+
+
+def qkv_fp8_cpu(w: Workload, heads=None, frames=None, pass_=0):
+    """E4M3 Q, K, V for the selected heads/frames: codes uint8 [B, nh, nf*S, D] and scales
+    float32 [B, nh, nf], for each of Q, K, V (lists of three)."""
+    import torch
+    heads = range(w.H) if heads is None else list(heads)
+    frames = range(w.F) if frames is None else list(frames)
+    codes, scales = [], []
+    for tid in (TID_Q, TID_K, TID_V):
+        c = np.empty((w.B, len(heads), len(frames) * w.S, w.D), np.uint8)
+        sc = np.empty((w.B, len(heads), len(frames)), np.float32)
+        for b in range(w.B):
+            for hi, h in enumerate(heads):
+                for fi, f in enumerate(frames):
+                    z = torch.from_numpy(normal_slice(w.seed, tid, b, h, f, w.S, w.D, pass_))
+                    cc, ss = e4m3_codes(z, w.S, w.D)
+                    c[b, hi, fi * w.S:(fi + 1) * w.S] = cc.numpy()
+                    sc[b, hi, fi] = ss.numpy()[0]
+        codes.append(c)
+        scales.append(sc)
+    return codes, scales
 
 
 # --------------------------------------------------------------------------- device (torch)
@@ -250,11 +297,51 @@ class TorchGen:
             del w, z
 
 
+    def fill_e4m3(self, codes, scales, seed, tid, b, h, f0, S, D, pass_=0, chunk=32):
+        """Write E4M3 codes of frames f0 .. f0 + nf - 1 of slice (tid, b, h) into codes, a
+        [nf*S, D] uint8 view, and their scales into scales, a [nf] float32 view."""
+        torch = self.torch
+        nf = codes.shape[0] // S
+        eh = self.elem_hash(S * D)
+        for c0 in range(0, nf, chunk):
+            c1 = min(nf, c0 + chunk)
+            keys = torch.tensor([slice_key(seed, tid, b, h, f0 + f, pass_) for f in range(c0, c1)],
+                                dtype=torch.int64, device=self.device)
+            wd = self.hash32(eh[None, :] ^ keys[:, None])
+            z = self.table[wd >> (32 - NLEVELS_BITS)].view((c1 - c0) * S, D)
+            cc, ss = e4m3_codes(z, S, D)
+            codes[c0 * S:c1 * S].copy_(cc)
+            scales[c0:c1].copy_(ss)
+            del wd, z, cc, ss
+
+
 def gates_torch(w: Workload, device, pass_=0):
     """gamma, beta [B, H, F] fp32 on the device (made on the host: they are tiny)."""
     import torch
     g, bt = gates_cpu(w, pass_=pass_)
     return torch.from_numpy(g).to(device), torch.from_numpy(bt).to(device)
+
+
+def qkv_fp8_torch(w: Workload, device, layout="head", frames=None, pass_=0, gen=None):
+    """E4M3 Q, K, V on the device: ([q, k, v] uint8 codes [B, H, T, D] (layout as qkv_torch),
+    [q_scale, k_scale, v_scale] float32 [B, H, nf])."""
+    import torch
+    f0, nf = (0, w.F) if frames is None else frames
+    gen = gen or TorchGen(device)
+    T = nf * w.S
+    codes, scales = [], []
+    for tid in (TID_Q, TID_K, TID_V):
+        if layout == "head":
+            x = torch.empty((w.B, w.H, T, w.D), dtype=torch.uint8, device=device)
+        else:
+            x = torch.empty((w.B, T, w.H, w.D), dtype=torch.uint8, device=device).permute(0, 2, 1, 3)
+        sc = torch.empty((w.B, w.H, nf), dtype=torch.float32, device=device)
+        for b in range(w.B):
+            for h in range(w.H):
+                gen.fill_e4m3(x[b, h], sc[b, h], w.seed, tid, b, h, f0, w.S, w.D, pass_)
+        codes.append(x)
+        scales.append(sc)
+    return codes, scales
 
 
 def qkv_torch(w: Workload, device, layout="head", frames=None, pass_=0, gen=None):

@@ -39,7 +39,9 @@
  *   [B,T,H,D] storage are both expressible. Gates gamma, beta are fp32 [B][H][F] contiguous
  *   (step: [B][H]). States are fp32 [B][H][D][D] contiguous, row = key dim.
  * Types. Q, K, V, O are all GDN_F32 or all GDN_BF16; states and gates are always fp32;
- *   arithmetic accumulates in fp32; bf16 outputs are rounded to nearest even.
+ *   arithmetic accumulates in fp32; bf16 outputs are rounded to nearest even. With
+ *   GDN_FP8_E4M3 (gdn_forward_framewise_fp8 only) Q, K, V are 8-bit codes with per-frame
+ *   scales and O is bf16.
  * Supported shapes. D in {16, 32, 64, 128}; B, H, S, F >= 1; B*H*F*S*max-stride must fit the
  *   int64 element index. Pointers to Q, K, V, O must be 16-byte aligned, the strides multiples
  *   of 8 elements, gates and states 4-byte aligned (GDN_ERR_ALIGN otherwise).
@@ -63,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 2
+#define LIBGDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -77,7 +79,13 @@ typedef enum {
     GDN_ERR_HIP = 8           /* a HIP runtime call failed */
 } gdn_status;
 
-typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+/*
+ * GDN_FP8_E4M3: Q, K, V are OCP FP8 E4M3 codes (OCP 8-bit Floating Point Specification: sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, subnormals, S.1111.111 = NaN, no infinities),
+ * one byte per element (strides in elements = bytes), each with an fp32 scale per (b, h, f);
+ * O is bf16. Accepted only by gdn_forward_framewise_fp8.
+ */
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype;
 
 /*
  * How a forward is run. Both schedules compute the same recurrence; results agree to rounding
@@ -87,7 +95,8 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *           scan over those D x D records, then the outputs of every frame. Any dtype and D.
  *   FUSED   one pass: each (b, h, f) is a workgroup that computes its frame's products, waits
  *           for the state of frame f-1 of the same (b, h), applies the step, publishes M_f and
- *           writes O_f; only Q/K/V/O and the D x D states cross HBM. bf16 with D = 64 or 128
+ *           writes O_f; only Q/K/V/O and the D x D states cross HBM. bf16 (or E4M3) with
+ *           D = 64 or 128, and a frame's rows ((S-1) * qkv_stride_t + D elements) within 2 GiB
  *           (GDN_ERR_UNSUPPORTED otherwise).
  *   AUTO    FUSED where supported and B*H*F >= 1024, else STAGED.
  */
@@ -129,6 +138,27 @@ gdn_status gdn_forward_framewise(const gdn_problem* p, const void* q, const void
                                  const float* gamma, const float* beta, const float* state_in,
                                  void* o, float* state_out,
                                  void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * All F frames from 8-bit inputs (the low-precision Q/K/V that SANA-Streaming fuses with its
+ * GDN kernel through mixed-precision quantisation: jefxiong.cn daily digest, SANA-Streaming
+ * item, contribution (3); SANA-WM's NVFP4 deployment: chatpaper.ai English abstract).
+ * p->dtype must be GDN_FP8_E4M3; D = 64 or 128; the schedule is always FUSED (AUTO or FUSED
+ * accepted, STAGED is GDN_ERR_UNSUPPORTED).
+ *   q, k, v      E4M3 codes, [B,H,T,D] with the qkv strides (bytes); the value of an element
+ *                of frame f is scale[b][h][f] * E4M3(code), with the scale of its tensor
+ *   q_scale, k_scale, v_scale   fp32 [B][H][F] contiguous
+ *   o            bf16 output, o strides in elements
+ *   other arguments, errors and workspace (gdn_workspace_size(p, 0)) as gdn_forward_framewise.
+ * The recurrence runs on the scaled values; codes are decoded exactly, products of codes
+ * accumulate in fp32 and the scales are applied to those sums (K's twice in the key-key
+ * product), so the result equals the bf16 path on the decoded values up to rounding order.
+ */
+gdn_status gdn_forward_framewise_fp8(const gdn_problem* p, const void* q, const void* k,
+                                     const void* v, const float* q_scale, const float* k_scale,
+                                     const float* v_scale, const float* gamma, const float* beta,
+                                     const float* state_in, void* o, float* state_out,
+                                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * One frame for streaming / autoregressive rollout: compute the frame's contribution, add it

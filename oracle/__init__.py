@@ -26,6 +26,7 @@ _lock = threading.Lock()
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
+_u8p = ctypes.POINTER(ctypes.c_ubyte)
 
 
 def build(force: bool = False) -> str:
@@ -47,6 +48,12 @@ def _bind(path):
                                     + [ctypes.c_int])
     lib.gdn_oracle_step.restype = ctypes.c_int
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
+    if hasattr(lib, "gdn_oracle_forward_fp8"):
+        lib.gdn_oracle_e4m3.argtypes = [ctypes.c_uint]
+        lib.gdn_oracle_e4m3.restype = ctypes.c_double
+        lib.gdn_oracle_forward_fp8.argtypes = ([ctypes.c_int] * 6 + [ctypes.c_double] + [_u8p] * 3
+                                               + [_dp] * 8 + [ctypes.c_int])
+        lib.gdn_oracle_forward_fp8.restype = ctypes.c_int
     if hasattr(lib, "gdn_oracle_backward"):
         lib.gdn_oracle_backward.argtypes = ([ctypes.c_int] * 6 + [ctypes.c_double] + [_dp] * 14
                                             + [ctypes.c_int])
@@ -118,6 +125,40 @@ def forward(q, k, v, gamma, beta, state_in=None, *, use_delta=True, key_scale=No
                                     _ptr(so), int(nthreads))
     if rc != 0:
         raise RuntimeError("gdn_oracle_forward failed with code %d" % rc)
+    return o, so
+
+
+def e4m3_value(code: int, lib=None) -> float:
+    """Value of one OCP FP8 E4M3 code (0..255)."""
+    return float((lib or _load()).gdn_oracle_e4m3(int(code)))
+
+
+def forward_fp8(q8, k8, v8, q_scale, k_scale, v_scale, gamma, beta, state_in=None, *,
+                use_delta=True, key_scale=None, nthreads=0, lib=None):
+    """All frames from 8-bit inputs. q8, k8, v8: uint8 OCP FP8 E4M3 codes [B, H, F*S, D];
+    q_scale, k_scale, v_scale, gamma, beta: [B, H, F]; element value = scale[b, h, f] * E4M3(code).
+
+    Returns (o [B, H, F*S, D], state_out [B, H, D, D]) as fp64 arrays.
+    """
+    q8, k8, v8 = (np.ascontiguousarray(x, dtype=np.uint8) for x in (q8, k8, v8))
+    q_scale, k_scale, v_scale, gamma, beta = map(_f64, (q_scale, k_scale, v_scale, gamma, beta))
+    B, H, T, D = q8.shape
+    F = gamma.shape[2]
+    assert T % F == 0, "token count must be a whole number of frames"
+    S = T // F
+    assert k8.shape == q8.shape and v8.shape == q8.shape
+    assert q_scale.shape == gamma.shape and k_scale.shape == gamma.shape and v_scale.shape == gamma.shape
+    st = None if state_in is None else _f64(state_in)
+    o = np.empty(q8.shape, dtype=np.float64)
+    so = np.empty((B, H, D, D), dtype=np.float64)
+    c = 0.0 if key_scale is None else float(key_scale)
+    u8 = lambda a: a.ctypes.data_as(_u8p)
+    rc = (lib or _load()).gdn_oracle_forward_fp8(
+        B, H, D, S, F, int(bool(use_delta)), c, u8(q8), u8(k8), u8(v8), _ptr(q_scale),
+        _ptr(k_scale), _ptr(v_scale), _ptr(gamma), _ptr(beta), _ptr(st), _ptr(o), _ptr(so),
+        int(nthreads))
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_forward_fp8 failed with code %d" % rc)
     return o, so
 
 

@@ -170,6 +170,58 @@ int gdn_oracle_step(int B, int H, int D, int S, int use_delta, double key_scale,
 }
 
 /*
+ * Low-precision inputs: Q, K and V given as 8-bit floating-point codes with one fp32 scale per
+ * (b, h, frame) for each tensor (the mixed-precision quantisation that SANA-Streaming fuses with
+ * its GDN kernel: jefxiong.cn daily digest, SANA-Streaming item, contribution (3); SANA-WM's
+ * NVFP4 deployment: chatpaper.ai English abstract). The code format is OCP FP8 E4M3 (OCP 8-bit
+ * Floating Point Specification, E4M3): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent field 0 encodes subnormals m * 2^-9; S.1111.111 is NaN; there are no infinities.
+ * An element's value is scale[b][h][f] * E4M3(code). The recurrence then runs unchanged on
+ * those values (gdn_oracle_forward).
+ */
+double gdn_oracle_e4m3(unsigned code)
+{
+    const int sgn = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);                 /* 2^(1-7) * (m / 8) */
+    else
+        mag = ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -mag : mag;
+}
+
+/* q8, k8, v8: codes [B][H][F*S][D]; q_scale, k_scale, v_scale: [B][H][F]. Other arguments and
+   return codes as gdn_oracle_forward. */
+int gdn_oracle_forward_fp8(int B, int H, int D, int S, int F, int use_delta, double key_scale,
+                           const unsigned char* q8, const unsigned char* k8, const unsigned char* v8,
+                           const double* q_scale, const double* k_scale, const double* v_scale,
+                           const double* gamma, const double* beta, const double* state_in,
+                           double* o, double* state_out, int nthreads)
+{
+    if (B < 1 || H < 1 || D < 1 || S < 1 || F < 1) return 1;
+    if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale) return 2;
+    const size_t n = (size_t)B * H * F * S * D;
+    double* q = (double*)malloc(n * sizeof(double));
+    double* k = (double*)malloc(n * sizeof(double));
+    double* v = (double*)malloc(n * sizeof(double));
+    int rc = 3;
+    if (q && k && v) {
+        for (size_t e = 0; e < n; ++e) {
+            const size_t frame = e / ((size_t)S * D);       /* (b h) * F + f */
+            q[e] = q_scale[frame] * gdn_oracle_e4m3(q8[e]);
+            k[e] = k_scale[frame] * gdn_oracle_e4m3(k8[e]);
+            v[e] = v_scale[frame] * gdn_oracle_e4m3(v8[e]);
+        }
+        rc = gdn_oracle_forward(B, H, D, S, F, use_delta, key_scale, q, k, v, gamma, beta, state_in,
+                                o, state_out, nthreads);
+    }
+    free(q); free(k); free(v);
+    return rc;
+}
+
+/*
  * Backward (gradients) of the forward above for a scalar loss L whose gradients with respect
  * to the outputs are given: d_o = dL/dO [B][H][F*S][D] and d_state_out = dL/dstate_out
  * [B][H][D][D] (NULL: zero). Returns dq, dk, dv [B][H][F*S][D], dgamma, dbeta [B][H][F] and,

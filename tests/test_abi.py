@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 2
+    assert gdn.abi_version() == 3
     lib = gdn.load()
     for code in range(9):
         assert lib.gdn_status_string(code)
@@ -62,12 +62,12 @@ def msg():
 @pytest.mark.parametrize("name", gdn_synth.WORKLOAD_ORDER)
 def test_workspace_size_for_workloads(name):
     w = gdn_synth.WORKLOADS[name]
-    p = gdn.Problem(w.B, w.H, w.D, w.S, 1 if w.step_mode else w.F,
-                    gdn.GDN_F32 if w.dtype == "f32" else gdn.GDN_BF16, int(w.use_delta), 0.0,
+    code = {"f32": gdn.GDN_F32, "bf16": gdn.GDN_BF16, "fp8": gdn.GDN_FP8_E4M3}[w.dtype]
+    p = gdn.Problem(w.B, w.H, w.D, w.S, 1 if w.step_mode else w.F, code, int(w.use_delta), 0.0,
                     0, 0, w.D, 0, 0, w.D)
     n = gdn.workspace_size(p, w.step_mode)
     assert n > 0
-    fused = (w.dtype == "bf16" and w.D in (64, 128) and w.B * w.H * w.F >= 1024)
+    fused = w.dtype == "fp8" or (w.dtype == "bf16" and w.D in (64, 128) and w.B * w.H * w.F >= 1024)
     if not w.step_mode and fused:
         # two fp32 D x D states per (b, h)
         assert n >= 2 * w.B * w.H * w.D * w.D * 4
@@ -239,3 +239,47 @@ def test_backward_workspace():
     assert gdn.workspace_size(prob(F=60), 2) > n
     n3 = ctypes.c_size_t(0)
     assert gdn.load().gdn_workspace_size(ctypes.byref(p), 3, ctypes.byref(n3)) == 2
+
+
+def call_fp8(p, q=A, k=2 * A, v=3 * A, qs=15 * A, ks=16 * A, vs=17 * A, g=4 * A, b=5 * A, si=None,
+             o=6 * A, so=None, ws=8 * A, wsb=1 << 40):
+    lib = gdn.load()
+    pp = None if p is None else ctypes.byref(p)
+    return lib.gdn_forward_framewise_fp8(pp, q, k, v, qs, ks, vs, g, b, si, o, so, ws, wsb, None)
+
+
+def test_fp8_validation():
+    p8 = prob(dtype=gdn.GDN_FP8_E4M3)
+    assert call_fp8(None) == 1
+    assert call_fp8(p8, ks=None) == 1                  # scales required
+    assert call_fp8(prob()) == 3                        # bf16 data through the fp8 entry
+    assert "GDN_FP8_E4M3" in msg()
+    assert call(p8) == 3                                # fp8 data through the bf16 entry
+    assert "gdn_forward_framewise_fp8" in msg()
+    assert call(p8, step=True, si=7 * A) == 3           # no step mode
+    assert call_fp8(prob(dtype=gdn.GDN_FP8_E4M3, D=32)) == 3
+    p = prob(dtype=gdn.GDN_FP8_E4M3)
+    p.schedule = 1
+    assert call_fp8(p) == 3                             # staged: not for E4M3
+    assert call_fp8(p8, qs=15 * A + 2) == 5             # scales 4-byte aligned
+    assert call_fp8(p8, o=15 * A) == 6                  # o overlaps a scale array
+    assert call_fp8(p8, wsb=16) == 7                    # reaches the workspace check
+    n = ctypes.c_size_t(0)
+    assert gdn.load().gdn_workspace_size(ctypes.byref(p8), 2, ctypes.byref(n)) == 3
+
+
+def test_fp8_workspace_is_the_fused_one():
+    p8, pb = prob(dtype=gdn.GDN_FP8_E4M3, F=30), prob(F=30)
+    pb.schedule = 2
+    assert gdn.workspace_size(p8, 0) == gdn.workspace_size(pb, 0)
+
+
+def test_fused_needs_frame_rows_within_2gib():
+    p = prob(F=3000)                          # auto: fused (6000 items)
+    big = prob(F=3000)
+    big.qkv_stride_t = 1 << 25                 # 39 rows of 2^25 bf16 elements: > 2 GiB
+    big.qkv_stride_h = big.qkv_stride_t * 40 * 3000
+    big.qkv_stride_b = big.qkv_stride_h * 2
+    assert gdn.workspace_size(big, False) != gdn.workspace_size(p, False)   # falls back to staged
+    big.schedule = 2
+    assert call(big) == 3 and "2 GiB" in msg()
