@@ -339,6 +339,31 @@ def fp8_mode(dev, steps, warmup, ev, stream):
                              "frac": round(bytes_alg / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if fms else None}}
 
 
+def streaming_ceiling(dev, gib=4.0, reps=10):
+    """Bandwidth of a plain torch streaming kernel with the fused kernel's mix of traffic (three
+    tensors read, one written: y = a + b * c in one elementwise kernel), for reading `frac`
+    against what a simple kernel reaches on the same device."""
+    import torch
+    n = int(gib * (1 << 30)) // 2
+    a, b, c, y = (torch.empty(n, dtype=torch.bfloat16, device=dev).normal_() for _ in range(4))
+
+    def f():
+        torch.addcmul(a, b, c, out=y)
+
+    f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c, y
+    torch.cuda.empty_cache()
+    return 4 * n * 2 / (ms * 1e-3) / 1e9   # a, b, c read, y written
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -467,6 +492,11 @@ def main():
     ev.close()
     del q, k, v, o, ws
     torch.cuda.empty_cache()
+    ceil = streaming_ceiling(dev)
+    result["roofline"]["streaming_ceiling"] = {
+        "kind": "torch bf16 addcmul y = a + b * c: 3 tensors read, 1 written, 4 GiB each",
+        "gb_s": round(ceil, 1), "frac_of_ceiling": round(achieved / ceil, 4)}
+    log("streaming ceiling (torch addcmul): %.0f GB/s" % ceil)
     if not args.no_stream:
         ev2 = HipEvents()
         log("streaming step mode: %d frames x 4 passes" % args.stream_frames)
