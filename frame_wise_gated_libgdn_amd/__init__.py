@@ -27,7 +27,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
           4: "GDN_ERR_STRIDE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
           8: "GDN_ERR_HIP"}
 KERNEL_NAMES = {0: "products", 1: "combine", 2: "scan", 3: "step_partial", 4: "step_reduce",
-                5: "fused_reset", 6: "fused", 7: "scan_bwd", 8: "bwd", 9: "scan_states"}
+                5: "fused_reset", 6: "fused", 7: "scan_bwd", 8: "bwd", 9: "scan_states",
+                10: "tconv"}
 SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
 
 
@@ -48,6 +49,17 @@ class Problem(ctypes.Structure):
                 ("qkv_stride_t", ctypes.c_int64), ("o_stride_b", ctypes.c_int64),
                 ("o_stride_h", ctypes.c_int64), ("o_stride_t", ctypes.c_int64),
                 ("schedule", ctypes.c_int32)]
+
+
+class TconvProblem(ctypes.Structure):
+    """gdn_tconv_problem of include/libgdn.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("frames", ctypes.c_int32), ("tokens", ctypes.c_int32),
+                ("channels", ctypes.c_int32), ("block_frames", ctypes.c_int32),
+                ("dtype", ctypes.c_int32),
+                ("x_stride_b", ctypes.c_int64), ("x_stride_t", ctypes.c_int64),
+                ("x_stride_s", ctypes.c_int64),
+                ("y_stride_b", ctypes.c_int64), ("y_stride_t", ctypes.c_int64),
+                ("y_stride_s", ctypes.c_int64)]
 
 
 class TraceEntry(ctypes.Structure):
@@ -83,6 +95,8 @@ def load():
             for fn in (lib.gdn_forward_framewise, lib.gdn_step_frame):
                 fn.argtypes = [P] + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp]
                 fn.restype = ctypes.c_int
+            lib.gdn_tconv_forward.argtypes = [ctypes.POINTER(TconvProblem)] + [_vp] * 7
+            lib.gdn_tconv_forward.restype = ctypes.c_int
             lib.gdn_forward_framewise_fp8.argtypes = [P] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
             lib.gdn_forward_framewise_fp8.restype = ctypes.c_int
             lib.gdn_backward_framewise.argtypes = [P] + [_vp] * 14 + [_vp, ctypes.c_size_t, _vp]
@@ -267,6 +281,33 @@ def forward_framewise_fp8(q, k, v, q_scale, k_scale, v_scale, gamma, beta, state
         _ptr(gamma), _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out), _ptr(ws), nbytes,
         _stream(stream)))
     return out, state_out
+
+
+def temporal_conv(x, weight, bias=None, cache=None, *, block_frames, out=None, cache_out=None,
+                  return_cache=True, stream=None):
+    """Block-causal temporal convolution (gdn_tconv_forward). x [B, T, S, C] (bf16 or fp32,
+    channels contiguous); weight fp32 [C, 3] (taps on frames t-1, t, t+1); bias fp32 [C] or
+    None; cache [B, S, C] (x's dtype, contiguous): the previous block's last frame, or None for
+    the first block. Returns (y, cache_out); cache_out (x[:, -1]) may be `cache` itself."""
+    import torch
+    B, T, S, C = x.shape
+    if out is None:
+        out = torch.empty((B, T, S, C), dtype=x.dtype, device=x.device)
+    if cache_out is None and return_cache:
+        cache_out = torch.empty((B, S, C), dtype=x.dtype, device=x.device)
+    if x.stride(3) != 1 or out.stride(3) != 1:
+        raise GdnError(4, "the channel dimension must be contiguous")
+    for name, t in (("cache", cache), ("cache_out", cache_out)):
+        if t is not None and (t.dtype != x.dtype or tuple(t.shape) != (B, S, C) or not t.is_contiguous()):
+            raise GdnError(4, "%s must be a contiguous %s tensor of shape %s" % (name, x.dtype, (B, S, C)))
+    _check_f32("weight", weight, (C, 3))
+    _check_f32("bias", bias, (C,))
+    code = _dtype_code(x)
+    p = TconvProblem(B, T, S, C, int(block_frames), code, x.stride(0), x.stride(1), x.stride(2),
+                     out.stride(0), out.stride(1), out.stride(2))
+    _check(load().gdn_tconv_forward(ctypes.byref(p), _ptr(x), _ptr(weight), _ptr(bias), _ptr(cache),
+                                    _ptr(out), _ptr(cache_out), _stream(stream)))
+    return out, cache_out
 
 
 def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_scale=None,

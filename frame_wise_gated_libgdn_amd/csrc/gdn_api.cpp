@@ -394,6 +394,58 @@ gdn_status run_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     return GDN_OK;
 }
 
+gdn_status run_tconv(const gdn_tconv_problem* p, const void* x, const float* weight,
+                     const float* bias, const void* cache_in, void* y, void* cache_out,
+                     void* stream) {
+    g_msg[0] = '\0';
+    if (!p) return fail(GDN_ERR_NULL, "problem descriptor is NULL");
+    if (p->batch < 1 || p->frames < 1 || p->tokens < 1 || p->channels < 1 || p->block_frames < 1)
+        return fail(GDN_ERR_SHAPE, "sizes must be >= 1 (B=%d T=%d S=%d C=%d block_frames=%d)",
+                    p->batch, p->frames, p->tokens, p->channels, p->block_frames);
+    if (p->frames % p->block_frames)
+        return fail(GDN_ERR_SHAPE, "frames (%d) must be a multiple of block_frames (%d)", p->frames,
+                    p->block_frames);
+    if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "dtype %d not supported (GDN_F32, GDN_BF16)", p->dtype);
+    if (p->channels % 8) return fail(GDN_ERR_ALIGN, "channels must be a multiple of 8");
+    if (!x || !weight || !y) return fail(GDN_ERR_NULL, "x, weight and y are required");
+    const int64_t B = p->batch, T = p->frames, S = p->tokens, C = p->channels;
+    const int64_t esz = p->dtype == GDN_BF16 ? 2 : 4;
+    if (B * T * S * (C / 4) > ((int64_t)1 << 40)) return fail(GDN_ERR_SHAPE, "problem too large for one call");
+    if (!layout_ok(B, T, S, C, p->x_stride_b, p->x_stride_t, p->x_stride_s))
+        return fail(GDN_ERR_STRIDE, "x strides overlap rows or are negative");
+    if (!layout_ok(B, T, S, C, p->y_stride_b, p->y_stride_t, p->y_stride_s))
+        return fail(GDN_ERR_STRIDE, "y strides overlap rows or are negative");
+    for (const void* ptr : {x, (const void*)y, cache_in, (const void*)cache_out})
+        if (ptr && !aligned(ptr, 16)) return fail(GDN_ERR_ALIGN, "x, y and the caches must be 16-byte aligned");
+    for (int64_t st : {p->x_stride_b, p->x_stride_t, p->x_stride_s, p->y_stride_b, p->y_stride_t, p->y_stride_s})
+        if (st % 8) return fail(GDN_ERR_ALIGN, "strides must be multiples of 8 elements");
+    for (const void* ptr : {(const void*)weight, (const void*)bias})
+        if (ptr && !aligned(ptr, 4)) return fail(GDN_ERR_ALIGN, "weight and bias must be 4-byte aligned");
+    const Span none = {nullptr, nullptr};
+    const Span sx = span_of(x, B, T, S, C, p->x_stride_b, p->x_stride_t, p->x_stride_s, esz);
+    const Span sy = span_of(y, B, T, S, C, p->y_stride_b, p->y_stride_t, p->y_stride_s, esz);
+    const Span sw = {(const char*)weight, (const char*)(weight + 3 * C)};
+    const Span sbias = bias ? Span{(const char*)bias, (const char*)(bias + C)} : none;
+    const Span sci = cache_in ? Span{(const char*)cache_in, (const char*)cache_in + B * S * C * esz} : none;
+    const Span sco = cache_out ? Span{(const char*)cache_out, (const char*)cache_out + B * S * C * esz} : none;
+    for (Span in : {sx, sw, sbias, sci, sco})
+        if (overlap(sy, in)) return fail(GDN_ERR_ALIAS, "y overlaps an input or cache_out");
+    for (Span in : {sx, sw, sbias})
+        if (overlap(sco, in)) return fail(GDN_ERR_ALIAS, "cache_out overlaps an input");
+    if (cache_in && cache_out && cache_in != cache_out && overlap(sco, sci))
+        return fail(GDN_ERR_ALIAS, "cache_out partially overlaps cache_in");
+    gdn::TconvLaunch L{};
+    L.B = (int)B; L.T = (int)T; L.S = (int)S; L.C = (int)C; L.Tb = p->block_frames;
+    L.bf16 = p->dtype == GDN_BF16;
+    L.xsb = p->x_stride_b; L.xst = p->x_stride_t; L.xss = p->x_stride_s;
+    L.ysb = p->y_stride_b; L.yst = p->y_stride_t; L.yss = p->y_stride_s;
+    L.x = x; L.weight = weight; L.bias = bias; L.cache_in = cache_in; L.y = y; L.cache_out = cache_out;
+    const hipError_t e = gdn::run_tconv(L, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -443,6 +495,12 @@ gdn_status gdn_backward_framewise(const gdn_problem* p, const void* q, const voi
                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
     return run_bwd(p, q, k, v, gamma, beta, state_in, d_o, d_state_out, dq, dk, dv, dgamma, dbeta,
                    d_state_in, workspace, workspace_bytes, hip_stream);
+}
+
+gdn_status gdn_tconv_forward(const gdn_tconv_problem* p, const void* x, const float* weight,
+                             const float* bias, const void* cache_in, void* y, void* cache_out,
+                             void* hip_stream) {
+    return run_tconv(p, x, weight, bias, cache_in, y, cache_out, hip_stream);
 }
 
 gdn_status gdn_set_trace(void* const* events, int pairs) {

@@ -57,8 +57,24 @@ struct Launch {
 enum Kernel {
     K_PRODUCTS = 0, K_COMBINE = 1, K_SCAN = 2, K_STEP_PARTIAL = 3, K_STEP_REDUCE = 4,
     K_FUSED_RESET = 5, K_FUSED = 6, K_SCAN_BWD = 7, K_BWD = 8,
-    K_SCAN_STATES = 9    // the forward scan with fp32 per-frame states (backward's recompute)
+    K_SCAN_STATES = 9,   // the forward scan with fp32 per-frame states (backward's recompute)
+    K_TCONV = 10         // block-causal temporal convolution
 };
+
+// Arguments of the temporal convolution (gdn_tconv.hip). x, y: [B][T][S][C] with the strides
+// below (elements, channel stride 1); caches [B][S][C] contiguous; weight [C][3], bias [C].
+struct TconvLaunch {
+    int B, T, S, C, Tb;
+    int bf16;            // 1: x, y and the caches are bf16; 0: fp32
+    int64_t xsb, xst, xss, ysb, yst, yss;
+    const void* x;
+    const float *weight, *bias;
+    const void* cache_in;
+    void* y;
+    void* cache_out;
+};
+hipError_t tconv_launch(const TconvLaunch& L, hipStream_t s);
+hipError_t run_tconv(const TconvLaunch& L, hipStream_t s);
 
 // Fused forward: value-column groups pipelined through the frame chain (one flag each per (b, h)).
 constexpr int kChainGroups = 4;

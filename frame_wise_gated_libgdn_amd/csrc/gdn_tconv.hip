@@ -1,0 +1,153 @@
+// Block-causal temporal convolution with a last-frame cache (SANA-Video talk, passage on the
+// causal FFN with temporal conv): a depthwise convolution over latent frames, kernel 3 centred,
+// in which a block's last frame sees zero on its right (the zero token between blocks) and a
+// block's first frame sees the previous block's last frame on its left (the carried token; the
+// cache when the previous block came in an earlier call).
+//
+//   y[t] = bias + w0 * L(t) + w1 * x[t] + w2 * R(t)
+//   L(t) = x[t-1] for t > 0; cache_in (or 0) for t = 0
+//   R(t) = x[t+1] unless t + 1 ends a block or the call (then 0)
+//   cache_out = x[T-1]
+//
+// HBM-bound streaming. A thread owns 16 bytes of channels of one (b, s) and TF consecutive
+// frames: it loads the TF + 2 frames of its window at once (addresses clamped into the tensor,
+// out-of-range values replaced by selects after the loads, so no load sits behind a branch),
+// and writes TF outputs with 16-byte stores. Consecutive threads walk channels, then frame
+// chunks, so the one-frame halos of neighbouring chunks are read close together in time (from
+// L2). The thread of the first chunk reads cache_in and writes cache_out, so the two may be the
+// same buffer.
+#include <stdint.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTconvThreads = 256;
+constexpr int kTconvFrames = 16;   // frames per thread
+
+template <typename T> struct Vec;
+template <> struct Vec<float> {
+    static constexpr int N = 4;
+    // whole-vector casts: a cast of one ext-vector element lvalue reads element 0
+    static __device__ __forceinline__ void unpack(u32x4 w, float (&v)[N]) {
+        const f32x4 f = __builtin_bit_cast(f32x4, w);
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = f[i];
+    }
+    static __device__ __forceinline__ u32x4 pack(const float (&v)[N]) {
+        return __builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]});
+    }
+};
+template <> struct Vec<__bf16> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ void unpack(u32x4 w, float (&v)[N]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+            v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+        }
+    }
+    static __device__ __forceinline__ u32x4 pack(const float (&v)[N]) {
+        // round to nearest even (gfx950 converts pairs in one instruction)
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2 * i], (__bf16)v[2 * i + 1]});
+        return w;
+    }
+};
+
+template <typename T, int TF>
+__global__ __launch_bounds__(kTconvThreads) void tconv_kernel(TconvLaunch L) {
+    using V = Vec<T>;
+    constexpr int N = V::N;
+    const int ncv = L.C / N;
+    const int ntc = (L.T + TF - 1) / TF;
+    int64_t r = (int64_t)blockIdx.x * kTconvThreads + threadIdx.x;
+    const int cv = (int)(r % ncv);
+    r /= ncv;
+    const int tc = (int)(r % ntc);
+    r /= ntc;
+    const int s = (int)(r % L.S);
+    r /= L.S;
+    if (r >= L.B) return;
+    const int b = (int)r;
+    const int c0 = cv * N;
+    const int t0 = tc * TF;
+    const T* xs = (const T*)L.x + (int64_t)b * L.xsb + (int64_t)s * L.xss + c0;
+    const int64_t cache_off = ((int64_t)b * L.S + s) * L.C + c0;
+
+    // window: frames t0 - 1 .. t0 + TF; slot 0 is the left neighbour of frame t0
+    u32x4 raw[TF + 2];
+    {
+        const T* left = t0 > 0 ? xs + (int64_t)(t0 - 1) * L.xst
+                               : (L.cache_in ? (const T*)L.cache_in + cache_off : xs);
+        raw[0] = *(const u32x4*)left;
+    }
+#pragma unroll
+    for (int i = 1; i < TF + 2; ++i) {
+        const int t = min(t0 - 1 + i, L.T - 1);
+        raw[i] = *(const u32x4*)(xs + (int64_t)t * L.xst);
+    }
+    // the frame for cache_out (the last one), read by the first chunk's threads; the others
+    // re-read a frame of their own window instead of branching around the load
+    const bool keep_cache = tc == 0 && L.cache_out;
+    const u32x4 last = *(const u32x4*)(xs + (int64_t)(keep_cache ? L.T - 1 : min(t0, L.T - 1)) * L.xst);
+
+    float w0[N], w1[N], w2[N], bs[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        w0[j] = L.weight[3 * (c0 + j)];
+        w1[j] = L.weight[3 * (c0 + j) + 1];
+        w2[j] = L.weight[3 * (c0 + j) + 2];
+        bs[j] = L.bias ? L.bias[c0 + j] : 0.f;
+    }
+    float prev[N], cur[N], next[N];
+    V::unpack(raw[0], prev);
+    if (t0 == 0 && !L.cache_in) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) prev[j] = 0.f;
+    }
+    V::unpack(raw[1], cur);
+    T* ys = (T*)L.y + (int64_t)b * L.ysb + (int64_t)s * L.yss + c0;
+#pragma unroll
+    for (int i = 0; i < TF; ++i) {
+        const int t = t0 + i;
+        V::unpack(raw[i + 2], next);
+        const bool right = t + 1 < L.T && (t + 1) % L.Tb != 0;
+        float out[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const float nx = right ? next[j] : 0.f;
+            out[j] = __builtin_fmaf(w2[j], nx, __builtin_fmaf(w1[j], cur[j], __builtin_fmaf(w0[j], prev[j], bs[j])));
+        }
+        if (t < L.T) *(u32x4*)(ys + (int64_t)t * L.yst) = V::pack(out);
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            prev[j] = cur[j];
+            cur[j] = next[j];
+        }
+    }
+    if (keep_cache) *(u32x4*)((T*)L.cache_out + cache_off) = last;
+}
+
+}  // namespace
+
+hipError_t tconv_launch(const TconvLaunch& L, hipStream_t s) {
+    constexpr int TF = kTconvFrames;
+    const int N = L.bf16 ? 8 : 4;
+    const int64_t threads = (int64_t)L.B * L.S * (L.C / N) * ((L.T + TF - 1) / TF);
+    const int64_t blocks = (threads + kTconvThreads - 1) / kTconvThreads;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (L.bf16)
+        hipLaunchKernelGGL((tconv_kernel<__bf16, TF>), dim3((unsigned)blocks), dim3(kTconvThreads), 0, s, L);
+    else
+        hipLaunchKernelGGL((tconv_kernel<float, TF>), dim3((unsigned)blocks), dim3(kTconvThreads), 0, s, L);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -210,6 +210,50 @@ def qkv_cpu(w: Workload, heads=None, frames=None, pass_=0):
     return out_vals, out_raw
 
 
+@dataclasses.dataclass(frozen=True)
+class TconvWorkload:
+    """Block-causal temporal convolution at the GDN block's width: x [B, T, S, C] ~ N(0, 1),
+    taps [C, 3] ~ N(0, 1/3), bias [C] ~ N(0, 0.1^2) (synthetic weights)."""
+    name: str
+    seed: int
+    B: int
+    T: int
+    S: int
+    C: int
+    block_frames: int
+    dtype: str
+
+
+TCONV_WORKLOADS = {
+    w.name: w for w in [
+        # the 720p 60 s video at the width H*D = 16*128 of the GDN block, one block per latent
+        # frame (frame-wise generation)
+        TconvWorkload("tconv_720p_60s_bf16", 6, 1, 961, 3520, 2048, 1, "bf16"),
+    ]
+}
+TID_TCONV_X, TID_TCONV_W = 7, 8
+
+
+def tconv_weights(w: TconvWorkload):
+    """taps [C, 3] and bias [C], fp32, from the counter-based normal generator."""
+    z = normal_slice(w.seed, TID_TCONV_W, 0, 0, 0, 4, w.C)   # [4, C]
+    taps = (z[:3].T / np.sqrt(3.0)).astype(np.float32)
+    bias = (0.1 * z[3]).astype(np.float32)
+    return np.ascontiguousarray(taps), bias
+
+
+def tconv_x_cpu(w: TconvWorkload, frames=None, batches=None):
+    """x values [nb, nf, S, C] fp32 (bf16-rounded for bf16) for the selected frames."""
+    frames = range(w.T) if frames is None else list(frames)
+    batches = range(w.B) if batches is None else list(batches)
+    out = np.empty((len(batches), len(frames), w.S, w.C), np.float32)
+    for bi, b in enumerate(batches):
+        for fi, f in enumerate(frames):
+            z = normal_slice(w.seed, TID_TCONV_X, b, 0, f, w.S, w.C)
+            out[bi, fi] = z if w.dtype == "f32" else bf16_bits_to_f32(f32_to_bf16_bits(z))
+    return out
+
+
 def e4m3_codes(x, S, D):
     """Quantise frames of fp32 values to E4M3 with one power-of-two scale per frame.
 
@@ -313,6 +357,17 @@ class TorchGen:
             codes[c0 * S:c1 * S].copy_(cc)
             scales[c0:c1].copy_(ss)
             del wd, z, cc, ss
+
+
+def tconv_x_torch(w: TconvWorkload, device, gen=None):
+    """x [B, T, S, C] on the device (the same values as tconv_x_cpu)."""
+    import torch
+    gen = gen or TorchGen(device)
+    x = torch.empty((w.B, w.T, w.S, w.C), dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                    device=device)
+    for b in range(w.B):
+        gen.fill_normal(x[b].view(w.T * w.S, w.C), w.seed, TID_TCONV_X, b, 0, 0, w.S, w.C)
+    return x
 
 
 def gates_torch(w: Workload, device, pass_=0):

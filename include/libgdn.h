@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 3
+#define LIBGDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -115,6 +115,49 @@ typedef struct {
     int64_t o_stride_b, o_stride_h, o_stride_t;         /* elements */
     int32_t schedule;          /* forward only, a gdn_schedule; ignored in step mode */
 } gdn_problem;
+
+/*
+ * Block-causal temporal convolution (SANA-Video talk, shadowingenglish.com, passage on the
+ * causal FFN with temporal conv): the spatial-temporal Mix-FFN convolves along time; in training
+ * a zero token separates consecutive blocks so that a block cannot see the next one, and the
+ * last token of each block is carried in as the first token of the next; in streaming that
+ * carried token is a cache. libgdn's reading: a depthwise convolution over latent frames,
+ * kernel 3 centred, per spatial token and channel:
+ *   y[t] = bias + w[c][0] * L(t) + w[c][1] * x[t] + w[c][2] * R(t)
+ *   L(t) = x[t-1] (t > 0), cache_in (t = 0; zero when cache_in is NULL)
+ *   R(t) = x[t+1], or zero when frame t ends a block ((t + 1) % block_frames == 0) or the call
+ *   cache_out = x[T-1]
+ * One call covers a whole sequence of T / block_frames blocks (training form) or one block from
+ * the cache of the previous one (streaming form: T = block_frames).
+ */
+typedef struct {
+    int32_t batch;             /* B */
+    int32_t frames;            /* T, a multiple of block_frames */
+    int32_t tokens;            /* S spatial tokens per frame */
+    int32_t channels;          /* C, a multiple of 8 */
+    int32_t block_frames;      /* frames per block */
+    int32_t dtype;             /* GDN_F32 or GDN_BF16: x, y and the caches */
+    int64_t x_stride_b, x_stride_t, x_stride_s;   /* elements; channel stride 1 */
+    int64_t y_stride_b, y_stride_t, y_stride_s;   /* elements; channel stride 1 */
+} gdn_tconv_problem;
+
+/*
+ *   x          input [B][T][S][C] with the x strides
+ *   weight     fp32 [C][3]: taps on frames t-1, t, t+1
+ *   bias       fp32 [C], or NULL (zero)
+ *   cache_in   [B][S][C] contiguous, the last frame of the previous block, or NULL (zero: the
+ *              first block)
+ *   y          output [B][T][S][C] with the y strides; fp32 accumulation, bf16 rounded to
+ *              nearest even
+ *   cache_out  [B][S][C] contiguous, receives x[T-1], or NULL; may equal cache_in exactly
+ * Pointers to x, y and the caches must be 16-byte aligned and strides multiples of 8 elements
+ * (GDN_ERR_ALIGN); y and cache_out must not overlap any input (GDN_ERR_ALIAS). No workspace.
+ * Asynchronous on hip_stream; errors and tracing as gdn_forward_framewise (trace kind
+ * GDN_KERNEL_TCONV, units B*T*S).
+ */
+gdn_status gdn_tconv_forward(const gdn_tconv_problem* p, const void* x, const float* weight,
+                             const float* bias, const void* cache_in, void* y, void* cache_out,
+                             void* hip_stream);
 
 /*
  * Workspace bytes needed by gdn_forward_framewise (mode = 0), gdn_step_frame (mode = 1) or
@@ -230,7 +273,8 @@ typedef enum {
     GDN_KERNEL_FUSED = 6,         /* fused: products, state step and outputs of every frame */
     GDN_KERNEL_SCAN_BWD = 7,      /* backward: reverse scan of the state gradients */
     GDN_KERNEL_BWD = 8,           /* backward: per-frame gradients of Q, K, V, gamma, beta */
-    GDN_KERNEL_SCAN_STATES = 9    /* backward: forward scan keeping every state in fp32 */
+    GDN_KERNEL_SCAN_STATES = 9,   /* backward: forward scan keeping every state in fp32 */
+    GDN_KERNEL_TCONV = 10         /* block-causal temporal convolution */
 } gdn_kernel_kind;
 
 typedef struct {

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 3
+    assert gdn.abi_version() == 4
     lib = gdn.load()
     for code in range(9):
         assert lib.gdn_status_string(code)
@@ -283,3 +283,29 @@ def test_fused_needs_frame_rows_within_2gib():
     assert gdn.workspace_size(big, False) != gdn.workspace_size(p, False)   # falls back to staged
     big.schedule = 2
     assert call(big) == 3 and "2 GiB" in msg()
+
+
+def tprob(B=1, T=6, S=5, C=16, tb=2, dtype=gdn.GDN_BF16):
+    return gdn.TconvProblem(B, T, S, C, tb, dtype, T * S * C, S * C, C, T * S * C, S * C, C)
+
+
+def call_tconv(p, x=A, w=2 * A, b=3 * A, ci=None, y=4 * A, co=None):
+    lib = gdn.load()
+    pp = None if p is None else ctypes.byref(p)
+    return lib.gdn_tconv_forward(pp, x, w, b, ci, y, co, None)
+
+
+def test_tconv_validation():
+    assert call_tconv(None) == 1
+    assert call_tconv(tprob(), x=None) == 1
+    assert call_tconv(tprob(T=0)) == 2
+    assert call_tconv(tprob(T=5, tb=2)) == 2              # whole blocks only
+    assert "block_frames" in msg()
+    assert call_tconv(tprob(C=12)) == 5                    # channels multiple of 8
+    assert call_tconv(tprob(dtype=gdn.GDN_FP8_E4M3)) == 3
+    assert call_tconv(tprob(), y=A + 64) == 6              # y overlaps x
+    assert call_tconv(tprob(), ci=5 * A, co=5 * A + 32) == 6   # partial overlap of the caches
+    assert call_tconv(tprob(), x=A + 8) == 5
+    p = tprob()
+    p.x_stride_s = 8                                       # rows of 16 channels overlap
+    assert call_tconv(p) == 4
