@@ -18,6 +18,8 @@ Prints one JSON line. Extra objects:
   fp8           the same forward from E4M3 Q, K, V with per-frame scales
                 (gdn_forward_framewise_fp8): ms per call and its own roofline (Q, K, V at one
                 byte per element, O at two).
+  tconv         the block-causal temporal conv (gdn_tconv_forward) over the same video at the
+                GDN block's width: whole video per call, and per-frame streaming latency.
   backward      gdn_backward_framewise over the workload: ms per call, per-kernel ms and the
                 call's roofline (Q, K, V, dO read; dQ, dK, dV written).
 """
@@ -90,6 +92,7 @@ def parse():
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-tconv", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--stream-frames", type=int, default=240)
     ap.add_argument("--schedule", default="auto", choices=["auto", "staged", "fused"],
@@ -339,6 +342,76 @@ def fp8_mode(dev, steps, warmup, ev, stream):
                              "frac": round(bytes_alg / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if fms else None}}
 
 
+def tconv_mode(dev, steps, warmup, ev, stream, stream_frames=240):
+    """Block-causal temporal conv at the GDN block's width (tconv_720p_60s_bf16): the whole
+    video in one call (training form), then frame-by-frame streaming from the cache (one block
+    per call, cache updated in place)."""
+    import numpy as np
+    import torch
+    import frame_wise_gated_libgdn_amd as gdn
+    import gdn_synth
+    w = gdn_synth.TCONV_WORKLOADS["tconv_720p_60s_bf16"]
+    x = gdn_synth.tconv_x_torch(w, dev)
+    taps, bias = gdn_synth.tconv_weights(w)
+    wt, bt = torch.from_numpy(taps).to(dev), torch.from_numpy(bias).to(dev)
+    y = torch.empty_like(x)
+    cache = torch.empty((w.B, w.S, w.C), dtype=x.dtype, device=dev)
+    sh = stream.cuda_stream
+
+    def whole():
+        gdn.temporal_conv(x, wt, bt, None, block_frames=w.block_frames, out=y, cache_out=cache,
+                          stream=stream)
+
+    for _ in range(warmup + 1):
+        whole()
+    torch.cuda.synchronize()
+    trace = [[ev.new(), ev.new()] for _ in range(steps)]
+    t0, t1 = ev.new(), ev.new()
+    ev.record(t0, sh)
+    for i in range(steps):
+        gdn.set_trace(trace[i])
+        whole()
+    gdn.set_trace(None)
+    ev.record(t1, sh)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    kms = sum(ev.ms(a, b) for a, b in trace) / steps
+    n = w.B * w.T * w.S * w.C
+    bytes_alg = 2 * n * 2                      # x read, y written (bf16)
+    # streaming: one frame per call from the previous frame's cache
+    nf = min(stream_frames, w.T)
+    yf = torch.empty((w.B, 1, w.S, w.C), dtype=x.dtype, device=dev)
+    c = torch.zeros_like(cache)
+    for f in range(3):
+        gdn.temporal_conv(x[:, f:f + 1], wt, bt, c, block_frames=1, out=yf, cache_out=c, stream=stream)
+    torch.cuda.synchronize()
+    evs = [(ev.new(), ev.new()) for _ in range(nf)]
+    kev = [[ev.new(), ev.new()] for _ in range(nf)]
+    for f in range(nf):
+        ev.record(evs[f][0], sh)
+        gdn.set_trace(kev[f])
+        gdn.temporal_conv(x[:, f:f + 1], wt, bt, c, block_frames=1, out=yf, cache_out=c, stream=stream)
+        ev.record(evs[f][1], sh)
+    gdn.set_trace(None)
+    torch.cuda.synchronize()
+    lat = np.array([ev.ms(a, b) * 1e3 for a, b in evs])       # includes the host's launch work
+    klat = np.array([ev.ms(a, b) * 1e3 for a, b in kev])      # the launch alone
+    step_bytes = 4 * w.B * w.S * w.C * 2       # x, cache_in read; y, cache_out written
+    del x, y
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms_per_call": round(ms, 4), "kernel_ms": round(kms, 4),
+            "frames_per_s": round(w.T / (ms * 1e-3), 1),
+            "bytes_alg_gb": round(bytes_alg / 1e9, 3),
+            "achieved_gb_s": round(bytes_alg / (kms * 1e-3) / 1e9, 1),
+            "frac": round(bytes_alg / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stream": {"frames": nf, "us_per_frame_median": round(float(np.median(lat)), 2),
+                       "us_per_frame_p90": round(float(np.percentile(lat, 90)), 2),
+                       "kernel_us_median": round(float(np.median(klat)), 2),
+                       "kernel_gb_s": round(step_bytes / (float(np.median(klat)) * 1e-6) / 1e9, 1),
+                       "bytes_per_frame_mb": round(step_bytes / 1e6, 2),
+                       "floor_us": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}}
+
+
 def streaming_ceiling(dev, gib=4.0, reps=10):
     """Bandwidth of a plain torch streaming kernel with the fused kernel's mix of traffic (three
     tensors read, one written: y = a + b * c in one elementwise kernel), for reading `frac`
@@ -510,6 +583,13 @@ def main():
         ev4.close()
         torch.cuda.empty_cache()
         log("fp8 done: %.3f ms/call" % result["fp8"]["ms_per_call"])
+    if not args.no_tconv and w.name == "gdn_720p_60s_bf16":
+        ev5 = HipEvents()
+        log("temporal conv: %d calls" % args.steps)
+        result["tconv"] = tconv_mode(dev, args.steps, args.warmup, ev5, torch.cuda.current_stream())
+        ev5.close()
+        torch.cuda.empty_cache()
+        log("temporal conv done: %.3f ms/call" % result["tconv"]["ms_per_call"])
     if not args.no_backward and w.dtype == "bf16" and w.D in (64, 128):
         ev3 = HipEvents()
         log("backward: %d calls" % args.backward_steps)

@@ -409,9 +409,14 @@ gdn_status run_tconv(const gdn_tconv_problem* p, const void* x, const float* wei
         return fail(GDN_ERR_UNSUPPORTED, "dtype %d not supported (GDN_F32, GDN_BF16)", p->dtype);
     if (p->channels % 8) return fail(GDN_ERR_ALIGN, "channels must be a multiple of 8");
     if (!x || !weight || !y) return fail(GDN_ERR_NULL, "x, weight and y are required");
+    if (!aligned(weight, 16) || (bias && !aligned(bias, 16)))
+        return fail(GDN_ERR_ALIGN, "weight and bias must be 16-byte aligned");
     const int64_t B = p->batch, T = p->frames, S = p->tokens, C = p->channels;
     const int64_t esz = p->dtype == GDN_BF16 ? 2 : 4;
-    if (B * T * S * (C / 4) > ((int64_t)1 << 40)) return fail(GDN_ERR_SHAPE, "problem too large for one call");
+    // one thread per 16 bytes of channels and (up to) 16 frames; the kernel indexes threads
+    // in 32 bits
+    if (B * S * (C / (16 / esz)) * ((T + 15) / 16) > ((int64_t)1 << 31) - 256)
+        return fail(GDN_ERR_SHAPE, "problem too large for one call");
     if (!layout_ok(B, T, S, C, p->x_stride_b, p->x_stride_t, p->x_stride_s))
         return fail(GDN_ERR_STRIDE, "x strides overlap rows or are negative");
     if (!layout_ok(B, T, S, C, p->y_stride_b, p->y_stride_t, p->y_stride_s))

@@ -27,7 +27,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTconvThreads = 256;
-constexpr int kTconvFrames = 16;   // frames per thread
+constexpr int kTconvFrames = 16;   // frames per thread (long calls)
 
 template <typename T> struct Vec;
 template <> struct Vec<float> {
@@ -65,16 +65,17 @@ template <typename T, int TF>
 __global__ __launch_bounds__(kTconvThreads) void tconv_kernel(TconvLaunch L) {
     using V = Vec<T>;
     constexpr int N = V::N;
-    const int ncv = L.C / N;
-    const int ntc = (L.T + TF - 1) / TF;
-    int64_t r = (int64_t)blockIdx.x * kTconvThreads + threadIdx.x;
+    // 32-bit index arithmetic: the host keeps the thread count below 2^31
+    const uint32_t ncv = (uint32_t)L.C / N;
+    const uint32_t ntc = (uint32_t)(L.T + TF - 1) / TF;
+    uint32_t r = blockIdx.x * (uint32_t)kTconvThreads + threadIdx.x;
     const int cv = (int)(r % ncv);
     r /= ncv;
     const int tc = (int)(r % ntc);
     r /= ntc;
-    const int s = (int)(r % L.S);
-    r /= L.S;
-    if (r >= L.B) return;
+    const int s = (int)(r % (uint32_t)L.S);
+    r /= (uint32_t)L.S;
+    if (r >= (uint32_t)L.B) return;
     const int b = (int)r;
     const int c0 = cv * N;
     const int t0 = tc * TF;
@@ -98,13 +99,23 @@ __global__ __launch_bounds__(kTconvThreads) void tconv_kernel(TconvLaunch L) {
     const bool keep_cache = tc == 0 && L.cache_out;
     const u32x4 last = *(const u32x4*)(xs + (int64_t)(keep_cache ? L.T - 1 : min(t0, L.T - 1)) * L.xst);
 
+    // taps of the N channels: 3 N consecutive floats (16-byte aligned: c0 is a multiple of N
+    // and 3 N floats are a whole number of 16-byte words), bias likewise
     float w0[N], w1[N], w2[N], bs[N];
+    {
+        f32x4 tw[3 * N / 4], tb[N / 4];
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-        w0[j] = L.weight[3 * (c0 + j)];
-        w1[j] = L.weight[3 * (c0 + j) + 1];
-        w2[j] = L.weight[3 * (c0 + j) + 2];
-        bs[j] = L.bias ? L.bias[c0 + j] : 0.f;
+        for (int k = 0; k < 3 * N / 4; ++k) tw[k] = *(const f32x4*)(L.weight + 3 * c0 + 4 * k);
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k)
+            tb[k] = L.bias ? *(const f32x4*)(L.bias + c0 + 4 * k) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            w0[j] = tw[(3 * j) / 4][(3 * j) % 4];
+            w1[j] = tw[(3 * j + 1) / 4][(3 * j + 1) % 4];
+            w2[j] = tw[(3 * j + 2) / 4][(3 * j + 2) % 4];
+            bs[j] = tb[j / 4][j % 4];
+        }
     }
     float prev[N], cur[N], next[N];
     V::unpack(raw[0], prev);
@@ -135,19 +146,26 @@ __global__ __launch_bounds__(kTconvThreads) void tconv_kernel(TconvLaunch L) {
     if (keep_cache) *(u32x4*)((T*)L.cache_out + cache_off) = last;
 }
 
+template <typename T, int TF> hipError_t launch_tf(const TconvLaunch& L, hipStream_t s) {
+    constexpr int N = Vec<T>::N;
+    const int64_t threads = (int64_t)L.B * L.S * (L.C / N) * ((L.T + TF - 1) / TF);
+    const int64_t blocks = (threads + kTconvThreads - 1) / kTconvThreads;
+    if (blocks * kTconvThreads > 0x7FFFFFFF) return hipErrorInvalidValue;   // 32-bit indices
+    hipLaunchKernelGGL((tconv_kernel<T, TF>), dim3((unsigned)blocks), dim3(kTconvThreads), 0, s, L);
+    return hipGetLastError();
+}
+
+// frames per thread: the window fits short calls (a streaming block of one or a few frames)
+template <typename T> hipError_t launch_t(const TconvLaunch& L, hipStream_t s) {
+    if (L.T <= 1) return launch_tf<T, 1>(L, s);
+    if (L.T <= 4) return launch_tf<T, 4>(L, s);
+    return launch_tf<T, kTconvFrames>(L, s);
+}
+
 }  // namespace
 
 hipError_t tconv_launch(const TconvLaunch& L, hipStream_t s) {
-    constexpr int TF = kTconvFrames;
-    const int N = L.bf16 ? 8 : 4;
-    const int64_t threads = (int64_t)L.B * L.S * (L.C / N) * ((L.T + TF - 1) / TF);
-    const int64_t blocks = (threads + kTconvThreads - 1) / kTconvThreads;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (L.bf16)
-        hipLaunchKernelGGL((tconv_kernel<__bf16, TF>), dim3((unsigned)blocks), dim3(kTconvThreads), 0, s, L);
-    else
-        hipLaunchKernelGGL((tconv_kernel<float, TF>), dim3((unsigned)blocks), dim3(kTconvThreads), 0, s, L);
-    return hipGetLastError();
+    return L.bf16 ? launch_t<__bf16>(L, s) : launch_t<float>(L, s);
 }
 
 }  // namespace gdn

@@ -150,7 +150,7 @@ typedef struct {
  *   y          output [B][T][S][C] with the y strides; fp32 accumulation, bf16 rounded to
  *              nearest even
  *   cache_out  [B][S][C] contiguous, receives x[T-1], or NULL; may equal cache_in exactly
- * Pointers to x, y and the caches must be 16-byte aligned and strides multiples of 8 elements
+ * Pointers to x, y, the caches, weight and bias must be 16-byte aligned and strides multiples of 8 elements
  * (GDN_ERR_ALIGN); y and cache_out must not overlap any input (GDN_ERR_ALIAS). No workspace.
  * Asynchronous on hip_stream; errors and tracing as gdn_forward_framewise (trace kind
  * GDN_KERNEL_TCONV, units B*T*S).
