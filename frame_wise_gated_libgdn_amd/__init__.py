@@ -28,7 +28,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
           8: "GDN_ERR_HIP"}
 KERNEL_NAMES = {0: "products", 1: "combine", 2: "scan", 3: "step_partial", 4: "step_reduce",
                 5: "fused_reset", 6: "fused", 7: "scan_bwd", 8: "bwd", 9: "scan_states",
-                10: "tconv"}
+                10: "tconv", 11: "attn"}
 SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
 
 
@@ -60,6 +60,20 @@ class TconvProblem(ctypes.Structure):
                 ("x_stride_s", ctypes.c_int64),
                 ("y_stride_b", ctypes.c_int64), ("y_stride_t", ctypes.c_int64),
                 ("y_stride_s", ctypes.c_int64)]
+
+
+class AttnProblem(ctypes.Structure):
+    """gdn_attn_problem of include/libgdn.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("tokens_per_frame", ctypes.c_int32), ("q_frames", ctypes.c_int32),
+                ("kv_frames", ctypes.c_int32), ("q_frame0", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("q_stride_b", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+                ("q_stride_t", ctypes.c_int64),
+                ("kv_stride_b", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
+                ("kv_stride_t", ctypes.c_int64),
+                ("o_stride_b", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
+                ("o_stride_t", ctypes.c_int64)]
 
 
 class TraceEntry(ctypes.Structure):
@@ -97,6 +111,8 @@ def load():
                 fn.restype = ctypes.c_int
             lib.gdn_tconv_forward.argtypes = [ctypes.POINTER(TconvProblem)] + [_vp] * 7
             lib.gdn_tconv_forward.restype = ctypes.c_int
+            lib.gdn_attention_framecausal.argtypes = [ctypes.POINTER(AttnProblem)] + [_vp] * 5
+            lib.gdn_attention_framecausal.restype = ctypes.c_int
             lib.gdn_forward_framewise_fp8.argtypes = [P] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
             lib.gdn_forward_framewise_fp8.restype = ctypes.c_int
             lib.gdn_backward_framewise.argtypes = [P] + [_vp] * 14 + [_vp, ctypes.c_size_t, _vp]
@@ -308,6 +324,33 @@ def temporal_conv(x, weight, bias=None, cache=None, *, block_frames, out=None, c
     _check(load().gdn_tconv_forward(ctypes.byref(p), _ptr(x), _ptr(weight), _ptr(bias), _ptr(cache),
                                     _ptr(out), _ptr(cache_out), _stream(stream)))
     return out, cache_out
+
+
+def attention_framecausal(q, k, v, *, tokens_per_frame, q_frame0=0, scale=None, out=None,
+                          stream=None):
+    """Frame-causal softmax attention (gdn_attention_framecausal). q [B, H, Tq, D], k, v
+    [B, H, Tk, D] (bf16, D contiguous, k and v with the same strides); q's rows are frames
+    q_frame0 .. q_frame0 + Tq/S - 1, k's and v's frames 0 .. Tk/S - 1. Returns o like q."""
+    import torch
+    B, H, Tq, D = q.shape
+    Tk = k.shape[2]
+    S = int(tokens_per_frame)
+    if Tq % S or Tk % S:
+        raise GdnError(2, "token counts must be whole frames of %d tokens" % S)
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise GdnError(4, "k and v must share shape and strides")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise GdnError(3, "attention takes bfloat16 q, k, v")
+    if out is None:
+        out = torch.empty((B, H, Tq, D), dtype=torch.bfloat16, device=q.device)
+    if q.stride(3) != 1 or k.stride(3) != 1 or out.stride(3) != 1:
+        raise GdnError(4, "the head dimension must be contiguous")
+    p = AttnProblem(B, H, D, S, Tq // S, Tk // S, int(q_frame0), GDN_BF16,
+                    0.0 if scale is None else float(scale), *q.stride()[:3], *k.stride()[:3],
+                    *out.stride()[:3])
+    _check(load().gdn_attention_framecausal(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                            _stream(stream)))
+    return out
 
 
 def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_scale=None,

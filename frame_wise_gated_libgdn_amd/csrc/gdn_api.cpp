@@ -451,6 +451,51 @@ gdn_status run_tconv(const gdn_tconv_problem* p, const void* x, const float* wei
     return GDN_OK;
 }
 
+gdn_status run_attn(const gdn_attn_problem* p, const void* q, const void* k, const void* v,
+                    void* o, void* stream) {
+    g_msg[0] = '\0';
+    if (!p) return fail(GDN_ERR_NULL, "problem descriptor is NULL");
+    if (p->batch < 1 || p->heads < 1 || p->tokens_per_frame < 1 || p->q_frames < 1 ||
+        p->kv_frames < 1 || p->q_frame0 < 0)
+        return fail(GDN_ERR_SHAPE, "sizes must be >= 1 and q_frame0 >= 0");
+    if (p->q_frame0 + (int64_t)p->q_frames > p->kv_frames)
+        return fail(GDN_ERR_SHAPE, "the query frames (%d .. %d) must lie within the key frames (0 .. %d)",
+                    p->q_frame0, p->q_frame0 + p->q_frames - 1, p->kv_frames - 1);
+    if (!gdn::attn_supported(p->head_dim))
+        return fail(GDN_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", p->head_dim);
+    if (p->dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "attention takes bf16 data");
+    if (!q || !k || !v || !o) return fail(GDN_ERR_NULL, "q, k, v and o are required");
+    const int64_t B = p->batch, H = p->heads, D = p->head_dim, S = p->tokens_per_frame;
+    const int64_t Tq = (int64_t)p->q_frames * S, Tk = (int64_t)p->kv_frames * S;
+    if (Tk > ((int64_t)1 << 31) - 1 || B * H * ((Tq + 127) / 128) > ((int64_t)1 << 31) - 1)
+        return fail(GDN_ERR_SHAPE, "problem too large for one call");
+    if (!layout_ok(B, H, Tq, D, p->q_stride_b, p->q_stride_h, p->q_stride_t) ||
+        !layout_ok(B, H, Tk, D, p->kv_stride_b, p->kv_stride_h, p->kv_stride_t) ||
+        !layout_ok(B, H, Tq, D, p->o_stride_b, p->o_stride_h, p->o_stride_t))
+        return fail(GDN_ERR_STRIDE, "strides overlap rows or are negative");
+    for (const void* ptr : {q, k, v, (const void*)o})
+        if (!aligned(ptr, 16)) return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+    for (int64_t st : {p->q_stride_b, p->q_stride_h, p->q_stride_t, p->kv_stride_b, p->kv_stride_h,
+                       p->kv_stride_t, p->o_stride_b, p->o_stride_h, p->o_stride_t})
+        if (st % 8) return fail(GDN_ERR_ALIGN, "strides must be multiples of 8 elements");
+    const Span so = span_of(o, B, H, Tq, D, p->o_stride_b, p->o_stride_h, p->o_stride_t, 2);
+    for (Span in : {span_of(q, B, H, Tq, D, p->q_stride_b, p->q_stride_h, p->q_stride_t, 2),
+                    span_of(k, B, H, Tk, D, p->kv_stride_b, p->kv_stride_h, p->kv_stride_t, 2),
+                    span_of(v, B, H, Tk, D, p->kv_stride_b, p->kv_stride_h, p->kv_stride_t, 2)})
+        if (overlap(so, in)) return fail(GDN_ERR_ALIAS, "o overlaps q, k or v");
+    gdn::AttnLaunch L{};
+    L.B = (int)B; L.H = (int)H; L.D = (int)D; L.S = (int)S; L.Tq = (int)Tq; L.Tk = (int)Tk;
+    L.q_frame0 = p->q_frame0;
+    L.scale = p->scale > 0.f ? p->scale : (float)(1.0 / std::sqrt((double)D));
+    L.qsb = p->q_stride_b; L.qsh = p->q_stride_h; L.qst = p->q_stride_t;
+    L.ksb = p->kv_stride_b; L.ksh = p->kv_stride_h; L.kst = p->kv_stride_t;
+    L.osb = p->o_stride_b; L.osh = p->o_stride_h; L.ost = p->o_stride_t;
+    L.q = q; L.k = k; L.v = v; L.o = o;
+    const hipError_t e = gdn::run_attn(L, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -506,6 +551,11 @@ gdn_status gdn_tconv_forward(const gdn_tconv_problem* p, const void* x, const fl
                              const float* bias, const void* cache_in, void* y, void* cache_out,
                              void* hip_stream) {
     return run_tconv(p, x, weight, bias, cache_in, y, cache_out, hip_stream);
+}
+
+gdn_status gdn_attention_framecausal(const gdn_attn_problem* p, const void* q, const void* k,
+                                     const void* v, void* o, void* hip_stream) {
+    return run_attn(p, q, k, v, o, hip_stream);
 }
 
 gdn_status gdn_set_trace(void* const* events, int pairs) {

@@ -1,0 +1,244 @@
+// Frame-causal softmax attention: the softmax blocks that the hybrid video models interleave
+// with frame-wise GDN blocks (SANA-WM: gen-hub.ru article, architecture section; SANA-Streaming:
+// jefxiong.cn digest). A query of frame f attends to every key of frames 0..f (its own frame in
+// both directions), o = softmax(scale q k^T) v, per (b, h). Queries may be a later slice of the
+// frames than the keys (a streaming step against the cache of all frames so far).
+//
+// One workgroup of 4 waves takes 128 queries of one (b, h); a wave owns 32 of them (two 16-query
+// MFMA tiles) and walks the visible keys in tiles of 64:
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the wave's Q rows,
+//     held in registers for the whole call), so lane (r, g) holds the scores of query r for
+//     keys 4 g .. 4 g + 3 of each 16-key block;
+//   * online softmax per query in that layout (exp2 with scale * log2 e folded in; row maxima
+//     across the four lanes of a query by lane exchange);
+//   * O^T += V^T P^T: the score tiles are the B operand as they stand, taking the k order of a
+//     32-key step as keys {4 g + j} then {16 + 4 g + j} from two 16-key tiles; the A operand V^T
+//     is read in that same order with transposed LDS reads (ds_read_tr16_b64).
+// The next K/V tile is prefetched into registers while the current one is used. Key tiles that
+// every query of the workgroup sees completely skip the mask; the others mask per element.
+#include <stdint.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kAttnThreads = 256;
+constexpr int kQW = 32;        // queries per wave
+constexpr int kQB = 4 * kQW;   // queries per workgroup
+constexpr int kKT = 64;        // keys per tile
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, bf16x2{(bf16)lo, (bf16)hi});
+}
+
+// lane (r, g) of each 16-lane group receives X[k0 + 4 g + j][c0 + r], j = 0..3, from a
+// row-major [key][dim] LDS tile with row length MR (ds_read_tr16_b64: destination lane i takes
+// element i mod 4 of the four b16 values at the address of source lane 4 j + i / 4, so source
+// lane s points at row k0 + 4 g + s / 4, columns c0 + 4 (s mod 4) .. + 3)
+template <int MR> __device__ __forceinline__ u32x2 read_tr(const bf16* X, int k0, int c0, int r, int g) {
+    const bf16* a = X + (k0 + 4 * g + (r >> 2)) * MR + c0 + 4 * (r & 3);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a));
+}
+
+// number of keys visible to query row t (keys of frames 0 .. its frame)
+__device__ __forceinline__ int visible(const AttnLaunch& L, int t) {
+    const int64_t n = (int64_t)(L.q_frame0 + t / L.S + 1) * L.S;
+    return n < L.Tk ? (int)n : L.Tk;
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
+    constexpr int KSD = D / 32;           // k steps over the head dim
+    constexpr int DT = D / 16;            // 16-dim tiles of O
+    constexpr int MRK = D + 8, MRV = D + 16;
+    constexpr int CH = D / 8;             // 16-byte chunks per row
+    constexpr int PER = kKT * CH / 128;   // chunks per thread (K by threads 0-127, V by 128-255)
+    __shared__ __attribute__((aligned(16))) bf16 ks[kKT * MRK];
+    __shared__ __attribute__((aligned(16))) bf16 vs[kKT * MRV];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int nqb = (L.Tq + kQB - 1) / kQB;
+    const int bh = blockIdx.x / nqb, qb = blockIdx.x % nqb;
+    const int b = bh / L.H, h = bh % L.H;
+    const int qw0 = qb * kQB + wave * kQW;    // first query of this wave
+
+    // the wave's Q rows as B operands; rows past Tq repeat the last row (never stored)
+    bf16x8 qf[2][KSD];
+    int nlim[2];
+    {
+        const bf16* qbase = (const bf16*)L.q + (int64_t)b * L.qsb + (int64_t)h * L.qsh;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            const int t = min(qw0 + 16 * qt + r, L.Tq - 1);
+            nlim[qt] = visible(L, t);
+#pragma unroll
+            for (int k = 0; k < KSD; ++k)
+                qf[qt][k] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qbase + (int64_t)t * L.qst + 32 * k + 8 * g));
+        }
+    }
+    // keys every query of the workgroup sees, and the keys any of them sees
+    const int kfull = visible(L, qb * kQB);
+    const int kmax = visible(L, min(qb * kQB + kQB, L.Tq) - 1);
+
+    const bf16* kbase = (const bf16*)L.k + (int64_t)b * L.ksb + (int64_t)h * L.ksh;
+    const bf16* vbase = (const bf16*)L.v + (int64_t)b * L.ksb + (int64_t)h * L.ksh;
+    const bool loads_k = tid < 128;
+    const bf16* src = loads_k ? kbase : vbase;
+    const int lt = tid & 127;
+    // next tile's rows in registers; rows past Tk are loaded clamped and zeroed when staged
+    // (a select right after the load would wait for it)
+    u32x4 pre[PER];
+    int pre_k0 = 0;
+    auto prefetch = [&](int k0) {
+        pre_k0 = k0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = lt + 128 * i, row = c / CH, col = (c % CH) * 8;
+            pre[i] = *(const u32x4*)(src + (int64_t)min(k0 + row, L.Tk - 1) * L.kst + col);
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = lt + 128 * i, row = c / CH, col = (c % CH) * 8;
+            const u32x4 x = pre_k0 + row < L.Tk ? pre[i] : u32x4{0u, 0u, 0u, 0u};
+            if (loads_k)
+                *(u32x4*)(ks + row * MRK + col) = x;
+            else
+                *(u32x4*)(vs + row * MRV + col) = x;
+        }
+    };
+
+    const float c2 = L.scale * 1.4426950408889634f;   // scores in log2 units
+    float m[2] = {-__builtin_inff(), -__builtin_inff()}, l[2] = {0.f, 0.f};
+    f32x4 oacc[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    prefetch(0);
+    for (int k0 = 0; k0 < kmax; k0 += kKT) {
+        __syncthreads();   // the previous tile is no longer read
+        stage();
+        __syncthreads();
+        if (k0 + kKT < kmax) prefetch(k0 + kKT);
+
+        // S^T = K Q^T for 64 keys x 32 queries
+        f32x4 sacc[4][2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KSD; ++k)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + (16 * kt + r) * MRK + 32 * k + 8 * g));
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = mfma(a, qf[qt][k], sacc[kt][qt]);
+            }
+        const bool masked = k0 + kKT > kfull;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            float tmax = -__builtin_inff();
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float s = sacc[kt][qt][q] * c2;
+                    if (masked && k0 + 16 * kt + 4 * g + q >= nlim[qt]) s = -__builtin_inff();
+                    sacc[kt][qt][q] = s;
+                    tmax = __builtin_fmaxf(tmax, s);
+                }
+            tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float mnew = __builtin_fmaxf(m[qt], tmax);   // finite: key 0 is visible to all
+            const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
+            float sum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float p = __builtin_amdgcn_exp2f(sacc[kt][qt][q] - mnew);
+                    sacc[kt][qt][q] = p;
+                    sum += p;
+                }
+            l[qt] = l[qt] * alpha + sum;
+            m[qt] = mnew;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+        }
+        // O^T += V^T P^T, two 32-key steps
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+            bf16x8 pb[2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                const f32x4 x = sacc[2 * ks2][qt], y = sacc[2 * ks2 + 1][qt];
+                pb[qt] = __builtin_bit_cast(bf16x8, u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]),
+                                                          pack2(y[0], y[1]), pack2(y[2], y[3])});
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const u32x2 v0 = read_tr<MRV>(vs, 32 * ks2, 16 * dt, r, g);
+                const u32x2 v1 = read_tr<MRV>(vs, 32 * ks2 + 16, 16 * dt, r, g);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = mfma(a, pb[qt], oacc[dt][qt]);
+            }
+        }
+    }
+
+    // normalise and store: lane (r, g) holds O[query 16 qt + r][dims 16 dt + 4 g .. + 3]
+    bf16* obase = (bf16*)L.o + (int64_t)b * L.osb + (int64_t)h * L.osh;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        float lt_ = l[qt];
+        lt_ += __shfl_xor(lt_, 16);
+        lt_ += __shfl_xor(lt_, 32);
+        const float inv = 1.f / lt_;
+        const int t = qw0 + 16 * qt + r;
+        if (t < L.Tq) {
+            bf16* orow = obase + (int64_t)t * L.ost;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 x = oacc[dt][qt] * inv;
+                *(u32x2*)(orow + 16 * dt + 4 * g) = u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])};
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool attn_supported(int D) { return D == 64 || D == 128; }
+
+hipError_t attn_launch(const AttnLaunch& L, hipStream_t s) {
+    const int64_t blocks = (int64_t)L.B * L.H * ((L.Tq + kQB - 1) / kQB);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (L.D == 128)
+        hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, L);
+    else if (L.D == 64)
+        hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, L);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace gdn

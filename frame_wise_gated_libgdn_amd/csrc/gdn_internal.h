@@ -58,8 +58,23 @@ enum Kernel {
     K_PRODUCTS = 0, K_COMBINE = 1, K_SCAN = 2, K_STEP_PARTIAL = 3, K_STEP_REDUCE = 4,
     K_FUSED_RESET = 5, K_FUSED = 6, K_SCAN_BWD = 7, K_BWD = 8,
     K_SCAN_STATES = 9,   // the forward scan with fp32 per-frame states (backward's recompute)
-    K_TCONV = 10         // block-causal temporal convolution
+    K_TCONV = 10,        // block-causal temporal convolution
+    K_ATTN = 11          // frame-causal softmax attention
 };
+
+// Arguments of the frame-causal softmax attention (gdn_attn.hip). q: [B][H][Tq][D], k, v:
+// [B][H][Tk][D] (shared strides), o like q (own strides); elements, D contiguous; bf16.
+// Query row t belongs to frame q_frame0 + t / S and sees keys 0 .. (frame + 1) * S - 1.
+struct AttnLaunch {
+    int B, H, D, S, Tq, Tk, q_frame0;
+    float scale;
+    int64_t qsb, qsh, qst, ksb, ksh, kst, osb, osh, ost;
+    const void *q, *k, *v;
+    void* o;
+};
+bool attn_supported(int D);
+hipError_t attn_launch(const AttnLaunch& L, hipStream_t s);
+hipError_t run_attn(const AttnLaunch& L, hipStream_t s);
 
 // Arguments of the temporal convolution (gdn_tconv.hip). x, y: [B][T][S][C] with the strides
 // below (elements, channel stride 1); caches [B][S][C] contiguous; weight [C][3], bias [C].

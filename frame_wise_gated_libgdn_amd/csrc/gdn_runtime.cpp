@@ -6,6 +6,7 @@
 // Forward, fused:   reset of the ticket counter and frame flags -> fused kernel.
 // Step:             step_partial -> step_reduce -> products (output items of the one frame).
 // Temporal conv:    one launch (the whole block or sequence).
+// Attention:        one launch.
 // Backward:         products + [combine] + scan (forward states), products + [combine] of
 //                   C_f = Q_f^T dO_f, reverse scan (state gradients), per-frame gradients;
 //                   the states and state gradients are kept in fp32.
@@ -129,6 +130,18 @@ hipError_t run_tconv(const TconvLaunch& L, hipStream_t s) {
     if ((e = tconv_launch(L, s)) != hipSuccess) return e;
     if (timed && (e = hipEventRecord(t_trace_events[1], s)) != hipSuccess) return e;
     if (armed) t_trace_log.push_back({(int32_t)K_TCONV, 0, (int64_t)L.B * L.T * L.S});
+    return hipSuccess;
+}
+
+hipError_t run_attn(const AttnLaunch& L, hipStream_t s) {
+    t_trace_log.clear();
+    const bool armed = !t_trace_events.empty();
+    const bool timed = armed && t_trace_events.size() >= 2;
+    hipError_t e = hipSuccess;
+    if (timed && (e = hipEventRecord(t_trace_events[0], s)) != hipSuccess) return e;
+    if ((e = attn_launch(L, s)) != hipSuccess) return e;
+    if (timed && (e = hipEventRecord(t_trace_events[1], s)) != hipSuccess) return e;
+    if (armed) t_trace_log.push_back({(int32_t)K_ATTN, 0, (int64_t)L.B * L.H * L.Tq});
     return hipSuccess;
 }
 

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 4
+#define LIBGDN_ABI_VERSION 5
 
 typedef enum {
     GDN_OK = 0,
@@ -158,6 +158,42 @@ typedef struct {
 gdn_status gdn_tconv_forward(const gdn_tconv_problem* p, const void* x, const float* weight,
                              const float* bias, const void* cache_in, void* y, void* cache_out,
                              void* hip_stream);
+
+/*
+ * Frame-causal softmax attention: the softmax blocks that the pages' hybrid video models
+ * interleave with frame-wise GDN blocks (SANA-WM: 5 of 20 blocks, gen-hub.ru article,
+ * architecture section; an all-softmax model runs out of memory on the 60 s video because its
+ * key/value cache grows with every frame; SANA-Streaming's hybrid is 3.7x faster than
+ * all-softmax, jefxiong.cn digest). Per (b, h), a query row t of frame q_frame0 + t / S attends
+ * to every key of frames 0 .. that frame (its own frame in both directions):
+ *   o[t] = sum_j softmax_j(scale q[t] . k[j]) v[j],  j < min(Tk, (frame + 1) * S)
+ * With q_frames = kv_frames and q_frame0 = 0 this is the whole video; with q_frames = 1 it is a
+ * streaming step of frame q_frame0 against the key/value cache of frames 0 .. kv_frames - 1.
+ */
+typedef struct {
+    int32_t batch, heads, head_dim;       /* B, H, D in {64, 128} */
+    int32_t tokens_per_frame;             /* S */
+    int32_t q_frames;                     /* frames of q and o: Tq = q_frames * S */
+    int32_t kv_frames;                    /* frames of k and v: Tk = kv_frames * S */
+    int32_t q_frame0;                     /* frame index of q's first frame */
+    int32_t dtype;                        /* GDN_BF16 */
+    float   scale;                        /* <= 0 selects 1/sqrt(D) */
+    int64_t q_stride_b, q_stride_h, q_stride_t;    /* elements; D contiguous */
+    int64_t kv_stride_b, kv_stride_h, kv_stride_t; /* shared by k and v */
+    int64_t o_stride_b, o_stride_h, o_stride_t;
+} gdn_attn_problem;
+
+/*
+ *   q        [B][H][Tq][D] bf16
+ *   k, v     [B][H][Tk][D] bf16, the same strides; q_frame0 + q_frames <= kv_frames (every
+ *            query's own frame must be present)
+ *   o        [B][H][Tq][D] bf16, must not overlap q, k or v
+ * fp32 softmax and accumulation; the weights enter the value product rounded to bf16. Pointers
+ * 16-byte aligned, strides multiples of 8 elements. No workspace. Asynchronous on hip_stream;
+ * errors and tracing as gdn_forward_framewise (trace kind GDN_KERNEL_ATTN, units B*H*Tq).
+ */
+gdn_status gdn_attention_framecausal(const gdn_attn_problem* p, const void* q, const void* k,
+                                     const void* v, void* o, void* hip_stream);
 
 /*
  * Workspace bytes needed by gdn_forward_framewise (mode = 0), gdn_step_frame (mode = 1) or
@@ -274,7 +310,8 @@ typedef enum {
     GDN_KERNEL_SCAN_BWD = 7,      /* backward: reverse scan of the state gradients */
     GDN_KERNEL_BWD = 8,           /* backward: per-frame gradients of Q, K, V, gamma, beta */
     GDN_KERNEL_SCAN_STATES = 9,   /* backward: forward scan keeping every state in fp32 */
-    GDN_KERNEL_TCONV = 10         /* block-causal temporal convolution */
+    GDN_KERNEL_TCONV = 10,        /* block-causal temporal convolution */
+    GDN_KERNEL_ATTN = 11          /* frame-causal softmax attention */
 } gdn_kernel_kind;
 
 typedef struct {

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 4
+    assert gdn.abi_version() == 5
     lib = gdn.load()
     for code in range(9):
         assert lib.gdn_status_string(code)
@@ -309,3 +309,27 @@ def test_tconv_validation():
     p = tprob()
     p.x_stride_s = 8                                       # rows of 16 channels overlap
     assert call_tconv(p) == 4
+
+
+def aprob(B=1, H=2, D=128, S=40, fq=3, fk=3, f0=0):
+    st = (H * fk * S * D, fk * S * D, D)
+    sq = (H * fq * S * D, fq * S * D, D)
+    return gdn.AttnProblem(B, H, D, S, fq, fk, f0, gdn.GDN_BF16, 0.0, *sq, *st, *sq)
+
+
+def call_attn(p, q=A, k=2 * A, v=3 * A, o=4 * A):
+    pp = None if p is None else ctypes.byref(p)
+    return gdn.load().gdn_attention_framecausal(pp, q, k, v, o, None)
+
+
+def test_attention_validation():
+    assert call_attn(None) == 1
+    assert call_attn(aprob(), v=None) == 1
+    assert call_attn(aprob(fq=2, fk=3, f0=2)) == 2        # query frames past the key frames
+    assert "within the key frames" in msg()
+    assert call_attn(aprob(D=32)) == 3
+    p = aprob()
+    p.dtype = gdn.GDN_F32
+    assert call_attn(p) == 3
+    assert call_attn(aprob(), o=A + 256) == 6               # o overlaps q
+    assert call_attn(aprob(), k=2 * A + 8) == 5
