@@ -20,6 +20,10 @@ Prints one JSON line. Extra objects:
                 byte per element, O at two).
   tconv         the block-causal temporal conv (gdn_tconv_forward) over the same video at the
                 GDN block's width: whole video per call, and per-frame streaming latency.
+  attention     frame-causal softmax attention (gdn_attention_framecausal), the hybrid's
+                softmax block: the whole 880x81 sequence (TFLOP/s against the bf16 MFMA peak)
+                and one 720p frame against the cache of frames 0..f (cost per frame growing with
+                f, against the GDN's constant D x D state).
   backward      gdn_backward_framewise over the workload: ms per call, per-kernel ms and the
                 call's roofline (Q, K, V, dO read; dQ, dK, dV written).
 """
@@ -93,6 +97,7 @@ def parse():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-tconv", action="store_true")
+    ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--stream-frames", type=int, default=240)
     ap.add_argument("--schedule", default="auto", choices=["auto", "staged", "fused"],
@@ -412,6 +417,61 @@ def tconv_mode(dev, steps, warmup, ev, stream, stream_frames=240):
                        "floor_us": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}}
 
 
+def attention_mode(dev, steps, warmup, ev, stream):
+    """Frame-causal softmax attention (the hybrid's softmax block) at the pages' frame shapes:
+    the whole 880x81 sequence, and one 720p frame against the key/value cache of frames 0..f,
+    the per-frame cost that the GDN's constant state replaces."""
+    import torch
+    import frame_wise_gated_libgdn_amd as gdn
+    import gdn_synth
+    sh = stream.cuda_stream
+
+    def timed(fn, reps):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        tr = [[ev.new(), ev.new()] for _ in range(reps)]
+        for i in range(reps):
+            gdn.set_trace(tr[i])
+            fn()
+        gdn.set_trace(None)
+        torch.cuda.synchronize()
+        return sum(ev.ms(a, b) for a, b in tr) / reps
+
+    out = {}
+    w = gdn_synth.WORKLOADS["gdn_880x81_bf16"]
+    q, k, v = gdn_synth.qkv_torch(w, dev)
+    o = torch.empty_like(q)
+    ms = timed(lambda: gdn.attention_framecausal(q, k, v, tokens_per_frame=w.S, out=o, stream=stream),
+               steps)
+    flops = 4 * w.D * w.S * w.S * w.F * (w.F + 1) // 2 * w.B * w.H
+    out["whole_880x81"] = {"workload": w.name, "kernel_ms": round(ms, 4),
+                           "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                           "frac_of_bf16_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "flops_alg_tf": round(flops / 1e12, 3)}
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    w = gdn_synth.WORKLOADS["gdn_720p_60s_bf16"]
+    S = w.S
+    q, k, v = gdn_synth.qkv_torch(w, dev)
+    o = torch.empty((w.B, w.H, S, w.D), dtype=torch.bfloat16, device=dev)
+    per = []
+    for f in (60, 240, w.F - 1):
+        n = (f + 1) * S
+        ms = timed(lambda: gdn.attention_framecausal(q[:, :, f * S:(f + 1) * S], k[:, :, :n], v[:, :, :n],
+                                                     tokens_per_frame=S, q_frame0=f, out=o, stream=stream),
+                   max(1, min(steps, 5)))
+        flops = 4 * w.D * S * n * w.B * w.H
+        per.append({"frame": f, "kernel_ms": round(ms, 3),
+                    "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                    "kv_cache_gb": round(2 * n * w.D * 2 * w.B * w.H / 1e9, 2)})
+    out["stream_720p_frame"] = {"workload": w.name, "per_frame": per,
+                                "gdn_state_mb": round(w.B * w.H * w.D * w.D * 4 / 1e6, 2)}
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return out
+
+
 def streaming_ceiling(dev, gib=4.0, reps=10):
     """Bandwidth of a plain torch streaming kernel with the fused kernel's mix of traffic (three
     tensors read, one written: y = a + b * c in one elementwise kernel), for reading `frac`
@@ -590,6 +650,14 @@ def main():
         ev5.close()
         torch.cuda.empty_cache()
         log("temporal conv done: %.3f ms/call" % result["tconv"]["ms_per_call"])
+    if not args.no_attention and w.name == "gdn_720p_60s_bf16":
+        ev6 = HipEvents()
+        log("softmax attention")
+        result["attention"] = attention_mode(dev, args.steps, min(args.warmup, 1), ev6,
+                                             torch.cuda.current_stream())
+        ev6.close()
+        torch.cuda.empty_cache()
+        log("attention done: %s" % result["attention"]["whole_880x81"])
     if not args.no_backward and w.dtype == "bf16" and w.D in (64, 128):
         ev3 = HipEvents()
         log("backward: %d calls" % args.backward_steps)
