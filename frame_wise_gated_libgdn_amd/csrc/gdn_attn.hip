@@ -32,8 +32,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kAttnThreads = 256;
-constexpr int kQW = 32;        // queries per wave
-constexpr int kQB = 4 * kQW;   // queries per workgroup
 constexpr int kKT = 64;        // keys per tile
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -60,13 +58,17 @@ __device__ __forceinline__ int visible(const AttnLaunch& L, int t) {
     return n < L.Tk ? (int)n : L.Tk;
 }
 
-template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
+// QT 16-query tiles per wave: each K / V^T fragment read from LDS feeds QT MFMAs
+template <int D, int QT>
+__global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(AttnLaunch L) {
+    constexpr int kQW = 16 * QT;     // queries per wave
+    constexpr int kQB = 4 * kQW;     // queries per workgroup
     constexpr int KSD = D / 32;           // k steps over the head dim
     constexpr int DT = D / 16;            // 16-dim tiles of O
     constexpr int MRK = D + 8, MRV = D + 16;
     constexpr int CH = D / 8;             // 16-byte chunks per row
     constexpr int PER = kKT * CH / 128;   // chunks per thread (K by threads 0-127, V by 128-255)
+    constexpr int NKT = kKT / 16;         // 16-key tiles per key tile
     __shared__ __attribute__((aligned(16))) bf16 ks[kKT * MRK];
     __shared__ __attribute__((aligned(16))) bf16 vs[kKT * MRV];
 
@@ -78,12 +80,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
     const int qw0 = qb * kQB + wave * kQW;    // first query of this wave
 
     // the wave's Q rows as B operands; rows past Tq repeat the last row (never stored)
-    bf16x8 qf[2][KSD];
-    int nlim[2];
+    bf16x8 qf[QT][KSD];
+    int nlim[QT];
     {
         const bf16* qbase = (const bf16*)L.q + (int64_t)b * L.qsb + (int64_t)h * L.qsh;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int qt = 0; qt < QT; ++qt) {
             const int t = min(qw0 + 16 * qt + r, L.Tq - 1);
             nlim[qt] = visible(L, t);
 #pragma unroll
@@ -125,12 +127,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
     };
 
     const float c2 = L.scale * 1.4426950408889634f;   // scores in log2 units
-    float m[2] = {-__builtin_inff(), -__builtin_inff()}, l[2] = {0.f, 0.f};
-    f32x4 oacc[DT][2];
+    float m[QT], l[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        m[qt] = -__builtin_inff();
+        l[qt] = 0.f;
+    }
+    f32x4 oacc[DT][QT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     prefetch(0);
     for (int k0 = 0; k0 < kmax; k0 += kKT) {
@@ -140,25 +147,25 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
         if (k0 + kKT < kmax) prefetch(k0 + kKT);
 
         // S^T = K Q^T for 64 keys x 32 queries
-        f32x4 sacc[4][2];
+        f32x4 sacc[NKT][QT];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KSD; ++k)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
+            for (int kt = 0; kt < NKT; ++kt) {
                 const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + (16 * kt + r) * MRK + 32 * k + 8 * g));
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) sacc[kt][qt] = mfma(a, qf[qt][k], sacc[kt][qt]);
+                for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma(a, qf[qt][k], sacc[kt][qt]);
             }
         const bool masked = k0 + kKT > kfull;
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int qt = 0; qt < QT; ++qt) {
             float tmax = -__builtin_inff();
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float s = sacc[kt][qt][q] * c2;
@@ -172,7 +179,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
             const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
             float sum = 0.f;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float p = __builtin_amdgcn_exp2f(sacc[kt][qt][q] - mnew);
@@ -186,10 +193,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
         }
         // O^T += V^T P^T, two 32-key steps
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-            bf16x8 pb[2];
+        for (int ks2 = 0; ks2 < NKT / 2; ++ks2) {
+            bf16x8 pb[QT];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
+            for (int qt = 0; qt < QT; ++qt) {
                 const f32x4 x = sacc[2 * ks2][qt], y = sacc[2 * ks2 + 1][qt];
                 pb[qt] = __builtin_bit_cast(bf16x8, u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]),
                                                           pack2(y[0], y[1]), pack2(y[2], y[3])});
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
                 const u32x2 v1 = read_tr<MRV>(vs, 32 * ks2 + 16, 16 * dt, r, g);
                 const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) oacc[dt][qt] = mfma(a, pb[qt], oacc[dt][qt]);
+                for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma(a, pb[qt], oacc[dt][qt]);
             }
         }
     }
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
     // normalise and store: lane (r, g) holds O[query 16 qt + r][dims 16 dt + 4 g .. + 3]
     bf16* obase = (bf16*)L.o + (int64_t)b * L.osb + (int64_t)h * L.osh;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < QT; ++qt) {
         float lt_ = l[qt];
         lt_ += __shfl_xor(lt_, 16);
         lt_ += __shfl_xor(lt_, 32);
@@ -229,16 +236,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_kernel(AttnLaunch L) {
 
 bool attn_supported(int D) { return D == 64 || D == 128; }
 
-hipError_t attn_launch(const AttnLaunch& L, hipStream_t s) {
+template <int D, int QT> hipError_t launch_qt(const AttnLaunch& L, hipStream_t s) {
+    constexpr int kQB = 4 * 16 * QT;
     const int64_t blocks = (int64_t)L.B * L.H * ((L.Tq + kQB - 1) / kQB);
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (L.D == 128)
-        hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, L);
-    else if (L.D == 64)
-        hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, L);
-    else
-        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_kernel<D, QT>), dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, L);
     return hipGetLastError();
+}
+
+constexpr int kAttnQT = 2;   // 16-query tiles per wave (4: one wave per SIMD, measured slower)
+
+hipError_t attn_launch(const AttnLaunch& L, hipStream_t s) {
+    if (L.D == 128) return launch_qt<128, kAttnQT>(L, s);
+    if (L.D == 64) return launch_qt<64, kAttnQT>(L, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace gdn
