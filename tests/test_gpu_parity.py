@@ -162,6 +162,76 @@ def test_fused_forward(case):
     assert d2 <= 1e-5 and d1 <= 1e-2
 
 
+GATE_CASES = [
+    # name, gamma, beta
+    ("gamma 0: every frame forgets the state", 0.0, None),
+    ("beta 0: pure decay of the initial state", None, 0.0),
+    ("gamma 1, beta 1", 1.0, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=[c[0].split(":")[0] for c in GATE_CASES])
+def test_fused_gate_extremes(case):
+    """Extreme gate values through both schedules: gamma = 0 (M_f built from frame f alone),
+    beta = 0 (M_f = gamma^f M_0, outputs Q M_f), gamma = beta = 1."""
+    name, gv, bv = case
+    B, H, D, S, F = 1, 2, 128, 70, 6
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    g = (np.full((B, H, F), gv) if gv is not None else rng.uniform(0.85, 1.0, (B, H, F))).astype(np.float32)
+    b = (np.full((B, H, F), bv) if bv is not None else rng.uniform(0.1, 0.9, (B, H, F))).astype(np.float32)
+    s0 = (0.3 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV)]
+    ro, rs = oracle.forward(q, k, v, g, b, s0)
+    for sched in ("fused", "staged"):
+        o, st = gdn.forward_framewise(*args, torch.from_numpy(s0).to(DEV), schedule=sched)
+        torch.cuda.synchronize()
+        e1, e2 = rel_err(to_np(o), ro), rel_err(to_np(st), rs)
+        say("  %s %s: O err %.3e state err %.3e" % (name, sched, e1, e2))
+        assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+def test_fused_many_short_chains():
+    """1024 (b, h) chains of 3 frames each: tickets spread every chain's frames far apart."""
+    B, H, D, S, F = 4, 256, 64, 24, 3
+    rng = np.random.default_rng(21)
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV)]
+    o, st = gdn.forward_framewise(*args, schedule="fused")
+    torch.cuda.synchronize()
+    ro, rs = oracle.forward(q, k, v, g, b)
+    e1, e2 = rel_err(to_np(o), ro), rel_err(to_np(st), rs)
+    say("  O err %.3e state err %.3e" % (e1, e2))
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+def test_fused_nan_stays_in_its_head():
+    """A NaN in one head's initial state reaches every output of that head and nothing else."""
+    B, H, D, S, F = 1, 3, 64, 40, 4
+    rng = np.random.default_rng(22)
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    s0 = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    s0[0, 1, :, :] = np.nan
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV)]
+    o, st = gdn.forward_framewise(*args, torch.from_numpy(s0).to(DEV), schedule="fused")
+    torch.cuda.synchronize()
+    o = to_np(o)
+    assert np.isnan(o[0, 1]).all() and np.isnan(to_np(st)[0, 1]).all()
+    s_ok = s0.copy()
+    s_ok[0, 1] = 0.0
+    ro, rs = oracle.forward(q, k, v, g, b, s_ok)
+    for h in (0, 2):
+        assert rel_err(o[0, h], ro[0, h]) <= TOL["bf16"]
+        assert rel_err(to_np(st)[0, h], rs[0, h]) <= TOL["bf16"]
+
+
 def test_fused_in_place_state_and_determinism():
     rng = np.random.default_rng(11)
     B, H, D, S, F = 1, 2, 128, 50, 9
