@@ -3,6 +3,7 @@
 // gdn_kernels.hip.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -189,6 +190,18 @@ bool layout_ok(int64_t B, int64_t H, int64_t T, int64_t D, int64_t sb, int64_t s
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Polls of a frame flag before a fused-schedule workgroup gives up: GDN_FUSED_SPIN_LIMIT from
+// the environment (a diagnostic; 0 makes every frame after the first time out at once, so the
+// time-out path can be exercised), else the default.
+int fused_spin_limit() {
+    const char* e = getenv("GDN_FUSED_SPIN_LIMIT");
+    if (!e || !*e) return gdn::kSpinLimitDefault;
+    char* end = nullptr;
+    const long v = strtol(e, &end, 10);
+    if (*end || v < 0 || v > (1L << 30)) return gdn::kSpinLimitDefault;
+    return (int)v;
+}
+
 // scales: the three E4M3 scale arrays (gdn_forward_framewise_fp8), or NULL
 gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k, const void* v,
                const float* const* scales, const float* gamma, const float* beta,
@@ -280,6 +293,7 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     L.xsb = L.sb; L.xsh = L.sh; L.xst = L.st;
     L.gamma = gamma; L.beta = beta; L.state_in = state_in; L.state_out = state_out;
     if (pl.fused) {
+        L.spin_limit = fused_spin_limit();
         L.ctl = (int*)ws;
         L.chain = (float*)((char*)ws + align256(pl.ctl_bytes));
         // the fused kernel finds the end of a frame's rows from the token stride (rows past

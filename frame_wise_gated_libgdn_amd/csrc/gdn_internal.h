@@ -28,6 +28,8 @@ struct Launch {
     void* canon;         // workspace: per-frame record handed from the products kernel to the scan
     float* part;         // workspace: per-split fp32 partial products (when nsplit > 1)
     void* mt;            // workspace: materialised per-frame states, transposed, in the I/O type
+    int spin_limit;      // fused: polls of a frame flag before a workgroup gives up (0: never
+                         //   wait, every frame after the first times out)
     int* ctl;            // workspace (fused): [0] ticket counter, [1] wait time-out flag,
                          //   [2 + bh * kChainGroups + g] last frame of (b, h) whose column
                          //   group g of the state is published
@@ -93,6 +95,7 @@ hipError_t run_tconv(const TconvLaunch& L, hipStream_t s);
 
 // Fused forward: value-column groups pipelined through the frame chain (one flag each per (b, h)).
 constexpr int kChainGroups = 4;
+constexpr int kSpinLimitDefault = 1 << 20;  // polls of about a microsecond each
 
 // Whether the fused single-pass forward has a kernel for this type / head size.
 bool fused_supported(int bf16, int D);

@@ -775,7 +775,7 @@ __global__ __launch_bounds__(NT, 2) void products_kernel(Launch L) {
 // t / BH of (b h) = t % BH, so a workgroup only ever waits for a smaller ticket, whose
 // workgroup is already running (it took its ticket first) and waits only for smaller tickets
 // in turn: the chain always completes whatever order the hardware dispatches workgroups in.
-// The wait is bounded (kSpinLimit polls); on time-out the workgroup raises ctl[1], continues
+// The wait is bounded (L.spin_limit polls); on time-out the workgroup raises ctl[1], continues
 // with a NaN state so the failure is visible in every later output, and still publishes, so
 // the kernel always ends.
 //
@@ -802,7 +802,6 @@ __global__ __launch_bounds__(NT, 2) void products_kernel(Launch L) {
 // The codes are decoded exactly to bf16 on the way into LDS or into MFMA operands, the
 // products run on the codes, and the scales enter as scalars: Ghat takes k_scale^2, Bhat
 // k_scale v_scale, and the output tile q_scale before rounding to bf16.
-constexpr int kSpinLimit = 1 << 20;  // polls of about a microsecond each
 constexpr int kCoherent = 16;        // cache-policy operand of the buffer intrinsics: sc1
 
 
@@ -933,8 +932,9 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
             int ok = 1;
             if (f > 0) {
                 int polls = 0;
-                while (__hip_atomic_load(flags + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < f - 1) {
-                    if (++polls > kSpinLimit) {
+                while (L.spin_limit == 0 ||
+                       __hip_atomic_load(flags + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < f - 1) {
+                    if (++polls > L.spin_limit) {
                         ok = 0;
                         __hip_atomic_store(&L.ctl[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;

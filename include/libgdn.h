@@ -99,6 +99,11 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype;
  *           D = 64 or 128, and a frame's rows ((S-1) * qkv_stride_t + D elements) within 2 GiB
  *           (GDN_ERR_UNSUPPORTED otherwise).
  *   AUTO    FUSED where supported and B*H*F >= 1024, else STAGED.
+ * FUSED waits for the previous frame's state are bounded: after GDN_FUSED_SPIN_LIMIT polls
+ * (environment, default 2^20, about a microsecond each) a workgroup gives up, continues with a
+ * NaN state (every later output of that (b, h) is NaN) and sets the int32 time-out flag at byte
+ * 4 of the workspace; the kernel always ends. GDN_FUSED_SPIN_LIMIT=0 times out every frame
+ * after the first at once (for exercising that path).
  */
 typedef enum { GDN_SCHEDULE_AUTO = 0, GDN_SCHEDULE_STAGED = 1, GDN_SCHEDULE_FUSED = 2 } gdn_schedule;
 

@@ -366,3 +366,33 @@ def test_determinism_bitwise():
     o2, s2 = gdn.forward_framewise(*args)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_fused_wait_timeout_path(monkeypatch):
+    """The bounded wait's time-out path, forced from the host: with GDN_FUSED_SPIN_LIMIT=0 every
+    frame after the first gives up at once, so frame 0 is exact, every later output and the
+    final state are NaN, and the workspace's time-out flag is set; the default clears it."""
+    B, H, D, S, F = 1, 2, 128, 64, 5
+    rng = np.random.default_rng(23)
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV)]
+    p = gdn.Problem(B, H, D, S, F, gdn.GDN_BF16, 1, 0.0, H * F * S * D, F * S * D, D,
+                    H * F * S * D, F * S * D, D, gdn.SCHEDULES["fused"])
+    ws = torch.zeros(gdn.workspace_size(p, False), dtype=torch.uint8, device=DEV)
+    ro, _ = oracle.forward(q, k, v, g, b)
+    monkeypatch.setenv("GDN_FUSED_SPIN_LIMIT", "0")
+    o, st = gdn.forward_framewise(*args, workspace=ws, schedule="fused")
+    torch.cuda.synchronize()
+    flag = int(ws[4:8].view(torch.int32).item())
+    o = to_np(o)
+    assert flag == 1
+    assert rel_err(o[:, :, :S], ro[:, :, :S]) <= TOL["bf16"]
+    assert np.isnan(o[:, :, S:]).all() and np.isnan(to_np(st)).all()
+    monkeypatch.delenv("GDN_FUSED_SPIN_LIMIT")
+    o, st = gdn.forward_framewise(*args, workspace=ws, schedule="fused")
+    torch.cuda.synchronize()
+    assert int(ws[4:8].view(torch.int32).item()) == 0
+    assert rel_err(to_np(o), ro) <= TOL["bf16"]
