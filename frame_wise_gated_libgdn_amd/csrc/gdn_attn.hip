@@ -14,7 +14,10 @@
 //   * O^T += V^T P^T: the score tiles are the B operand as they stand, taking the k order of a
 //     32-key step as keys {4 g + j} then {16 + 4 g + j} from two 16-key tiles; the A operand V^T
 //     is read in that same order with transposed LDS reads (ds_read_tr16_b64).
-// The next K/V tile is prefetched into registers while the current one is used. Key tiles that
+// K/V tiles go from global memory straight into LDS (gfx950's 16-byte global_load_lds), double
+// buffered, so the next tile is in flight while this one is used and no registers hold it: the
+// tile lands unpadded, one 1 KB stretch per instruction, and bank conflicts are avoided by the
+// choice of source chunk per lane (an XOR swizzle of each row's 16-byte chunks). Key tiles that
 // every query of the workgroup sees completely skip the mask; the others mask per element.
 #include <stdint.h>
 
@@ -43,12 +46,24 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, bf16x2{(bf16)lo, (bf16)hi});
 }
 
-// lane (r, g) of each 16-lane group receives X[k0 + 4 g + j][c0 + r], j = 0..3, from a
-// row-major [key][dim] LDS tile with row length MR (ds_read_tr16_b64: destination lane i takes
-// element i mod 4 of the four b16 values at the address of source lane 4 j + i / 4, so source
-// lane s points at row k0 + 4 g + s / 4, columns c0 + 4 (s mod 4) .. + 3)
-template <int MR> __device__ __forceinline__ u32x2 read_tr(const bf16* X, int k0, int c0, int r, int g) {
-    const bf16* a = X + (k0 + 4 * g + (r >> 2)) * MR + c0 + 4 * (r & 3);
+// XOR swizzle of the 16-byte chunks of a key row in an unpadded [key][dim] LDS tile with CH
+// chunks per row: chunk c of row r is stored at chunk c ^ swz(r). For CH = 16 (D = 128) it is a
+// bijection on every 16 consecutive rows (K fragment reads: 16 rows, one chunk) whose values on
+// 4 rows 4m .. 4m + 3 differ above bit 0 (V^T reads: 4 rows, chunks 2d and 2d + 1).
+template <int CH> __device__ __forceinline__ int swz(int r) {
+    if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (r >> 1) & (CH - 1);
+}
+
+// lane (r, g) of each 16-lane group receives X[k0 + 4 g + j][c0 + r], j = 0..3, from a swizzled
+// [key][dim] LDS tile (ds_read_tr16_b64: destination lane i takes element i mod 4 of the four
+// b16 values at the address of source lane 4 j + i / 4, so source lane s points at row
+// k0 + 4 g + s / 4, columns c0 + 4 (s mod 4) .. + 3: chunk c0 / 8 + (s mod 4) / 2, half s mod 2)
+template <int D> __device__ __forceinline__ u32x2 read_tr(const bf16* X, int k0, int c0, int r, int g) {
+    constexpr int CH = D / 8;
+    const int row = k0 + 4 * g + (r >> 2);
+    const int c = c0 / 8 + ((r & 3) >> 1);
+    const bf16* a = X + row * D + ((c ^ swz<CH>(row)) * 8) + 4 * (r & 1);
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a));
 }
 
@@ -65,12 +80,12 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
     constexpr int kQB = 4 * kQW;     // queries per workgroup
     constexpr int KSD = D / 32;           // k steps over the head dim
     constexpr int DT = D / 16;            // 16-dim tiles of O
-    constexpr int MRK = D + 8, MRV = D + 16;
     constexpr int CH = D / 8;             // 16-byte chunks per row
-    constexpr int PER = kKT * CH / 128;   // chunks per thread (K by threads 0-127, V by 128-255)
     constexpr int NKT = kKT / 16;         // 16-key tiles per key tile
-    __shared__ __attribute__((aligned(16))) bf16 ks[kKT * MRK];
-    __shared__ __attribute__((aligned(16))) bf16 vs[kKT * MRV];
+    constexpr int SLOTS = kKT * CH;       // 16-byte slots of one operand tile
+    constexpr int INSTR = 2 * SLOTS / (64 * 4);   // load instructions per wave per tile (K and V)
+    static_assert(SLOTS % 64 == 0 && (2 * SLOTS) % 256 == 0, "whole instructions per wave");
+    __shared__ __attribute__((aligned(16))) bf16 tiles[2][2][kKT * D];   // [buffer][K, V]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -99,30 +114,19 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
 
     const bf16* kbase = (const bf16*)L.k + (int64_t)b * L.ksb + (int64_t)h * L.ksh;
     const bf16* vbase = (const bf16*)L.v + (int64_t)b * L.ksb + (int64_t)h * L.ksh;
-    const bool loads_k = tid < 128;
-    const bf16* src = loads_k ? kbase : vbase;
-    const int lt = tid & 127;
-    // next tile's rows in registers; rows past Tk are loaded clamped and zeroed when staged
-    // (a select right after the load would wait for it)
-    u32x4 pre[PER];
-    int pre_k0 = 0;
-    auto prefetch = [&](int k0) {
-        pre_k0 = k0;
+    // tile of keys k0 .. k0 + kKT - 1 into buffer buf: instruction ins of the workgroup fills
+    // slots 64 ins .. 64 ins + 63 of the K | V pair; rows past Tk are loaded clamped (finite
+    // values: their scores are masked and their weights are zero)
+    auto issue = [&](int k0, int buf) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = lt + 128 * i, row = c / CH, col = (c % CH) * 8;
-            pre[i] = *(const u32x4*)(src + (int64_t)min(k0 + row, L.Tk - 1) * L.kst + col);
-        }
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = lt + 128 * i, row = c / CH, col = (c % CH) * 8;
-            const u32x4 x = pre_k0 + row < L.Tk ? pre[i] : u32x4{0u, 0u, 0u, 0u};
-            if (loads_k)
-                *(u32x4*)(ks + row * MRK + col) = x;
-            else
-                *(u32x4*)(vs + row * MRV + col) = x;
+        for (int i = 0; i < INSTR; ++i) {
+            const int ins = wave * INSTR + i;
+            const bool isv = ins * 64 >= SLOTS;              // the same for the whole wave
+            const int u = ins * 64 + lane - (isv ? SLOTS : 0);
+            const int row = u / CH, c = (u % CH) ^ swz<CH>(row);
+            const bf16* src = (isv ? vbase : kbase) + (int64_t)min(k0 + row, L.Tk - 1) * L.kst + c * 8;
+            bf16* dst = &tiles[buf][isv ? 1 : 0][(ins * 64 - (isv ? SLOTS : 0)) * 8];
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
     };
 
@@ -139,12 +143,16 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    prefetch(0);
-    for (int k0 = 0; k0 < kmax; k0 += kKT) {
-        __syncthreads();   // the previous tile is no longer read
-        stage();
+    issue(0, 0);
+    int buf = 0;
+    for (int k0 = 0; k0 < kmax; k0 += kKT, buf ^= 1) {
+        // this wave's loads of tile k0 are done; after the barrier every wave's are, and every
+        // wave is done reading the other buffer (the previous tile), which the next tile fills
+        __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (k0 + kKT < kmax) prefetch(k0 + kKT);
+        if (k0 + kKT < kmax) issue(k0 + kKT, buf ^ 1);
+        const bf16* ks = tiles[buf][0];
+        const bf16* vs = tiles[buf][1];
 
         // S^T = K Q^T for 64 keys x 32 queries
         f32x4 sacc[NKT][QT];
@@ -156,7 +164,8 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
         for (int k = 0; k < KSD; ++k)
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + (16 * kt + r) * MRK + 32 * k + 8 * g));
+                const int row = 16 * kt + r;
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + row * D + (((4 * k + g) ^ swz<CH>(row)) * 8)));
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma(a, qf[qt][k], sacc[kt][qt]);
             }
@@ -203,8 +212,8 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
             }
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const u32x2 v0 = read_tr<MRV>(vs, 32 * ks2, 16 * dt, r, g);
-                const u32x2 v1 = read_tr<MRV>(vs, 32 * ks2 + 16, 16 * dt, r, g);
+                const u32x2 v0 = read_tr<D>(vs, 32 * ks2, 16 * dt, r, g);
+                const u32x2 v1 = read_tr<D>(vs, 32 * ks2 + 16, 16 * dt, r, g);
                 const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma(a, pb[qt], oacc[dt][qt]);
