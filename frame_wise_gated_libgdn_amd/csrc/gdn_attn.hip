@@ -9,8 +9,9 @@
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the wave's Q rows,
 //     held in registers for the whole call), so lane (r, g) holds the scores of query r for
 //     keys 4 g .. 4 g + 3 of each 16-key block;
-//   * online softmax per query in that layout (exp2 with scale * log2 e folded in; row maxima
-//     across the four lanes of a query by lane exchange);
+//   * online softmax per query in that layout (exp2 of one fma with scale * log2 e folded in;
+//     row maxima across the four lanes of a query by lane exchange; the running maximum moves
+//     only by more than 8 in log2 units, so most tiles skip rescaling the accumulators);
 //   * O^T += V^T P^T: the score tiles are the B operand as they stand, taking the k order of a
 //     32-key step as keys {4 g + j} then {16 + 4 g + j} from two 16-key tiles; the A operand V^T
 //     is read in that same order with transposed LDS reads (ds_read_tr16_b64).
@@ -169,36 +170,49 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma(a, qf[qt][k], sacc[kt][qt]);
             }
-        const bool masked = k0 + kKT > kfull;
+        if (k0 + kKT > kfull) {   // a tile some query does not see completely
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (k0 + 16 * kt + 4 * g + q >= nlim[qt]) sacc[kt][qt][q] = -__builtin_inff();
+        }
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
+            // tile maximum on the raw scores (the scale is positive), across the query's 4 lanes
             float tmax = -__builtin_inff();
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float s = sacc[kt][qt][q] * c2;
-                    if (masked && k0 + 16 * kt + 4 * g + q >= nlim[qt]) s = -__builtin_inff();
-                    sacc[kt][qt][q] = s;
-                    tmax = __builtin_fmaxf(tmax, s);
-                }
+                for (int q = 0; q < 4; ++q) tmax = __builtin_fmaxf(tmax, sacc[kt][qt][q]);
             tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float mnew = __builtin_fmaxf(m[qt], tmax);   // finite: key 0 is visible to all
-            const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
+            // the running maximum (log2 units) moves only when the tile's exceeds it by more than
+            // 8, so weights stay below 2^8 and most tiles skip the rescale; exact, since the
+            // final normalisation uses the same maximum. Finite after the first tile (key 0 is
+            // visible to every query).
+            const float cand = tmax * c2;
+            const bool move = cand > m[qt] + 8.f;
+            if (__any(move)) {
+                const float mnew = move ? cand : m[qt];
+                const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
+                l[qt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+                m[qt] = mnew;
+            }
             float sum = 0.f;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[kt][qt][q] - mnew);
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][qt][q], c2, -m[qt]));
                     sacc[kt][qt][q] = p;
                     sum += p;
                 }
-            l[qt] = l[qt] * alpha + sum;
-            m[qt] = mnew;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
+            l[qt] += sum;
         }
         // O^T += V^T P^T, two 32-key steps
 #pragma unroll
