@@ -30,7 +30,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // function of it.
 struct Plan {
     int mode;                   // 0 forward, 1 step, 2 backward
-    bool fused;                 // forward: fused single pass (else staged)
+    bool fused;                 // forward: fused single pass (else staged); step: column blocks
     int nsplit, split_tokens;   // partial-product kernel
     int nchunk, chunk_tokens;   // output kernel
     size_t canon_bytes, part_bytes, mt_bytes;   // staged forward and step
@@ -40,6 +40,7 @@ struct Plan {
         if (mode == 2)
             return align256(canon_bytes) + align256(part_bytes) + align256(mt_bytes) +
                    align256(crec_bytes) + gt_bytes;
+        if (mode == 1 && fused) return align256(part_bytes) + mt_bytes;
         return fused ? align256(ctl_bytes) + chain_bytes
                      : align256(canon_bytes) + align256(part_bytes) + mt_bytes;
     }
@@ -65,14 +66,32 @@ bool choose_fused(const gdn_problem& p, int step_mode) {
     return (int64_t)p.batch * p.heads * p.frames >= kFusedMinItems;
 }
 
+// The column-block step reads a frame's Q rows and writes its O rows through 32-bit buffer
+// offsets (rows up to S, the first past the frame, are addressed): S rows of either stride
+// must stay below 2 GiB. A single-token frame is addressed with a stride of one row.
+bool step_rows_fit(const gdn_problem& p) {
+    const int64_t S = p.tokens_per_frame, D = p.head_dim;
+    for (int64_t st : {p.qkv_stride_t, p.o_stride_t}) {
+        const int64_t s = S == 1 ? std::max<int64_t>(st, D) : st;
+        if (s < 0 || (S * s + D) * 2 >= ((int64_t)1 << 31)) return false;
+    }
+    return true;
+}
+
+bool choose_step_cols(const gdn_problem& p) {
+    return gdn::step_cols_supported(p.dtype == GDN_BF16, p.head_dim) && step_rows_fit(p);
+}
+
 constexpr int kTargetGroups = 2048;  // workgroups wanted per parallel launch (256 CUs x 8)
+constexpr int kStepPartials = 512;   // column-block step: partial workgroups (two per CU)
+constexpr int kStepOutputs = 256;    // column-block step: output workgroups
 
 // mode: 0 forward, 1 step, 2 backward
 Plan make_plan(const gdn_problem& p, int mode) {
     const int step_mode = mode == 1;
     Plan pl{};
     pl.mode = mode;
-    pl.fused = mode == 0 && choose_fused(p, 0);
+    pl.fused = mode == 0 ? choose_fused(p, 0) : mode == 1 && choose_step_cols(p);
     const int64_t D = p.head_dim, S = p.tokens_per_frame;
     const int64_t BH = (int64_t)p.batch * p.heads;
     const int64_t F = step_mode ? 1 : p.frames;
@@ -111,6 +130,24 @@ Plan make_plan(const gdn_problem& p, int mode) {
     // fp32 state buffers per (b, h)
     pl.ctl_bytes = (size_t)(2 + BH * gdn::kChainGroups) * 4;
     pl.chain_bytes = (size_t)(2 * BH * D * D * 4);
+    if (step_mode && pl.fused) {
+        // partials: 32 value columns x one token split (a multiple of 64 tokens); outputs: at
+        // most 256 tokens each; fp32 partials [BH][D/32][splits][D][32]; the new state
+        // transposed in bf16
+        const int64_t NJ = D / 32;
+        want = (kStepPartials + BH * NJ - 1) / (BH * NJ);
+        want = std::max<int64_t>(1, std::min<int64_t>(want, tiles64));
+        pl.split_tokens = (int)(((tiles64 + want - 1) / want) * 64);
+        pl.nsplit = (int)((S + pl.split_tokens - 1) / pl.split_tokens);
+        int64_t oc = (kStepOutputs + BH - 1) / BH;
+        oc = std::max<int64_t>((tiles16 + 15) / 16, std::min<int64_t>(oc, tiles16));
+        pl.chunk_tokens = (int)(((tiles16 + oc - 1) / oc) * 16);
+        pl.nchunk = (int)((S + pl.chunk_tokens - 1) / pl.chunk_tokens);
+        pl.part_bytes = (size_t)(BH * pl.nsplit * D * D * 4);
+        pl.mt_bytes = (size_t)(BH * D * D * 2);
+        pl.canon_bytes = 0;
+        pl.chain_bytes = 0;
+    }
     if (mode == 2) {
         // fp32 forward states and state gradients get F + 1 slots (slot 0: initial state / its
         // gradient); the C_f records hold one fp32 D x D matrix each
@@ -292,7 +329,15 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     L.ob = p->o_stride_b; L.oh = p->o_stride_h; L.ot = p->o_stride_t;
     L.xsb = L.sb; L.xsh = L.sh; L.xst = L.st;
     L.gamma = gamma; L.beta = beta; L.state_in = state_in; L.state_out = state_out;
-    if (pl.fused) {
+    if (step_mode && pl.fused) {
+        L.step_cols = 1;
+        L.part = (float*)ws;
+        L.mt = (char*)ws + align256(pl.part_bytes);
+        if (S == 1) {
+            L.st = std::max<int64_t>(L.st, D);
+            L.ot = std::max<int64_t>(L.ot, D);
+        }
+    } else if (pl.fused) {
         L.spin_limit = fused_spin_limit();
         L.ctl = (int*)ws;
         L.chain = (float*)((char*)ws + align256(pl.ctl_bytes));

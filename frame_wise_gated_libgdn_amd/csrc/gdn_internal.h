@@ -34,6 +34,7 @@ struct Launch {
                          //   [2 + bh * kChainGroups + g] last frame of (b, h) whose column
                          //   group g of the state is published
     float* chain;        // workspace (fused): published states, [2][B*H][D][D] fp32, [c][n] order
+    int step_cols;       // step: the column-block kernels of gdn_step.hip (bf16, D = 64 / 128)
     int nsplit;          // S splits of the gram products
     int split_tokens;    // tokens per split (multiple of 64)
     int nchunk;          // S chunks of the output products
@@ -61,7 +62,8 @@ enum Kernel {
     K_FUSED_RESET = 5, K_FUSED = 6, K_SCAN_BWD = 7, K_BWD = 8,
     K_SCAN_STATES = 9,   // the forward scan with fp32 per-frame states (backward's recompute)
     K_TCONV = 10,        // block-causal temporal convolution
-    K_ATTN = 11          // frame-causal softmax attention
+    K_ATTN = 11,         // frame-causal softmax attention
+    K_STEP_OUTPUT = 12   // step (column-block kernels): outputs of the frame
 };
 
 // Arguments of the frame-causal softmax attention (gdn_attn.hip). q: [B][H][Tq][D], k, v:
@@ -99,6 +101,10 @@ constexpr int kSpinLimitDefault = 1 << 20;  // polls of about a microsecond each
 
 // Whether the fused single-pass forward has a kernel for this type / head size.
 bool fused_supported(int bf16, int D);
+// Step mode's column-block kernels (gdn_step.hip): whether they cover this type / head size,
+// and the launch of K_STEP_PARTIAL, K_STEP_REDUCE or K_STEP_OUTPUT.
+bool step_cols_supported(int bf16, int D);
+hipError_t step_launch(Kernel k, const Launch& L, hipStream_t s);
 // Whether the backward has kernels for this type / head size.
 bool backward_supported(int bf16, int D);
 

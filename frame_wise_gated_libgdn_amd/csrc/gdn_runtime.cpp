@@ -4,7 +4,9 @@
 // Forward, staged:  products (gram items of every frame) -> [combine] -> scan -> products
 //                   (output items of every frame).
 // Forward, fused:   reset of the ticket counter and frame flags -> fused kernel.
-// Step:             step_partial -> step_reduce -> products (output items of the one frame).
+// Step:             bf16 with D = 64 or 128: the column-block kernels step_partial ->
+//                   step_reduce -> step_output; otherwise step_partial -> step_reduce ->
+//                   products (output items of the one frame).
 // Temporal conv:    one launch (the whole block or sequence).
 // Attention:        one launch.
 // Backward:         products + [combine] + scan (forward states), products + [combine] of
@@ -31,7 +33,7 @@ struct Launcher {
         const bool timed = armed && 2 * i + 1 < t_trace_events.size();
         hipError_t e = hipSuccess;
         if (timed && (e = hipEventRecord(t_trace_events[2 * i], s)) != hipSuccess) return e;
-        if ((e = launch_kernel(k, A, s)) != hipSuccess) return e;
+        if ((e = A.step_cols ? step_launch(k, A, s) : launch_kernel(k, A, s)) != hipSuccess) return e;
         if (timed && (e = hipEventRecord(t_trace_events[2 * i + 1], s)) != hipSuccess) return e;
         if (armed) t_trace_log.push_back({(int32_t)k, s == caller ? 0 : 1, units});
         return hipSuccess;
@@ -71,6 +73,11 @@ hipError_t run_step(const Launch& L0, hipStream_t s) {
     t_trace_log.clear();
     Launcher run{L0, s};
     const int64_t BH = (int64_t)L0.B * L0.H;
+    if (L0.step_cols) {
+        GDN_TRY(run.go(K_STEP_PARTIAL, L0, s, BH));
+        GDN_TRY(run.go(K_STEP_REDUCE, L0, s, BH));
+        return run.go(K_STEP_OUTPUT, L0, s, BH);
+    }
     GDN_TRY(run.go(K_STEP_PARTIAL, L0, s, BH));
     GDN_TRY(run.go(K_STEP_REDUCE, L0, s, BH));
     Launch A = L0;

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 5
+#define LIBGDN_ABI_VERSION 6
 
 typedef enum {
     GDN_OK = 0,
@@ -256,6 +256,11 @@ gdn_status gdn_forward_framewise_fp8(const gdn_problem* p, const void* q, const 
  *   state_out    NULL: the new state is not committed (a denoising pass that will be redone);
  *                otherwise it receives the new state and may equal state_in exactly
  *   workspace    at least gdn_workspace_size(p, 1) bytes, 256-byte aligned
+ * Three launches: partial products over token splits, the state update, the outputs. bf16
+ * data with D = 64 or 128 (and S rows of either token stride within 2 GiB) splits the partial
+ * products into blocks of 32 value columns (trace kinds STEP_PARTIAL, STEP_REDUCE,
+ * STEP_OUTPUT); other types and head sizes use whole-state partials and the forward's output
+ * kernel (STEP_PARTIAL, STEP_REDUCE, PRODUCTS). Results are bitwise reproducible.
  */
 gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, const void* v,
                           const float* gamma, const float* beta, const float* state_in,
@@ -316,7 +321,8 @@ typedef enum {
     GDN_KERNEL_BWD = 8,           /* backward: per-frame gradients of Q, K, V, gamma, beta */
     GDN_KERNEL_SCAN_STATES = 9,   /* backward: forward scan keeping every state in fp32 */
     GDN_KERNEL_TCONV = 10,        /* block-causal temporal convolution */
-    GDN_KERNEL_ATTN = 11          /* frame-causal softmax attention */
+    GDN_KERNEL_ATTN = 11,         /* frame-causal softmax attention */
+    GDN_KERNEL_STEP_OUTPUT = 12   /* step, bf16 with D = 64 or 128: outputs of the frame */
 } gdn_kernel_kind;
 
 typedef struct {

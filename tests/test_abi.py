@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 5
+    assert gdn.abi_version() == 6
     lib = gdn.load()
     for code in range(9):
         assert lib.gdn_status_string(code)
@@ -81,6 +81,16 @@ def test_step_workspace_independent_of_frames():
     # constant memory in video length (the fixed D x D state of the pages)
     sizes = {gdn.workspace_size(prob(F=f), True) for f in (1, 10, 961, 100000)}
     assert len(sizes) == 1
+
+
+def test_column_block_step_workspace():
+    # the streaming shape (B 1, H 16, D 128, S 3520, bf16): fp32 partials of 8 token splits of
+    # 448 tokens (512 partial workgroups of 32 value columns), the new state transposed in bf16
+    p = gdn.Problem(1, 16, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 0, 0, 128, 0, 0, 128)
+    assert gdn.workspace_size(p, True) == 16 * 8 * 128 * 128 * 4 + 16 * 128 * 128 * 2
+    # rows beyond 2 GiB: the whole-state step kernels
+    big = gdn.Problem(1, 16, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 0, 0, 1 << 20, 0, 0, 128)
+    assert gdn.workspace_size(big, True) != gdn.workspace_size(p, True)
 
 
 def test_forward_workspace_grows_with_frames():

@@ -312,6 +312,64 @@ def test_step_sweep(case):
     assert np.array_equal(to_np(ds), s0), "state_in must not change"
 
 
+# column-block step (bf16, D = 64 / 128): single token, many heads (one split per block), ragged
+# splits and chunks, no delta term, the streaming shape
+STEP_COLS = [
+    (1, 3, 128, 700, True),
+    (2, 2, 64, 257, True),
+    (1, 2, 128, 1, True),
+    (2, 40, 64, 100, True),
+    (1, 2, 128, 333, False),
+    (1, 16, 128, 3520, True),
+]
+
+
+@pytest.mark.parametrize("case", STEP_COLS, ids=["-".join(map(str, c)) for c in STEP_COLS])
+def test_step_column_blocks(case):
+    """The column-block step kernels against the oracle; a second call is bitwise identical."""
+    say("step, column blocks", case)
+    B, H, D, S, delta = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    q, k, v = random_qkv(rng, (B, H, S, D), "bf16")
+    g = rng.uniform(0.85, 1.0, (B, H)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H)).astype(np.float32)
+    s0 = (0.3 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    dev = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(x).to(DEV) for x in (g, b, s0)]
+    o1, s1 = gdn.step_frame(*dev, use_delta=delta)
+    o2, s2 = gdn.step_frame(*dev, use_delta=delta)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    ro, rs = oracle.step(q, k, v, g, b, s0, use_delta=delta)
+    e1, e2 = rel_err(to_np(o1), ro), rel_err(to_np(s1), rs)
+    say("  O err %.3e state err %.3e" % (e1, e2))
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+def test_step_launch_trace():
+    """bf16 with D = 128 runs the column-block step kernels; fp32 the whole-state ones and the
+    forward's output kernel."""
+    ev = HipEvents()
+    handles = [ev.new() for _ in range(2 * 4)]
+    try:
+        kinds = {}
+        for dt in ("bf16", "f32"):
+            rng = np.random.default_rng(3)
+            q, k, v = random_qkv(rng, (1, 2, 100, 128), dt)
+            args = [to_dev(x, dt, DEV) for x in (q, k, v)] + [
+                torch.full((1, 2), 0.9, device=DEV), torch.full((1, 2), 0.5, device=DEV),
+                torch.zeros((1, 2, 128, 128), device=DEV)]
+            gdn.set_trace(handles)
+            gdn.step_frame(*args)
+            kinds[dt] = [k_ for k_, _, _ in gdn.read_trace()]
+            gdn.set_trace(None)
+        torch.cuda.synchronize()
+        assert kinds["bf16"] == ["step_partial", "step_reduce", "step_output"]
+        assert kinds["f32"] == ["step_partial", "step_reduce", "products"]
+    finally:
+        gdn.set_trace(None)
+        ev.close()
+
+
 def test_step_in_place_commit():
     rng = np.random.default_rng(5)
     B, H, D, S = 1, 2, 64, 96
