@@ -313,14 +313,17 @@ def test_step_sweep(case):
 
 
 # column-block step (bf16, D = 64 / 128): single token, many heads (one split per block), ragged
-# splits and chunks, no delta term, the streaming shape
+# splits and chunks, no delta term, token-major storage ([B, T, H, D] viewed as [B, H, T, D]),
+# the streaming shape
 STEP_COLS = [
-    (1, 3, 128, 700, True),
-    (2, 2, 64, 257, True),
-    (1, 2, 128, 1, True),
-    (2, 40, 64, 100, True),
-    (1, 2, 128, 333, False),
-    (1, 16, 128, 3520, True),
+    (1, 3, 128, 700, True, "head"),
+    (2, 2, 64, 257, True, "head"),
+    (1, 2, 128, 1, True, "head"),
+    (2, 40, 64, 100, True, "head"),
+    (1, 2, 128, 333, False, "head"),
+    (2, 3, 128, 500, True, "token"),
+    (1, 4, 64, 130, False, "token"),
+    (1, 16, 128, 3520, True, "head"),
 ]
 
 
@@ -328,13 +331,13 @@ STEP_COLS = [
 def test_step_column_blocks(case):
     """The column-block step kernels against the oracle; a second call is bitwise identical."""
     say("step, column blocks", case)
-    B, H, D, S, delta = case
+    B, H, D, S, delta, layout = case
     rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
     q, k, v = random_qkv(rng, (B, H, S, D), "bf16")
     g = rng.uniform(0.85, 1.0, (B, H)).astype(np.float32)
     b = rng.uniform(0.1, 0.9, (B, H)).astype(np.float32)
     s0 = (0.3 * rng.standard_normal((B, H, D, D))).astype(np.float32)
-    dev = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(x).to(DEV) for x in (g, b, s0)]
+    dev = [to_dev(x, "bf16", DEV, layout) for x in (q, k, v)] + [torch.from_numpy(x).to(DEV) for x in (g, b, s0)]
     o1, s1 = gdn.step_frame(*dev, use_delta=delta)
     o2, s2 = gdn.step_frame(*dev, use_delta=delta)
     torch.cuda.synchronize()
