@@ -276,8 +276,44 @@ def backward_mode(w, dev, steps, ev, stream):
     t_roof = max(bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
     bwd_ms = kms.get("bwd", 0.0)
     bwd_bytes = 6 * w.B * w.H * w.F * w.S * w.D * esz   # per-frame gradient kernel: K, V, dO, dQ, dK, dV
-    del q, k, v, d_o, dq, dk, dv, ws
+    del ws
+
+    # training with saved states: the fused forward that keeps the states and Ghat records,
+    # then the backward from them (no forward recompute)
+    o = torch.empty_like(q)
+    pf = gdn.Problem(w.B, w.H, w.D, w.S, w.F, gdn.GDN_BF16, int(w.use_delta), 0.0, *q.stride()[:3],
+                     *o.stride()[:3], gdn.SCHEDULES["fused"])
+    saved = torch.empty(gdn.saved_size(pf), dtype=torch.uint8, device=dev)
+    wsf = torch.empty(gdn.workspace_size(pf, 0), dtype=torch.uint8, device=dev)
+    ws3 = torch.empty(gdn.workspace_size(p, 3), dtype=torch.uint8, device=dev)
+
+    def fwd_save():
+        gdn.forward_framewise_save(q, k, v, g, b, use_delta=w.use_delta, out=o, return_state=False,
+                                   saved=saved, workspace=wsf, stream=stream)
+
+    def bwd_saved():
+        gdn.backward_framewise(q, k, v, g, b, d_o, use_delta=w.use_delta, dq=dq, dk=dk, dv=dv,
+                               saved=saved, workspace=ws3, stream=stream)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        a, z = ev.new(), ev.new()
+        ev.record(a, sh)
+        for _ in range(steps):
+            f()
+        ev.record(z, sh)
+        torch.cuda.synchronize()
+        return ev.ms(a, z) / steps
+
+    fs_ms = timed(fwd_save)
+    bs_ms = timed(bwd_saved)
+    saved_gb = saved.numel() / 1e9
+    del q, k, v, d_o, dq, dk, dv, o, saved, wsf, ws3
     return {"workload": w.name, "ms_per_call": round(ms, 4),
+            "from_saved_states": {"forward_save_ms": round(fs_ms, 4), "saved_gb": round(saved_gb, 3),
+                                  "backward_ms": round(bs_ms, 4),
+                                  "backward_frac_of_roofline": round(t_roof / bs_ms, 4)},
             "tokens_per_s": round(w.B * w.F * w.S / (ms * 1e-3), 1),
             "launches": [k_ for k_, _, _ in plan],
             "kernel_ms_per_call": {k_: round(x, 4) for k_, x in kms.items()},
@@ -664,7 +700,9 @@ def main():
         result["backward"] = backward_mode(w, dev, args.backward_steps, ev3, torch.cuda.current_stream())
         ev3.close()
         torch.cuda.empty_cache()
-        log("backward done: %.3f ms/call" % result["backward"]["ms_per_call"])
+        log("backward done: %.3f ms/call; from saved states %.3f ms/call (saving forward %.3f ms)" % (
+            result["backward"]["ms_per_call"], result["backward"]["from_saved_states"]["backward_ms"],
+            result["backward"]["from_saved_states"]["forward_save_ms"]))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

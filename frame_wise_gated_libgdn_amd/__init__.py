@@ -16,7 +16,7 @@ import os
 import threading
 
 __all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "forward_framewise",
-           "step_frame", "backward_framewise", "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES",
+           "forward_framewise_save", "saved_size", "step_frame", "backward_framewise", "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES",
            "GDN_F32", "GDN_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -117,6 +117,14 @@ def load():
             lib.gdn_forward_framewise_fp8.restype = ctypes.c_int
             lib.gdn_backward_framewise.argtypes = [P] + [_vp] * 14 + [_vp, ctypes.c_size_t, _vp]
             lib.gdn_backward_framewise.restype = ctypes.c_int
+            lib.gdn_saved_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+            lib.gdn_saved_size.restype = ctypes.c_int
+            lib.gdn_forward_framewise_save.argtypes = ([P] + [_vp] * 8 + [_vp, ctypes.c_size_t]
+                                                       + [_vp, ctypes.c_size_t, _vp])
+            lib.gdn_forward_framewise_save.restype = ctypes.c_int
+            lib.gdn_backward_framewise_saved.argtypes = ([P] + [_vp] * 5 + [_vp, ctypes.c_size_t]
+                                                         + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp])
+            lib.gdn_backward_framewise_saved.restype = ctypes.c_int
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_last_error_message.restype = ctypes.c_char_p
@@ -166,7 +174,7 @@ def _check(code):
 
 
 def workspace_size(p: Problem, mode) -> int:
-    """mode: 0 / False forward, 1 / True step, 2 backward."""
+    """mode: 0 / False forward, 1 / True step, 2 backward, 3 backward from saved states."""
     n = ctypes.c_size_t(0)
     _check(load().gdn_workspace_size(ctypes.byref(p), int(mode), ctypes.byref(n)))
     return int(n.value)
@@ -262,6 +270,45 @@ def forward_framewise(q, k, v, gamma, beta, state=None, *, use_delta=True, key_s
                                         _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),
                                         _ptr(ws), nbytes, _stream(stream)))
     return out, state_out
+
+
+def saved_size(p) -> int:
+    """Bytes of the buffer forward_framewise_save keeps for backward_framewise (saved=...)."""
+    n = ctypes.c_size_t(0)
+    _check(load().gdn_saved_size(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def forward_framewise_save(q, k, v, gamma, beta, state=None, *, use_delta=True, key_scale=None,
+                           out=None, state_out=None, return_state=True, saved=None,
+                           workspace=None, stream=None):
+    """forward_framewise on the fused schedule (bf16, D = 64 or 128) that also keeps what the
+    backward needs (the frames' key-key products and every state), so that
+    backward_framewise(..., saved=saved) skips recomputing the forward.
+    Returns (o, state_out, saved); saved is a uint8 device tensor of saved_size bytes."""
+    import torch
+    B, H, T, D = q.shape
+    F = gamma.shape[2]
+    if k.stride() != q.stride() or v.stride() != q.stride() or k.shape != q.shape \
+            or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise GdnError(4, "q, k and v must share shape, dtype and strides")
+    if out is None:
+        out = torch.empty((B, H, T, D), dtype=q.dtype, device=q.device)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    _check_f32("gamma", gamma, (B, H, F))
+    _check_f32("beta", beta, (B, H, F))
+    _check_f32("state", state, (B, H, D, D))
+    _check_f32("state_out", state_out, (B, H, D, D))
+    p = _problem(q, out, F, use_delta, key_scale, "fused")
+    if saved is None:
+        saved = torch.empty(saved_size(p), dtype=torch.uint8, device=q.device)
+    ws, nbytes = _workspace(p, False, workspace, q.device)
+    _check(load().gdn_forward_framewise_save(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(state),
+        _ptr(out), _ptr(state_out), _ptr(saved), saved.numel() * saved.element_size(), _ptr(ws),
+        nbytes, _stream(stream)))
+    return out, state_out, saved
 
 
 def forward_framewise_fp8(q, k, v, q_scale, k_scale, v_scale, gamma, beta, state=None, *,
@@ -382,10 +429,12 @@ def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_
 
 def backward_framewise(q, k, v, gamma, beta, d_o, state=None, d_state_out=None, *,
                        use_delta=True, key_scale=None, dq=None, dk=None, dv=None,
-                       return_state_grad=True, workspace=None, stream=None):
+                       return_state_grad=True, saved=None, workspace=None, stream=None):
     """Gradients of forward_framewise. q, k, v [B, H, F*S, D] (bf16, D = 64 or 128, same
     strides); d_o: dL/dO with o's shape (any strides with D contiguous); gamma, beta fp32
-    [B, H, F]; state, d_state_out fp32 [B, H, D, D] or None.
+    [B, H, F]; state, d_state_out fp32 [B, H, D, D] or None. With saved (from
+    forward_framewise_save on the same inputs) the forward states are not recomputed and state
+    is not read.
     Returns (dq, dk, dv, dgamma, dbeta, d_state_in); d_state_in is None when
     return_state_grad is False."""
     import torch
@@ -414,6 +463,13 @@ def backward_framewise(q, k, v, gamma, beta, d_o, state=None, d_state_out=None, 
     _check_f32("state", state, (B, H, D, D))
     _check_f32("d_state_out", d_state_out, (B, H, D, D))
     p = _problem(q, d_o, F, use_delta, key_scale)
+    if saved is not None:
+        ws, nbytes = _workspace(p, 3, workspace, q.device)
+        _check(load().gdn_backward_framewise_saved(
+            ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(saved),
+            saved.numel() * saved.element_size(), _ptr(d_o), _ptr(d_state_out), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(dg), _ptr(db), _ptr(dsi), _ptr(ws), nbytes, _stream(stream)))
+        return dq, dk, dv, dg, db, dsi
     ws, nbytes = _workspace(p, 2, workspace, q.device)
     _check(load().gdn_backward_framewise(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(state),

@@ -29,7 +29,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Schedule and splits chosen from the problem only, so that the workspace size is a pure
 // function of it.
 struct Plan {
-    int mode;                   // 0 forward, 1 step, 2 backward
+    int mode;                   // 0 forward, 1 step, 2 backward, 3 backward from saved states
     bool fused;                 // forward: fused single pass (else staged); step: column blocks
     int nsplit, split_tokens;   // partial-product kernel
     int nchunk, chunk_tokens;   // output kernel
@@ -37,7 +37,7 @@ struct Plan {
     size_t ctl_bytes, chain_bytes;              // fused forward
     size_t crec_bytes, gt_bytes;                // backward
     size_t total() const {
-        if (mode == 2)
+        if (mode >= 2)
             return align256(canon_bytes) + align256(part_bytes) + align256(mt_bytes) +
                    align256(crec_bytes) + gt_bytes;
         if (mode == 1 && fused) return align256(part_bytes) + mt_bytes;
@@ -86,7 +86,7 @@ constexpr int kTargetGroups = 2048;  // workgroups wanted per parallel launch (2
 constexpr int kStepPartials = 512;   // column-block step: partial workgroups (two per CU)
 constexpr int kStepOutputs = 256;    // column-block step: output workgroups
 
-// mode: 0 forward, 1 step, 2 backward
+// mode: 0 forward, 1 step, 2 backward, 3 backward from saved states (no forward recompute)
 Plan make_plan(const gdn_problem& p, int mode) {
     const int step_mode = mode == 1;
     Plan pl{};
@@ -155,7 +155,29 @@ Plan make_plan(const gdn_problem& p, int mode) {
         pl.crec_bytes = (size_t)(BH * F * D * D * 4);
         pl.gt_bytes = pl.mt_bytes;
     }
+    if (mode == 3) {
+        pl.gt_bytes = (size_t)(BH * (F + 1) * D * D * 4);
+        pl.crec_bytes = (size_t)(BH * F * D * D * 4);
+        pl.canon_bytes = 0;   // the forward's records and states come from the saved buffer
+        pl.mt_bytes = 0;
+    }
     return pl;
+}
+
+// Buffer kept by gdn_forward_framewise_save for gdn_backward_framewise_saved: the frames' Ghat
+// planes (delta rule only), then the initial state and every M_f in fp32, transposed.
+struct SavedPlan {
+    size_t rec_bytes;     // per frame record
+    size_t recs, states;
+    size_t total() const { return align256(recs) + states; }
+};
+SavedPlan saved_plan(const gdn_problem& p) {
+    const int64_t D = p.head_dim, BH = (int64_t)p.batch * p.heads, F = p.frames;
+    SavedPlan sp{};
+    sp.rec_bytes = p.use_delta ? (size_t)((D / 16) * 2 * ((D + 31) / 32) * 1024) : 0;
+    sp.recs = (size_t)(BH * F) * sp.rec_bytes;
+    sp.states = (size_t)(BH * (F + 1) * D * D * 4);
+    return sp;
 }
 
 gdn_status check_sizes(const gdn_problem* p, int mode) {
@@ -243,7 +265,7 @@ int fused_spin_limit() {
 gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k, const void* v,
                const float* const* scales, const float* gamma, const float* beta,
                const float* state_in, void* o, float* state_out, void* ws, size_t ws_bytes,
-               void* stream) {
+               void* stream, void* saved = nullptr, size_t saved_bytes = 0) {
     g_msg[0] = '\0';
     gdn_status s = check_sizes(p, step_mode);
     if (s != GDN_OK) return s;
@@ -283,6 +305,8 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
 
     const Plan pl = make_plan(*p, step_mode);
     const size_t need = pl.total();
+    const SavedPlan sp = saved_plan(*p);
+    if (saved && !pl.fused) return fail(GDN_ERR_UNSUPPORTED, "saving for the backward needs the fused schedule");
 
     const Span sq = span_of(q, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
     const Span sk = span_of(k, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
@@ -304,6 +328,14 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
         }
     for (Span in : {sq, sk, sv, sg, sbt, so, si})
         if (overlap(sw, in)) return fail(GDN_ERR_ALIAS, "workspace overlaps an input or output");
+    if (saved) {
+        const Span ssv = {(const char*)saved, (const char*)saved + sp.total()};
+        for (Span in : {sq, sk, sv, sg, sbt, so, si, sw, sso})
+            if (overlap(ssv, in)) return fail(GDN_ERR_ALIAS, "the saved buffer overlaps another buffer");
+        if (saved_bytes < sp.total())
+            return fail(GDN_ERR_WORKSPACE, "saved buffer of %zu bytes needed, %zu given", sp.total(), saved_bytes);
+        if (!aligned(saved, 256)) return fail(GDN_ERR_ALIGN, "the saved buffer must be 256-byte aligned");
+    }
     if (state_out) {
         for (Span in : {sq, sk, sv, sg, sbt, so, sw})
             if (overlap(sso, in)) return fail(GDN_ERR_ALIAS, "state_out overlaps another buffer");
@@ -338,6 +370,10 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
             L.ot = std::max<int64_t>(L.ot, D);
         }
     } else if (pl.fused) {
+        if (saved) {
+            L.save_recs = saved;
+            L.save_states = (float*)((char*)saved + align256(sp.recs));
+        }
         L.spin_limit = fused_spin_limit();
         L.ctl = (int*)ws;
         L.chain = (float*)((char*)ws + align256(pl.ctl_bytes));
@@ -369,7 +405,8 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
 gdn_status run_bwd(const gdn_problem* p, const void* q, const void* k, const void* v,
                    const float* gamma, const float* beta, const float* state_in, const void* d_o,
                    const float* d_state_out, void* dq, void* dk, void* dv, float* dgamma,
-                   float* dbeta, float* d_state_in, void* ws, size_t ws_bytes, void* stream) {
+                   float* dbeta, float* d_state_in, void* ws, size_t ws_bytes, void* stream,
+                   const void* saved = nullptr, size_t saved_bytes = 0) {
     g_msg[0] = '\0';
     gdn_status s = check_sizes(p, 2);
     if (s != GDN_OK) return s;
@@ -395,8 +432,14 @@ gdn_status run_bwd(const gdn_problem* p, const void* q, const void* k, const voi
                             (const void*)d_state_in})
         if (ptr && !aligned(ptr, 4)) return fail(GDN_ERR_ALIGN, "gates, states and their gradients must be 4-byte aligned");
 
-    const Plan pl = make_plan(*p, 2);
+    const Plan pl = make_plan(*p, saved ? 3 : 2);
     const size_t need = pl.total();
+    const SavedPlan sp = saved_plan(*p);
+    if (saved) {
+        if (saved_bytes < sp.total())
+            return fail(GDN_ERR_WORKSPACE, "saved buffer of %zu bytes needed, %zu given", sp.total(), saved_bytes);
+        if (!aligned(saved, 256)) return fail(GDN_ERR_ALIGN, "the saved buffer must be 256-byte aligned");
+    }
     auto qkv_span = [&](const void* x) {
         return span_of(x, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
     };
@@ -407,7 +450,8 @@ gdn_status run_bwd(const gdn_problem* p, const void* q, const void* k, const voi
                        state_in ? Span{(const char*)state_in, (const char*)(state_in + B * H * D * D)} : none,
                        span_of(d_o, B, H, T, D, p->o_stride_b, p->o_stride_h, p->o_stride_t, esz),
                        d_state_out ? Span{(const char*)d_state_out, (const char*)(d_state_out + B * H * D * D)} : none,
-                       ws ? Span{(const char*)ws, (const char*)ws + need} : none};
+                       ws ? Span{(const char*)ws, (const char*)ws + need} : none,
+                       saved ? Span{(const char*)saved, (const char*)saved + sp.total()} : none};
     const Span dsi = d_state_in ? Span{(const char*)d_state_in, (const char*)(d_state_in + B * H * D * D)} : none;
     const Span out[] = {qkv_span(dq), qkv_span(dk), qkv_span(dv),
                         {(const char*)dgamma, (const char*)(dgamma + B * H * F)},
@@ -418,11 +462,15 @@ gdn_status run_bwd(const gdn_problem* p, const void* q, const void* k, const voi
             // the state gradient may be computed in place (d_state_in == d_state_out)
             if (i == nout - 1 && j == 7 && d_state_in && (const void*)d_state_in == (const void*)d_state_out)
                 continue;
-            if (overlap(out[i], in[j])) return fail(GDN_ERR_ALIAS, "a gradient output overlaps an input or the workspace");
+            if (overlap(out[i], in[j]))
+                return fail(GDN_ERR_ALIAS, "a gradient output overlaps an input, the saved buffer or the workspace");
         }
         for (int j = 0; j < i; ++j)
             if (overlap(out[i], out[j])) return fail(GDN_ERR_ALIAS, "two gradient outputs overlap");
     }
+    if (saved && overlap(Span{(const char*)saved, (const char*)saved + sp.total()},
+                         ws ? Span{(const char*)ws, (const char*)ws + need} : none))
+        return fail(GDN_ERR_ALIAS, "the saved buffer overlaps the workspace");
     if (!ws || ws_bytes < need)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     ws ? ws_bytes : (size_t)0);
@@ -446,6 +494,12 @@ gdn_status run_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     L.mt = w;                          w += align256(pl.mt_bytes);
     L.crec = w;                        w += align256(pl.crec_bytes);
     L.gt = w;
+    if (saved) {
+        L.saved = 1;
+        L.canon = const_cast<void*>(saved);
+        L.rec_stride = (int64_t)sp.rec_bytes;
+        L.mt = (char*)const_cast<void*>(saved) + align256(sp.recs);
+    }
     L.nsplit = pl.nsplit; L.split_tokens = pl.split_tokens;
     L.nchunk = pl.nchunk; L.chunk_tokens = pl.chunk_tokens;
     const hipError_t e = gdn::run_backward(L, (hipStream_t)stream);
@@ -562,8 +616,8 @@ extern "C" {
 gdn_status gdn_workspace_size(const gdn_problem* p, int mode, size_t* bytes_out) {
     g_msg[0] = '\0';
     if (!bytes_out) return fail(GDN_ERR_NULL, "bytes_out is NULL");
-    if (mode < 0 || mode > 2) return fail(GDN_ERR_SHAPE, "mode must be 0, 1 or 2, got %d", mode);
-    gdn_status s = check_sizes(p, mode);
+    if (mode < 0 || mode > 3) return fail(GDN_ERR_SHAPE, "mode must be 0, 1, 2 or 3, got %d", mode);
+    gdn_status s = check_sizes(p, mode == 3 ? 2 : mode);
     if (s != GDN_OK) return s;
     const Plan pl = make_plan(*p, mode);
     *bytes_out = pl.total();
@@ -596,6 +650,45 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                workspace_bytes, hip_stream);
 }
 
+gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes_out) {
+    g_msg[0] = '\0';
+    if (!bytes_out) return fail(GDN_ERR_NULL, "bytes_out is NULL");
+    gdn_status s = check_sizes(p, 2);
+    if (s != GDN_OK) return s;
+    if (!fused_rows_fit(*p)) return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs a frame's q/k/v rows within 2 GiB");
+    *bytes_out = saved_plan(*p).total();
+    return GDN_OK;
+}
+gdn_status gdn_forward_framewise_save(const gdn_problem* p, const void* q, const void* k,
+                                      const void* v, const float* gamma, const float* beta,
+                                      const float* state_in, void* o, float* state_out,
+                                      void* saved, size_t saved_bytes, void* workspace,
+                                      size_t workspace_bytes, void* hip_stream) {
+    g_msg[0] = '\0';
+    if (!p) return fail(GDN_ERR_NULL, "problem descriptor is NULL");
+    if (!saved) return fail(GDN_ERR_NULL, "saved is required");
+    gdn_status s = check_sizes(p, 2);   // what the backward supports
+    if (s != GDN_OK) return s;
+    if (p->schedule == GDN_SCHEDULE_STAGED)
+        return fail(GDN_ERR_UNSUPPORTED, "saving for the backward runs on the fused schedule");
+    gdn_problem pf = *p;
+    pf.schedule = GDN_SCHEDULE_FUSED;
+    return run(0, &pf, q, k, v, nullptr, gamma, beta, state_in, o, state_out, workspace,
+               workspace_bytes, hip_stream, saved, saved_bytes);
+}
+gdn_status gdn_backward_framewise_saved(const gdn_problem* p, const void* q, const void* k,
+                                        const void* v, const float* gamma, const float* beta,
+                                        const void* saved, size_t saved_bytes, const void* d_o,
+                                        const float* d_state_out, void* dq, void* dk, void* dv,
+                                        float* dgamma, float* dbeta, float* d_state_in,
+                                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!saved) {
+        g_msg[0] = '\0';
+        return fail(GDN_ERR_NULL, "saved is required");
+    }
+    return run_bwd(p, q, k, v, gamma, beta, nullptr, d_o, d_state_out, dq, dk, dv, dgamma, dbeta,
+                   d_state_in, workspace, workspace_bytes, hip_stream, saved, saved_bytes);
+}
 gdn_status gdn_backward_framewise(const gdn_problem* p, const void* q, const void* k,
                                   const void* v, const float* gamma, const float* beta,
                                   const float* state_in, const void* d_o,

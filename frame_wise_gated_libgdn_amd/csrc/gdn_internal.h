@@ -35,6 +35,11 @@ struct Launch {
                          //   group g of the state is published
     float* chain;        // workspace (fused): published states, [2][B*H][D][D] fp32, [c][n] order
     int step_cols;       // step: the column-block kernels of gdn_step.hip (bf16, D = 64 / 128)
+    float* save_states;  // fused forward, training: fp32 states, [B*H][F + 1][D][D] transposed
+                         //   (slot 0 the initial state, slot f + 1 = M_f), or NULL
+    void* save_recs;     // ... and the frames' Ghat planes ([B*H][F] records of rec_stride bytes)
+    int64_t rec_stride;  // bytes per frame record read by the scan (0: the full record)
+    int saved;           // backward: states and Ghat records come from a forward's saved buffer
     int nsplit;          // S splits of the gram products
     int split_tokens;    // tokens per split (multiple of 64)
     int nchunk;          // S chunks of the output products

@@ -532,7 +532,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
     const int row0 = wave * 16 + 4 * g;  // this lane's 4 state rows
     const int F = L.F, s0 = L.s0, s1 = L.s1;
     const int lead = L.mt_lead;         // per-step outputs have F + lead slots per (b, h)
-    const char* rec_bh = (const char*)L.canon + (int64_t)bh * F * REC;
+    const int64_t rstride = L.rec_stride ? L.rec_stride : REC;   // bytes per frame record
+    const char* rec_bh = (const char*)L.canon + (int64_t)bh * F * rstride;
     const char* crec_bh = (const char*)L.crec + (int64_t)bh * F * CREC;
     OT* mt_bh = (OT*)L.mt + (int64_t)bh * (F + lead) * D * D;
 
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void scan_kernel(Launch L) {
         f = min(f, s1 - 1);
         const int gf = BWD ? F - f : f;                  // frame of Ghat
         const bool gzero = BWD && gf >= F;               // uniform
-        const char* rec = rec_bh + (int64_t)min(gf, F - 1) * REC;
+        const char* rec = rec_bh + (int64_t)min(gf, F - 1) * rstride;
         if constexpr (DELTA) {
 #pragma unroll
             for (int ks = 0; ks < KSN; ++ks) {
@@ -810,7 +811,12 @@ __global__ void fused_reset_kernel(int* ctl, int n) {
     if (i < n) ctl[i] = i < 2 ? 0 : -1;
 }
 
-template <int D, bool DELTA, bool FP8>
+// SAVE (training): also keep what the backward needs, so that it need not recompute the forward
+// states: each frame's -Ghat planes (as +Ghat, the sign flipped exactly) in the scan record
+// layout at save_recs, and the initial state and every M_f in fp32, transposed, at save_states
+// (slot f + 1 per frame, slot 0 the initial state). These stores come after the frame's flag,
+// so they do not lengthen the frame-to-frame chain.
+template <int D, bool DELTA, bool FP8, bool SAVE = false>
 __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
     using MM = Mma<bf16>;
     constexpr int SC = 64;          // tokens per staged chunk (128 measured slower for E4M3)
@@ -909,6 +915,21 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
                                                  y - __builtin_bit_cast(float, hh & 0xFFFF0000u));
                 }
     }
+    if constexpr (SAVE && DELTA) {
+        // Ghat[m][k] with m = nw + 16 nb + r (symmetry) and k = 16 kb + 4 g .. + 3: 8 bytes of
+        // 4 consecutive k in each plane of the record
+        bf16* grec = (bf16*)L.save_recs + (int64_t)(bh * F + f) * (rec_g_bytes<D, DELTA>() / 2);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int m = nw + 16 * nb + r16, k0 = 16 * kb + 4 * g;
+                const uint32_t sign = 0x80008000u;
+                *(u32x2*)(grec + rec_g_off<D>(0, m, k0)) = u32x2{gh[kb][nb][0] ^ sign, gh[kb][nb][1] ^ sign};
+                *(u32x2*)(grec + rec_g_off<D>(1, m, k0)) = u32x2{gl[kb][nb][0] ^ sign, gl[kb][nb][1] ^ sign};
+            }
+    }
+    float* save_bh = SAVE ? L.save_states + (int64_t)bh * (F + 1) * D * D : nullptr;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -970,6 +991,13 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
                         mp[nb][j][q] = L.state_in ? L.state_in[((int64_t)bh * D + nw + 16 * nb + 4 * g + q) * D +
                                                                16 * (grp * CPG + j) + r16]
                                                   : 0.f;
+            if constexpr (SAVE) {   // slot 0: the initial state, transposed
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int j = 0; j < CPG; ++j)
+                        *(f32x4*)(save_bh + (16 * (grp * CPG + j) + r16) * D + nw + 16 * nb + 4 * g) = mp[nb][j];
+            }
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -1026,6 +1054,15 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
         __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's state stores are done
         __syncthreads();  // ... and every wave's; also: the group's planes are no longer read
         if (tid == 0) __hip_atomic_store(flags + grp, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (SAVE) {   // slot f + 1: M_f, transposed
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int j = 0; j < CPG; ++j) {
+                    const int cb = grp * CPG + j;
+                    *(f32x4*)(save_bh + ((int64_t)(f + 1) * D + 16 * cb + r16) * D + nw + 16 * nb + 4 * g) = bacc[nb][cb];
+                }
+        }
     }
     if (f == F - 1 && L.state_out) {
         float* so = L.state_out + (int64_t)bh * D * D;
@@ -1622,6 +1659,8 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
         if constexpr (std::is_same<T, bf16>::value && (D == 64 || D == 128)) {
             if (L.fp8)
                 hipLaunchKernelGGL((fused_kernel<D, DELTA, true>), dim3(BH * L.F), dim3(NT), 0, s, L);
+            else if (L.save_states)
+                hipLaunchKernelGGL((fused_kernel<D, DELTA, false, true>), dim3(BH * L.F), dim3(NT), 0, s, L);
             else
                 hipLaunchKernelGGL((fused_kernel<D, DELTA, false>), dim3(BH * L.F), dim3(NT), 0, s, L);
         } else {

@@ -94,16 +94,18 @@ hipError_t run_backward(const Launch& L0, hipStream_t s) {
     const int64_t BH = (int64_t)L0.B * L0.H;
     const int F = L0.F;
     // 1. forward states: products of every frame, then the scan, M_f to slot f + 1 (slot 0:
-    //    the initial state)
-    Launch A = L0;
-    A.g0 = 0; A.gn = F; A.o0 = 0; A.on = 0;
-    GDN_TRY(run.go(K_PRODUCTS, A, s, BH * F));
-    if (L0.nsplit > 1) GDN_TRY(run.go(K_COMBINE, A, s, BH * F));
-    A.s0 = 0; A.s1 = F;
-    A.scan_in = L0.state_in;
-    A.scan_out = nullptr;
-    A.mt_lead = 1;
-    GDN_TRY(run.go(K_SCAN_STATES, A, s, BH * F));
+    //    the initial state); taken from a forward's saved buffer instead when given
+    if (!L0.saved) {
+        Launch A = L0;
+        A.g0 = 0; A.gn = F; A.o0 = 0; A.on = 0;
+        GDN_TRY(run.go(K_PRODUCTS, A, s, BH * F));
+        if (L0.nsplit > 1) GDN_TRY(run.go(K_COMBINE, A, s, BH * F));
+        A.s0 = 0; A.s1 = F;
+        A.scan_in = L0.state_in;
+        A.scan_out = nullptr;
+        A.mt_lead = 1;
+        GDN_TRY(run.go(K_SCAN_STATES, A, s, BH * F));
+    }
     // 2. C_f = Q_f^T dO_f of every frame: the gram products without the delta term and the
     //    gates, first operand Q (Q/K/V strides), second dO (O strides)
     Launch C = L0;

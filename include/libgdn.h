@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 6
+#define LIBGDN_ABI_VERSION 7
 
 typedef enum {
     GDN_OK = 0,
@@ -201,10 +201,10 @@ gdn_status gdn_attention_framecausal(const gdn_attn_problem* p, const void* q, c
                                      const void* v, void* o, void* hip_stream);
 
 /*
- * Workspace bytes needed by gdn_forward_framewise (mode = 0), gdn_step_frame (mode = 1) or
- * gdn_backward_framewise (mode = 2) for this problem. The step-mode size does not depend on
- * `frames`. Validates the sizes in `p` (not the pointers or strides); other modes are
- * GDN_ERR_SHAPE.
+ * Workspace bytes needed by gdn_forward_framewise (mode = 0; also gdn_forward_framewise_save),
+ * gdn_step_frame (mode = 1), gdn_backward_framewise (mode = 2) or gdn_backward_framewise_saved
+ * (mode = 3) for this problem. The step-mode size does not depend on `frames`. Validates the
+ * sizes in `p` (not the pointers or strides); other modes are GDN_ERR_SHAPE.
  */
 gdn_status gdn_workspace_size(const gdn_problem* p, int mode, size_t* bytes_out);
 
@@ -297,6 +297,38 @@ gdn_status gdn_backward_framewise(const gdn_problem* p, const void* q, const voi
                                   const float* d_state_out, void* dq, void* dk, void* dv,
                                   float* dgamma, float* dbeta, float* d_state_in,
                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Training without recomputing the forward states: gdn_forward_framewise_save is the forward
+ * (FUSED schedule; AUTO is taken as FUSED, STAGED is GDN_ERR_UNSUPPORTED) that also fills a
+ * caller-owned buffer `saved` with what gdn_backward_framewise_saved needs, so that the backward
+ * skips its first two launches (the frames' key-key products and the state scan).
+ *   gdn_saved_size   bytes of `saved` for the problem (a pure function of it; bf16 data with
+ *                    D = 64 or 128 and a frame's q/k/v rows within 2 GiB, else
+ *                    GDN_ERR_UNSUPPORTED). Layout, for reference: the frames' Ghat products
+ *                    (delta rule only; bf16 hi + lo planes, the library's record order), then,
+ *                    256-byte aligned, the initial state and every M_f in fp32, [B][H][F+1][D][D]
+ *                    with element [b][h][f+1][c][n] = M_f[n][c] (slot 0: state_in, or zero).
+ *   saved            at least gdn_saved_size bytes, 256-byte aligned, must not overlap any
+ *                    other argument; arguments otherwise as gdn_forward_framewise
+ * gdn_backward_framewise_saved takes the same problem and inputs as the forward that filled
+ * `saved` (it does not read state_in: slot 0 holds it) and computes what
+ * gdn_backward_framewise computes, from the forward's own states (so the two agree to
+ * rounding: the fused forward and the backward's own scan round differently); its workspace
+ * is gdn_workspace_size(p, 3) bytes.
+ */
+gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes_out);
+gdn_status gdn_forward_framewise_save(const gdn_problem* p, const void* q, const void* k,
+                                      const void* v, const float* gamma, const float* beta,
+                                      const float* state_in, void* o, float* state_out,
+                                      void* saved, size_t saved_bytes, void* workspace,
+                                      size_t workspace_bytes, void* hip_stream);
+gdn_status gdn_backward_framewise_saved(const gdn_problem* p, const void* q, const void* k,
+                                        const void* v, const float* gamma, const float* beta,
+                                        const void* saved, size_t saved_bytes, const void* d_o,
+                                        const float* d_state_out, void* dq, void* dk, void* dv,
+                                        float* dgamma, float* dbeta, float* d_state_in,
+                                        void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * Instrumentation (launch trace). gdn_set_trace arms `pairs` pairs of caller-created,

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 6
+    assert gdn.abi_version() == 7
     lib = gdn.load()
     for code in range(9):
         assert lib.gdn_status_string(code)
@@ -247,8 +247,52 @@ def test_backward_workspace():
     # fp32 forward states and state gradients (F + 1 slots), the forward records and C_f records
     assert n >= 2 * (31 * 2 * 64 * 64 * 4) + 30 * 2 * 64 * 64 * 4
     assert gdn.workspace_size(prob(F=60), 2) > n
-    n3 = ctypes.c_size_t(0)
-    assert gdn.load().gdn_workspace_size(ctypes.byref(p), 3, ctypes.byref(n3)) == 2
+    # from saved states: only the C_f records and the state gradients (no forward records or
+    # states)
+    n3 = gdn.workspace_size(p, 3)
+    assert n3 < n and n3 >= 31 * 2 * 64 * 64 * 4 + 30 * 2 * 64 * 64 * 4
+    n4 = ctypes.c_size_t(0)
+    assert gdn.load().gdn_workspace_size(ctypes.byref(p), 4, ctypes.byref(n4)) == 2
+
+
+def test_saved_size():
+    # B=1, H=2, D=64, F=30, delta: Ghat planes (hi + lo bf16, D/16 x 2 x 2 fragments of 1 KB
+    # per frame), then 256-byte aligned fp32 states for F + 1 slots
+    p = prob(F=30)
+    recs = 2 * 30 * (64 // 16) * 2 * 2 * 1024
+    states = 2 * 31 * 64 * 64 * 4
+    assert gdn.saved_size(p) == (recs + 255) // 256 * 256 + states
+    assert gdn.saved_size(prob(F=30, delta=0)) == states          # no Ghat without the delta term
+    n = ctypes.c_size_t(0)
+    assert gdn.load().gdn_saved_size(ctypes.byref(prob(dtype=gdn.GDN_F32)), ctypes.byref(n)) == 3
+    assert gdn.load().gdn_saved_size(ctypes.byref(prob(D=32)), ctypes.byref(n)) == 3
+
+
+def test_saved_entry_points_validate():
+    lib = gdn.load()
+    p = prob(F=30)
+    need = gdn.saved_size(p)
+    ws = gdn.workspace_size(p, 0)
+    # forward: saved required, large enough, aligned, not overlapping anything
+    def fwd(saved, saved_bytes, pp=p):
+        return lib.gdn_forward_framewise_save(ctypes.byref(pp), A, 2 * A, 3 * A, 4 * A, 5 * A, None,
+                                              6 * A, None, saved, saved_bytes, 64 * A, ws, None)
+    assert fwd(None, 0) == 1
+    assert fwd(128 * A, need - 1) == 7
+    assert fwd(128 * A + 16, need) == 5
+    assert fwd(6 * A, need) == 6                           # overlaps o
+    staged = prob(F=30)
+    staged.schedule = 1
+    assert fwd(128 * A, need, staged) == 3
+    # backward: saved required and large enough
+    ws3 = gdn.workspace_size(p, 3)
+    def bwd(saved, saved_bytes):
+        return lib.gdn_backward_framewise_saved(ctypes.byref(p), A, 2 * A, 3 * A, 4 * A, 5 * A, saved,
+                                                saved_bytes, 6 * A, None, 7 * A, 8 * A, 9 * A, 10 * A,
+                                                11 * A, None, 64 * A, ws3, None)
+    assert bwd(None, 0) == 1
+    assert bwd(128 * A, need - 1) == 7
+    assert bwd(7 * A, need) == 6                           # dq inside the saved buffer
 
 
 def call_fp8(p, q=A, k=2 * A, v=3 * A, qs=15 * A, ks=16 * A, vs=17 * A, g=4 * A, b=5 * A, si=None,

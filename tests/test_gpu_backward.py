@@ -131,3 +131,54 @@ def test_backward_880x81_sampled_heads():
         errs[name] = rel_err(to_np(x[1:2, heads]), r)
     say("  " + " ".join("%s %.2e" % kv for kv in errs.items()))
     assert max(errs.values()) <= TOL["bf16"], errs
+
+
+SAVED_CASES = [
+    # B, H, D, S, F, delta, initial state, dstate_out, layout
+    (1, 2, 128, 200, 5, True, True, True, "head"),
+    (2, 2, 64, 130, 4, True, True, True, "token"),
+    (1, 2, 128, 96, 6, False, True, False, "head"),
+    (1, 1, 128, 1, 9, True, False, True, "head"),     # one token per frame
+    (1, 16, 128, 3520, 2, True, True, True, "head"),  # the 720p frame size
+]
+
+
+@pytest.mark.parametrize("case", SAVED_CASES, ids=["-".join(map(str, c)) for c in SAVED_CASES])
+def test_backward_from_saved_forward(case):
+    """forward_framewise_save gives the fused forward's outputs bitwise and keeps the states (slot
+    0 = the initial state and slot F = the final state, transposed, bitwise); the backward from
+    that buffer matches the oracle and the recomputing backward."""
+    say("backward from saved", case)
+    B, H, D, S, F, delta, with_state, with_dm, layout = case
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + 1)
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    d_o = bf16_round(rng.standard_normal((B, H, F * S, D)))
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    s0 = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32) if with_state else None
+    dm = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32) if with_dm else None
+    dev = [to_dev(x, "bf16", DEV, layout) for x in (q, k, v)]
+    ddo = to_dev(d_o, "bf16", DEV, layout)
+    tg, tb = torch.from_numpy(g).to(DEV), torch.from_numpy(b).to(DEV)
+    ts0 = None if s0 is None else torch.from_numpy(s0).to(DEV)
+    tdm = None if dm is None else torch.from_numpy(dm).to(DEV)
+    o_f, st_f = gdn.forward_framewise(*dev, tg, tb, ts0, use_delta=delta, schedule="fused")
+    o_s, st_s, saved = gdn.forward_framewise_save(*dev, tg, tb, ts0, use_delta=delta)
+    got = gdn.backward_framewise(*dev, tg, tb, ddo, None, tdm, use_delta=delta, saved=saved)
+    rec = gdn.backward_framewise(*dev, tg, tb, ddo, ts0, tdm, use_delta=delta)
+    torch.cuda.synchronize()
+    assert torch.equal(o_f, o_s) and torch.equal(st_f, st_s)
+    p = gdn.Problem(B, H, D, S, F, gdn.GDN_BF16, int(delta), 0.0, 0, 0, D, 0, 0, D)
+    nst = B * H * (F + 1) * D * D
+    states = saved[saved.numel() - 4 * nst:].view(torch.float32).view(B, H, F + 1, D, D)
+    assert saved.numel() == gdn.saved_size(p)
+    init = ts0 if ts0 is not None else torch.zeros((B, H, D, D), device=DEV)
+    assert torch.equal(states[:, :, 0], init.transpose(2, 3))
+    assert torch.equal(states[:, :, F], st_s.transpose(2, 3))
+    ref = oracle.backward(q, k, v, g, b, s0, d_o, dm, use_delta=delta)
+    errs = {n: rel_err(to_np(x), r) for n, x, r in zip(NAMES, got, ref)}
+    agree = {n: rel_err(to_np(x), to_np(y)) for n, x, y in zip(NAMES, got, rec)}
+    say("  oracle " + " ".join("%s %.2e" % kv for kv in errs.items()))
+    say("  vs recomputing " + " ".join("%s %.2e" % kv for kv in agree.items()))
+    assert max(errs.values()) <= TOL["bf16"], errs
+    assert max(agree.values()) <= TOL["bf16"], agree
