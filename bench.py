@@ -275,7 +275,9 @@ def backward_mode(w, dev, steps, ev, stream):
     flops_alg = (10 if w.use_delta else 6) * w.B * w.H * w.F * w.S * w.D * w.D
     t_roof = max(bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
     bwd_ms = kms.get("bwd", 0.0)
-    bwd_bytes = 6 * w.B * w.H * w.F * w.S * w.D * esz   # per-frame gradient kernel: K, V, dO, dQ, dK, dV
+    bwd_bytes = 4 * w.B * w.H * w.F * w.S * w.D * esz   # per-frame gradient kernel: K, V, dK, dV
+    qdo_ms = kms.get("bwd_qdo", 0.0)
+    qdo_bytes = 3 * w.B * w.H * w.F * w.S * w.D * esz   # pass over Q and dO: Q, dO, dQ
     del ws
 
     # training with saved states: the fused forward that keeps the states and Ghat records,
@@ -321,7 +323,9 @@ def backward_mode(w, dev, steps, ev, stream):
                      "frac_of_roofline": round(t_roof / ms, 4),
                      "achieved_gb_s": round(bytes_alg / (ms * 1e-3) / 1e9, 1)},
             "bwd_kernel": {"achieved_gb_s": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1) if bwd_ms else None,
-                           "frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if bwd_ms else None}}
+                           "frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if bwd_ms else None},
+            "qdo_kernel": {"achieved_gb_s": round(qdo_bytes / (qdo_ms * 1e-3) / 1e9, 1) if qdo_ms else None,
+                           "frac": round(qdo_bytes / (qdo_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if qdo_ms else None}}
 
 
 def fp8_mode(dev, steps, warmup, ev, stream):

@@ -28,7 +28,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
           8: "GDN_ERR_HIP"}
 KERNEL_NAMES = {0: "products", 1: "combine", 2: "scan", 3: "step_partial", 4: "step_reduce",
                 5: "fused_reset", 6: "fused", 7: "scan_bwd", 8: "bwd", 9: "scan_states",
-                10: "tconv", 11: "attn", 12: "step_output"}
+                10: "tconv", 11: "attn", 12: "step_output", 13: "bwd_qdo"}
 SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
 
 

@@ -68,7 +68,8 @@ enum Kernel {
     K_SCAN_STATES = 9,   // the forward scan with fp32 per-frame states (backward's recompute)
     K_TCONV = 10,        // block-causal temporal convolution
     K_ATTN = 11,         // frame-causal softmax attention
-    K_STEP_OUTPUT = 12   // step (column-block kernels): outputs of the frame
+    K_STEP_OUTPUT = 12,  // step (column-block kernels): outputs of the frame
+    K_BWD_QDO = 13       // backward: C_f = Q_f^T dO_f and dQ_f in one pass over Q and dO
 };
 
 // Arguments of the frame-causal softmax attention (gdn_attn.hip). q: [B][H][Tq][D], k, v:

@@ -1153,32 +1153,59 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Backward, per (b, h, f): the gradients of the frame's inputs from G_f = dL/dM_f, the states
-// before and after the frame (M_{f-1}, M_f) and the frame's K, V, dO. With Kt = c K and
+// Backward, per (b, h, f): the gradients of the frame's K, V, gamma and beta from
+// G_f = dL/dM_f, the state before the frame (M_{f-1}) and the frame's K, V (dQ = dO M_f^T needs
+// neither G_f nor K, V: qdo_kernel forms it on its pass over Q and dO). With Kt = c K and
 // P = Kt M_{f-1} (the reverse-mode derivative of the forward update):
-//     dQ = dO M_f^T                       dV = beta Kt G
+//     dV = beta Kt G
 //     dKt = beta R G^T - gamma beta (Kt G) M_{f-1}^T,   R = V - gamma P,   dK = c dKt
 //     dgamma = <G, M_{f-1}> - beta <Kt G, P>            dbeta = <Kt G, R>
-// (no delta term: R = V and only the first term of dKt and of dgamma). The states and G_f
-// come from the workspace in fp32, transposed ([c][n]), and are staged in LDS as bf16. Every
+// (no delta term: R = V and only the first term of dKt and of dgamma). M_{f-1} and G_f come
+// from the workspace in fp32, transposed ([c][n]), and are staged in LDS as bf16. Every
 // product runs transposed on MFMA, so that each lane ends up with 4 consecutive feature rows
 // of one token: P^T and (Kt G)^T from A = M_{f-1}^T / G^T rows and B = K rows; their C tiles
 // are then the B operand of dKt^T = G (beta R^T) + M_{f-1} (-gamma beta (Kt G)^T), with the
 // k order of a 32-long step taken from two C tiles (slots 0-3 and 4-7) and the A operand read
-// transposed from the same LDS copies (ds_read_tr16_b64); dQ^T = M_f dO^T likewise.
+// transposed from the same LDS copies (ds_read_tr16_b64).
 // dgamma and dbeta are summed over the frame inside the workgroup in a fixed order.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// A operand slice of Y = X^T from a [k][n] LDS matrix X (row length MR), with the rows of the
-// 16-row tile jt permuted as in out_col (tiles 2p and 2p + 1 together cover 32 p .. 32 p + 31
-// so that lane (r, g) of their C tiles holds 8 consecutive rows): lane (r, g) of a 16-lane
-// group receives Y[out_col(jt, r)][k0 + 4 g + j] = X[k0 + 4 g + j][out_col(jt, r)], j = 0..3.
+// Swizzled LDS layout of the backward's bf16 matrices (D x D states, token x D chunks): rows of
+// D elements without padding, the 8-byte units of row r (4 elements each) permuted by XOR with
+// a mask of the bits 0, 1, 3, 4 of r. The masks make the three access patterns of the backward
+// free of bank conflicts, whether the LDS serves 64 banks per clock (16 lanes of a 16-byte
+// access, 32 lanes of an 8-byte one) or 32: transposed reads (read_tr4: rows k0 + 8 g' + 0..3,
+// units 8 (jt >> 1) + 2 (r & 3) + (jt & 1)), 16-byte fragment reads of the rows out_col(cb, r),
+// and 16-byte row stores (16 lanes per row). A 16-byte access covers the unit pair 2u, 2u + 1;
+// with an odd mask the pair lies swapped in LDS, so its two 8-byte halves swap in registers.
+template <int D> __device__ __forceinline__ int sw_mask(int r) {
+    const int b0 = r & 1, b1 = (r >> 1) & 1, b3 = (r >> 3) & 1, b4 = (r >> 4) & 1;
+    if constexpr (D == 128) return b0 | b0 << 1 | (b4 ^ b3) << 2 | b1 << 3 | b3 << 4;
+    else return (b0 ^ b3) | b3 << 1 | (b4 ^ b0) << 2 | b1 << 3;
+}
+// 16 bytes of row r, columns [c, c + 8) (c a multiple of 8), to / from a swizzled matrix
+template <int D> __device__ __forceinline__ void st16_sw(bf16* X, int r, int c, u32x4 v) {
+    const int m = sw_mask<D>(r);
+    st16(X + r * D + (((c >> 2) ^ (m & ~1)) << 2), (m & 1) ? u32x4{v[2], v[3], v[0], v[1]} : v);
+}
+template <int D> __device__ __forceinline__ bf16x8 ld16_sw(const bf16* X, int r, int c) {
+    const int m = sw_mask<D>(r);
+    const u32x4 v = ld16(X + r * D + (((c >> 2) ^ (m & ~1)) << 2));
+    return __builtin_bit_cast(bf16x8, (m & 1) ? u32x4{v[2], v[3], v[0], v[1]} : v);
+}
+
+// A operand slice of Y = X^T from a swizzled [k][n] LDS matrix X, with the rows of the 16-row
+// tile jt permuted as in out_col (tiles 2p and 2p + 1 together cover 32 p .. 32 p + 31 so that
+// lane (r, g) of their C tiles holds 8 consecutive rows): lane (r, g) of a 16-lane group
+// receives Y[out_col(jt, r)][k0 + 4 g + j] = X[k0 + 4 g + j][out_col(jt, r)], j = 0..3.
 // (ds_read_tr16_b64: in each 16-lane group, destination lane i takes element i mod 4 of the four
 // b16 values at the address of source lane 4 j + i / 4; source lane 4 j + a points at row
-// k0 + 4 g + j, columns out_col(jt, 4 a) .. + 3.)
-template <int MR> __device__ __forceinline__ u32x2 read_tr4(const bf16* X, int k0, int jt, int r16, int g) {
-    const bf16* a = X + (k0 + 4 * g + (r16 >> 2)) * MR + 32 * (jt >> 1) + 8 * (r16 & 3) + 4 * (jt & 1);
+// k0 + 4 g + j, columns out_col(jt, 4 a) .. + 3, one 8-byte unit.)
+template <int D> __device__ __forceinline__ u32x2 read_tr4(const bf16* X, int k0, int jt, int r16, int g) {
+    const int r = k0 + 4 * g + (r16 >> 2);
+    const int u = 8 * (jt >> 1) + 2 * (r16 & 3) + (jt & 1);
+    const bf16* a = X + r * D + ((u ^ sw_mask<D>(r)) << 2);
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a));
 }
 
@@ -1191,9 +1218,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
     constexpr int CT = D / 16;        // 16-row tiles of a feature dimension
     constexpr int CP = CT / 2;        // tile pairs (32 features)
     constexpr int KS = D / 32;        // 32-long k steps over a feature dimension
-    constexpr int MR = D + 8;         // LDS row length (bf16)
-    constexpr int PLANE = D * MR;
-    __shared__ __attribute__((aligned(16))) bf16 sm[3 * PLANE];  // M_{f-1}^T, G_f^T, M_f^T
+    constexpr int PLANE = D * D;      // swizzled (sw_mask)
+    __shared__ __attribute__((aligned(16))) bf16 sm[2 * PLANE];  // M_{f-1}^T, G_f^T
     __shared__ float red[2][NW];
     static_assert(D == 64 || D == 128, "backward: D = 64 or 128");
 
@@ -1206,16 +1232,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
     const float gm = L.gamma[gi], bt = L.beta[gi], c = L.c;
     bf16* Mp = sm;              // M_{f-1}^T [c][n]
     bf16* Gs = sm + PLANE;      // G_f^T
-    bf16* Mn = sm + 2 * PLANE;  // M_f^T
 
-    // stage the three matrices (fp32 slots f and f + 1 of the states, f + 1 of G) as bf16 and
-    // form the frame term <G_f, M_{f-1}> of dgamma from the fp32 values on the way
+    // stage the two matrices (fp32 slot f of the states, f + 1 of G) as bf16 and form the frame
+    // term <G_f, M_{f-1}> of dgamma from the fp32 values on the way
     float dg = 0.f, db = 0.f;
     {
         const float* mt = (const float*)L.mt + ((int64_t)bh * (F + 1) + f) * D * D;
         const float* gt = (const float*)L.gt + ((int64_t)bh * (F + 1) + f + 1) * D * D;
         constexpr int NE = D * D / 8, PT = (NE + kBwdThreads - 1) / kBwdThreads;
-        f32x4 xm[PT][2], xg[PT][2], xn[PT][2];
+        f32x4 xm[PT][2], xg[PT][2];
 #pragma unroll
         for (int k = 0; k < PT; ++k) {
             const int e = min(tid + k * kBwdThreads, NE - 1);
@@ -1223,7 +1248,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
             for (int hh = 0; hh < 2; ++hh) {
                 xm[k][hh] = *(const f32x4*)(mt + e * 8 + 4 * hh);
                 xg[k][hh] = *(const f32x4*)(gt + e * 8 + 4 * hh);
-                xn[k][hh] = *(const f32x4*)(mt + D * D + e * 8 + 4 * hh);
             }
         }
         auto pack8 = [](const f32x4 (&x)[2]) {
@@ -1235,9 +1259,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
             const int e = tid + k * kBwdThreads;
             if (NE % kBwdThreads == 0 || e < NE) {
                 const int row = e / (D / 8), cb8 = e % (D / 8);
-                st16(Mp + row * MR + cb8 * 8, pack8(xm[k]));
-                st16(Gs + row * MR + cb8 * 8, pack8(xg[k]));
-                st16(Mn + row * MR + cb8 * 8, pack8(xn[k]));
+                st16_sw<D>(Mp, row, cb8 * 8, pack8(xm[k]));
+                st16_sw<D>(Gs, row, cb8 * 8, pack8(xg[k]));
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -1248,11 +1271,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
     __syncthreads();
 
     const int64_t io = (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * S * L.st;
-    const int64_t oo = (int64_t)b * L.ob + (int64_t)h * L.oh + (int64_t)f * S * L.ot;
     const bf16* kf = (const bf16*)L.k + io;
     const bf16* vf = (const bf16*)L.v + io;
-    const bf16* dof = (const bf16*)L.d_o + oo;   // dO (o strides)
-    bf16* dqf = (bf16*)L.dq + io;
     bf16* dkf = (bf16*)L.dk + io;
     bf16* dvf = (bf16*)L.dv + io;
 
@@ -1260,7 +1280,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
         const int s = s0 + r16;
         const bool in = s < S;
         // operands are loaded where their use begins, to keep live ranges short
-        bf16x8 bk[KS], bo[KS];
+        bf16x8 bk[KS];
         u32x4 vv[CP];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -1279,9 +1299,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
             const int row = out_col<bf16, D>(cb, r16);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int off = row * MR + ks * 32 + 8 * g;
-                if constexpr (DELTA) pt[cb] = MM::run(ld_frag<bf16>(Mp + off), bk[ks], pt[cb]);
-                kg[cb] = MM::run(ld_frag<bf16>(Gs + off), bk[ks], kg[cb]);
+                if constexpr (DELTA) pt[cb] = MM::run(ld16_sw<D>(Mp, row, ks * 32 + 8 * g), bk[ks], pt[cb]);
+                kg[cb] = MM::run(ld16_sw<D>(Gs, row, ks * 32 + 8 * g), bk[ks], kg[cb]);
             }
             __builtin_amdgcn_sched_barrier(0);  // keep each tile's LDS reads next to its MFMAs
         }
@@ -1315,15 +1334,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
             }
             if (in) st16(dvf + (int64_t)s * L.st + 32 * p + 8 * g, u32x4{dvw[0], dvw[1], dvw[2], dvw[3]});
         }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            bo[ks] = in ? ld_frag<bf16>(dof + (int64_t)s * L.ot + ks * 32 + 8 * g) : zero_frag<bf16>();
-        // dKt^T and dQ^T, a pair of 16-row tiles (32 features) at a time (not unrolled: it
-        // indexes no register array, and unrolling lets the compiler hoist every LDS read)
+        // dKt^T, a pair of 16-row tiles (32 features) at a time (not unrolled: it indexes no
+        // register array, and unrolling lets the compiler hoist every LDS read)
 #pragma unroll 1
         for (int p = 0; p < CP; ++p) {
             f32x4 ak[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            f32x4 aq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8 B1 = __builtin_bit_cast(bf16x8, u32x4{b1[2 * ks][0], b1[2 * ks][1],
@@ -1336,28 +1351,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
                 for (int hh = 0; hh < 2; ++hh) {
                     const int jt = 2 * p + hh;
                     // slots 0-3: features 32 ks + 8 g + j; slots 4-7: 32 ks + 8 g + 4 + j
-                    const u32x2 g0 = read_tr4<MR>(Gs, 32 * ks, jt, r16, 2 * g);
-                    const u32x2 g1 = read_tr4<MR>(Gs, 32 * ks + 4, jt, r16, 2 * g);
+                    const u32x2 g0 = read_tr4<D>(Gs, 32 * ks, jt, r16, 2 * g);
+                    const u32x2 g1 = read_tr4<D>(Gs, 32 * ks + 4, jt, r16, 2 * g);
                     ak[hh] = MM::run(__builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]}), B1, ak[hh]);
                     if constexpr (DELTA) {
-                        const u32x2 m0 = read_tr4<MR>(Mp, 32 * ks, jt, r16, 2 * g);
-                        const u32x2 m1 = read_tr4<MR>(Mp, 32 * ks + 4, jt, r16, 2 * g);
+                        const u32x2 m0 = read_tr4<D>(Mp, 32 * ks, jt, r16, 2 * g);
+                        const u32x2 m1 = read_tr4<D>(Mp, 32 * ks + 4, jt, r16, 2 * g);
                         ak[hh] = MM::run(__builtin_bit_cast(bf16x8, u32x4{m0[0], m0[1], m1[0], m1[1]}), B2, ak[hh]);
                     }
-                    const u32x2 n0 = read_tr4<MR>(Mn, 32 * ks, jt, r16, 2 * g);
-                    const u32x2 n1 = read_tr4<MR>(Mn, 32 * ks + 4, jt, r16, 2 * g);
-                    aq[hh] = MM::run(__builtin_bit_cast(bf16x8, u32x4{n0[0], n0[1], n1[0], n1[1]}), bo[ks], aq[hh]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (in) {
+            if (in)
                 st16(dkf + (int64_t)s * L.st + 32 * p + 8 * g,
                      u32x4{pack_bf16x2(c * ak[0][0], c * ak[0][1]), pack_bf16x2(c * ak[0][2], c * ak[0][3]),
                            pack_bf16x2(c * ak[1][0], c * ak[1][1]), pack_bf16x2(c * ak[1][2], c * ak[1][3])});
-                st16(dqf + (int64_t)s * L.st + 32 * p + 8 * g,
-                     u32x4{pack_bf16x2(aq[0][0], aq[0][1]), pack_bf16x2(aq[0][2], aq[0][3]),
-                           pack_bf16x2(aq[1][0], aq[1][1]), pack_bf16x2(aq[1][2], aq[1][3])});
-            }
         }
     }
 
@@ -1380,6 +1388,173 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
         }
         L.dgamma[gi] = sg;
         L.dbeta[gi] = sbt;
+    }
+}
+
+// ----------------------------------------------------------------------------------------
+// Backward, per (b, h, f, token split): the two products that need Q and dO,
+//     C_f = Q_f^T dO_f  (the per-frame term of the reverse chain)   and   dQ_f = dO_f M_f^T,
+// in one pass over Q and dO (dQ needs only the forward state M_f, not G_f). Chunks of 64 tokens
+// of Q and dO go through registers into LDS as rows (token-major, as in memory); the next
+// chunk's loads are in flight while the current chunk is used. C contracts over tokens on MFMA
+// with both operands read transposed from the row tiles (ds_read_tr16_b64): A = Q^T, B = dO,
+// and lane (r, g) of the C tile for feature tiles (ja, jb) holds C[i0 + q][out_col(jb, r)],
+// i0 = out_col(ja, 4 g); each of the four waves owns a quarter of C. dQ^T = M_f dO^T runs with
+// A = M_f read transposed from an LDS copy of M_f^T and B = dO rows: wave w takes the 16 chunk
+// rows out_col(w, r), r = 0..15. Every LDS matrix uses the swizzled layout of sw_mask. With one split C goes to the per-frame record the
+// reverse scan reads (the no-delta record layout of the gram products), with several to fp32
+// partials that combine_kernel sums. Q and dO are read through L.q and L.d_o with their own
+// strides; the record (or partial) buffer is L.canon (L.part).
+constexpr int kQdoThreads = 256;
+
+// Barrier for LDS hand-offs only: waits for this wave's LDS accesses, not for its global loads
+// and stores (__syncthreads would also drain the prefetch of the next chunk and the dQ stores).
+__device__ __forceinline__ void lds_sync() { __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int D>
+__global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
+    using MM = Mma<bf16>;
+    constexpr int NW = kQdoThreads / 64;
+    constexpr int SC = 16 * NW;              // tokens per chunk: one 16-token dQ tile per wave
+    constexpr int CT = D / 16, CP = CT / 2, KS = D / 32;
+    constexpr int TA = CT / 2, TB = CT / 2;  // C tiles of a wave: TA feature tiles of Q x TB of dO
+    constexpr int FB = D / 8;                // 16-byte blocks per token row
+    constexpr int NLD = SC * FB / kQdoThreads;
+    static_assert(D == 64 || D == 128, "backward: D = 64 or 128");
+    static_assert(NW == 4 && (SC * FB) % kQdoThreads == 0 && (D * FB) % kQdoThreads == 0,
+                  "four waves, whole rows per chunk");
+    __shared__ __attribute__((aligned(16))) bf16 sm[(D + 2 * SC) * D];   // swizzled (sw_mask)
+    bf16* Mn = sm;               // M_f^T [c][n]
+    bf16* Qt = sm + D * D;       // Q chunk [token][feature]
+    bf16* Ot = Qt + SC * D;      // dO chunk [token][feature]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    int blk = blockIdx.x;
+    const int p = blk % L.nsplit;
+    blk /= L.nsplit;
+    const int F = L.F, S = L.S;
+    const int f = blk % F, bh = blk / F;
+    const int b = bh / L.H, h = bh % L.H;
+    const int gi = bh * F + f;
+    const int t0 = p * L.split_tokens, t1 = min(S, t0 + L.split_tokens);
+    const int64_t io = (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * S * L.st;
+    const bf16* qf = (const bf16*)L.q + io;
+    bf16* dqf = (bf16*)L.dq + io;
+    const bf16* of = (const bf16*)L.d_o + (int64_t)b * L.ob + (int64_t)h * L.oh + (int64_t)f * S * L.ot;
+
+    // M_f^T (fp32 state slot f + 1) to LDS as bf16
+    {
+        const float* mt = (const float*)L.mt + ((int64_t)bh * (F + 1) + f + 1) * D * D;
+        constexpr int PT = D * FB / kQdoThreads;
+        f32x4 x[PT][2];
+#pragma unroll
+        for (int k = 0; k < PT; ++k)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) x[k][hh] = *(const f32x4*)(mt + (tid + k * kQdoThreads) * 8 + 4 * hh);
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const int e = tid + k * kQdoThreads;
+            st16_sw<D>(Mn, e / FB, (e % FB) * 8,
+                 u32x4{pack_bf16x2(x[k][0][0], x[k][0][1]), pack_bf16x2(x[k][0][2], x[k][0][3]),
+                       pack_bf16x2(x[k][1][0], x[k][1][1]), pack_bf16x2(x[k][1][2], x[k][1][3])});
+        }
+    }
+
+    // tokens [c0, c0 + SC) of Q and dO into registers; rows at or beyond t1 are zero
+    u32x4 rq[NLD], ro[NLD];
+    auto load = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int e = tid + i * kQdoThreads, tok = c0 + e / FB, fb = e % FB;
+            const bool in = tok < t1;
+            rq[i] = in ? ld16(qf + (int64_t)tok * L.st + fb * 8) : u32x4{0u, 0u, 0u, 0u};
+            ro[i] = in ? ld16(of + (int64_t)tok * L.ot + fb * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    f32x4 acc[TA][TB];
+#pragma unroll
+    for (int a = 0; a < TA; ++a)
+#pragma unroll
+        for (int bb = 0; bb < TB; ++bb) acc[a][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ja0 = TA * (wave & 1), jb0 = TB * (wave >> 1);
+
+    load(t0);
+    for (int c0 = t0; c0 < t1; c0 += SC) {
+        lds_sync();   // the previous chunk's readers are done (first pass: M_f^T is written)
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int e = tid + i * kQdoThreads, row = e / FB, fb = e % FB;
+            st16_sw<D>(Qt, row, fb * 8, rq[i]);
+            st16_sw<D>(Ot, row, fb * 8, ro[i]);
+        }
+        lds_sync();
+        if (c0 + SC < t1) load(c0 + SC);
+
+        // C += Q^T dO over the chunk's tokens, 32 at a time (k slots 0-7 of lane group g:
+        // tokens k0 + 8 g + 0..7, the same in both operands)
+#pragma unroll
+        for (int k0 = 0; k0 < SC; k0 += 32) {
+            bf16x8 af[TA], bf[TB];
+#pragma unroll
+            for (int a = 0; a < TA; ++a) {
+                const u32x2 x0 = read_tr4<D>(Qt, k0, ja0 + a, r16, 2 * g);
+                const u32x2 x1 = read_tr4<D>(Qt, k0 + 4, ja0 + a, r16, 2 * g);
+                af[a] = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+            }
+#pragma unroll
+            for (int bb = 0; bb < TB; ++bb) {
+                const u32x2 x0 = read_tr4<D>(Ot, k0, jb0 + bb, r16, 2 * g);
+                const u32x2 x1 = read_tr4<D>(Ot, k0 + 4, jb0 + bb, r16, 2 * g);
+                bf[bb] = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+            }
+#pragma unroll
+            for (int a = 0; a < TA; ++a)
+#pragma unroll
+                for (int bb = 0; bb < TB; ++bb) acc[a][bb] = MM::run(af[a], bf[bb], acc[a][bb]);
+        }
+
+        // dQ^T = M_f dO^T for the wave's 16 tokens (chunk rows out_col(wave, r): the fragment
+        // reads of the swizzled tile are then free of bank conflicts), 32 features at a time
+        const int trow = out_col<bf16, 64>(wave, r16);
+        const int s = c0 + trow;
+        bf16x8 bo[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bo[ks] = ld16_sw<D>(Ot, trow, ks * 32 + 8 * g);
+#pragma unroll 1
+        for (int pp = 0; pp < CP; ++pp) {
+            f32x4 aq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const u32x2 n0 = read_tr4<D>(Mn, 32 * ks, 2 * pp + hh, r16, 2 * g);
+                    const u32x2 n1 = read_tr4<D>(Mn, 32 * ks + 4, 2 * pp + hh, r16, 2 * g);
+                    aq[hh] = MM::run(__builtin_bit_cast(bf16x8, u32x4{n0[0], n0[1], n1[0], n1[1]}), bo[ks], aq[hh]);
+                }
+            }
+            if (s < t1)
+                st16(dqf + (int64_t)s * L.st + 32 * pp + 8 * g,
+                     u32x4{pack_bf16x2(aq[0][0], aq[0][1]), pack_bf16x2(aq[0][2], aq[0][3]),
+                           pack_bf16x2(aq[1][0], aq[1][1]), pack_bf16x2(aq[1][2], aq[1][3])});
+        }
+    }
+
+    // C tile (a, bb): lane (r, g) holds C[i0 + q][j], i0 = 32 (ja >> 1) + 8 g + 4 (ja & 1)
+#pragma unroll
+    for (int a = 0; a < TA; ++a) {
+        const int ja = ja0 + a;
+        const int i0 = 32 * (ja >> 1) + 8 * g + 4 * (ja & 1);
+#pragma unroll
+        for (int bb = 0; bb < TB; ++bb) {
+            const int j = out_col<bf16, D>(jb0 + bb, r16);
+            if (L.nsplit == 1)
+                *(f32x4*)((float*)((char*)L.canon + (int64_t)gi * canon_bytes<D, false>()) + rec_b_off<D>(i0, j)) =
+                    acc[a][bb];
+            else
+                *(f32x4*)(L.part + ((int64_t)gi * L.nsplit + p) * (D * D) + j * D + i0) = acc[a][bb];
+        }
     }
 }
 
@@ -1678,6 +1853,14 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
     case K_BWD: {
         if constexpr (std::is_same<T, bf16>::value && (D == 64 || D == 128)) {
             hipLaunchKernelGGL((bwd_kernel<D, DELTA>), dim3(BH * L.F), dim3(kBwdThreads), 0, s, L);
+        } else {
+            return hipErrorInvalidValue;
+        }
+        break;
+    }
+    case K_BWD_QDO: {
+        if constexpr (std::is_same<T, bf16>::value && (D == 64 || D == 128)) {
+            hipLaunchKernelGGL((qdo_kernel<D>), dim3(BH * L.F * L.nsplit), dim3(kQdoThreads), 0, s, L);
         } else {
             return hipErrorInvalidValue;
         }

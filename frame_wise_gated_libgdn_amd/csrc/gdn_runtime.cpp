@@ -106,17 +106,14 @@ hipError_t run_backward(const Launch& L0, hipStream_t s) {
         A.mt_lead = 1;
         GDN_TRY(run.go(K_SCAN_STATES, A, s, BH * F));
     }
-    // 2. C_f = Q_f^T dO_f of every frame: the gram products without the delta term and the
-    //    gates, first operand Q (Q/K/V strides), second dO (O strides)
+    // 2. one pass over Q and dO: C_f = Q_f^T dO_f of every frame (its per-frame record, in the
+    //    no-delta layout of the gram products; S-split partials summed by the combine kernel)
+    //    and dQ_f = dO_f M_f^T from the forward states
     Launch C = L0;
     C.use_delta = 0;
-    C.unit_scale = 1;
-    C.k = L0.q;
-    C.v = L0.d_o;
-    C.xsb = L0.ob; C.xsh = L0.oh; C.xst = L0.ot;
     C.canon = L0.crec;
     C.g0 = 0; C.gn = F; C.o0 = 0; C.on = 0;
-    GDN_TRY(run.go(K_PRODUCTS, C, s, BH * F));
+    GDN_TRY(run.go(K_BWD_QDO, C, s, BH * F));
     if (L0.nsplit > 1) GDN_TRY(run.go(K_COMBINE, C, s, BH * F));
     // 3. reverse scan: G_f for every frame (slot f + 1) and the gradient of the initial state
     Launch R = L0;
@@ -126,7 +123,7 @@ hipError_t run_backward(const Launch& L0, hipStream_t s) {
     R.mt = L0.gt;
     R.mt_lead = 1;
     GDN_TRY(run.go(K_SCAN_BWD, R, s, BH * (F + 1)));
-    // 4. per-frame gradients
+    // 4. per-frame gradients of K, V, gamma and beta
     return run.go(K_BWD, L0, s, BH * F);
 }
 

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 7
+#define LIBGDN_ABI_VERSION 8
 
 typedef enum {
     GDN_OK = 0,
@@ -280,7 +280,10 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
  *     dgamma_f = <G_f, M> - beta_f <Kt G_f, P>,    dbeta_f = <Kt G_f, R>
  *     dstate_in = (gamma_0 I - gamma_0 beta_0 Kt_0^T Kt_0) G_0
  * (without the delta term: R = V_f, dK_f = c beta_f V_f G_f^T, dgamma_f = <G_f, M>, and the
- * chain uses gamma I). The forward states are recomputed inside the call.
+ * chain uses gamma I). The forward states are recomputed inside the call. Launches (trace
+ * kinds): the forward states (PRODUCTS, SCAN_STATES), Q_f^T dO_f and dQ in one pass over Q and
+ * dO (BWD_QDO), the reverse chain (SCAN_BWD), the gradients of K, V, gamma and beta (BWD);
+ * COMBINE follows PRODUCTS and BWD_QDO when frames are split over tokens.
  *   q, k, v, gamma, beta, state_in   the forward's inputs (state_in NULL: zero)
  *   d_o          dL/dO, layout of o (o_stride_*)
  *   d_state_out  dL/dstate_out fp32 [B][H][D][D], or NULL for zero
@@ -350,11 +353,12 @@ typedef enum {
     GDN_KERNEL_FUSED_RESET = 5,   /* fused: clears the ticket counter and frame flags */
     GDN_KERNEL_FUSED = 6,         /* fused: products, state step and outputs of every frame */
     GDN_KERNEL_SCAN_BWD = 7,      /* backward: reverse scan of the state gradients */
-    GDN_KERNEL_BWD = 8,           /* backward: per-frame gradients of Q, K, V, gamma, beta */
+    GDN_KERNEL_BWD = 8,           /* backward: per-frame gradients of K, V, gamma, beta */
     GDN_KERNEL_SCAN_STATES = 9,   /* backward: forward scan keeping every state in fp32 */
     GDN_KERNEL_TCONV = 10,        /* block-causal temporal convolution */
     GDN_KERNEL_ATTN = 11,         /* frame-causal softmax attention */
-    GDN_KERNEL_STEP_OUTPUT = 12   /* step, bf16 with D = 64 or 128: outputs of the frame */
+    GDN_KERNEL_STEP_OUTPUT = 12,  /* step, bf16 with D = 64 or 128: outputs of the frame */
+    GDN_KERNEL_BWD_QDO = 13       /* backward: Q_f^T dO_f and dQ in one pass over Q and dO */
 } gdn_kernel_kind;
 
 typedef struct {

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 7
+    assert gdn.abi_version() == 8
     lib = gdn.load()
     for code in range(9):
         assert lib.gdn_status_string(code)
