@@ -65,13 +65,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int
 }
 
 // XOR swizzle of the 16-byte chunks of row r of an unpadded LDS tile with CH chunks per row:
-// chunk c of row r is stored at chunk c ^ swz(r). CH = 16: a bijection on any 16 consecutive
-// rows (row reads: 16 rows, one chunk each, hit every bank once) whose values on rows
-// 4m .. 4m + 3 differ above bit 0 (transposed reads). CH = 8: rows 2m, 2m + 1 share a value.
+// chunk c of row r is stored at chunk c ^ swz(r). The masks (functions of the bits b_i of r) make
+// the tile's accesses free of bank conflicts whether the LDS serves 64 banks per clock (16 lanes
+// of a 16-byte access, 32 lanes of an 8-byte one) or 32 (8 and 16 lanes):
+//   CH = 16, 8 (K chunk, D = 128, 64): 16-byte row stores (16 rows, one chunk each) and
+//            transposed reads (rows k0 + 4 g + 0..3, two neighbouring chunks);
+//   CH = 4 (V chunk): transposed reads of two neighbouring chunks (the stores fill whole rows).
 template <int CH> __device__ __forceinline__ int swz(int r) {
-    if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (r >> 1) & (CH - 1);
+    const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
+    if constexpr (CH == 16) return (b3 ^ b2) | b0 << 1 | b1 << 2 | b2 << 3;
+    else if constexpr (CH == 8) return (b3 ^ b2) | b1 << 1 | (b0 ^ b2) << 2;
+    else return (b1 ^ b2) << 1;
 }
+// The prediction tile [kCW][kSC] (8-byte accesses, 16 rows x 4 units): unit u of row r is
+// stored at unit u ^ (r mod 16).
+__device__ __forceinline__ int pct_off(int row, int col) { return row * kSC + ((((col >> 2) ^ row) & 15) << 2); }
 
 // Lane (r, g) of each 16-lane group receives X[k0 + 4 g + j][c0 + r], j = 0..3, from a swizzled
 // [row][CH chunks] bf16 LDS tile (ds_read_tr16_b64: destination lane i takes element i mod 4 of
@@ -93,19 +101,32 @@ template <int D> struct PartLds {
     static constexpr int KB = kSC * D * 2;     // K chunk [token][D]
     static constexpr int VB = kSC * kCW * 2;   // V chunk [token][kCW]
     static constexpr int BUF = KB + VB;
-    static constexpr int PR = kSC + 8;         // row length (bf16) of the prediction tile
-    static constexpr int PB = kCW * PR * 2;    // prediction tile [kCW][PR]
+    static constexpr int PB = kCW * kSC * 2;   // prediction tile [kCW][kSC] (pct_off)
     static constexpr int MTOFF = kRing * (BUF + PB);   // M[:, J]^T in bf16: [kCW][D + 8]
     static constexpr int BYTES = MTOFF + kCW * (D + 8) * 2;
 };
 template <int D> struct OutLds {
-    static constexpr int MR = D + 8;           // padded row length (bf16) of M'^T
-    static constexpr int BYTES = D * MR * 2;
+    static constexpr int BYTES = D * D * 2;    // M'^T, swizzled (out_mask)
 };
 
 // Output column of row m of 16-row tile jt of the A operand M'^T: tiles 2p and 2p + 1 cover
 // columns 32p .. 32p + 31 so that lane (r, g) of their C tiles holds 8 consecutive columns.
 __device__ __forceinline__ int out_col(int jt, int m) { return 32 * (jt >> 1) + 8 * (m >> 2) + 4 * (jt & 1) + (m & 3); }
+
+// M'^T in the output kernel's LDS: unpadded rows whose 8-byte units are permuted by XOR with
+// a mask of the row's bits 0, 1, 3, 4, free of bank conflicts for 16-byte row stores and for
+// the 16-byte reads of the rows out_col(jt, r) (64 or 32 banks per clock). A 16-byte access
+// covers the unit pair 2u, 2u + 1; with an odd mask the pair lies swapped in LDS, so the two
+// 8-byte halves swap in registers.
+template <int D> __device__ __forceinline__ int out_mask(int r) {
+    const int b0 = r & 1, b1 = (r >> 1) & 1, b3 = (r >> 3) & 1, b4 = (r >> 4) & 1;
+    if constexpr (D == 128) return b0 | b0 << 1 | (b4 ^ b3) << 2 | b1 << 3 | b3 << 4;
+    else return (b0 ^ b3) | b3 << 1 | (b4 ^ b0) << 2 | b1 << 3;
+}
+template <int D> __device__ __forceinline__ int out_off(int r, int c) {   // c: a multiple of 8
+    return r * D + (((c >> 2) ^ (out_mask<D>(r) & ~1)) << 2);
+}
+__device__ __forceinline__ u32x4 half_swap(u32x4 v, bool sw) { return sw ? u32x4{v[2], v[3], v[0], v[1]} : v; }
 
 // Partial of role ((b h) * nsplit + p) * NJ + J.
 template <int D, bool DELTA>
@@ -196,7 +217,7 @@ __device__ void partial_body(const Launch& L, int role, char* lds) {
         const int buf = n & 1;
         bf16* kc = (bf16*)(lds + buf * PL::BUF);
         bf16* vc = (bf16*)(lds + buf * PL::BUF + PL::KB);
-        bf16* pct = (bf16*)(lds + kRing * PL::BUF + buf * PL::PB);   // -gamma c P^T: [kCW][PR]
+        bf16* pct = (bf16*)(lds + kRing * PL::BUF + buf * PL::PB);   // -gamma c P^T: [kCW][kSC]
         const int tv = t1 - c0;   // tokens of the split left, from this chunk on
         const u32x4 z = {0u, 0u, 0u, 0u};
         const int krow = 16 * wave + r;
@@ -212,7 +233,7 @@ __device__ void partial_body(const Launch& L, int role, char* lds) {
                 for (int ct = 0; ct < 2; ++ct) pa[ct] = mfma(__builtin_bit_cast(bf16x8, kx[ks]), bm[ct][ks], pa[ct]);
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
-                *(u32x2*)(pct + (16 * ct + r) * PL::PR + 16 * wave + 4 * g) =
+                *(u32x2*)(pct + pct_off(16 * ct + r, 16 * wave + 4 * g)) =
                     u32x2{pack2(-gc * pa[ct][0], -gc * pa[ct][1]), pack2(-gc * pa[ct][2], -gc * pa[ct][3])};
         }
 #pragma unroll
@@ -230,8 +251,8 @@ __device__ void partial_body(const Launch& L, int role, char* lds) {
             for (int ct = 0; ct < 2; ++ct) {
                 bv[ct] = join(read_tr<kCW / 8>(vc, tg, 16 * ct, r, g), read_tr<kCW / 8>(vc, tg + 16, 16 * ct, r, g));
                 if constexpr (DELTA) {
-                    const bf16* pr = pct + (16 * ct + r) * PL::PR + tg + 4 * g;
-                    bp[ct] = join(*(const u32x2*)pr, *(const u32x2*)(pr + 16));
+                    bp[ct] = join(*(const u32x2*)(pct + pct_off(16 * ct + r, tg + 4 * g)),
+                                  *(const u32x2*)(pct + pct_off(16 * ct + r, tg + 16 + 4 * g)));
                 }
             }
 #pragma unroll
@@ -317,7 +338,6 @@ __global__ __launch_bounds__(kThreads) void step_merge_kernel(Launch L) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void step_output_kernel(Launch L) {
     constexpr int KSN = D / 32, TJ = D / 16;
-    constexpr int MR = OutLds<D>::MR;
     __shared__ __attribute__((aligned(16))) char lds[OutLds<D>::BYTES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -348,11 +368,11 @@ __global__ __launch_bounds__(kThreads, 2) void step_output_kernel(Launch L) {
         for (int ks = 0; ks < KSN; ++ks)
             bq[d][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, row * qstb + (32 * ks + 8 * g) * 2, 0, 0));
     }
-    bf16* ms = (bf16*)lds;   // M'^T with padded rows
+    bf16* ms = (bf16*)lds;   // M'^T, swizzled
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
-        const int e = tid + k * kThreads;
-        *(u32x4*)(ms + (e / (D / 8)) * MR + (e % (D / 8)) * 8) = x[k];
+        const int e = tid + k * kThreads, row = e / (D / 8), c = (e % (D / 8)) * 8;
+        *(u32x4*)(ms + out_off<D>(row, c)) = half_swap(x[k], out_mask<D>(row) & 1);
     }
     __syncthreads();
     bf16x8 am[TJ][KSN];
@@ -360,7 +380,8 @@ __global__ __launch_bounds__(kThreads, 2) void step_output_kernel(Launch L) {
     for (int jt = 0; jt < TJ; ++jt)
 #pragma unroll
         for (int ks = 0; ks < KSN; ++ks)
-            am[jt][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(ms + out_col(jt, r) * MR + 32 * ks + 8 * g));
+            am[jt][ks] = __builtin_bit_cast(bf16x8, half_swap(*(const u32x4*)(ms + out_off<D>(out_col(jt, r), 32 * ks + 8 * g)),
+                                                              out_mask<D>(out_col(jt, r)) & 1));
 
 #pragma unroll
     for (int d = 0; d < kQD; ++d) {
