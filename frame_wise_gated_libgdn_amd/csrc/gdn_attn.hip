@@ -48,12 +48,15 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // XOR swizzle of the 16-byte chunks of a key row in an unpadded [key][dim] LDS tile with CH
-// chunks per row: chunk c of row r is stored at chunk c ^ swz(r). For CH = 16 (D = 128) it is a
-// bijection on every 16 consecutive rows (K fragment reads: 16 rows, one chunk) whose values on
-// 4 rows 4m .. 4m + 3 differ above bit 0 (V^T reads: 4 rows, chunks 2d and 2d + 1).
+// chunks per row: chunk c of row r is stored at chunk c ^ swz(r). The masks (functions of the
+// bits b_i of r) keep both reads of the tile free of bank conflicts whether the LDS serves 64
+// banks per clock (16 lanes of a 16-byte access, 32 lanes of an 8-byte one) or 32 (8 and 16
+// lanes): K fragment reads (rows 16 kt + 0..15, one chunk) and V^T reads (rows k0 + 4 g + 0..3,
+// chunks 2d and 2d + 1, 8 bytes per lane).
 template <int CH> __device__ __forceinline__ int swz(int r) {
-    if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (r >> 1) & (CH - 1);
+    const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
+    if constexpr (CH == 16) return (b3 ^ b2) | b0 << 1 | b1 << 2 | b2 << 3;
+    else return (b3 ^ b2) | b1 << 1 | (b0 ^ b2) << 2;
 }
 
 // lane (r, g) of each 16-lane group receives X[k0 + 4 g + j][c0 + r], j = 0..3, from a swizzled
