@@ -429,12 +429,14 @@ def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_
 
 def backward_framewise(q, k, v, gamma, beta, d_o, state=None, d_state_out=None, *,
                        use_delta=True, key_scale=None, dq=None, dk=None, dv=None,
-                       return_state_grad=True, saved=None, workspace=None, stream=None):
+                       return_state_grad=True, saved=None, workspace=None, stream=None,
+                       schedule="auto"):
     """Gradients of forward_framewise. q, k, v [B, H, F*S, D] (bf16, D = 64 or 128, same
     strides); d_o: dL/dO with o's shape (any strides with D contiguous); gamma, beta fp32
     [B, H, F]; state, d_state_out fp32 [B, H, D, D] or None. With saved (from
     forward_framewise_save on the same inputs) the forward states are not recomputed and state
-    is not read.
+    is not read. schedule: "fused" runs the reverse chain inside the pass over Q and dO
+    (ticket-ordered), "staged" as a separate scan, "auto" picks by problem size.
     Returns (dq, dk, dv, dgamma, dbeta, d_state_in); d_state_in is None when
     return_state_grad is False."""
     import torch
@@ -462,7 +464,7 @@ def backward_framewise(q, k, v, gamma, beta, d_o, state=None, d_state_out=None, 
     _check_f32("beta", beta, (B, H, F))
     _check_f32("state", state, (B, H, D, D))
     _check_f32("d_state_out", d_state_out, (B, H, D, D))
-    p = _problem(q, d_o, F, use_delta, key_scale)
+    p = _problem(q, d_o, F, use_delta, key_scale, schedule)
     if saved is not None:
         ws, nbytes = _workspace(p, 3, workspace, q.device)
         _check(load().gdn_backward_framewise_saved(

@@ -30,16 +30,17 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // function of it.
 struct Plan {
     int mode;                   // 0 forward, 1 step, 2 backward, 3 backward from saved states
-    bool fused;                 // forward: fused single pass (else staged); step: column blocks
+    bool fused;                 // forward: fused single pass (else staged); step: column
+                                // blocks; backward: the reverse chain in the Q/dO pass
     int nsplit, split_tokens;   // partial-product kernel
     int nchunk, chunk_tokens;   // output kernel
     size_t canon_bytes, part_bytes, mt_bytes;   // staged forward and step
-    size_t ctl_bytes, chain_bytes;              // fused forward
+    size_t ctl_bytes, chain_bytes;              // fused forward; chained backward
     size_t crec_bytes, gt_bytes;                // backward
     size_t total() const {
         if (mode >= 2)
-            return align256(canon_bytes) + align256(part_bytes) + align256(mt_bytes) +
-                   align256(crec_bytes) + gt_bytes;
+            return align256(ctl_bytes) + align256(chain_bytes) + align256(canon_bytes) +
+                   align256(part_bytes) + align256(mt_bytes) + align256(crec_bytes) + gt_bytes;
         if (mode == 1 && fused) return align256(part_bytes) + mt_bytes;
         return fused ? align256(ctl_bytes) + chain_bytes
                      : align256(canon_bytes) + align256(part_bytes) + mt_bytes;
@@ -82,6 +83,16 @@ bool choose_step_cols(const gdn_problem& p) {
     return gdn::step_cols_supported(p.dtype == GDN_BF16, p.head_dim) && step_rows_fit(p);
 }
 
+// The backward's reverse chain runs inside its pass over Q and dO (one workgroup per whole
+// frame, ticket-ordered) once there are enough frames to fill the chip, like the fused forward;
+// otherwise that pass may split frames over tokens and a separate scan runs the chain.
+bool choose_bwd_chain(const gdn_problem& p) {
+    if (!gdn::backward_supported(p.dtype == GDN_BF16, p.head_dim)) return false;
+    if (p.schedule == GDN_SCHEDULE_FUSED) return true;
+    if (p.schedule == GDN_SCHEDULE_STAGED) return false;
+    return (int64_t)p.batch * p.heads * p.frames >= kFusedMinItems;
+}
+
 constexpr int kTargetGroups = 2048;  // workgroups wanted per parallel launch (256 CUs x 8)
 constexpr int kStepPartials = 512;   // column-block step: partial workgroups (two per CU)
 constexpr int kStepOutputs = 256;    // column-block step: output workgroups
@@ -91,7 +102,7 @@ Plan make_plan(const gdn_problem& p, int mode) {
     const int step_mode = mode == 1;
     Plan pl{};
     pl.mode = mode;
-    pl.fused = mode == 0 ? choose_fused(p, 0) : mode == 1 && choose_step_cols(p);
+    pl.fused = mode == 0 ? choose_fused(p, 0) : mode == 1 ? choose_step_cols(p) : choose_bwd_chain(p);
     const int64_t D = p.head_dim, S = p.tokens_per_frame;
     const int64_t BH = (int64_t)p.batch * p.heads;
     const int64_t F = step_mode ? 1 : p.frames;
@@ -160,6 +171,12 @@ Plan make_plan(const gdn_problem& p, int mode) {
         pl.crec_bytes = (size_t)(BH * F * D * D * 4);
         pl.canon_bytes = 0;   // the forward's records and states come from the saved buffer
         pl.mt_bytes = 0;
+    }
+    if (mode >= 2) {
+        // chained: ticket counter, time-out flag and frame flags first (the time-out flag at byte
+        // 4, as in the fused forward), two fp32 state-gradient buffers per (b, h), no C records
+        if (pl.fused) pl.crec_bytes = 0;
+        else pl.ctl_bytes = pl.chain_bytes = 0;
     }
     return pl;
 }
@@ -489,11 +506,19 @@ gdn_status run_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     L.d_o = d_o; L.d_state_out = d_state_out; L.d_state_in = d_state_in;
     L.dq = dq; L.dk = dk; L.dv = dv; L.dgamma = dgamma; L.dbeta = dbeta;
     char* w = (char*)ws;
+    if (pl.fused) {
+        L.bwd_chain = 1;
+        L.spin_limit = fused_spin_limit();
+        L.ctl = (int*)w;               w += align256(pl.ctl_bytes);
+        L.chain = (float*)w;           w += align256(pl.chain_bytes);
+    }
     L.canon = w;                       w += align256(pl.canon_bytes);
     L.part = (float*)w;                w += align256(pl.part_bytes);
     L.mt = w;                          w += align256(pl.mt_bytes);
     L.crec = w;                        w += align256(pl.crec_bytes);
     L.gt = w;
+    // bytes per frame record of Ghat (and Bhat): the products' full record, or the saved planes
+    L.rec_stride = (p->use_delta ? (D / 16) * 2 * ((D + 31) / 32) * 1024 : 0) + 4 * D * D;
     if (saved) {
         L.saved = 1;
         L.canon = const_cast<void*>(saved);

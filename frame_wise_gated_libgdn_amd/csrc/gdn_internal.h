@@ -40,6 +40,9 @@ struct Launch {
     void* save_recs;     // ... and the frames' Ghat planes ([B*H][F] records of rec_stride bytes)
     int64_t rec_stride;  // bytes per frame record read by the scan (0: the full record)
     int saved;           // backward: states and Ghat records come from a forward's saved buffer
+    int bwd_chain;       // backward: the reverse chain inside the Q/dO kernel, ticket-ordered
+                         //   (ctl, chain and spin_limit as in the fused forward; one flag per
+                         //   (b, h) at ctl[2 + bh * kChainGroups]: the last published step)
     int nsplit;          // S splits of the gram products
     int split_tokens;    // tokens per split (multiple of 64)
     int nchunk;          // S chunks of the output products

@@ -1392,52 +1392,87 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
 }
 
 // ----------------------------------------------------------------------------------------
-// Backward, per (b, h, f, token split): the two products that need Q and dO,
+// Backward, per (b, h, f): the two products that need Q and dO,
 //     C_f = Q_f^T dO_f  (the per-frame term of the reverse chain)   and   dQ_f = dO_f M_f^T,
 // in one pass over Q and dO (dQ needs only the forward state M_f, not G_f). Chunks of 64 tokens
 // of Q and dO go through registers into LDS as rows (token-major, as in memory); the next
 // chunk's loads are in flight while the current chunk is used. C contracts over tokens on MFMA
-// with both operands read transposed from the row tiles (ds_read_tr16_b64): A = Q^T, B = dO,
-// and lane (r, g) of the C tile for feature tiles (ja, jb) holds C[i0 + q][out_col(jb, r)],
-// i0 = out_col(ja, 4 g); each of the four waves owns a quarter of C. dQ^T = M_f dO^T runs with
-// A = M_f read transposed from an LDS copy of M_f^T and B = dO rows: wave w takes the 16 chunk
-// rows out_col(w, r), r = 0..15. Every LDS matrix uses the swizzled layout of sw_mask. With one split C goes to the per-frame record the
-// reverse scan reads (the no-delta record layout of the gram products), with several to fp32
-// partials that combine_kernel sums. Q and dO are read through L.q and L.d_o with their own
-// strides; the record (or partial) buffer is L.canon (L.part).
+// with both operands read transposed from the row tiles (ds_read_tr16_b64): A = Q^T, B = dO.
+// Wave w owns the C row tiles ja = RW w .. RW w + RW - 1 against every column tile jb; lane
+// (r, g) of tile (ja, jb) holds C[i0 + q][out_col(jb, r)], i0 = out_col(ja, 4 g), q = 0..3
+// ("C layout" below). dQ^T = M_f dO^T runs with A = M_f read transposed from an LDS copy of
+// M_f^T and B = dO rows: wave w takes the 16 chunk rows out_col(w, r), r = 0..15. Every LDS
+// matrix uses the swizzled layout of sw_mask. Q and dO are read through L.q and L.d_o with
+// their own strides.
+//
+// Without CHAIN, one workgroup per (b, h, f, token split): C goes to the per-frame record the
+// reverse scan reads (L.canon, the no-delta record layout of the gram products), or with
+// several splits to fp32 partials (L.part) that combine_kernel sums.
+//
+// With CHAIN (whole frames), the reverse chain runs inside the kernel, ticket-ordered like the
+// fused forward: ticket k takes frame t = F - 1 - k / BH of (b h) = k mod BH, and after its
+// pass over Q and dO the workgroup forms
+//     G_t = gamma_{t+1} G_{t+1} - Ghat_{t+1} G_{t+1} + C_t      (step u = F - 1 - t)
+// from G_{t+1}, which the workgroup of ticket k - BH published (G_F = dstate_out, or zero, with
+// gamma_F = 1 and Ghat_F = 0), and publishes G_t in turn. Ghat_{t+1} comes from the forward's
+// per-frame records (L.canon, L.rec_stride bytes apart, +Ghat as bf16 hi/lo planes); the
+// product Ghat G runs on MFMA with both operands split into hi + lo (hi.hi + hi.lo + lo.hi),
+// G_{t+1} as the B operand from LDS planes [column][row]. G_t goes to the state-gradient slot
+// t + 1 (fp32, transposed) for the gradient kernel; the workgroup of frame 0 also forms
+// dstate_in = gamma_0 G_0 - Ghat_0 G_0. A workgroup only waits for a smaller ticket, whose
+// workgroup is already running, so the chain always completes. Hand-off as in the fused
+// forward: G moves through two fp32 buffers per (b, h) (step u writes buffer u mod 2) with
+// device-coherent (sc1) accesses in the lanes' own order, in kBwdChainGroups groups of columns
+// with one flag each (the last step that published the group), so that the next frame starts
+// on a group as soon as it is published; the wait is bounded by L.spin_limit polls, after
+// which the workgroup raises the time-out flag L.ctl[1], continues with a NaN G_{t+1} (visible
+// in every later gradient) and still publishes.
 constexpr int kQdoThreads = 256;
+constexpr int kBwdChainGroups = 4;   // column groups of the backward's chain hand-off
 
 // Barrier for LDS hand-offs only: waits for this wave's LDS accesses, not for its global loads
 // and stores (__syncthreads would also drain the prefetch of the next chunk and the dQ stores).
 __device__ __forceinline__ void lds_sync() { __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int D>
+template <int D, bool CHAIN, bool DELTA>
 __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
     using MM = Mma<bf16>;
     constexpr int NW = kQdoThreads / 64;
     constexpr int SC = 16 * NW;              // tokens per chunk: one 16-token dQ tile per wave
     constexpr int CT = D / 16, CP = CT / 2, KS = D / 32;
-    constexpr int TA = CT / 2, TB = CT / 2;  // C tiles of a wave: TA feature tiles of Q x TB of dO
+    constexpr int RW = CT / NW;              // C row tiles per wave
     constexpr int FB = D / 8;                // 16-byte blocks per token row
     constexpr int NLD = SC * FB / kQdoThreads;
     static_assert(D == 64 || D == 128, "backward: D = 64 or 128");
     static_assert(NW == 4 && (SC * FB) % kQdoThreads == 0 && (D * FB) % kQdoThreads == 0,
                   "four waves, whole rows per chunk");
+    static_assert(!CHAIN || 2 * D * D <= (D + 2 * SC) * D, "the G planes fit in the chunk LDS");
     __shared__ __attribute__((aligned(16))) bf16 sm[(D + 2 * SC) * D];   // swizzled (sw_mask)
+    __shared__ int s_ticket, s_ok;
     bf16* Mn = sm;               // M_f^T [c][n]
     bf16* Qt = sm + D * D;       // Q chunk [token][feature]
     bf16* Ot = Qt + SC * D;      // dO chunk [token][feature]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    int blk = blockIdx.x;
-    const int p = blk % L.nsplit;
-    blk /= L.nsplit;
-    const int F = L.F, S = L.S;
-    const int f = blk % F, bh = blk / F;
+    const int F = L.F, S = L.S, BH = L.B * L.H;
+    int f, bh, p;
+    if constexpr (CHAIN) {
+        if (tid == 0) s_ticket = atomicAdd(&L.ctl[0], 1);
+        __syncthreads();
+        f = F - 1 - s_ticket / BH;
+        bh = s_ticket % BH;
+        p = 0;
+    } else {
+        int blk = blockIdx.x;
+        p = blk % L.nsplit;
+        blk /= L.nsplit;
+        f = blk % F;
+        bh = blk / F;
+    }
     const int b = bh / L.H, h = bh % L.H;
     const int gi = bh * F + f;
-    const int t0 = p * L.split_tokens, t1 = min(S, t0 + L.split_tokens);
+    const int t0 = CHAIN ? 0 : p * L.split_tokens, t1 = CHAIN ? S : min(S, t0 + L.split_tokens);
     const int64_t io = (int64_t)b * L.sb + (int64_t)h * L.sh + (int64_t)f * S * L.st;
     const bf16* qf = (const bf16*)L.q + io;
     bf16* dqf = (bf16*)L.dq + io;
@@ -1456,8 +1491,8 @@ __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
         for (int k = 0; k < PT; ++k) {
             const int e = tid + k * kQdoThreads;
             st16_sw<D>(Mn, e / FB, (e % FB) * 8,
-                 u32x4{pack_bf16x2(x[k][0][0], x[k][0][1]), pack_bf16x2(x[k][0][2], x[k][0][3]),
-                       pack_bf16x2(x[k][1][0], x[k][1][1]), pack_bf16x2(x[k][1][2], x[k][1][3])});
+                       u32x4{pack_bf16x2(x[k][0][0], x[k][0][1]), pack_bf16x2(x[k][0][2], x[k][0][3]),
+                             pack_bf16x2(x[k][1][0], x[k][1][1]), pack_bf16x2(x[k][1][2], x[k][1][3])});
         }
     }
 
@@ -1473,12 +1508,12 @@ __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
         }
     };
 
-    f32x4 acc[TA][TB];
+    f32x4 acc[RW][CT];
 #pragma unroll
-    for (int a = 0; a < TA; ++a)
+    for (int a = 0; a < RW; ++a)
 #pragma unroll
-        for (int bb = 0; bb < TB; ++bb) acc[a][bb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int ja0 = TA * (wave & 1), jb0 = TB * (wave >> 1);
+        for (int jb = 0; jb < CT; ++jb) acc[a][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ja0 = RW * wave;
 
     load(t0);
     for (int c0 = t0; c0 < t1; c0 += SC) {
@@ -1496,23 +1531,21 @@ __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
         // tokens k0 + 8 g + 0..7, the same in both operands)
 #pragma unroll
         for (int k0 = 0; k0 < SC; k0 += 32) {
-            bf16x8 af[TA], bf[TB];
+            bf16x8 af[RW];
 #pragma unroll
-            for (int a = 0; a < TA; ++a) {
+            for (int a = 0; a < RW; ++a) {
                 const u32x2 x0 = read_tr4<D>(Qt, k0, ja0 + a, r16, 2 * g);
                 const u32x2 x1 = read_tr4<D>(Qt, k0 + 4, ja0 + a, r16, 2 * g);
                 af[a] = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
             }
 #pragma unroll
-            for (int bb = 0; bb < TB; ++bb) {
-                const u32x2 x0 = read_tr4<D>(Ot, k0, jb0 + bb, r16, 2 * g);
-                const u32x2 x1 = read_tr4<D>(Ot, k0 + 4, jb0 + bb, r16, 2 * g);
-                bf[bb] = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+            for (int jb = 0; jb < CT; ++jb) {
+                const u32x2 x0 = read_tr4<D>(Ot, k0, jb, r16, 2 * g);
+                const u32x2 x1 = read_tr4<D>(Ot, k0 + 4, jb, r16, 2 * g);
+                const bf16x8 bfr = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+#pragma unroll
+                for (int a = 0; a < RW; ++a) acc[a][jb] = MM::run(af[a], bfr, acc[a][jb]);
             }
-#pragma unroll
-            for (int a = 0; a < TA; ++a)
-#pragma unroll
-                for (int bb = 0; bb < TB; ++bb) acc[a][bb] = MM::run(af[a], bf[bb], acc[a][bb]);
         }
 
         // dQ^T = M_f dO^T for the wave's 16 tokens (chunk rows out_col(wave, r): the fragment
@@ -1541,19 +1574,214 @@ __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
         }
     }
 
-    // C tile (a, bb): lane (r, g) holds C[i0 + q][j], i0 = 32 (ja >> 1) + 8 g + 4 (ja & 1)
+    // row of C-layout register q of tile (a, .) is ri(a) + q; column of tile jb is out_col(jb, r)
+    auto ri = [&](int a) { const int ja = ja0 + a; return 32 * (ja >> 1) + 8 * g + 4 * (ja & 1); };
+
+    if constexpr (!CHAIN) {
 #pragma unroll
-    for (int a = 0; a < TA; ++a) {
-        const int ja = ja0 + a;
-        const int i0 = 32 * (ja >> 1) + 8 * g + 4 * (ja & 1);
+        for (int a = 0; a < RW; ++a) {
+            const int i0 = ri(a);
 #pragma unroll
-        for (int bb = 0; bb < TB; ++bb) {
-            const int j = out_col<bf16, D>(jb0 + bb, r16);
-            if (L.nsplit == 1)
-                *(f32x4*)((float*)((char*)L.canon + (int64_t)gi * canon_bytes<D, false>()) + rec_b_off<D>(i0, j)) =
-                    acc[a][bb];
-            else
-                *(f32x4*)(L.part + ((int64_t)gi * L.nsplit + p) * (D * D) + j * D + i0) = acc[a][bb];
+            for (int jb = 0; jb < CT; ++jb) {
+                const int j = out_col<bf16, D>(jb, r16);
+                if (L.nsplit == 1)
+                    *(f32x4*)((float*)((char*)L.canon + (int64_t)gi * canon_bytes<D, false>()) + rec_b_off<D>(i0, j)) =
+                        acc[a][jb];
+                else
+                    *(f32x4*)(L.part + ((int64_t)gi * L.nsplit + p) * (D * D) + j * D + i0) = acc[a][jb];
+            }
+        }
+    } else {
+        const int u = F - 1 - f;   // chain step
+        // dst -= Ghat_fr src, with src (fp32, C layout) split into bf16 hi/lo planes
+        // [column][row] in LDS as the B operand and Ghat_fr (A rows out_col(ja, r), i.e. the
+        // C-layout rows ri(a) + q of the product) from frame fr's record
+        auto ghat_step = [&](const f32x4 (&src)[RW][CT], f32x4 (&dst)[RW][CT], int fr) {
+            bf16* Ph = sm;
+            bf16* Pl = sm + D * D;
+            __syncthreads();   // earlier readers of the LDS are done
+#pragma unroll
+            for (int a = 0; a < RW; ++a)
+#pragma unroll
+                for (int jb = 0; jb < CT; ++jb) {
+                    const int j = out_col<bf16, D>(jb, r16);
+                    const int off = j * D + (((ri(a) >> 2) ^ sw_mask<D>(j)) << 2);
+                    store_split4(Ph + off, Pl + off, src[a][jb]);
+                }
+            __syncthreads();
+            constexpr int KSN = rec_ksn<D>();
+            const char* rec = (const char*)L.canon + ((int64_t)bh * F + fr) * L.rec_stride;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 ah[RW], al[RW];
+#pragma unroll
+                for (int a = 0; a < RW; ++a) {
+                    const int m = out_col<bf16, D>(ja0 + a, r16);
+                    const char* fa = rec + (((m >> 4) * 2) * KSN + ks) * 1024 + (16 * g + (m & 15)) * 16;
+                    ah[a] = ld_frag<bf16>((const bf16*)fa);
+                    al[a] = ld_frag<bf16>((const bf16*)(fa + KSN * 1024));
+                }
+#pragma unroll
+                for (int jb = 0; jb < CT; ++jb) {
+                    const int j = out_col<bf16, D>(jb, r16);
+                    const bf16x8 bh_ = ld16_sw<D>(Ph, j, 32 * ks + 8 * g);
+                    const bf16x8 bl_ = ld16_sw<D>(Pl, j, 32 * ks + 8 * g);
+#pragma unroll
+                    for (int a = 0; a < RW; ++a) {
+                        f32x4 x = MM::run(ah[a], bh_, f32x4{0.f, 0.f, 0.f, 0.f});
+                        x = MM::run(ah[a], bl_, x);
+                        x = MM::run(al[a], bh_, x);
+                        dst[a][jb] -= x;
+                    }
+                }
+            }
+        };
+
+        // The step runs over kBwdChainGroups groups of column tiles (columns of G evolve
+        // independently): group c of G_t needs only group c of G_{t+1}, so the next frame's
+        // workgroup starts on group c as soon as this one has published it, and the
+        // frame-to-frame period is one group's latency.
+        constexpr int CG = kBwdChainGroups, TPG = CT / CG;   // groups, column tiles per group
+        static_assert(CT % CG == 0 && CG <= kChainGroups, "column tiles split evenly into groups");
+        int* flags = L.ctl + 2 + bh * kChainGroups;
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_over(L.chain + ((int64_t)((u + 1) & 1) * BH + bh) * D * D, D * D * 4);   // G_{t+1}
+        const __amdgpu_buffer_rsrc_t rd =
+            buffer_over(L.chain + ((int64_t)(u & 1) * BH + bh) * D * D, D * D * 4);         // G_t
+        auto cidx = [&](int a, int jb) { return (((wave * RW + a) * CT + jb) * 64 + lane) * 16; };
+        const float gnext = u > 0 ? L.gamma[gi + 1] : 1.f;
+
+        // Ghat_{t+1} rows of this wave (A operand, hi and lo, every k step), loaded before the
+        // first wait
+        constexpr int KSN = rec_ksn<D>();
+        bf16x8 ga[DELTA ? RW : 1][DELTA ? KS : 1][2];
+        if constexpr (DELTA) {
+            if (u > 0) {
+                const char* rec = (const char*)L.canon + ((int64_t)bh * F + f + 1) * L.rec_stride;
+#pragma unroll
+                for (int a = 0; a < RW; ++a) {
+                    const int m = out_col<bf16, D>(ja0 + a, r16);
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const char* fa = rec + (((m >> 4) * 2) * KSN + ks) * 1024 + (16 * g + (m & 15)) * 16;
+                        ga[a][ks][0] = ld_frag<bf16>((const bf16*)fa);
+                        ga[a][ks][1] = ld_frag<bf16>((const bf16*)(fa + KSN * 1024));
+                    }
+                }
+            }
+        }
+        bf16* Ph = sm;            // G_{t+1} planes [column][row], the group's columns only
+        bf16* Pl = sm + D * D;
+#pragma unroll
+        for (int grp = 0; grp < CG; ++grp) {
+            if (tid == 0) {
+                int ok = 1;
+                if (u > 0) {
+                    int polls = 0;
+                    while (L.spin_limit == 0 ||
+                           __hip_atomic_load(flags + grp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < u - 1) {
+                        if (++polls > L.spin_limit) {
+                            ok = 0;
+                            __hip_atomic_store(&L.ctl[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+                s_ok = ok;
+            }
+            // also: the LDS readers of the last chunk (group 0) are done
+            __syncthreads();
+            const bool ok = s_ok != 0;
+            // group grp of G_{t+1} in C layout (dstate_out for t = F - 1)
+            f32x4 gn[RW][TPG];
+#pragma unroll
+            for (int a = 0; a < RW; ++a)
+#pragma unroll
+                for (int jj = 0; jj < TPG; ++jj) {
+                    const int jb = grp * TPG + jj;
+                    if (u > 0) {
+                        gn[a][jj] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, cidx(a, jb), 0, kCoherent));
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            gn[a][jj][q] = L.d_state_out ? L.d_state_out[((int64_t)bh * D + ri(a) + q) * D +
+                                                                         out_col<bf16, D>(jb, r16)]
+                                                         : 0.f;
+                    }
+                }
+            const float nan = __builtin_nanf("");
+            // G_t = C_t + gamma_{t+1} G_{t+1} - Ghat_{t+1} G_{t+1}, for the group's columns
+#pragma unroll
+            for (int a = 0; a < RW; ++a)
+#pragma unroll
+                for (int jj = 0; jj < TPG; ++jj) {
+                    if (!ok) gn[a][jj] = f32x4{nan, nan, nan, nan};
+                    acc[a][grp * TPG + jj] += gnext * gn[a][jj];
+                }
+            if constexpr (DELTA) {
+                if (u > 0) {
+#pragma unroll
+                    for (int a = 0; a < RW; ++a)
+#pragma unroll
+                        for (int jj = 0; jj < TPG; ++jj) {
+                            const int j = out_col<bf16, D>(grp * TPG + jj, r16);
+                            const int off = j * D + (((ri(a) >> 2) ^ sw_mask<D>(j)) << 2);
+                            store_split4(Ph + off, Pl + off, gn[a][jj]);
+                        }
+                    __syncthreads();
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                        for (int jj = 0; jj < TPG; ++jj) {
+                            const int j = out_col<bf16, D>(grp * TPG + jj, r16);
+                            const bf16x8 bh_ = ld16_sw<D>(Ph, j, 32 * ks + 8 * g);
+                            const bf16x8 bl_ = ld16_sw<D>(Pl, j, 32 * ks + 8 * g);
+#pragma unroll
+                            for (int a = 0; a < RW; ++a) {
+                                f32x4 x = MM::run(ga[a][ks][0], bh_, f32x4{0.f, 0.f, 0.f, 0.f});
+                                x = MM::run(ga[a][ks][0], bl_, x);
+                                x = MM::run(ga[a][ks][1], bh_, x);
+                                acc[a][grp * TPG + jj] -= x;
+                            }
+                        }
+                }
+            }
+            // publish group grp of G_t
+#pragma unroll
+            for (int a = 0; a < RW; ++a)
+#pragma unroll
+                for (int jj = 0; jj < TPG; ++jj)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[a][grp * TPG + jj]), rd,
+                                                           cidx(a, grp * TPG + jj), 0, kCoherent);
+            __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are done
+            __syncthreads();                                          // ... and every wave's
+            if (tid == 0) __hip_atomic_store(flags + grp, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        // state-gradient slot t + 1 for the gradient kernel: G_t transposed, [column][row]
+        float* gt = (float*)L.gt + ((int64_t)bh * (F + 1) + f + 1) * D * D;
+#pragma unroll
+        for (int a = 0; a < RW; ++a)
+#pragma unroll
+            for (int jb = 0; jb < CT; ++jb) *(f32x4*)(gt + out_col<bf16, D>(jb, r16) * D + ri(a)) = acc[a][jb];
+
+        // frame 0: dstate_in = gamma_0 G_0 - Ghat_0 G_0
+        if (f == 0 && L.d_state_in) {
+            const float g0 = L.gamma[gi];
+            f32x4 ds[RW][CT];
+#pragma unroll
+            for (int a = 0; a < RW; ++a)
+#pragma unroll
+                for (int jb = 0; jb < CT; ++jb) ds[a][jb] = g0 * acc[a][jb];
+            if constexpr (DELTA) ghat_step(acc, ds, 0);
+#pragma unroll
+            for (int a = 0; a < RW; ++a)
+#pragma unroll
+                for (int jb = 0; jb < CT; ++jb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        L.d_state_in[((int64_t)bh * D + ri(a) + q) * D + out_col<bf16, D>(jb, r16)] = ds[a][jb][q];
         }
     }
 }
@@ -1860,7 +2088,10 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
     }
     case K_BWD_QDO: {
         if constexpr (std::is_same<T, bf16>::value && (D == 64 || D == 128)) {
-            hipLaunchKernelGGL((qdo_kernel<D>), dim3(BH * L.F * L.nsplit), dim3(kQdoThreads), 0, s, L);
+            if (L.bwd_chain)
+                hipLaunchKernelGGL((qdo_kernel<D, true, DELTA>), dim3(BH * L.F), dim3(kQdoThreads), 0, s, L);
+            else
+                hipLaunchKernelGGL((qdo_kernel<D, false, false>), dim3(BH * L.F * L.nsplit), dim3(kQdoThreads), 0, s, L);
         } else {
             return hipErrorInvalidValue;
         }

@@ -9,9 +9,12 @@
 //                   products (output items of the one frame).
 // Temporal conv:    one launch (the whole block or sequence).
 // Attention:        one launch.
-// Backward:         products + [combine] + scan (forward states), products + [combine] of
-//                   C_f = Q_f^T dO_f, reverse scan (state gradients), per-frame gradients;
-//                   the states and state gradients are kept in fp32.
+// Backward:         products + [combine] + scan (forward states) unless a saving forward kept
+//                   them; then either (chained) reset + one ticket-ordered pass over Q and dO
+//                   forming dQ, C_f = Q_f^T dO_f and the reverse chain of state gradients, or
+//                   the same pass without the chain + [combine] + reverse scan; then the
+//                   per-frame gradients of K, V, gamma and beta. States and state gradients are
+//                   kept in fp32.
 #include <vector>
 
 #include "../../include/libgdn.h"
@@ -105,6 +108,13 @@ hipError_t run_backward(const Launch& L0, hipStream_t s) {
         A.scan_out = nullptr;
         A.mt_lead = 1;
         GDN_TRY(run.go(K_SCAN_STATES, A, s, BH * F));
+    }
+    if (L0.bwd_chain) {
+        // 2'. one ticket-ordered pass over Q and dO in descending frame order: dQ_f, C_f and the
+        //     reverse chain G_f (slot f + 1), dstate_in from the workgroup of frame 0
+        GDN_TRY(run.go(K_FUSED_RESET, L0, s, BH));
+        GDN_TRY(run.go(K_BWD_QDO, L0, s, BH * F));
+        return run.go(K_BWD, L0, s, BH * F);
     }
     // 2. one pass over Q and dO: C_f = Q_f^T dO_f of every frame (its per-frame record, in the
     //    no-delta layout of the gram products; S-split partials summed by the combine kernel)

@@ -280,10 +280,19 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
  *     dgamma_f = <G_f, M> - beta_f <Kt G_f, P>,    dbeta_f = <Kt G_f, R>
  *     dstate_in = (gamma_0 I - gamma_0 beta_0 Kt_0^T Kt_0) G_0
  * (without the delta term: R = V_f, dK_f = c beta_f V_f G_f^T, dgamma_f = <G_f, M>, and the
- * chain uses gamma I). The forward states are recomputed inside the call. Launches (trace
- * kinds): the forward states (PRODUCTS, SCAN_STATES), Q_f^T dO_f and dQ in one pass over Q and
- * dO (BWD_QDO), the reverse chain (SCAN_BWD), the gradients of K, V, gamma and beta (BWD);
- * COMBINE follows PRODUCTS and BWD_QDO when frames are split over tokens.
+ * chain uses gamma I). The forward states are recomputed inside the call (PRODUCTS, then
+ * SCAN_STATES; COMBINE between them when frames are split over tokens). p->schedule picks how
+ * the reverse chain G_f runs:
+ *   FUSED    inside the pass over Q and dO that forms Q_f^T dO_f and dQ: workgroups take frames
+ *            in descending order by ticket and hand G_f on through the workspace, as the fused
+ *            forward hands on M_f (trace kinds FUSED_RESET, BWD_QDO, then BWD for the gradients
+ *            of K, V, gamma and beta). Waits are bounded as in the forward
+ *            (GDN_FUSED_SPIN_LIMIT): on time-out a workgroup continues with a NaN G, so every
+ *            earlier frame's gradients and dstate_in are NaN, and sets the int32 time-out flag
+ *            at byte 4 of the workspace; the kernel always ends.
+ *   STAGED   the same pass without the chain (BWD_QDO; COMBINE when frames are split over
+ *            tokens), then the chain as a separate scan (SCAN_BWD), then BWD.
+ *   AUTO     FUSED once B*H*F >= 1024, else STAGED.
  *   q, k, v, gamma, beta, state_in   the forward's inputs (state_in NULL: zero)
  *   d_o          dL/dO, layout of o (o_stride_*)
  *   d_state_out  dL/dstate_out fp32 [B][H][D][D], or NULL for zero
@@ -318,7 +327,8 @@ gdn_status gdn_backward_framewise(const gdn_problem* p, const void* q, const voi
  * `saved` (it does not read state_in: slot 0 holds it) and computes what
  * gdn_backward_framewise computes, from the forward's own states (so the two agree to
  * rounding: the fused forward and the backward's own scan round differently); its workspace
- * is gdn_workspace_size(p, 3) bytes.
+ * is gdn_workspace_size(p, 3) bytes. p->schedule picks the reverse chain's schedule as for
+ * gdn_backward_framewise (the forward's FUSED schedule does not depend on it).
  */
 gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes_out);
 gdn_status gdn_forward_framewise_save(const gdn_problem* p, const void* q, const void* k,

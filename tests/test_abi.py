@@ -255,6 +255,28 @@ def test_backward_workspace():
     assert gdn.load().gdn_workspace_size(ctypes.byref(p), 4, ctypes.byref(n4)) == 2
 
 
+def test_backward_chain_workspace():
+    """The chained schedule (explicit, or AUTO once B*H*F >= 1024) puts the ticket counter, the
+    time-out flag (byte 4) and one flag per (b, h) and column group first, then two fp32
+    state-gradient buffers per (b, h), and keeps no C_f records."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    B, H, D, F = 1, 2, 64, 30
+    staged, fused = prob(F=F), prob(F=F)
+    staged.schedule, fused.schedule = 1, 2
+    crec = B * H * F * D * D * 4
+    extra = a256((2 + B * H * 4) * 4) + a256(2 * B * H * D * D * 4)
+    for mode in (2, 3):
+        ns, nf = gdn.workspace_size(staged, mode), gdn.workspace_size(fused, mode)
+        assert nf == ns - a256(crec) + extra, (mode, ns, nf)
+    assert gdn.workspace_size(prob(F=30), 2) == gdn.workspace_size(staged, 2)        # AUTO, 60 items
+    big = prob(H=4, S=8, F=256)                                                       # AUTO, 1024 items
+    big_f = prob(H=4, S=8, F=256)
+    big_f.schedule = 2
+    assert gdn.workspace_size(big, 2) == gdn.workspace_size(big_f, 2)
+    assert gdn.workspace_size(big, 3) == gdn.workspace_size(big_f, 3)
+
+
 def test_saved_size():
     # B=1, H=2, D=64, F=30, delta: Ghat planes (hi + lo bf16, D/16 x 2 x 2 fragments of 1 KB
     # per frame), then 256-byte aligned fp32 states for F + 1 slots

@@ -30,7 +30,7 @@ def bf16_round(x):
     return gdn_synth.bf16_bits_to_f32(gdn_synth.f32_to_bf16_bits(np.asarray(x, np.float32)))
 
 
-def run_case(B, H, D, S, F, delta, with_state, with_dm, layout, seed):
+def run_case(B, H, D, S, F, delta, with_state, with_dm, layout, seed, schedule="auto"):
     rng = np.random.default_rng(seed)
     q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
     d_o = bf16_round(rng.standard_normal((B, H, F * S, D)))
@@ -43,7 +43,7 @@ def run_case(B, H, D, S, F, delta, with_state, with_dm, layout, seed):
     tg, tb = torch.from_numpy(g).to(DEV), torch.from_numpy(b).to(DEV)
     ts0 = None if s0 is None else torch.from_numpy(s0).to(DEV)
     tdm = None if dm is None else torch.from_numpy(dm).to(DEV)
-    got = gdn.backward_framewise(*dev, tg, tb, ddo, ts0, tdm, use_delta=delta)
+    got = gdn.backward_framewise(*dev, tg, tb, ddo, ts0, tdm, use_delta=delta, schedule=schedule)
     torch.cuda.synchronize()
     ref = oracle.backward(q, k, v, g, b, s0, d_o, dm, use_delta=delta)
     return got, ref
@@ -62,10 +62,13 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("schedule", ["staged", "fused"])
 @pytest.mark.parametrize("case", CASES, ids=["-".join(map(str, c)) for c in CASES])
-def test_backward_matches_oracle(case):
-    say("backward", case)
-    got, ref = run_case(*case, seed=zlib.crc32(repr(case).encode()))
+def test_backward_matches_oracle(case, schedule):
+    """Both schedules of the reverse chain: a separate scan (staged) and the ticket-ordered chain
+    inside the pass over Q and dO (fused)."""
+    say("backward", schedule, case)
+    got, ref = run_case(*case, seed=zlib.crc32(repr(case).encode()), schedule=schedule)
     errs = {}
     for name, x, r in zip(NAMES, got, ref):
         errs[name] = rel_err(to_np(x), r)
@@ -143,12 +146,14 @@ SAVED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("schedule", ["staged", "fused"])
 @pytest.mark.parametrize("case", SAVED_CASES, ids=["-".join(map(str, c)) for c in SAVED_CASES])
-def test_backward_from_saved_forward(case):
+def test_backward_from_saved_forward(case, schedule):
     """forward_framewise_save gives the fused forward's outputs bitwise and keeps the states (slot
     0 = the initial state and slot F = the final state, transposed, bitwise); the backward from
-    that buffer matches the oracle and the recomputing backward."""
-    say("backward from saved", case)
+    that buffer (either schedule of the reverse chain) matches the oracle and the recomputing
+    backward."""
+    say("backward from saved", schedule, case)
     B, H, D, S, F, delta, with_state, with_dm, layout = case
     rng = np.random.default_rng(zlib.crc32(repr(case).encode()) + 1)
     q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
@@ -164,8 +169,8 @@ def test_backward_from_saved_forward(case):
     tdm = None if dm is None else torch.from_numpy(dm).to(DEV)
     o_f, st_f = gdn.forward_framewise(*dev, tg, tb, ts0, use_delta=delta, schedule="fused")
     o_s, st_s, saved = gdn.forward_framewise_save(*dev, tg, tb, ts0, use_delta=delta)
-    got = gdn.backward_framewise(*dev, tg, tb, ddo, None, tdm, use_delta=delta, saved=saved)
-    rec = gdn.backward_framewise(*dev, tg, tb, ddo, ts0, tdm, use_delta=delta)
+    got = gdn.backward_framewise(*dev, tg, tb, ddo, None, tdm, use_delta=delta, saved=saved, schedule=schedule)
+    rec = gdn.backward_framewise(*dev, tg, tb, ddo, ts0, tdm, use_delta=delta, schedule=schedule)
     torch.cuda.synchronize()
     assert torch.equal(o_f, o_s) and torch.equal(st_f, st_s)
     p = gdn.Problem(B, H, D, S, F, gdn.GDN_BF16, int(delta), 0.0, 0, 0, D, 0, 0, D)
@@ -182,3 +187,64 @@ def test_backward_from_saved_forward(case):
     say("  vs recomputing " + " ".join("%s %.2e" % kv for kv in agree.items()))
     assert max(errs.values()) <= TOL["bf16"], errs
     assert max(agree.values()) <= TOL["bf16"], agree
+
+
+def test_backward_chain_deterministic_and_in_place():
+    """The chained schedule: bitwise repeatable, and the state gradient may overwrite dstate_out."""
+    B, H, D, S, F = 1, 3, 128, 150, 6
+    rng = np.random.default_rng(53)
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    d_o = bf16_round(rng.standard_normal((B, H, F * S, D)))
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    dm = (0.1 * rng.standard_normal((B, H, D, D))).astype(np.float32)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV),
+                                                          to_dev(d_o, "bf16", DEV)]
+    tdm = torch.from_numpy(dm).to(DEV)
+    r1 = gdn.backward_framewise(*args, None, tdm.clone(), schedule="fused")
+    r2 = gdn.backward_framewise(*args, None, tdm.clone(), schedule="fused")
+    inplace = tdm.clone()
+    r3 = gdn.backward_framewise(*args, None, inplace, schedule="fused", return_state_grad=False)
+    torch.cuda.synchronize()
+    for a, c in zip(r1, r2):
+        assert torch.equal(a, c), "chained backward is not bitwise repeatable"
+    for a, c in zip(r1[:5], r3[:5]):
+        assert torch.equal(a, c)
+
+
+def test_backward_chain_time_out_path(monkeypatch):
+    """The chain's bounded wait, forced from the host: with GDN_FUSED_SPIN_LIMIT=0 every step
+    after the first gives up at once and continues with a NaN state gradient, so the gradients
+    of every frame but the last that depend on G (dK, dV, dgamma, dbeta, dstate_in) are NaN,
+    dQ (which needs no G) stays finite, the time-out flag at byte 4 of the workspace is set and
+    the kernel ends; without the override the same call is finite."""
+    B, H, D, S, F = 1, 2, 64, 64, 4
+    rng = np.random.default_rng(59)
+    q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
+    d_o = bf16_round(rng.standard_normal((B, H, F * S, D)))
+    g = rng.uniform(0.85, 1.0, (B, H, F)).astype(np.float32)
+    b = rng.uniform(0.1, 0.9, (B, H, F)).astype(np.float32)
+    args = [to_dev(x, "bf16", DEV) for x in (q, k, v)] + [torch.from_numpy(g).to(DEV),
+                                                          torch.from_numpy(b).to(DEV),
+                                                          to_dev(d_o, "bf16", DEV)]
+    p = gdn._problem(args[0], args[5], F, True, None, "fused")
+    ws = torch.zeros(gdn.workspace_size(p, 2), dtype=torch.uint8, device=DEV)
+    monkeypatch.setenv("GDN_FUSED_SPIN_LIMIT", "0")
+    bad = gdn.backward_framewise(*args, schedule="fused", workspace=ws)
+    torch.cuda.synchronize()
+    flag = int(ws[4:8].view(torch.int32).item())
+    monkeypatch.delenv("GDN_FUSED_SPIN_LIMIT")
+    good = gdn.backward_framewise(*args, schedule="fused", workspace=ws)
+    torch.cuda.synchronize()
+    assert flag == 1
+    assert int(ws[4:8].view(torch.int32).item()) == 0
+    dq, dk, dv, dg, db, dsi = bad
+    assert torch.isfinite(dq).all()
+    last = slice((F - 1) * S, F * S)
+    assert torch.isfinite(dk[:, :, last]).all() and torch.isfinite(dv[:, :, last]).all()
+    assert torch.isnan(dk[:, :, :(F - 1) * S].float()).all() and torch.isnan(dv[:, :, :(F - 1) * S].float()).all()
+    assert torch.isnan(dg[:, :, :F - 1]).all() and torch.isnan(db[:, :, :F - 1]).all()
+    assert torch.isnan(dsi).all()
+    for t in good:
+        assert torch.isfinite(t.float()).all()

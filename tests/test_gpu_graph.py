@@ -2,10 +2,10 @@
 
 Every call only launches kernels on the caller's stream (no memset or copy nodes), so it can be
 captured. The graph below holds the fused and staged forwards, both step paths, the saving
-forward with the backward from its buffer, the recomputing backward, the temporal convolution and
-the attention; it is replayed several times with eager work (clearing the outputs) and
-synchronisations between the replays, and every replay must reproduce the eager results bitwise
-(the kernels are deterministic).
+forward with the backward from its buffer, the recomputing backward, both schedules of the
+backward's reverse chain, the temporal convolution and the attention; it is replayed several
+times with eager work (clearing the outputs) and synchronisations between the replays, and every
+replay must reproduce the eager results bitwise (the kernels are deterministic).
 """
 import sys
 
@@ -42,10 +42,10 @@ def test_graph_capture_and_replay():
     bt = torch.randn((64,), device=DEV) * 0.1
 
     # outputs and workspaces allocated before the capture
-    def problem(x, F_, o_strides=None):
+    def problem(x, F_, o_strides=None, schedule=0):
         st = x.stride()[:3]
         return gdn.Problem(B, H, D, S, F_, gdn.GDN_BF16 if x.dtype == torch.bfloat16 else gdn.GDN_F32,
-                           1, 0.0, *st, *(o_strides or st), 0)
+                           1, 0.0, *st, *(o_strides or st), schedule)
 
     def ws(p, mode):
         return torch.empty(gdn.workspace_size(p, mode), dtype=torch.uint8, device=DEV)
@@ -62,6 +62,11 @@ def test_graph_capture_and_replay():
     ws_b3 = ws(pf, 3)
     grads_r = [torch.empty_like(q) for _ in range(3)]
     ws_b2 = ws(pf, 2)
+    pc = problem(q, F, schedule=2)
+    grads_c = [torch.empty_like(q) for _ in range(3)]
+    ws_c2 = ws(pc, 2)
+    grads_cs = [torch.empty_like(q) for _ in range(3)]
+    ws_c3 = ws(pc, 3)
     yt, ct = torch.empty_like(xt), torch.empty((1, 8, 64), device=DEV, dtype=torch.bfloat16)
     oa = torch.empty_like(q)
 
@@ -81,6 +86,11 @@ def test_graph_capture_and_replay():
                                                   workspace=ws_b3)
         out["bwd"] = gdn.backward_framewise(q, k, v, g, b, d_o, s0, None, dq=grads_r[0], dk=grads_r[1],
                                             dv=grads_r[2], workspace=ws_b2)
+        out["bwd_chain"] = gdn.backward_framewise(q, k, v, g, b, d_o, s0, None, dq=grads_c[0], dk=grads_c[1],
+                                                  dv=grads_c[2], workspace=ws_c2, schedule="fused")
+        out["bwd_chain_saved"] = gdn.backward_framewise(q, k, v, g, b, d_o, None, None, dq=grads_cs[0],
+                                                        dk=grads_cs[1], dv=grads_cs[2], saved=saved,
+                                                        workspace=ws_c3, schedule="fused")
         out["tconv"] = gdn.temporal_conv(xt, wt, bt, block_frames=2, out=yt, cache_out=ct)
         out["attn"] = gdn.attention_framecausal(q, k, v, tokens_per_frame=S, out=oa)
         return out
