@@ -93,8 +93,15 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
+    // XCD-aware order: workgroup i runs on XCD i mod 8; XCD x takes the contiguous stretch
+    // [x n8, (x + 1) n8) of the (b h)-major, query-block-minor order, so that the workgroups
+    // resident on one XCD are neighbouring query blocks of the same head and share its K/V tiles
+    // through that XCD's L2 (the grid is padded to 8 n8 workgroups; the padding returns at once)
     const int nqb = (L.Tq + kQB - 1) / kQB;
-    const int bh = blockIdx.x / nqb, qb = blockIdx.x % nqb;
+    const int n8 = (L.B * L.H * nqb + 7) / 8;
+    const int item = (int)(blockIdx.x % 8) * n8 + (int)(blockIdx.x / 8);
+    if (item >= L.B * L.H * nqb) return;
+    const int bh = item / nqb, qb = item % nqb;
     const int b = bh / L.H, h = bh % L.H;
     const int qw0 = qb * kQB + wave * kQW;    // first query of this wave
 
@@ -264,7 +271,8 @@ bool attn_supported(int D) { return D == 64 || D == 128; }
 
 template <int D, int QT> hipError_t launch_qt(const AttnLaunch& L, hipStream_t s) {
     constexpr int kQB = 4 * 16 * QT;
-    const int64_t blocks = (int64_t)L.B * L.H * ((L.Tq + kQB - 1) / kQB);
+    const int64_t items = (int64_t)L.B * L.H * ((L.Tq + kQB - 1) / kQB);
+    const int64_t blocks = (items + 7) / 8 * 8;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_kernel<D, QT>), dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, L);
     return hipGetLastError();
