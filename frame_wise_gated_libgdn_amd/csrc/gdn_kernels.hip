@@ -1424,9 +1424,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
 // forward: G moves through two fp32 buffers per (b, h) (step u writes buffer u mod 2) with
 // device-coherent (sc1) accesses in the lanes' own order, in kBwdChainGroups groups of columns
 // with one flag each (the last step that published the group), so that the next frame starts
-// on a group as soon as it is published; the wait is bounded by L.spin_limit polls, after
-// which the workgroup raises the time-out flag L.ctl[1], continues with a NaN G_{t+1} (visible
-// in every later gradient) and still publishes.
+// on a group as soon as it is published. Step u + 2 writes a group of buffer u mod 2 only after
+// step u + 1, the only reader of it, has published that group (after its loads of it were
+// used). The wait is bounded by L.spin_limit polls, after which the workgroup raises the
+// time-out flag L.ctl[1], continues with a NaN G_{t+1} (so the state gradients of frame t and
+// every earlier frame are NaN) and still publishes.
 constexpr int kQdoThreads = 256;
 constexpr int kBwdChainGroups = 4;   // column groups of the backward's chain hand-off
 
