@@ -9,10 +9,11 @@
 //   R(t) = x[t+1] unless t + 1 ends a block or the call (then 0)
 //   cache_out = x[T-1]
 //
-// HBM-bound streaming. A thread owns 16 bytes of channels of one (b, s) and TF consecutive
-// frames: it loads the TF + 2 frames of its window at once (addresses clamped into the tensor,
-// out-of-range values replaced by selects after the loads, so no load sits behind a branch),
-// and writes TF outputs with 16-byte stores. Consecutive threads walk channels, then frame
+// HBM-bound streaming (tconv_kernel; one-frame calls have tconv_frame_kernel below). A thread
+// owns 16 bytes of channels of one (b, s) and TF consecutive frames: it loads the TF + 2 frames
+// of its window at once (addresses clamped into the tensor, out-of-range values replaced by
+// selects after the loads, so no load sits behind a branch), and writes TF outputs with 16-byte
+// stores. Consecutive threads walk channels, then frame
 // chunks, so the one-frame halos of neighbouring chunks are read close together in time (from
 // L2). The thread of the first chunk reads cache_in and writes cache_out, so the two may be the
 // same buffer.
@@ -146,6 +147,68 @@ __global__ __launch_bounds__(kTconvThreads) void tconv_kernel(TconvLaunch L) {
     if (keep_cache) *(u32x4*)((T*)L.cache_out + cache_off) = last;
 }
 
+// One frame (T = 1, a streaming call of a one-frame block): y = bias + w0 * cache_in + w1 * x
+// (the right neighbour is past the call, so zero) and cache_out = x. A thread owns one 16-byte
+// channel chunk at P (b, s) positions, q + p * NQ for p = 0..P-1, so that each of its P slices is
+// coalesced across the threads; it issues all 2 P loads before the first use, the grid is small
+// enough to be resident at once, and the taps are loaded once per thread. Each position's
+// cache_in is read before its cache_out is written by the same thread, so the two may be the
+// same buffer.
+constexpr int kTconvPos = 4;
+
+template <typename T, int P>
+__global__ __launch_bounds__(kTconvThreads) void tconv_frame_kernel(TconvLaunch L) {
+    using V = Vec<T>;
+    constexpr int N = V::N;
+    const uint32_t ncv = (uint32_t)L.C / N;
+    const uint32_t npos = (uint32_t)L.B * (uint32_t)L.S;
+    const uint32_t nq = (npos + P - 1) / P;
+    const uint32_t r = blockIdx.x * (uint32_t)kTconvThreads + threadIdx.x;
+    const int cv = (int)(r % ncv);
+    const uint32_t q = r / ncv;
+    if (q >= nq) return;
+    const int c0 = cv * N;
+
+    u32x4 xv[P], cv_in[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const uint32_t pos = min(q + p * nq, npos - 1);   // past the end: re-read the last (unused)
+        const int b = (int)(pos / (uint32_t)L.S), s = (int)(pos % (uint32_t)L.S);
+        xv[p] = *(const u32x4*)((const T*)L.x + (int64_t)b * L.xsb + (int64_t)s * L.xss + c0);
+        cv_in[p] = L.cache_in ? *(const u32x4*)((const T*)L.cache_in + (int64_t)pos * L.C + c0)
+                              : u32x4{0u, 0u, 0u, 0u};
+    }
+    float w0[N], w1[N], bs[N];
+    {
+        f32x4 tw[3 * N / 4], tb[N / 4];
+#pragma unroll
+        for (int k = 0; k < 3 * N / 4; ++k) tw[k] = *(const f32x4*)(L.weight + 3 * c0 + 4 * k);
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k)
+            tb[k] = L.bias ? *(const f32x4*)(L.bias + c0 + 4 * k) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            w0[j] = tw[(3 * j) / 4][(3 * j) % 4];
+            w1[j] = tw[(3 * j + 1) / 4][(3 * j + 1) % 4];
+            bs[j] = tb[j / 4][j % 4];
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const uint32_t pos = q + p * nq;
+        if (pos < npos) {
+            const int b = (int)(pos / (uint32_t)L.S), s = (int)(pos % (uint32_t)L.S);
+            float cur[N], left[N], out[N];
+            V::unpack(xv[p], cur);
+            V::unpack(cv_in[p], left);
+#pragma unroll
+            for (int j = 0; j < N; ++j) out[j] = __builtin_fmaf(w1[j], cur[j], __builtin_fmaf(w0[j], left[j], bs[j]));
+            *(u32x4*)((T*)L.y + (int64_t)b * L.ysb + (int64_t)s * L.yss + c0) = V::pack(out);
+            if (L.cache_out) *(u32x4*)((T*)L.cache_out + (int64_t)pos * L.C + c0) = xv[p];
+        }
+    }
+}
+
 template <typename T, int TF> hipError_t launch_tf(const TconvLaunch& L, hipStream_t s) {
     constexpr int N = Vec<T>::N;
     const int64_t threads = (int64_t)L.B * L.S * (L.C / N) * ((L.T + TF - 1) / TF);
@@ -155,9 +218,19 @@ template <typename T, int TF> hipError_t launch_tf(const TconvLaunch& L, hipStre
     return hipGetLastError();
 }
 
-// frames per thread: the window fits short calls (a streaming block of one or a few frames)
+// one frame: tconv_frame_kernel; otherwise frames per thread to fit short calls (a streaming
+// block of a few frames) or long ones
 template <typename T> hipError_t launch_t(const TconvLaunch& L, hipStream_t s) {
-    if (L.T <= 1) return launch_tf<T, 1>(L, s);
+    if (L.T <= 1) {
+        constexpr int N = Vec<T>::N;
+        const int64_t nq = ((int64_t)L.B * L.S + kTconvPos - 1) / kTconvPos;
+        const int64_t threads = nq * (L.C / N);
+        const int64_t blocks = (threads + kTconvThreads - 1) / kTconvThreads;
+        if (blocks * kTconvThreads > 0x7FFFFFFF || (int64_t)L.B * L.S > 0x7FFFFFFF)
+            return hipErrorInvalidValue;   // 32-bit indices
+        hipLaunchKernelGGL((tconv_frame_kernel<T, kTconvPos>), dim3((unsigned)blocks), dim3(kTconvThreads), 0, s, L);
+        return hipGetLastError();
+    }
     if (L.T <= 4) return launch_tf<T, 4>(L, s);
     return launch_tf<T, kTconvFrames>(L, s);
 }

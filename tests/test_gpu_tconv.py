@@ -51,6 +51,9 @@ CASES = [
     (2, 17, 4, 32, 17, "f32", True, True, "bstc"),      # one block; frames not outermost
     (1, 3, 2, 8, 3, "bf16", False, False, "btsc"),
     (1, 48, 6, 2048, 3, "bf16", True, True, "bstc"),    # the GDN block's width
+    (2, 1, 7, 64, 1, "bf16", True, True, "btsc"),       # one frame (the streaming call)
+    (1, 1, 5, 24, 1, "f32", False, False, "bstc"),      # one frame, no cache: positions ragged
+    (3, 1, 3, 2048, 1, "bf16", True, False, "bstc"),
 ]
 
 
@@ -91,6 +94,23 @@ def test_tconv_streaming_in_place_cache():
     assert torch.equal(c, xd[:, -1])
     ry, _ = tconv.tconv_stream(f64(x), w, bias, tb, f64(cache))
     assert rel_err(f64(streamed), ry) <= TOL["bf16"]
+
+
+def test_tconv_one_frame_stream_in_place_cache():
+    """One frame per call (the streaming step), cache updated in place: equals the whole sequence
+    in one call bit for bit."""
+    B, T, S, C = 2, 6, 9, 64
+    x, cache, w, bias = make(B, T, S, C, "bf16", 11)
+    xd, wd, bd = x.to(DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(bias).to(DEV)
+    whole, _ = gdn.temporal_conv(xd, wd, bd, cache.to(DEV), block_frames=1)
+    c = cache.to(DEV).clone()
+    parts = []
+    for t in range(T):
+        y, _ = gdn.temporal_conv(xd[:, t:t + 1], wd, bd, c, block_frames=1, cache_out=c)
+        parts.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(parts, dim=1), whole)
+    assert torch.equal(c, xd[:, -1])
 
 
 def test_tconv_deterministic():
