@@ -32,6 +32,7 @@ struct Plan {
     int mode;                   // 0 forward, 1 step, 2 backward, 3 backward from saved states
     bool fused;                 // forward: fused single pass (else staged); step: column
                                 // blocks; backward: the reverse chain in the Q/dO pass
+    bool fused_states;          // backward: the forward states recomputed by the fused forward
     int nsplit, split_tokens;   // partial-product kernel
     int nchunk, chunk_tokens;   // output kernel
     size_t canon_bytes, part_bytes, mt_bytes;   // staged forward and step
@@ -177,6 +178,14 @@ Plan make_plan(const gdn_problem& p, int mode) {
         // 4, as in the fused forward), two fp32 state-gradient buffers per (b, h), no C records
         if (pl.fused) pl.crec_bytes = 0;
         else pl.ctl_bytes = pl.chain_bytes = 0;
+    }
+    if (mode == 2 && pl.fused && fused_rows_fit(p)) {
+        // chained, recomputing: the fused forward (no outputs) recomputes the states into the
+        // layout of a saving forward's buffer: the frames' Ghat planes, then F + 1 fp32 states
+        pl.fused_states = true;
+        pl.canon_bytes = p.use_delta ? (size_t)(BH * F * (D / 16) * 2 * ((D + 31) / 32) * 1024) : 0;
+        pl.part_bytes = 0;
+        pl.mt_bytes = (size_t)(BH * (F + 1) * D * D * 4);
     }
     return pl;
 }
@@ -519,6 +528,12 @@ gdn_status run_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     L.gt = w;
     // bytes per frame record of Ghat (and Bhat): the products' full record, or the saved planes
     L.rec_stride = (p->use_delta ? (D / 16) * 2 * ((D + 31) / 32) * 1024 : 0) + 4 * D * D;
+    if (pl.fused_states) {
+        L.fused_states = 1;
+        L.save_recs = L.canon;
+        L.save_states = (float*)L.mt;
+        L.rec_stride = p->use_delta ? (D / 16) * 2 * ((D + 31) / 32) * 1024 : 0;
+    }
     if (saved) {
         L.saved = 1;
         L.canon = const_cast<void*>(saved);

@@ -40,6 +40,10 @@ struct Launch {
     void* save_recs;     // ... and the frames' Ghat planes ([B*H][F] records of rec_stride bytes)
     int64_t rec_stride;  // bytes per frame record read by the scan (0: the full record)
     int saved;           // backward: states and Ghat records come from a forward's saved buffer
+    int no_output;       // fused forward with save_states: keep the states only, form no outputs
+    int keep_timeout;    // reset of the ticket counter and flags: leave the time-out flag as is
+    int fused_states;    // backward: recompute the forward states with the fused forward
+                         //   (no outputs) into save_recs / save_states, then run as from saved
     int bwd_chain;       // backward: the reverse chain inside the Q/dO kernel, ticket-ordered
                          //   (ctl, chain and spin_limit as in the fused forward; one flag per
                          //   (b, h) at ctl[2 + bh * kChainGroups]: the last published step)

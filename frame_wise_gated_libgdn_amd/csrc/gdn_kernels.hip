@@ -806,9 +806,11 @@ __global__ __launch_bounds__(NT, 2) void products_kernel(Launch L) {
 constexpr int kCoherent = 16;        // cache-policy operand of the buffer intrinsics: sc1
 
 
-__global__ void fused_reset_kernel(int* ctl, int n) {
+// Ticket counter 0, frame flags -1; the time-out flag 0 unless keep_timeout (a second ticketed
+// launch in the same call keeps the first one's time-out visible).
+__global__ void fused_reset_kernel(int* ctl, int n, int keep_timeout) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) ctl[i] = i < 2 ? 0 : -1;
+    if (i < n && !(i == 1 && keep_timeout)) ctl[i] = i < 2 ? 0 : -1;
 }
 
 // SAVE (training): also keep what the backward needs, so that it need not recompute the forward
@@ -816,7 +818,9 @@ __global__ void fused_reset_kernel(int* ctl, int n) {
 // layout at save_recs, and the initial state and every M_f in fp32, transposed, at save_states
 // (slot f + 1 per frame, slot 0 the initial state). These stores come after the frame's flag,
 // so they do not lengthen the frame-to-frame chain.
-template <int D, bool DELTA, bool FP8, bool SAVE = false>
+// OUT = false (with SAVE; the backward's recompute of the forward states): the outputs are
+// not formed, so Q and O are not touched and only K and V stream.
+template <int D, bool DELTA, bool FP8, bool SAVE = false, bool OUT = true>
 __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
     using MM = Mma<bf16>;
     constexpr int SC = 64;          // tokens per staged chunk (128 measured slower for E4M3)
@@ -1073,6 +1077,7 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) so[(nw + 16 * nb + 4 * g + q) * D + 16 * cb + r16] = bacc[nb][cb][q];
     }
+    if constexpr (!OUT) return;
 
     // ---- 3. O_f = Q_f M_f (as output_body, with bf16(M_f)^T from LDS)
     bf16* Mt = (bf16*)lds;  // [c][n]
@@ -2057,13 +2062,15 @@ template <typename T, int D, bool DELTA> static hipError_t launch(Kernel k, cons
     }
     case K_FUSED_RESET: {
         const int n = 2 + BH * kChainGroups;
-        hipLaunchKernelGGL(fused_reset_kernel, dim3((n + NT - 1) / NT), dim3(NT), 0, s, L.ctl, n);
+        hipLaunchKernelGGL(fused_reset_kernel, dim3((n + NT - 1) / NT), dim3(NT), 0, s, L.ctl, n, L.keep_timeout);
         break;
     }
     case K_FUSED: {
         if constexpr (std::is_same<T, bf16>::value && (D == 64 || D == 128)) {
             if (L.fp8)
                 hipLaunchKernelGGL((fused_kernel<D, DELTA, true>), dim3(BH * L.F), dim3(NT), 0, s, L);
+            else if (L.save_states && L.no_output)
+                hipLaunchKernelGGL((fused_kernel<D, DELTA, false, true, false>), dim3(BH * L.F), dim3(NT), 0, s, L);
             else if (L.save_states)
                 hipLaunchKernelGGL((fused_kernel<D, DELTA, false, true>), dim3(BH * L.F), dim3(NT), 0, s, L);
             else

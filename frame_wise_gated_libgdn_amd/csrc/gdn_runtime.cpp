@@ -98,7 +98,15 @@ hipError_t run_backward(const Launch& L0, hipStream_t s) {
     const int F = L0.F;
     // 1. forward states: products of every frame, then the scan, M_f to slot f + 1 (slot 0:
     //    the initial state); taken from a forward's saved buffer instead when given
-    if (!L0.saved) {
+    if (L0.fused_states) {
+        // 1'. the fused forward (ticket-ordered, no outputs) keeps each frame's Ghat planes and
+        //     M_f, laid out as a saving forward's buffer; the rest runs as from saved states
+        Launch A = L0;
+        A.state_out = nullptr;
+        A.no_output = 1;
+        GDN_TRY(run.go(K_FUSED_RESET, A, s, BH));
+        GDN_TRY(run.go(K_FUSED, A, s, BH * F));
+    } else if (!L0.saved) {
         Launch A = L0;
         A.g0 = 0; A.gn = F; A.o0 = 0; A.on = 0;
         GDN_TRY(run.go(K_PRODUCTS, A, s, BH * F));
@@ -112,7 +120,9 @@ hipError_t run_backward(const Launch& L0, hipStream_t s) {
     if (L0.bwd_chain) {
         // 2'. one ticket-ordered pass over Q and dO in descending frame order: dQ_f, C_f and the
         //     reverse chain G_f (slot f + 1), dstate_in from the workgroup of frame 0
-        GDN_TRY(run.go(K_FUSED_RESET, L0, s, BH));
+        Launch R = L0;
+        R.keep_timeout = L0.fused_states;   // a time-out of the recompute stays visible
+        GDN_TRY(run.go(K_FUSED_RESET, R, s, BH));
         GDN_TRY(run.go(K_BWD_QDO, L0, s, BH * F));
         return run.go(K_BWD, L0, s, BH * F);
     }

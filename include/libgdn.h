@@ -281,12 +281,14 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
  *     dstate_in = (gamma_0 I - gamma_0 beta_0 Kt_0^T Kt_0) G_0
  * (without the delta term: R = V_f, dK_f = c beta_f V_f G_f^T, dgamma_f = <G_f, M>, and the
  * chain uses gamma I). The forward states are recomputed inside the call (PRODUCTS, then
- * SCAN_STATES; COMBINE between them when frames are split over tokens). p->schedule picks how
- * the reverse chain G_f runs:
+ * SCAN_STATES, with COMBINE between them when frames are split over tokens; or see FUSED
+ * below). p->schedule picks how the reverse chain G_f runs:
  *   FUSED    inside the pass over Q and dO that forms Q_f^T dO_f and dQ: workgroups take frames
  *            in descending order by ticket and hand G_f on through the workspace, as the fused
  *            forward hands on M_f (trace kinds FUSED_RESET, BWD_QDO, then BWD for the gradients
- *            of K, V, gamma and beta). Waits are bounded as in the forward
+ *            of K, V, gamma and beta). The forward states are then recomputed by the fused
+ *            forward without its outputs (FUSED_RESET, FUSED) when a frame's q/k/v rows lie
+ *            within 2 GiB. Waits are bounded as in the forward
  *            (GDN_FUSED_SPIN_LIMIT): on time-out a workgroup continues with a NaN G, so every
  *            earlier frame's gradients and dstate_in are NaN, and sets the int32 time-out flag
  *            at byte 4 of the workspace; the kernel always ends.

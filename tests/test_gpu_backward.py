@@ -187,6 +187,11 @@ def test_backward_from_saved_forward(case, schedule):
     say("  vs recomputing " + " ".join("%s %.2e" % kv for kv in agree.items()))
     assert max(errs.values()) <= TOL["bf16"], errs
     assert max(agree.values()) <= TOL["bf16"], agree
+    if schedule == "fused":
+        # the chained recompute runs the same fused forward (without outputs), so the two
+        # backwards see the same states and agree bit for bit
+        for n, x, y in zip(NAMES, got, rec):
+            assert torch.equal(x, y), n
 
 
 def test_backward_chain_deterministic_and_in_place():
@@ -214,11 +219,15 @@ def test_backward_chain_deterministic_and_in_place():
 
 
 def test_backward_chain_time_out_path(monkeypatch):
-    """The chain's bounded wait, forced from the host: with GDN_FUSED_SPIN_LIMIT=0 every step
-    after the first gives up at once and continues with a NaN state gradient, so the gradients
-    of every frame but the last that depend on G (dK, dV, dgamma, dbeta, dstate_in) are NaN,
-    dQ (which needs no G) stays finite, the time-out flag at byte 4 of the workspace is set and
-    the kernel ends; without the override the same call is finite."""
+    """The chained schedule's bounded waits, forced from the host: with GDN_FUSED_SPIN_LIMIT=0
+    every step after the first gives up at once, continues with NaN and still ends; the time-out
+    flag at byte 4 of the workspace is set.
+    From saved states only the reverse chain waits: the gradients that depend on G (dK, dV,
+    dgamma, dbeta of every frame but the last, dstate_in) are NaN, dQ is finite.
+    Recomputing, the fused forward that rebuilds the states times out as well: every state
+    after frame 0 is NaN, so dQ is NaN past frame 0 (frame 0's state comes from the initial
+    state without a wait) and so is the last frame's dK (it reads the state before it).
+    Without the override the same calls are finite and the flag is clear."""
     B, H, D, S, F = 1, 2, 64, 64, 4
     rng = np.random.default_rng(59)
     q, k, v = random_qkv(rng, (B, H, F * S, D), "bf16")
@@ -229,22 +238,36 @@ def test_backward_chain_time_out_path(monkeypatch):
                                                           torch.from_numpy(b).to(DEV),
                                                           to_dev(d_o, "bf16", DEV)]
     p = gdn._problem(args[0], args[5], F, True, None, "fused")
-    ws = torch.zeros(gdn.workspace_size(p, 2), dtype=torch.uint8, device=DEV)
+    ws2 = torch.zeros(gdn.workspace_size(p, 2), dtype=torch.uint8, device=DEV)
+    ws3 = torch.zeros(gdn.workspace_size(p, 3), dtype=torch.uint8, device=DEV)
+    _, _, saved = gdn.forward_framewise_save(*args[:5])
+    torch.cuda.synchronize()
+
+    def flag(ws):
+        return int(ws[4:8].view(torch.int32).item())
+
     monkeypatch.setenv("GDN_FUSED_SPIN_LIMIT", "0")
-    bad = gdn.backward_framewise(*args, schedule="fused", workspace=ws)
+    bad_s = gdn.backward_framewise(*args, saved=saved, schedule="fused", workspace=ws3)
     torch.cuda.synchronize()
-    flag = int(ws[4:8].view(torch.int32).item())
+    flag_s = flag(ws3)
+    bad_r = gdn.backward_framewise(*args, schedule="fused", workspace=ws2)
+    torch.cuda.synchronize()
+    flag_r = flag(ws2)
     monkeypatch.delenv("GDN_FUSED_SPIN_LIMIT")
-    good = gdn.backward_framewise(*args, schedule="fused", workspace=ws)
+    good = gdn.backward_framewise(*args, schedule="fused", workspace=ws2)
     torch.cuda.synchronize()
-    assert flag == 1
-    assert int(ws[4:8].view(torch.int32).item()) == 0
-    dq, dk, dv, dg, db, dsi = bad
-    assert torch.isfinite(dq).all()
-    last = slice((F - 1) * S, F * S)
-    assert torch.isfinite(dk[:, :, last]).all() and torch.isfinite(dv[:, :, last]).all()
-    assert torch.isnan(dk[:, :, :(F - 1) * S].float()).all() and torch.isnan(dv[:, :, :(F - 1) * S].float()).all()
-    assert torch.isnan(dg[:, :, :F - 1]).all() and torch.isnan(db[:, :, :F - 1]).all()
-    assert torch.isnan(dsi).all()
+    assert flag_s == 1 and flag_r == 1
+    assert flag(ws2) == 0
+    last, early = slice((F - 1) * S, F * S), slice(0, (F - 1) * S)
+    for dq, dk, dv, dg, db, dsi in (bad_s, bad_r):
+        assert torch.isfinite(dv[:, :, last].float()).all()   # G of the last frame needs no wait
+        assert torch.isnan(dk[:, :, early].float()).all() and torch.isnan(dv[:, :, early].float()).all()
+        assert torch.isnan(dg[:, :, :F - 1]).all() and torch.isnan(db[:, :, :F - 1]).all()
+        assert torch.isnan(dsi).all()
+    assert torch.isfinite(bad_s[1][:, :, last].float()).all()   # saved M_{F-2} is finite
+    assert torch.isnan(bad_r[1][:, :, last].float()).all()      # recomputed M_{F-2} is NaN
+    assert torch.isfinite(bad_s[0].float()).all()
+    assert torch.isfinite(bad_r[0][:, :, :S].float()).all()
+    assert torch.isnan(bad_r[0][:, :, S:].float()).all()
     for t in good:
         assert torch.isfinite(t.float()).all()
