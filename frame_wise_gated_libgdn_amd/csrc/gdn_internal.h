@@ -109,7 +109,7 @@ hipError_t tconv_launch(const TconvLaunch& L, hipStream_t s);
 hipError_t run_tconv(const TconvLaunch& L, hipStream_t s);
 
 // Fused forward: value-column groups pipelined through the frame chain (one flag each per (b, h)).
-constexpr int kChainGroups = 4;
+constexpr int kChainGroups = 8;
 constexpr int kSpinLimitDefault = 1 << 20;  // polls of about a microsecond each
 
 // Whether the fused single-pass forward has a kernel for this type / head size.

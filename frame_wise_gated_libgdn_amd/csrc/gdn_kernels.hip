@@ -942,9 +942,10 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
     // ---- 2. the state step, pipelined over kChainGroups groups of value columns: column c of
     // M_f only depends on column c of M_{f-1}, so group g of frame f starts as soon as frame f-1
     // has published its group g, and the frame-to-frame period is one group's latency.
-    constexpr int CG = kChainGroups, CPG = CB / CG;  // groups, 16-column blocks per group
+    // groups (one 16-column block each at D = 128 and D = 64), 16-column blocks per group
+    constexpr int CG = kChainGroups < CB ? kChainGroups : CB, CPG = CB / CG;
     static_assert(CB % CG == 0, "column blocks split evenly into groups");
-    int* flags = L.ctl + 2 + bh * CG;
+    int* flags = L.ctl + 2 + bh * kChainGroups;
     bf16* Ph = (bf16*)lds;
     bf16* Pl = Ph + PLANE;
     const __amdgpu_buffer_rsrc_t rs =
