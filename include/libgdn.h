@@ -280,20 +280,22 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
  *     dgamma_f = <G_f, M> - beta_f <Kt G_f, P>,    dbeta_f = <Kt G_f, R>
  *     dstate_in = (gamma_0 I - gamma_0 beta_0 Kt_0^T Kt_0) G_0
  * (without the delta term: R = V_f, dK_f = c beta_f V_f G_f^T, dgamma_f = <G_f, M>, and the
- * chain uses gamma I). The forward states are recomputed inside the call (PRODUCTS, then
- * SCAN_STATES, with COMBINE between them when frames are split over tokens; or see FUSED
- * below). p->schedule picks how the reverse chain G_f runs:
- *   FUSED    inside the pass over Q and dO that forms Q_f^T dO_f and dQ: workgroups take frames
- *            in descending order by ticket and hand G_f on through the workspace, as the fused
- *            forward hands on M_f (trace kinds FUSED_RESET, BWD_QDO, then BWD for the gradients
- *            of K, V, gamma and beta). The forward states are then recomputed by the fused
- *            forward without its outputs (FUSED_RESET, FUSED) when a frame's q/k/v rows lie
- *            within 2 GiB. Waits are bounded as in the forward
- *            (GDN_FUSED_SPIN_LIMIT): on time-out a workgroup continues with a NaN G, so every
- *            earlier frame's gradients and dstate_in are NaN, and sets the int32 time-out flag
- *            at byte 4 of the workspace; the kernel always ends.
- *   STAGED   the same pass without the chain (BWD_QDO; COMBINE when frames are split over
- *            tokens), then the chain as a separate scan (SCAN_BWD), then BWD.
+ * chain uses gamma I). The forward states are recomputed inside the call. p->schedule picks
+ * how that and the reverse chain G_f run:
+ *   FUSED    the states: the fused forward without its outputs (trace kinds FUSED_RESET, FUSED)
+ *            when a frame's q/k/v rows lie within 2 GiB, else as STAGED. The chain: inside the
+ *            pass over Q and dO that forms Q_f^T dO_f and dQ, workgroups take frames in
+ *            descending order by ticket and hand G_f on through the workspace as the fused
+ *            forward hands on M_f (FUSED_RESET, BWD_QDO); then BWD for the gradients of K, V,
+ *            gamma and beta. Waits are bounded as in the forward (GDN_FUSED_SPIN_LIMIT): on
+ *            time-out a workgroup continues with NaN and sets the int32 time-out flag at byte 4
+ *            of the workspace, and the kernel always ends. A time-out of the chain makes the
+ *            gradients of the frames before it and dstate_in NaN; a time-out of the recompute
+ *            makes the later states NaN, hence dQ of those frames and everything the chain
+ *            forms from them.
+ *   STAGED   the states: PRODUCTS, then SCAN_STATES (COMBINE between them when frames are
+ *            split over tokens). The chain: the pass over Q and dO without it (BWD_QDO;
+ *            COMBINE when frames are split), then a separate scan (SCAN_BWD); then BWD.
  *   AUTO     FUSED once B*H*F >= 1024, else STAGED.
  *   q, k, v, gamma, beta, state_in   the forward's inputs (state_in NULL: zero)
  *   d_o          dL/dO, layout of o (o_stride_*)
