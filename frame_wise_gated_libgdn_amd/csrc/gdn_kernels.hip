@@ -16,13 +16,18 @@
 //                       owns 16 value columns of one head (columns of M evolve independently), so
 //                       no workgroup waits on another. Writes each M_f (transposed, I/O type).
 //   3. output products -- fully parallel O_f = Q_f M_f on MFMA.
-// Gram and output items share one kernel (products_kernel), so the host runtime can pipeline
-// the frames in chunks: the products of chunk c, the scan of chunk c - 1 and the outputs of
-// chunk c - 2 are in flight together.
-// Step (one frame from a cached state), the update as written:
+// Gram and output items share one kernel (products_kernel); these three launches are the
+// staged schedule (any dtype and D). The fused schedule (fused_kernel: bf16 or E4M3 data, D = 64
+// or 128) does all three per frame in one ticket-ordered launch, handing the state from frame
+// to frame through memory.
+// Step (one frame from a cached state), the update as written, for fp32 data or D = 16 / 32
+// (bf16 with D = 64 / 128 runs the column-block kernels of gdn_step.hip):
 //   4. step_partial_kernel -- per S split: P = K M (MFMA), R = V - (gamma c) P, U_p = K^T R (MFMA).
 //   5. step_reduce_kernel  -- M' = gamma M + beta c sum_p U_p; state_out; transposed copy.
 //   then the output products of the one frame.
+// Backward (bf16, D = 64 or 128): scan_kernel with fp32 states (forward and reverse), qdo_kernel
+// (C_f = Q_f^T dO_f and dQ in one pass over Q and dO, optionally with the reverse chain) and
+// bwd_kernel (dK, dV, dgamma, dbeta).
 //
 // MFMA: v_mfma_f32_16x16x32_bf16 for bf16 data, v_mfma_f32_16x16x4_f32 for fp32 data; fp32
 // accumulation throughout. Lane l = 16 g + r of a wave holds A row r / B column r and the
