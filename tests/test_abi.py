@@ -414,3 +414,17 @@ def test_attention_validation():
     assert call_attn(p) == 3
     assert call_attn(aprob(), o=A + 256) == 6               # o overlaps q
     assert call_attn(aprob(), k=2 * A + 8) == 5
+
+
+def test_trace_kinds_match_the_header():
+    """The binding's trace-kind names, the header's GDN_KERNEL_* values and the library's internal
+    launch kinds agree (a new kind must be added in all three)."""
+    import os
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hdr = open(os.path.join(root, "include", "libgdn.h")).read()
+    kinds = {int(v): n.lower() for n, v in re.findall(r"GDN_KERNEL_(\w+)\s*=\s*(\d+)", hdr)}
+    assert kinds == gdn.KERNEL_NAMES
+    internal = open(os.path.join(root, "frame_wise_gated_libgdn_amd", "csrc", "gdn_internal.h")).read()
+    ik = {int(v): n.lower() for n, v in re.findall(r"\bK_(\w+)\s*=\s*(\d+)", internal)}
+    assert ik == kinds
