@@ -4,17 +4,21 @@
 // both directions), o = softmax(scale q k^T) v, per (b, h). Queries may be a later slice of the
 // frames than the keys (a streaming step against the cache of all frames so far).
 //
-// One workgroup of 4 waves takes 128 queries of one (b, h); a wave owns 32 of them (two 16-query
-// MFMA tiles) and walks the visible keys in tiles of 64:
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the wave's Q rows,
-//     held in registers for the whole call), so lane (r, g) holds the scores of query r for
-//     keys 4 g .. 4 g + 3 of each 16-key block;
+// One workgroup of 8 waves takes 256 queries of one (b, h); a wave owns 32 of them and walks the
+// visible keys in tiles of 64. Products run on v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains
+// about 2.4 PFLOP/s, the 16x16x32 form about 1.45): lane l = 32 g + r holds A row r and B column
+// r over the contraction slice [8 g, 8 g + 8), and C rows 8 i + 4 g + q (register 4 i + q) of
+// column r.
+//   * S^T = K Q^T per 32-key block: A = K rows from LDS, B = the wave's Q rows, held in
+//     registers for the whole call; lane (r, g) ends up with the scores of query r for keys
+//     8 i + 4 g + q of each 32-key block (16 per block);
 //   * online softmax per query in that layout (exp2 of one fma with scale * log2 e folded in;
-//     row maxima across the four lanes of a query by lane exchange; the running maximum moves
-//     only by more than 8 in log2 units, so most tiles skip rescaling the accumulators);
-//   * O^T += V^T P^T: the score tiles are the B operand as they stand, taking the k order of a
-//     32-key step as keys {4 g + j} then {16 + 4 g + j} from two 16-key tiles; the A operand V^T
-//     is read in that same order with transposed LDS reads (ds_read_tr16_b64).
+//     the two lanes of a query meet by one lane exchange; the running maximum moves only by
+//     more than 8 in log2 units, so most tiles skip rescaling the accumulators);
+//   * O^T += V^T P^T per 16-key step s: B = P^T is registers 8 (s mod 2) .. + 7 of score block
+//     s / 2 as they stand, so k slot t of lane group g is key 16 s + 4 g + (t mod 4) + 8 (t / 4);
+//     the A operand V^T is read in that same order with transposed LDS reads (ds_read_tr16_b64,
+//     two per fragment).
 // K/V tiles go from global memory straight into LDS (gfx950's 16-byte global_load_lds), double
 // buffered, so the next tile is in flight while this one is used and no registers hold it: the
 // tile lands unpadded, one 1 KB stretch per instruction, and bank conflicts are avoided by the
@@ -28,18 +32,24 @@ namespace gdn {
 namespace {
 
 typedef __bf16 bf16;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kAttnThreads = 256;
 constexpr int kKT = 64;        // keys per tile
+constexpr int kQW = 32;        // queries per wave
+// waves per workgroup (one workgroup per CU, two waves per SIMD). They share each K/V tile, so
+// 8 halve the tile traffic per query against 4; measured on the 880 x 81 sequence and on 720p
+// streaming frames (224 workgroups) 8 were faster throughout (43.3 against 47.0 ms, 100.5 against
+// 117.1 ms at frame 960)
+constexpr int kNW = 8;
+constexpr int kQB = kNW * kQW; // queries per workgroup
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -48,26 +58,29 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 // XOR swizzle of the 16-byte chunks of a key row in an unpadded [key][dim] LDS tile with CH
-// chunks per row: chunk c of row r is stored at chunk c ^ swz(r). The masks (functions of the
-// bits b_i of r) keep both reads of the tile free of bank conflicts whether the LDS serves 64
-// banks per clock (16 lanes of a 16-byte access, 32 lanes of an 8-byte one) or 32 (8 and 16
-// lanes): K fragment reads (rows 16 kt + 0..15, one chunk) and V^T reads (rows k0 + 4 g + 0..3,
-// chunks 2d and 2d + 1, 8 bytes per lane).
+// chunks per row: chunk c of row r is stored at chunk c ^ swz(r). The masks (XOR combinations of
+// the bits b_i of r) keep both reads of the tile free of bank conflicts whether the LDS serves
+// 64 banks per clock (16 lanes of a 16-byte access, 32 lanes of an 8-byte one) or 32 (8 and 16
+// lanes): K fragment reads (rows 32 kb + 0..31, one chunk per 32 lanes) and V^T reads (per
+// 16-lane group 4 rows and 2 chunks; the four groups of a wave at rows +0 / +4, dims +0 / +16;
+// 8 bytes per lane).
 template <int CH> __device__ __forceinline__ int swz(int r) {
     const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
-    if constexpr (CH == 16) return (b3 ^ b2) | b0 << 1 | b1 << 2 | b2 << 3;
-    else return (b3 ^ b2) | b1 << 1 | (b0 ^ b2) << 2;
+    if constexpr (CH == 16) return b0 | b1 << 1 | (b0 ^ b2) << 2 | (b1 ^ b3) << 3;
+    else return b1 | (b0 ^ b2) << 1 | (b0 ^ b1 ^ b3) << 2;
 }
 
-// lane (r, g) of each 16-lane group receives X[k0 + 4 g + j][c0 + r], j = 0..3, from a swizzled
-// [key][dim] LDS tile (ds_read_tr16_b64: destination lane i takes element i mod 4 of the four
-// b16 values at the address of source lane 4 j + i / 4, so source lane s points at row
-// k0 + 4 g + s / 4, columns c0 + 4 (s mod 4) .. + 3: chunk c0 / 8 + (s mod 4) / 2, half s mod 2)
-template <int D> __device__ __forceinline__ u32x2 read_tr(const bf16* X, int k0, int c0, int r, int g) {
+// Slice of the A operand V^T for one 32-dim block: lane l = 32 g + r receives
+// X[krow + 4 g + j][c0 + r], j = 0..3, from a swizzled [key][dim] LDS tile. ds_read_tr16_b64
+// gives destination lane i of each 16-lane group element i mod 4 of the four b16 values at the
+// address of source lane 4 j + i / 4; so source lane s of group q = l / 16 points at row
+// krow + 4 (q / 2) + s / 4, dims c0 + 16 (q mod 2) + 4 (s mod 4) .. + 3.
+template <int D> __device__ __forceinline__ u32x2 read_vt(const bf16* X, int krow, int c0, int lane) {
     constexpr int CH = D / 8;
-    const int row = k0 + 4 * g + (r >> 2);
-    const int c = c0 / 8 + ((r & 3) >> 1);
-    const bf16* a = X + row * D + ((c ^ swz<CH>(row)) * 8) + 4 * (r & 1);
+    const int q = lane >> 4, s = lane & 15;
+    const int row = krow + 4 * (q >> 1) + (s >> 2);
+    const int col = c0 + 16 * (q & 1) + 4 * (s & 3);
+    const bf16* a = X + row * D + (((col >> 3) ^ swz<CH>(row)) * 8) + (col & 7);
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a));
 }
 
@@ -77,22 +90,19 @@ __device__ __forceinline__ int visible(const AttnLaunch& L, int t) {
     return n < L.Tk ? (int)n : L.Tk;
 }
 
-// QT 16-query tiles per wave: each K / V^T fragment read from LDS feeds QT MFMAs
-template <int D, int QT>
-__global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(AttnLaunch L) {
-    constexpr int kQW = 16 * QT;     // queries per wave
-    constexpr int kQB = 4 * kQW;     // queries per workgroup
-    constexpr int KSD = D / 32;           // k steps over the head dim
-    constexpr int DT = D / 16;            // 16-dim tiles of O
+template <int D>
+__global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
+    constexpr int KS = D / 16;            // 16-long k steps over the head dim (scores)
+    constexpr int DB = D / 32;            // 32-dim blocks of O
+    constexpr int KB = kKT / 32;          // 32-key blocks per tile
     constexpr int CH = D / 8;             // 16-byte chunks per row
-    constexpr int NKT = kKT / 16;         // 16-key tiles per key tile
     constexpr int SLOTS = kKT * CH;       // 16-byte slots of one operand tile
-    constexpr int INSTR = 2 * SLOTS / (64 * 4);   // load instructions per wave per tile (K and V)
-    static_assert(SLOTS % 64 == 0 && (2 * SLOTS) % 256 == 0, "whole instructions per wave");
+    constexpr int INSTR = 2 * SLOTS / (64 * kNW);   // load instructions per wave per tile (K and V)
+    static_assert(SLOTS % 64 == 0 && (2 * SLOTS) % (64 * kNW) == 0, "whole instructions per wave");
     __shared__ __attribute__((aligned(16))) bf16 tiles[2][2][kKT * D];   // [buffer][K, V]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, g = lane >> 4;
+    const int r = lane & 31, g = lane >> 5;
     // XCD-aware order: workgroup i runs on XCD i mod 8; XCD x takes the contiguous stretch
     // [x n8, (x + 1) n8) of the (b h)-major, query-block-minor order, so that the workgroups
     // resident on one XCD are neighbouring query blocks of the same head and share its K/V tiles
@@ -105,19 +115,17 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
     const int b = bh / L.H, h = bh % L.H;
     const int qw0 = qb * kQB + wave * kQW;    // first query of this wave
 
-    // the wave's Q rows as B operands; rows past Tq repeat the last row (never stored)
-    bf16x8 qf[QT][KSD];
-    int nlim[QT];
+    // the wave's Q rows as B operands (lane (r, g): query qw0 + r, dims 16 ks + 8 g .. + 7);
+    // rows past Tq repeat the last row (never stored)
+    bf16x8 qf[KS];
+    int nlim;
     {
         const bf16* qbase = (const bf16*)L.q + (int64_t)b * L.qsb + (int64_t)h * L.qsh;
+        const int t = min(qw0 + r, L.Tq - 1);
+        nlim = visible(L, t);
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-            const int t = min(qw0 + 16 * qt + r, L.Tq - 1);
-            nlim[qt] = visible(L, t);
-#pragma unroll
-            for (int k = 0; k < KSD; ++k)
-                qf[qt][k] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qbase + (int64_t)t * L.qst + 32 * k + 8 * g));
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qbase + (int64_t)t * L.qst + 16 * ks + 8 * g));
     }
     // keys every query of the workgroup sees, and the keys any of them sees
     const int kfull = visible(L, qb * kQB);
@@ -142,17 +150,12 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
     };
 
     const float c2 = L.scale * 1.4426950408889634f;   // scores in log2 units
-    float m[QT], l[QT];
+    float m = -__builtin_inff(), l = 0.f;
+    f32x16 oacc[DB];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        m[qt] = -__builtin_inff();
-        l[qt] = 0.f;
-    }
-    f32x4 oacc[DT][QT];
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
 
     issue(0, 0);
     int buf = 0;
@@ -162,106 +165,93 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
         __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (k0 + kKT < kmax) issue(k0 + kKT, buf ^ 1);
-        const bf16* ks = tiles[buf][0];
-        const bf16* vs = tiles[buf][1];
+        const bf16* kt = tiles[buf][0];
+        const bf16* vt = tiles[buf][1];
 
         // S^T = K Q^T for 64 keys x 32 queries
-        f32x4 sacc[NKT][QT];
+        f32x16 sacc[KB];
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
 #pragma unroll
-        for (int k = 0; k < KSD; ++k)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                const int row = 16 * kt + r;
-                const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(ks + row * D + (((4 * k + g) ^ swz<CH>(row)) * 8)));
-#pragma unroll
-                for (int qt = 0; qt < QT; ++qt) sacc[kt][qt] = mfma(a, qf[qt][k], sacc[kt][qt]);
+            for (int kb = 0; kb < KB; ++kb) {
+                const int row = 32 * kb + r;
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kt + row * D + (((2 * ks + g) ^ swz<CH>(row)) * 8)));
+                sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
             }
         if (k0 + kKT > kfull) {   // a tile some query does not see completely
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (k0 + 16 * kt + 4 * g + q >= nlim[qt]) sacc[kt][qt][q] = -__builtin_inff();
+                for (int j = 0; j < 16; ++j)
+                    if (k0 + 32 * kb + 8 * (j >> 2) + 4 * g + (j & 3) >= nlim) sacc[kb][j] = -__builtin_inff();
         }
+        // tile maximum on the raw scores (the scale is positive), across the query's two lanes
+        float tmax = -__builtin_inff();
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-            // tile maximum on the raw scores (the scale is positive), across the query's 4 lanes
-            float tmax = -__builtin_inff();
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
+            for (int j = 0; j < 16; ++j) tmax = __builtin_fmaxf(tmax, sacc[kb][j]);
+        tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+        // the running maximum (log2 units) moves only when the tile's exceeds it by more than 8,
+        // so weights stay below 2^8 and most tiles skip the rescale; exact, since the final
+        // normalisation uses the same maximum. Finite after the first tile (key 0 is visible to
+        // every query).
+        const float cand = tmax * c2;
+        const bool move = cand > m + 8.f;
+        if (__any(move)) {
+            const float mnew = move ? cand : m;
+            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+            l *= alpha;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) tmax = __builtin_fmaxf(tmax, sacc[kt][qt][q]);
-            tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-            // the running maximum (log2 units) moves only when the tile's exceeds it by more than
-            // 8, so weights stay below 2^8 and most tiles skip the rescale; exact, since the
-            // final normalisation uses the same maximum. Finite after the first tile (key 0 is
-            // visible to every query).
-            const float cand = tmax * c2;
-            const bool move = cand > m[qt] + 8.f;
-            if (__any(move)) {
-                const float mnew = move ? cand : m[qt];
-                const float alpha = __builtin_amdgcn_exp2f(m[qt] - mnew);
-                l[qt] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
-                m[qt] = mnew;
-            }
-            float sum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][qt][q], c2, -m[qt]));
-                    sacc[kt][qt][q] = p;
-                    sum += p;
-                }
-            l[qt] += sum;
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            m = mnew;
         }
-        // O^T += V^T P^T, two 32-key steps
+        float sum = 0.f;
 #pragma unroll
-        for (int ks2 = 0; ks2 < NKT / 2; ++ks2) {
-            bf16x8 pb[QT];
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) {
-                const f32x4 x = sacc[2 * ks2][qt], y = sacc[2 * ks2 + 1][qt];
-                pb[qt] = __builtin_bit_cast(bf16x8, u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]),
-                                                          pack2(y[0], y[1]), pack2(y[2], y[3])});
+            for (int j = 0; j < 16; ++j) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][j], c2, -m));
+                sacc[kb][j] = p;
+                sum += p;
             }
+        l += sum;
+        // O^T += V^T P^T, four 16-key steps
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const u32x2 v0 = read_tr<D>(vs, 32 * ks2, 16 * dt, r, g);
-                const u32x2 v1 = read_tr<D>(vs, 32 * ks2 + 16, 16 * dt, r, g);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+        for (int s = 0; s < kKT / 16; ++s) {
+            const int o = 8 * (s & 1);
+            const f32x16& x = sacc[s >> 1];
+            const bf16x8 pb = __builtin_bit_cast(
+                bf16x8, u32x4{pack2(x[o], x[o + 1]), pack2(x[o + 2], x[o + 3]), pack2(x[o + 4], x[o + 5]),
+                              pack2(x[o + 6], x[o + 7])});
 #pragma unroll
-                for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = mfma(a, pb[qt], oacc[dt][qt]);
+            for (int db = 0; db < DB; ++db) {
+                const u32x2 v0 = read_vt<D>(vt, 16 * s, 32 * db, lane);
+                const u32x2 v1 = read_vt<D>(vt, 16 * s + 8, 32 * db, lane);
+                oacc[db] = mfma32(__builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]}), pb, oacc[db]);
             }
         }
     }
 
-    // normalise and store: lane (r, g) holds O[query 16 qt + r][dims 16 dt + 4 g .. + 3]
+    // normalise and store: lane (r, g) holds O[query qw0 + r][dims 32 db + 8 i + 4 g .. + 3] in
+    // registers 4 i .. 4 i + 3 of block db
     bf16* obase = (bf16*)L.o + (int64_t)b * L.osb + (int64_t)h * L.osh;
+    const float inv = 1.f / (l + __shfl_xor(l, 32));
+    const int t = qw0 + r;
+    if (t < L.Tq) {
+        bf16* orow = obase + (int64_t)t * L.ost;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        float lt_ = l[qt];
-        lt_ += __shfl_xor(lt_, 16);
-        lt_ += __shfl_xor(lt_, 32);
-        const float inv = 1.f / lt_;
-        const int t = qw0 + 16 * qt + r;
-        if (t < L.Tq) {
-            bf16* orow = obase + (int64_t)t * L.ost;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const f32x4 x = oacc[dt][qt] * inv;
-                *(u32x2*)(orow + 16 * dt + 4 * g) = u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])};
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * i;
+                *(u32x2*)(orow + 32 * db + 8 * i + 4 * g) =
+                    u32x2{pack2(oacc[db][j] * inv, oacc[db][j + 1] * inv), pack2(oacc[db][j + 2] * inv, oacc[db][j + 3] * inv)};
             }
-        }
     }
 }
 
@@ -269,20 +259,17 @@ __global__ __launch_bounds__(kAttnThreads, QT >= 4 ? 1 : 2) void attn_kernel(Att
 
 bool attn_supported(int D) { return D == 64 || D == 128; }
 
-template <int D, int QT> hipError_t launch_qt(const AttnLaunch& L, hipStream_t s) {
-    constexpr int kQB = 4 * 16 * QT;
+template <int D> hipError_t launch_d(const AttnLaunch& L, hipStream_t s) {
     const int64_t items = (int64_t)L.B * L.H * ((L.Tq + kQB - 1) / kQB);
     const int64_t blocks = (items + 7) / 8 * 8;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_kernel<D, QT>), dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, L);
+    hipLaunchKernelGGL((attn_kernel<D>), dim3((unsigned)blocks), dim3(64 * kNW), 0, s, L);
     return hipGetLastError();
 }
 
-constexpr int kAttnQT = 2;   // 16-query tiles per wave (4: one wave per SIMD, measured slower)
-
 hipError_t attn_launch(const AttnLaunch& L, hipStream_t s) {
-    if (L.D == 128) return launch_qt<128, kAttnQT>(L, s);
-    if (L.D == 64) return launch_qt<64, kAttnQT>(L, s);
+    if (L.D == 128) return launch_d<128>(L, s);
+    if (L.D == 64) return launch_d<64>(L, s);
     return hipErrorInvalidValue;
 }
 

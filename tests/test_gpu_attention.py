@@ -46,6 +46,9 @@ CASES = [
     (1, 2, 64, 100, 2, 6, 2, "head"),        # later keys present, masked
     (1, 3, 128, 130, 3, 3, 0, "token"),
     (1, 2, 128, 3520, 1, 3, 2, "head"),      # a 720p frame against a 3-frame cache
+    # several 256-query workgroups per head, ragged last one
+    (2, 128, 128, 97, 3, 3, 0, "head"),
+    (2, 128, 64, 65, 5, 6, 1, "token"),      # later keys present, masked
 ]
 
 
