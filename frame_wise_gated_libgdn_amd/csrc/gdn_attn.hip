@@ -20,7 +20,8 @@
 //     the A operand V^T is read in that same order with transposed LDS reads (ds_read_tr16_b64,
 //     two per fragment).
 // K/V tiles go from global memory straight into LDS (gfx950's 16-byte global_load_lds), double
-// buffered, so the next tile is in flight while this one is used and no registers hold it: the
+// buffered (two arrays, the tile loop unrolled by two, so that the compiler keeps the next tile's
+// loads in flight across this tile's LDS reads), and no registers hold the next tile: the
 // tile lands unpadded, one 1 KB stretch per instruction, and bank conflicts are avoided by the
 // choice of source chunk per lane (an XOR swizzle of each row's 16-byte chunks). Key tiles that
 // every query of the workgroup sees completely skip the mask; the others mask per element.
@@ -99,7 +100,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
     constexpr int SLOTS = kKT * CH;       // 16-byte slots of one operand tile
     constexpr int INSTR = 2 * SLOTS / (64 * kNW);   // load instructions per wave per tile (K and V)
     static_assert(SLOTS % 64 == 0 && (2 * SLOTS) % (64 * kNW) == 0, "whole instructions per wave");
-    __shared__ __attribute__((aligned(16))) bf16 tiles[2][2][kKT * D];   // [buffer][K, V]
+    // the two buffers are separate arrays and the tile loop is unrolled by two, so that every
+    // LDS read names its buffer statically: the compiler can then tell the reads of one buffer
+    // from the direct-to-LDS loads into the other, and does not wait for those before them
+    __shared__ __attribute__((aligned(16))) bf16 tile0[2][kKT * D];   // [K, V] of even tiles
+    __shared__ __attribute__((aligned(16))) bf16 tile1[2][kKT * D];   // [K, V] of odd tiles
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 31, g = lane >> 5;
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
     // tile of keys k0 .. k0 + kKT - 1 into buffer buf: instruction ins of the workgroup fills
     // slots 64 ins .. 64 ins + 63 of the K | V pair; rows past Tk are loaded clamped (finite
     // values: their scores are masked and their weights are zero)
-    auto issue = [&](int k0, int buf) {
+    auto issue = [&](int k0, bf16 (&tl)[2][kKT * D]) {
 #pragma unroll
         for (int i = 0; i < INSTR; ++i) {
             const int ins = wave * INSTR + i;
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
             const int u = ins * 64 + lane - (isv ? SLOTS : 0);
             const int row = u / CH, c = (u % CH) ^ swz<CH>(row);
             const bf16* src = (isv ? vbase : kbase) + (int64_t)min(k0 + row, L.Tk - 1) * L.kst + c * 8;
-            bf16* dst = &tiles[buf][isv ? 1 : 0][(ins * 64 - (isv ? SLOTS : 0)) * 8];
+            bf16* dst = &tl[isv ? 1 : 0][(ins * 64 - (isv ? SLOTS : 0)) * 8];
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
     };
@@ -157,16 +162,15 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
 
-    issue(0, 0);
-    int buf = 0;
-    for (int k0 = 0; k0 < kmax; k0 += kKT, buf ^= 1) {
+    // one tile of keys k0 .. k0 + kKT - 1, held in cur; the next tile goes into nxt
+    auto step = [&](int k0, bf16 (&cur)[2][kKT * D], bf16 (&nxt)[2][kKT * D]) __attribute__((always_inline)) {
         // this wave's loads of tile k0 are done; after the barrier every wave's are, and every
         // wave is done reading the other buffer (the previous tile), which the next tile fills
         __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (k0 + kKT < kmax) issue(k0 + kKT, buf ^ 1);
-        const bf16* kt = tiles[buf][0];
-        const bf16* vt = tiles[buf][1];
+        if (k0 + kKT < kmax) issue(k0 + kKT, nxt);
+        const bf16* kt = cur[0];
+        const bf16* vt = cur[1];
 
         // S^T = K Q^T for 64 keys x 32 queries
         f32x16 sacc[KB];
@@ -235,6 +239,11 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
                 oacc[db] = mfma32(__builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]}), pb, oacc[db]);
             }
         }
+    };
+    issue(0, tile0);
+    for (int k0 = 0; k0 < kmax; k0 += 2 * kKT) {
+        step(k0, tile0, tile1);
+        if (k0 + kKT < kmax) step(k0 + kKT, tile1, tile0);
     }
 
     // normalise and store: lane (r, g) holds O[query qw0 + r][dims 32 db + 8 i + 4 g .. + 3] in
