@@ -16,8 +16,9 @@ import os
 import threading
 
 __all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "forward_framewise",
-           "forward_framewise_save", "saved_size", "step_frame", "backward_framewise", "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES",
-           "GDN_F32", "GDN_BF16"]
+           "forward_framewise_save", "saved_size", "step_frame", "backward_framewise", "check_timeout",
+           "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES", "GDN_F32",
+           "GDN_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -25,7 +26,7 @@ _LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_F32, GDN_BF16, GDN_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPPORTED",
           4: "GDN_ERR_STRIDE", 5: "GDN_ERR_ALIGN", 6: "GDN_ERR_ALIAS", 7: "GDN_ERR_WORKSPACE",
-          8: "GDN_ERR_HIP"}
+          8: "GDN_ERR_HIP", 9: "GDN_ERR_TIMEOUT"}
 KERNEL_NAMES = {0: "products", 1: "combine", 2: "scan", 3: "step_partial", 4: "step_reduce",
                 5: "fused_reset", 6: "fused", 7: "scan_bwd", 8: "bwd", 9: "scan_states",
                 10: "tconv", 11: "attn", 12: "step_output", 13: "bwd_qdo"}
@@ -125,6 +126,8 @@ def load():
             lib.gdn_backward_framewise_saved.argtypes = ([P] + [_vp] * 5 + [_vp, ctypes.c_size_t]
                                                          + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp])
             lib.gdn_backward_framewise_saved.restype = ctypes.c_int
+            lib.gdn_check_timeout.argtypes = [P, ctypes.c_int, _vp, _vp]
+            lib.gdn_check_timeout.restype = ctypes.c_int
             lib.gdn_status_string.argtypes = [ctypes.c_int]
             lib.gdn_status_string.restype = ctypes.c_char_p
             lib.gdn_last_error_message.restype = ctypes.c_char_p
@@ -178,6 +181,24 @@ def workspace_size(p: Problem, mode) -> int:
     n = ctypes.c_size_t(0)
     _check(load().gdn_workspace_size(ctypes.byref(p), int(mode), ctypes.byref(n)))
     return int(n.value)
+
+
+def check_timeout(p: Problem, mode, workspace, stream=None):
+    """Raise GdnError(GDN_ERR_TIMEOUT) if the last call that used `workspace` (problem p, the
+    workspace mode of gdn_workspace_size) gave up a bounded wait of the fused schedule (its
+    outputs after that wait are NaN). Synchronises the stream first; a no-op for schedules
+    without waits."""
+    _check(load().gdn_check_timeout(ctypes.byref(p), int(mode), _ptr(workspace), _stream(stream)))
+
+
+def _after(p, mode, ws, own_ws, stream, check):
+    """check None: check the time-out flag when the binding allocated the workspace itself (no
+    one else can read it) and the stream is not being captured into a graph."""
+    import torch
+    if check is None:
+        check = own_ws and not torch.cuda.is_current_stream_capturing()
+    if check:
+        check_timeout(p, mode, ws, stream)
 
 
 def _dtype_code(t):
@@ -243,11 +264,15 @@ def _workspace(p, step_mode, workspace, device):
 
 def forward_framewise(q, k, v, gamma, beta, state=None, *, use_delta=True, key_scale=None,
                       out=None, state_out=None, return_state=True, workspace=None, stream=None,
-                      schedule="auto"):
+                      schedule="auto", check_timeout=None):
     """All frames: q, k, v [B, H, F*S, D] (D contiguous, any other strides, same strides for
     all three); gamma, beta fp32 [B, H, F]; state fp32 [B, H, D, D] or None (zero).
     schedule: "auto", "staged" (products, scan, outputs as three passes) or "fused" (one pass;
     bf16 with D = 64 or 128).
+    check_timeout: after the call, synchronise and raise GdnError(GDN_ERR_TIMEOUT) if a bounded
+    wait of the fused schedule gave up (its later outputs are NaN); None (default) checks only
+    when the binding allocated the workspace itself and the stream is not being captured. The
+    other forward and backward calls take the same argument.
     Returns (o, state_out); o has q's shape and dtype, state_out is None when
     return_state is False."""
     import torch
@@ -269,6 +294,7 @@ def forward_framewise(q, k, v, gamma, beta, state=None, *, use_delta=True, key_s
     _check(load().gdn_forward_framewise(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                         _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),
                                         _ptr(ws), nbytes, _stream(stream)))
+    _after(p, 0, ws, workspace is None, stream, check_timeout)
     return out, state_out
 
 
@@ -281,7 +307,7 @@ def saved_size(p) -> int:
 
 def forward_framewise_save(q, k, v, gamma, beta, state=None, *, use_delta=True, key_scale=None,
                            out=None, state_out=None, return_state=True, saved=None,
-                           workspace=None, stream=None):
+                           workspace=None, stream=None, check_timeout=None):
     """forward_framewise on the fused schedule (bf16, D = 64 or 128) that also keeps what the
     backward needs (the frames' key-key products and every state), so that
     backward_framewise(..., saved=saved) skips recomputing the forward.
@@ -308,12 +334,14 @@ def forward_framewise_save(q, k, v, gamma, beta, state=None, *, use_delta=True, 
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(state),
         _ptr(out), _ptr(state_out), _ptr(saved), saved.numel() * saved.element_size(), _ptr(ws),
         nbytes, _stream(stream)))
+    _after(p, 0, ws, workspace is None, stream, check_timeout)
     return out, state_out, saved
 
 
 def forward_framewise_fp8(q, k, v, q_scale, k_scale, v_scale, gamma, beta, state=None, *,
                           use_delta=True, key_scale=None, out=None, state_out=None,
-                          return_state=True, workspace=None, stream=None, schedule="auto"):
+                          return_state=True, workspace=None, stream=None, schedule="auto",
+                          check_timeout=None):
     """All frames from E4M3 inputs: q, k, v [B, H, F*S, D] of OCP FP8 E4M3 codes (torch.uint8
     or torch.float8_e4m3fn, D contiguous, same strides); q_scale, k_scale, v_scale, gamma, beta
     fp32 [B, H, F]; an element's value is its frame's scale times the code's value.
@@ -343,6 +371,7 @@ def forward_framewise_fp8(q, k, v, q_scale, k_scale, v_scale, gamma, beta, state
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
         _ptr(gamma), _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out), _ptr(ws), nbytes,
         _stream(stream)))
+    _after(p, 0, ws, workspace is None, stream, check_timeout)
     return out, state_out
 
 
@@ -430,7 +459,7 @@ def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_
 def backward_framewise(q, k, v, gamma, beta, d_o, state=None, d_state_out=None, *,
                        use_delta=True, key_scale=None, dq=None, dk=None, dv=None,
                        return_state_grad=True, saved=None, workspace=None, stream=None,
-                       schedule="auto"):
+                       schedule="auto", check_timeout=None):
     """Gradients of forward_framewise. q, k, v [B, H, F*S, D] (bf16, D = 64 or 128, same
     strides); d_o: dL/dO with o's shape (any strides with D contiguous); gamma, beta fp32
     [B, H, F]; state, d_state_out fp32 [B, H, D, D] or None. With saved (from
@@ -471,10 +500,12 @@ def backward_framewise(q, k, v, gamma, beta, d_o, state=None, d_state_out=None, 
             ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(saved),
             saved.numel() * saved.element_size(), _ptr(d_o), _ptr(d_state_out), _ptr(dq), _ptr(dk),
             _ptr(dv), _ptr(dg), _ptr(db), _ptr(dsi), _ptr(ws), nbytes, _stream(stream)))
+        _after(p, 3, ws, workspace is None, stream, check_timeout)
         return dq, dk, dv, dg, db, dsi
     ws, nbytes = _workspace(p, 2, workspace, q.device)
     _check(load().gdn_backward_framewise(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(state),
         _ptr(d_o), _ptr(d_state_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db),
         _ptr(dsi), _ptr(ws), nbytes, _stream(stream)))
+    _after(p, 2, ws, workspace is None, stream, check_timeout)
     return dq, dk, dv, dg, db, dsi

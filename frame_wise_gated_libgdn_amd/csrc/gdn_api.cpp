@@ -51,12 +51,16 @@ struct Plan {
 // The fused forward pays off once there are enough (b, h, f) items to fill the chip.
 constexpr int64_t kFusedMinItems = 1024;
 
-// The fused kernel reads a frame's K and V rows through 32-bit buffer offsets: the bytes from
-// a frame's first row to the end of its last must stay below 2 GiB.
+// The fused kernel reads a frame's Q, K and V rows and writes its O rows through 32-bit buffer
+// offsets: for either tensor the bytes from a frame's first row to the end of its last must
+// stay below 2 GiB (O is bf16 for every input type the fused kernel takes).
 bool fused_rows_fit(const gdn_problem& p) {
     const int64_t esz = p.dtype == GDN_FP8_E4M3 ? 1 : 2;
-    const int64_t span = ((int64_t)(p.tokens_per_frame - 1) * p.qkv_stride_t + p.head_dim) * esz;
-    return p.qkv_stride_t >= 0 && span < ((int64_t)1 << 31);
+    const int64_t S = p.tokens_per_frame, D = p.head_dim;
+    const int64_t in_span = ((S - 1) * p.qkv_stride_t + D) * esz;
+    const int64_t out_span = ((S - 1) * p.o_stride_t + D) * 2;
+    return p.qkv_stride_t >= 0 && p.o_stride_t >= 0 && in_span < ((int64_t)1 << 31) &&
+           out_span < ((int64_t)1 << 31);
 }
 
 bool choose_fused(const gdn_problem& p, int step_mode) {
@@ -232,7 +236,7 @@ gdn_status check_sizes(const gdn_problem* p, int mode) {
         return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs bf16 data and D = 64 or 128");
     if (mode == 0 && (p->schedule == GDN_SCHEDULE_FUSED || p->dtype == GDN_FP8_E4M3) &&
         !fused_rows_fit(*p))
-        return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs a frame's q/k/v rows within 2 GiB");
+        return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs a frame's q/k/v rows and its o rows within 2 GiB");
     if (mode == 2 && !gdn::backward_supported(p->dtype == GDN_BF16, D))
         return fail(GDN_ERR_UNSUPPORTED, "the backward needs bf16 data and D = 64 or 128");
     const int64_t F = step_mode ? 1 : p->frames;
@@ -690,12 +694,34 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                workspace_bytes, hip_stream);
 }
 
+gdn_status gdn_check_timeout(const gdn_problem* p, int mode, const void* workspace,
+                             void* hip_stream) {
+    g_msg[0] = '\0';
+    if (mode < 0 || mode > 3) return fail(GDN_ERR_SHAPE, "mode must be 0, 1, 2 or 3, got %d", mode);
+    gdn_status s = check_sizes(p, mode == 3 ? 2 : mode);
+    if (s != GDN_OK) return s;
+    const Plan pl = make_plan(*p, mode);
+    // bounded waits: the fused forward, and the backward's chained schedule (its reverse chain
+    // and, recomputing, the fused forward that rebuilds the states); step mode never waits
+    const bool waits = mode != 1 && (pl.fused || pl.fused_states);
+    if (!waits) return GDN_OK;
+    if (!workspace) return fail(GDN_ERR_NULL, "workspace is NULL");
+    hipError_t e = hipStreamSynchronize((hipStream_t)hip_stream);
+    int32_t flag = 0;
+    if (e == hipSuccess) e = hipMemcpy(&flag, (const char*)workspace + 4, sizeof flag, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "reading the time-out flag failed: %s", hipGetErrorString(e));
+    if (flag)
+        return fail(GDN_ERR_TIMEOUT, "a bounded wait of the fused schedule timed out; the outputs "
+                                     "that depend on it are NaN");
+    return GDN_OK;
+}
+
 gdn_status gdn_saved_size(const gdn_problem* p, size_t* bytes_out) {
     g_msg[0] = '\0';
     if (!bytes_out) return fail(GDN_ERR_NULL, "bytes_out is NULL");
     gdn_status s = check_sizes(p, 2);
     if (s != GDN_OK) return s;
-    if (!fused_rows_fit(*p)) return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs a frame's q/k/v rows within 2 GiB");
+    if (!fused_rows_fit(*p)) return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs a frame's q/k/v rows and its o rows within 2 GiB");
     *bytes_out = saved_plan(*p).total();
     return GDN_OK;
 }
@@ -773,6 +799,7 @@ const char* gdn_status_string(gdn_status s) {
     case GDN_ERR_ALIAS: return "overlapping buffers";
     case GDN_ERR_WORKSPACE: return "workspace missing or too small";
     case GDN_ERR_HIP: return "HIP runtime error";
+    case GDN_ERR_TIMEOUT: return "a bounded wait timed out";
     }
     return "unknown status";
 }

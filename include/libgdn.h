@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 8
+#define LIBGDN_ABI_VERSION 9
 
 typedef enum {
     GDN_OK = 0,
@@ -76,7 +76,8 @@ typedef enum {
     GDN_ERR_ALIGN = 5,        /* pointer or stride alignment violated */
     GDN_ERR_ALIAS = 6,        /* an output overlaps an input (other than the allowed in-place state) */
     GDN_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than gdn_workspace_size() */
-    GDN_ERR_HIP = 8           /* a HIP runtime call failed */
+    GDN_ERR_HIP = 8,          /* a HIP runtime call failed */
+    GDN_ERR_TIMEOUT = 9       /* gdn_check_timeout: a bounded wait of the fused schedule gave up */
 } gdn_status;
 
 /*
@@ -96,14 +97,16 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype;
  *   FUSED   one pass: each (b, h, f) is a workgroup that computes its frame's products, waits
  *           for the state of frame f-1 of the same (b, h), applies the step, publishes M_f and
  *           writes O_f; only Q/K/V/O and the D x D states cross HBM. bf16 (or E4M3) with
- *           D = 64 or 128, and a frame's rows ((S-1) * qkv_stride_t + D elements) within 2 GiB
- *           (GDN_ERR_UNSUPPORTED otherwise).
+ *           D = 64 or 128, and a frame's q/k/v rows ((S-1) * qkv_stride_t + D elements) and o
+ *           rows ((S-1) * o_stride_t + D elements) each within 2 GiB (GDN_ERR_UNSUPPORTED
+ *           otherwise).
  *   AUTO    FUSED where supported and B*H*F >= 1024, else STAGED.
  * FUSED waits for the previous frame's state are bounded: after GDN_FUSED_SPIN_LIMIT polls
  * (environment, default 2^20, about a microsecond each) a workgroup gives up, continues with a
  * NaN state (every later output of that (b, h) is NaN) and sets the int32 time-out flag at byte
- * 4 of the workspace; the kernel always ends. GDN_FUSED_SPIN_LIMIT=0 times out every frame
- * after the first at once (for exercising that path).
+ * 4 of the workspace; the kernel always ends. gdn_check_timeout reads that flag.
+ * GDN_FUSED_SPIN_LIMIT=0 times out every frame after the first at once (for exercising that
+ * path).
  */
 typedef enum { GDN_SCHEDULE_AUTO = 0, GDN_SCHEDULE_STAGED = 1, GDN_SCHEDULE_FUSED = 2 } gdn_schedule;
 
@@ -346,6 +349,24 @@ gdn_status gdn_backward_framewise_saved(const gdn_problem* p, const void* q, con
                                         const float* d_state_out, void* dq, void* dk, void* dv,
                                         float* dgamma, float* dbeta, float* d_state_in,
                                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Whether the last call that used `workspace` gave up a bounded wait. The FUSED schedule of
+ * gdn_forward_framewise (also _fp8 and _save) and the chained schedule of the backward hand the
+ * state (or its gradient) from frame to frame between workgroups; a wait for the previous frame
+ * is bounded (GDN_FUSED_SPIN_LIMIT, see gdn_schedule above) and, when it gives up, the kernel
+ * still ends, with NaN in every output that depends on the missing state and the int32 time-out
+ * flag at byte 4 of the workspace set. This call synchronises hip_stream, so that the call on
+ * it has finished, then reads that flag.
+ *   p, mode    the problem and workspace mode of that call (as gdn_workspace_size: 0 forward,
+ *              1 step, 2 backward, 3 backward from saved states); they select the schedule
+ *   workspace  the workspace passed to that call
+ * Returns GDN_OK when the flag is clear or the call's schedule has no bounded wait (STAGED,
+ * step mode; nothing is read then), GDN_ERR_TIMEOUT when it is set, GDN_ERR_HIP when the
+ * synchronisation or the 4-byte read fails, and the argument errors of gdn_workspace_size.
+ * It blocks the host: not for use during graph capture.
+ */
+gdn_status gdn_check_timeout(const gdn_problem* p, int mode, const void* workspace, void* hip_stream);
 
 /*
  * Instrumentation (launch trace). gdn_set_trace arms `pairs` pairs of caller-created,

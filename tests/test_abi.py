@@ -31,9 +31,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 8
+    assert gdn.abi_version() == 9
     lib = gdn.load()
-    for code in range(9):
+    for code in range(10):
         assert lib.gdn_status_string(code)
     assert lib.gdn_status_string(99) == b"unknown status"
 
@@ -366,6 +366,22 @@ def test_fused_needs_frame_rows_within_2gib():
     assert call(big) == 3 and "2 GiB" in msg()
 
 
+def test_fused_needs_frame_output_rows_within_2gib():
+    # the fused kernel also writes O through 32-bit buffer offsets: a huge o token stride
+    # with small q/k/v strides must not select it
+    p = prob(F=3000)
+    big = prob(F=3000)
+    big.o_stride_t = 1 << 25                   # 39 rows of 2^25 bf16 elements: > 2 GiB
+    big.o_stride_h = big.o_stride_t * 40 * 3000
+    big.o_stride_b = big.o_stride_h * 2
+    assert gdn.workspace_size(big, False) != gdn.workspace_size(p, False)   # falls back to staged
+    staged = prob(F=3000)
+    staged.schedule = 1
+    assert gdn.workspace_size(big, False) == gdn.workspace_size(staged, False)
+    big.schedule = 2
+    assert call(big) == 3 and "2 GiB" in msg()
+
+
 def tprob(B=1, T=6, S=5, C=16, tb=2, dtype=gdn.GDN_BF16):
     return gdn.TconvProblem(B, T, S, C, tb, dtype, T * S * C, S * C, C, T * S * C, S * C, C)
 
@@ -428,3 +444,24 @@ def test_trace_kinds_match_the_header():
     internal = open(os.path.join(root, "frame_wise_gated_libgdn_amd", "csrc", "gdn_internal.h")).read()
     ik = {int(v): n.lower() for n, v in re.findall(r"\bK_(\w+)\s*=\s*(\d+)", internal)}
     assert ik == kinds
+
+
+def test_check_timeout_validation():
+    lib = gdn.load()
+    p = prob(F=3)                                 # auto: staged (6 items), no bounded waits
+    assert lib.gdn_check_timeout(None, 0, A, None) == 1
+    assert lib.gdn_check_timeout(ctypes.byref(p), 4, A, None) == 2
+    assert "mode" in msg()
+    bad = prob()
+    bad.head_dim = 48
+    assert lib.gdn_check_timeout(ctypes.byref(bad), 0, A, None) == 3
+    # schedules without waits read nothing (the fake address is never touched)
+    assert lib.gdn_check_timeout(ctypes.byref(p), 0, A, None) == 0
+    assert lib.gdn_check_timeout(ctypes.byref(p), 1, A, None) == 0
+    staged = prob(F=3000)
+    staged.schedule = 1
+    assert lib.gdn_check_timeout(ctypes.byref(staged), 0, A, None) == 0
+    assert lib.gdn_check_timeout(ctypes.byref(staged), 2, A, None) == 0
+    fused = prob(F=3000)
+    fused.schedule = 2
+    assert lib.gdn_check_timeout(ctypes.byref(fused), 0, None, None) == 1

@@ -70,6 +70,49 @@ def test_attention_matches_oracle(case):
     assert e <= TOL
 
 
+RESCALE_CASES = [
+    # B, H, D, S, q_frames, kv_frames, q_frame0, layout, scale x sqrt(D), key ramp
+    (1, 2, 128, 100, 3, 3, 0, "head", 8.0, True),
+    (1, 2, 64, 77, 3, 4, 1, "head", 16.0, True),     # ragged last key tile, later keys masked
+    (2, 3, 64, 40, 5, 5, 0, "token", 16.0, False),
+    (1, 1, 128, 130, 2, 6, 3, "head", 12.0, True),   # streaming rows, ragged tiles
+]
+
+
+@pytest.mark.parametrize("case", RESCALE_CASES, ids=["-".join(map(str, c)) for c in RESCALE_CASES])
+def test_attention_running_maximum_moves(case):
+    """The online softmax's deferred rescale: with a large explicit scale (and keys whose norm
+    grows with their index) a row's running maximum rises by more than the rescale threshold
+    after its first key tile, so the accumulated weights and values are rescaled while nonzero
+    (including on the masked, ragged last tile). The oracle takes the same scale."""
+    B, H, D, S, fq, fk, f0, layout, mult, ramp = case
+    say("attention rescale", case)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    q = bf16_host(rng, (B, H, fq * S, D))
+    kf = rng.standard_normal((B, H, fk * S, D)).astype(np.float32)
+    if ramp:
+        kf *= (1.0 + 2.0 * np.arange(fk * S, dtype=np.float32) / (fk * S))[None, None, :, None]
+    k = torch.from_numpy(kf).to(torch.bfloat16)
+    v = bf16_host(rng, (B, H, fk * S, D))
+    scale = mult / np.sqrt(D)
+    o = gdn.attention_framecausal(to_dev(q, layout), to_dev(k, layout), to_dev(v, layout),
+                                  tokens_per_frame=S, q_frame0=f0, scale=scale)
+    torch.cuda.synchronize()
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    ref = attention.frame_causal_attention(qd, kd, vd, S, q_frame0=f0, scale=scale)
+    # the running maximum does move after the first 64-key tile for many rows (log2 units)
+    first = (qd @ kd[:, :, :64].transpose(0, 1, 3, 2)).max(axis=3) * scale / np.log(2)
+    vis = [min(fk * S, (f0 + t // S + 1) * S) for t in range(fq * S)]
+    full = np.array([[[(qd[b, h, t] @ kd[b, h, :vis[t]].T).max() * scale / np.log(2)
+                       for t in range(fq * S)] for h in range(H)] for b in range(B)])
+    moved = float(np.mean(full - first > 8.0))
+    say("  rows whose maximum moves by > 8 after the first tile: %.0f%%" % (100 * moved))
+    assert moved > 0.2
+    e = rel_err(to_np(o), ref)
+    say("  o err %.2e" % e)
+    assert e <= TOL
+
+
 def test_attention_deterministic_and_streaming_consistent():
     """Each frame's rows of the whole-sequence call equal a streaming call of that frame alone
     against the full key set (future keys present), bit for bit, and reruns are identical."""

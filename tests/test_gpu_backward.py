@@ -253,11 +253,19 @@ def test_backward_chain_time_out_path(monkeypatch):
     bad_r = gdn.backward_framewise(*args, schedule="fused", workspace=ws2)
     torch.cuda.synchronize()
     flag_r = flag(ws2)
+    for mode, ws in ((3, ws3), (2, ws2)):
+        with pytest.raises(gdn.GdnError) as ei:   # the C ABI reports the flag
+            gdn.check_timeout(p, mode, ws)
+        assert ei.value.code == 9
+    with pytest.raises(gdn.GdnError) as ei:       # the binding checks its own workspace
+        gdn.backward_framewise(*args, saved=saved, schedule="fused")
+    assert ei.value.code == 9
     monkeypatch.delenv("GDN_FUSED_SPIN_LIMIT")
     good = gdn.backward_framewise(*args, schedule="fused", workspace=ws2)
     torch.cuda.synchronize()
     assert flag_s == 1 and flag_r == 1
     assert flag(ws2) == 0
+    gdn.check_timeout(p, 2, ws2)
     last, early = slice((F - 1) * S, F * S), slice(0, (F - 1) * S)
     for dq, dk, dv, dg, db, dsi in (bad_s, bad_r):
         assert torch.isfinite(dv[:, :, last].float()).all()   # G of the last frame needs no wait

@@ -448,6 +448,12 @@ def test_fused_wait_timeout_path(monkeypatch):
     o, st = gdn.forward_framewise(*args, workspace=ws, schedule="fused")
     torch.cuda.synchronize()
     flag = int(ws[4:8].view(torch.int32).item())
+    with pytest.raises(gdn.GdnError) as ei:      # the C ABI reports the flag
+        gdn.check_timeout(p, 0, ws)
+    assert ei.value.code == 9
+    with pytest.raises(gdn.GdnError) as ei:      # the binding checks its own workspace
+        gdn.forward_framewise(*args, schedule="fused")
+    assert ei.value.code == 9
     o = to_np(o)
     assert flag == 1
     assert rel_err(o[:, :, :S], ro[:, :, :S]) <= TOL["bf16"]
@@ -456,4 +462,6 @@ def test_fused_wait_timeout_path(monkeypatch):
     o, st = gdn.forward_framewise(*args, workspace=ws, schedule="fused")
     torch.cuda.synchronize()
     assert int(ws[4:8].view(torch.int32).item()) == 0
+    gdn.check_timeout(p, 0, ws)
+    gdn.forward_framewise(*args, schedule="fused", check_timeout=True)
     assert rel_err(to_np(o), ro) <= TOL["bf16"]
