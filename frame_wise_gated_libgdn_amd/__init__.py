@@ -16,7 +16,8 @@ import os
 import threading
 
 __all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "forward_framewise",
-           "forward_framewise_save", "saved_size", "step_frame", "backward_framewise", "check_timeout",
+           "forward_framewise_save", "saved_size", "step_frame", "step_frame_noalloc",
+           "backward_framewise", "check_timeout",
            "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES", "GDN_F32",
            "GDN_BF16"]
 
@@ -126,6 +127,8 @@ def load():
             lib.gdn_backward_framewise_saved.argtypes = ([P] + [_vp] * 5 + [_vp, ctypes.c_size_t]
                                                          + [_vp] * 8 + [_vp, ctypes.c_size_t, _vp])
             lib.gdn_backward_framewise_saved.restype = ctypes.c_int
+            lib.gdn_step_frame_noalloc.argtypes = [P] + [_vp] * 8 + [_vp]
+            lib.gdn_step_frame_noalloc.restype = ctypes.c_int
             lib.gdn_check_timeout.argtypes = [P, ctypes.c_int, _vp, _vp]
             lib.gdn_check_timeout.restype = ctypes.c_int
             lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -453,6 +456,34 @@ def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_
     _check(load().gdn_step_frame(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                  _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out), _ptr(ws),
                                  nbytes, _stream(stream)))
+    return out, state_out
+
+
+def step_frame_noalloc(q, k, v, gamma, beta, state, commit=True, *, use_delta=True,
+                       key_scale=None, out=None, state_out=None, stream=None):
+    """step_frame through gdn_step_frame_noalloc: the workspace is the library's own static
+    device scratch (no workspace argument, nothing allocated by the library; calls on one GPU
+    share it and must not overlap). out and state_out, when not given, are allocated here by
+    torch; pass them for a call that allocates nothing at all."""
+    import torch
+    B, H, S, D = q.shape
+    if k.stride() != q.stride() or v.stride() != q.stride() or k.shape != q.shape \
+            or v.shape != q.shape:
+        raise GdnError(4, "q, k and v must share shape and strides")
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=q.dtype, device=q.device)
+    if commit and state_out is None:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    if not commit:
+        state_out = None
+    _check_f32("gamma", gamma, (B, H))
+    _check_f32("beta", beta, (B, H))
+    _check_f32("state", state, (B, H, D, D))
+    _check_f32("state_out", state_out, (B, H, D, D))
+    p = _problem(q, out, 1, use_delta, key_scale)
+    _check(load().gdn_step_frame_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                         _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),
+                                         _stream(stream)))
     return out, state_out
 
 

@@ -292,10 +292,12 @@ int fused_spin_limit() {
 }
 
 // scales: the three E4M3 scale arrays (gdn_forward_framewise_fp8), or NULL
+// scratch: take the workspace from the library's own device scratch (ws and ws_bytes are
+// ignored); every argument is validated before its address is looked up
 gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k, const void* v,
                const float* const* scales, const float* gamma, const float* beta,
                const float* state_in, void* o, float* state_out, void* ws, size_t ws_bytes,
-               void* stream, void* saved = nullptr, size_t saved_bytes = 0) {
+               void* stream, void* saved = nullptr, size_t saved_bytes = 0, bool scratch = false) {
     g_msg[0] = '\0';
     gdn_status s = check_sizes(p, step_mode);
     if (s != GDN_OK) return s;
@@ -337,6 +339,14 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     const size_t need = pl.total();
     const SavedPlan sp = saved_plan(*p);
     if (saved && !pl.fused) return fail(GDN_ERR_UNSUPPORTED, "saving for the backward needs the fused schedule");
+    if (scratch) {
+        if (need > gdn::kScratchBytes)
+            return fail(GDN_ERR_WORKSPACE, "this problem needs %zu bytes of workspace, more than the "
+                        "library's static scratch of %zu bytes; pass a workspace to gdn_step_frame",
+                        need, gdn::kScratchBytes);
+        ws = nullptr;   // a library-owned array cannot overlap the caller's buffers
+        ws_bytes = gdn::kScratchBytes;
+    }
 
     const Span sq = span_of(q, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
     const Span sk = span_of(k, B, H, T, D, p->qkv_stride_b, p->qkv_stride_h, p->qkv_stride_t, esz);
@@ -371,6 +381,11 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
             if (overlap(sso, in)) return fail(GDN_ERR_ALIAS, "state_out overlaps another buffer");
         if (state_in && state_in != state_out && overlap(sso, si))
             return fail(GDN_ERR_ALIAS, "state_out partially overlaps state_in");
+    }
+    if (scratch) {
+        const hipError_t e = gdn::scratch_address(&ws);
+        if (e != hipSuccess)
+            return fail(GDN_ERR_HIP, "address of the library's scratch: %s", hipGetErrorString(e));
     }
     if (!ws || ws_bytes < need)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -692,6 +707,13 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                           void* hip_stream) {
     return run(1, p, q, k, v, nullptr, gamma, beta, state_in, o, state_out, workspace,
                workspace_bytes, hip_stream);
+}
+
+gdn_status gdn_step_frame_noalloc(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                  const float* gamma, const float* beta, const float* state_in,
+                                  void* o, float* state_out, void* hip_stream) {
+    return run(1, p, q, k, v, nullptr, gamma, beta, state_in, o, state_out, nullptr, 0, hip_stream,
+               nullptr, 0, true);
 }
 
 gdn_status gdn_check_timeout(const gdn_problem* p, int mode, const void* workspace,

@@ -121,6 +121,11 @@ hipError_t step_launch(Kernel k, const Launch& L, hipStream_t s);
 // Whether the backward has kernels for this type / head size.
 bool backward_supported(int bf16, int D);
 
+// gdn_scratch.hip: the library's own device scratch (kScratchBytes on every GPU, 256-byte
+// aligned) for gdn_step_frame_noalloc; `out` receives the current device's copy.
+constexpr size_t kScratchBytes = GDN_STEP_SCRATCH_BYTES;
+hipError_t scratch_address(void** out);
+
 // Enqueue one kernel on `s`. Returns the HIP error of the launch.
 hipError_t launch_kernel(Kernel k, const Launch& L, hipStream_t s);
 

@@ -27,7 +27,8 @@
  * ---------------------------------------
  * Memory. Every pointer is a device pointer on the current HIP device, owned by the caller.
  *   libgdn allocates no device memory and keeps no data between calls; it may be called from
- *   several host threads at once (distinct workspaces).
+ *   several host threads at once (distinct workspaces). The one exception is the static
+ *   scratch array of gdn_step_frame_noalloc (below), shared by all its calls on a GPU.
  * Asynchrony. Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream) and the
  *   call returns; buffers must stay valid until the stream has passed the call. Each call only
  *   launches kernels on `hip_stream` (no memset or copy nodes, so it can be captured into a
@@ -65,7 +66,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 9
+#define LIBGDN_ABI_VERSION 10
 
 typedef enum {
     GDN_OK = 0,
@@ -269,6 +270,25 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
                           const float* gamma, const float* beta, const float* state_in,
                           void* o, float* state_out,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * gdn_step_frame without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, hosts that forbid hipMalloc). The
+ * workspace comes from a static device array inside the library, GDN_STEP_SCRATCH_BYTES on
+ * every GPU the library runs on, held until the process ends. The call allocates nothing.
+ *   arguments, results and errors as gdn_step_frame; a problem whose step workspace
+ *   (gdn_workspace_size(p, 1)) exceeds GDN_STEP_SCRATCH_BYTES returns GDN_ERR_WORKSPACE (before
+ *   anything is enqueued; pass a workspace to gdn_step_frame instead). The first call on a
+ *   device looks up that device's copy of the array (GDN_ERR_HIP if that fails).
+ * Every call on one GPU shares that GPU's array, whatever the stream or host thread: calls that
+ * may run at the same time on one GPU race and must be ordered by the caller (one stream, or
+ * events). Nothing in the array needs to start at zero: each launch writes what the next reads.
+ */
+#define GDN_STEP_SCRATCH_BYTES ((size_t)16 << 20)
+gdn_status gdn_step_frame_noalloc(const gdn_problem* p, const void* q, const void* k,
+                                  const void* v, const float* gamma, const float* beta,
+                                  const float* state_in, void* o, float* state_out,
+                                  void* hip_stream);
 
 /*
  * Gradients of gdn_forward_framewise for training: given dL/dO and dL/dstate_out of a scalar

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 9
+    assert gdn.abi_version() == 10
     lib = gdn.load()
     for code in range(10):
         assert lib.gdn_status_string(code)
@@ -465,3 +465,22 @@ def test_check_timeout_validation():
     fused = prob(F=3000)
     fused.schedule = 2
     assert lib.gdn_check_timeout(ctypes.byref(fused), 0, None, None) == 1
+
+
+def test_step_noalloc_validation():
+    lib = gdn.load()
+
+    def call_na(p, q=A, k=2 * A, v=3 * A, g=4 * A, b=5 * A, si=9 * A, o=6 * A, so=None):
+        return lib.gdn_step_frame_noalloc(None if p is None else ctypes.byref(p), q, k, v, g, b,
+                                          si, o, so, None)
+
+    assert call_na(None) == 1
+    assert call_na(prob(), q=None) == 1
+    assert call_na(prob(), si=None) == 1 and "state_in" in msg()
+    assert call_na(prob(), q=A + 8) == 5
+    # beyond the static scratch (16 MiB): 256 heads of D = 128 at 3520 tokens need 24 MiB
+    big = gdn.Problem(1, 256, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 256 * 3520 * 128, 3520 * 128,
+                      128, 256 * 3520 * 128, 3520 * 128, 128)
+    assert gdn.workspace_size(big, 1) > (16 << 20)
+    assert call_na(big, q=A, k=A << 12, v=A << 13, o=A << 14) == 7
+    assert "static scratch" in msg()
