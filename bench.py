@@ -44,6 +44,8 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gdn_720p_60s_bf16.json")
 KERNEL_SRC = os.path.join(ROOT, "frame_wise_gated_libgdn_amd", "csrc", "gdn_kernels.hip")
+STEP_PROFILE = os.path.join(ROOT, "profiles", "step_kernels_stream_720p_bf16.json")
+STEP_SRC = os.path.join(ROOT, "frame_wise_gated_libgdn_amd", "csrc", "gdn_step.hip")
 
 
 def log(*a):
@@ -107,9 +109,22 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha():
-    with open(KERNEL_SRC, "rb") as fh:
+def source_sha(path=KERNEL_SRC):
+    with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()
+
+
+def step_profile():
+    """Average duration (us) of each step-mode kernel from the committed rocprofv3 kernel trace
+    of the streaming workload, if it was taken on the current step-kernel source; else None."""
+    try:
+        with open(STEP_PROFILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_sha(STEP_SRC):
+        return None
+    return {k: v["avg_us"] for k, v in t.get("kernels", {}).items()}
 
 
 def traffic_for(kernel, workload, plan):
@@ -138,29 +153,69 @@ def copy_calibration(gib):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, seconds):
+    """The fp64 oracle (plain C loops, OpenMP over independent heads) on a bounded sample of
+    the workload, on every core this process may run on; plus one head on one thread, and a
+    sample of the streaming protocol (whole-state passes of every head from the oracle's own
+    committed state)."""
     import numpy as np
     import gdn_synth
     import oracle
-    nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
+    # the oracle is parallel over independent (b, h) only, so more threads than heads idle
+    avail = len(os.sched_getaffinity(0))
+    nthreads = max(1, min(avail, w.B * w.H))
     heads = list(range(w.H))
 
-    def run(nf):
-        (q, k, v), _ = gdn_synth.qkv_cpu(w, heads=heads, frames=range(nf))
-        g, b = gdn_synth.gates_cpu(w, heads=heads, frames=range(nf))
+    def run(nf, hs, threads):
+        (q, k, v), _ = gdn_synth.qkv_cpu(w, heads=hs, frames=range(nf))
+        g, b = gdn_synth.gates_cpu(w, heads=hs, frames=range(nf))
         t = time.perf_counter()
-        oracle.forward(q, k, v, g, b, use_delta=w.use_delta, nthreads=nthreads)
+        oracle.forward(q, k, v, g, b, use_delta=w.use_delta, nthreads=threads)
         return time.perf_counter() - t
 
-    t1 = run(1)
+    t1 = run(1, heads, nthreads)
     nf = int(max(1, min(16, w.F, round(seconds / max(t1 * nthreads, 1e-6)))))
     log("cpu baseline: 1 frame took %.2f s; timing %d frames on %d threads" % (t1, nf, nthreads))
-    t = run(nf) if nf > 1 else t1
+    t = run(nf, heads, nthreads) if nf > 1 else t1
     tokens = w.B * nf * w.S
+    # one head on one thread
+    nf1 = 2
+    t_one = run(nf1, [0], 1)
+    # the streaming protocol (one frame, 4 passes, commit after the last) on a sample of frames
+    ws = gdn_synth.WORKLOADS["stream_720p_bf16"]
+    sf = 2
+    M = np.zeros((ws.B, ws.H, ws.D, ws.D))
+    ts = 0.0
+    for f in range(sf):
+        for p in range(ws.passes):
+            (q, k, v), _ = gdn_synth.qkv_cpu(ws, frames=[f], pass_=p)
+            g, b = gdn_synth.gates_cpu(ws, frames=[f], pass_=p)
+            t0 = time.perf_counter()
+            _, Mn = oracle.step(q, k, v, g[..., 0], b[..., 0], M, commit=True, nthreads=nthreads)
+            ts += time.perf_counter() - t0
+        M = Mn
     return {"value": round(tokens / t, 1), "unit": "tokens/s", "cores": nthreads,
-            "kind": "oracle", "seconds": round(t, 2),
+            "cores_available": avail,
+            "kind": "oracle", "seconds": round(t, 2), "cpu_model": cpu_model(),
             "sample": "all %d heads of batch 0, frames 0-%d of %s (S=%d, D=%d): fp64 oracle, "
-                      "OpenMP over heads" % (w.H, nf - 1, w.name, w.S, w.D)}
+                      "OpenMP over heads" % (w.H, nf - 1, w.name, w.S, w.D),
+            "single_thread_one_head": {"tokens_per_s": round(w.B * nf1 * w.S / t_one, 1),
+                                       "seconds": round(t_one, 2),
+                                       "sample": "head 0, frames 0-%d, 1 thread" % (nf1 - 1)},
+            "stream": {"frames_per_s": round(sf / ts, 3), "seconds": round(ts, 2),
+                       "sample": "%s: frames 0-%d x %d passes, all %d heads, %d threads"
+                                 % (ws.name, sf - 1, ws.passes, ws.H, nthreads)}}
 
 
 def stream_mode(dev, nframes, ev, stream):
@@ -222,7 +277,11 @@ def stream_mode(dev, nframes, ev, stream):
                                  "max": round(float(lat.max()), 4)},
             "frames_per_s": round(nframes / (total / 1e3), 1),
             "pass_us_median": round(float(np.median(lat)) * 1e3 / w.passes, 2),
-            "pass_kernel_us_median": {k_: round(float(np.median(v_)), 2) for k_, v_ in kus.items()}}
+            # each launch bracketed by its own events (the events add gaps between launches, so
+            # these sum to more than a pass), and the rocprofv3 kernel averages of the same
+            # workload from the committed summary (null when taken on other kernel source)
+            "pass_kernel_us_traced": {k_: round(float(np.median(v_)), 2) for k_, v_ in kus.items()},
+            "pass_kernel_us_rocprof": step_profile()}
 
 
 def backward_mode(w, dev, steps, ev, stream):
@@ -612,8 +671,11 @@ def main():
             acc[1] += ev.ms(trace[i][2 * j], trace[i][2 * j + 1])
             acc[2] += units
     kms = {k_: a[1] / args.steps for k_, a in per.items()}
-    log("timed %d steps: %.3f ms/step; summed launch ms per step %s" % (
-        args.steps, ms, {k_: round(x, 3) for k_, x in kms.items()}))
+    # per call: from the first launch's start event to the last launch's end event
+    calls = sorted(ev.ms(trace[i][0], trace[i][2 * nl - 1]) for i in range(args.steps))
+    call_median = calls[len(calls) // 2] if len(calls) % 2 else 0.5 * (calls[len(calls) // 2 - 1] + calls[len(calls) // 2])
+    log("timed %d steps: %.3f ms/step (median %.3f, min %.3f); summed launch ms per step %s" % (
+        args.steps, ms, call_median, calls[0], {k_: round(x, 3) for k_, x in kms.items()}))
 
     tokens = w.B * w.F * w.S
     bytes_alg = 4 * w.B * w.H * w.F * w.S * w.D * esz          # Q, K, V read + O written
@@ -633,6 +695,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_call_median": round(call_median, 4),
+        "ms_per_call_min": round(calls[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
