@@ -106,6 +106,8 @@ def parse():
                     help="forward schedule (auto: the library's choice)")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--stream-only", action="store_true",
+                    help="only the streaming step leg (for profiling its kernels); prints its JSON")
     return ap.parse_args()
 
 
@@ -610,6 +612,12 @@ def main():
         copy_calibration(args.copy_calib_gib)
         return
     gdn.load()
+    if args.stream_only:
+        ev = HipEvents()
+        print(json.dumps({"stream": stream_mode(torch.device("cuda:0"), args.stream_frames, ev,
+                                                torch.cuda.current_stream().cuda_stream)}), flush=True)
+        ev.close()
+        return
     w = gdn_synth.WORKLOADS[args.workload]
     assert not w.step_mode, "the forward bench needs a forward workload"
     dev = torch.device("cuda:0")

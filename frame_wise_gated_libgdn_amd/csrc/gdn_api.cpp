@@ -72,7 +72,7 @@ bool choose_fused(const gdn_problem& p, int step_mode) {
     return (int64_t)p.batch * p.heads * p.frames >= kFusedMinItems;
 }
 
-// The column-block step reads a frame's Q rows and writes its O rows through 32-bit buffer
+// The bf16 step (D = 64 / 128) reads a frame's Q rows and writes its O rows through 32-bit buffer
 // offsets (rows up to S, the first past the frame, are addressed): S rows of either stride
 // must stay below 2 GiB. A single-token frame is addressed with a stride of one row.
 bool step_rows_fit(const gdn_problem& p) {
@@ -99,8 +99,8 @@ bool choose_bwd_chain(const gdn_problem& p) {
 }
 
 constexpr int kTargetGroups = 2048;  // workgroups wanted per parallel launch (256 CUs x 8)
-constexpr int kStepPartials = 512;   // column-block step: partial workgroups (two per CU)
-constexpr int kStepOutputs = 256;    // column-block step: output workgroups
+constexpr int kStepPartials = 256;   // Gram step: partial workgroups (one per CU)
+constexpr int kStepOutputs = 256;    // Gram step: output workgroups
 
 // mode: 0 forward, 1 step, 2 backward, 3 backward from saved states (no forward recompute)
 Plan make_plan(const gdn_problem& p, int mode) {
@@ -147,13 +147,14 @@ Plan make_plan(const gdn_problem& p, int mode) {
     pl.ctl_bytes = (size_t)(2 + BH * gdn::kChainGroups) * 4;
     pl.chain_bytes = (size_t)(2 * BH * D * D * 4);
     if (step_mode && pl.fused) {
-        // partials: 32 value columns x one token split (a multiple of 64 tokens); outputs: at
-        // most 256 tokens each; fp32 partials [BH][D/32][splits][D][32]; the new state
-        // transposed in bf16
-        const int64_t NJ = D / 32;
-        want = (kStepPartials + BH * NJ - 1) / (BH * NJ);
-        want = std::max<int64_t>(1, std::min<int64_t>(want, tiles64));
-        pl.split_tokens = (int)(((tiles64 + want - 1) / want) * 64);
+        // Gram partials: step_halves(D) workgroups per (b, h, token split), about one per CU in
+        // all, splits of at least 128 tokens (each adds a D^3 product and a D x D partial), a
+        // multiple of 16; fp32 partials [BH][splits][D][D]; outputs: at most 256 tokens each;
+        // the new state transposed in bf16
+        const int64_t hv = gdn::step_halves((int)D);
+        int64_t ns = (kStepPartials + BH * hv - 1) / (BH * hv);
+        ns = std::max<int64_t>(1, std::min<int64_t>(ns, (S + 127) / 128));
+        pl.split_tokens = (int)(((tiles16 + ns - 1) / ns) * 16);
         pl.nsplit = (int)((S + pl.split_tokens - 1) / pl.split_tokens);
         int64_t oc = (kStepOutputs + BH - 1) / BH;
         oc = std::max<int64_t>((tiles16 + 15) / 16, std::min<int64_t>(oc, tiles16));

@@ -34,7 +34,7 @@ struct Launch {
                          //   [2 + bh * kChainGroups + g] last frame of (b, h) whose column
                          //   group g of the state is published
     float* chain;        // workspace (fused): published states, [2][B*H][D][D] fp32, [c][n] order
-    int step_cols;       // step: the column-block kernels of gdn_step.hip (bf16, D = 64 / 128)
+    int step_cols;       // step: the Gram-form kernels of gdn_step.hip (bf16, D = 64 / 128)
     float* save_states;  // fused forward, training: fp32 states, [B*H][F + 1][D][D] transposed
                          //   (slot 0 the initial state, slot f + 1 = M_f), or NULL
     void* save_recs;     // ... and the frames' Ghat planes ([B*H][F] records of rec_stride bytes)
@@ -75,7 +75,7 @@ enum Kernel {
     K_SCAN_STATES = 9,   // the forward scan with fp32 per-frame states (backward's recompute)
     K_TCONV = 10,        // block-causal temporal convolution
     K_ATTN = 11,         // frame-causal softmax attention
-    K_STEP_OUTPUT = 12,  // step (column-block kernels): outputs of the frame
+    K_STEP_OUTPUT = 12,  // step (Gram-form kernels): outputs of the frame
     K_BWD_QDO = 13       // backward: C_f = Q_f^T dO_f and dQ_f in one pass over Q and dO
 };
 
@@ -114,9 +114,11 @@ constexpr int kSpinLimitDefault = 1 << 20;  // polls of about a microsecond each
 
 // Whether the fused single-pass forward has a kernel for this type / head size.
 bool fused_supported(int bf16, int D);
-// Step mode's column-block kernels (gdn_step.hip): whether they cover this type / head size,
+// Step mode's Gram-form kernels (gdn_step.hip): whether they cover this type / head size,
 // and the launch of K_STEP_PARTIAL, K_STEP_REDUCE or K_STEP_OUTPUT.
 bool step_cols_supported(int bf16, int D);
+// Workgroups per token split in the Gram step (each forms D / halves rows of the split's update).
+constexpr int step_halves(int D) { return D == 128 ? 2 : 1; }
 hipError_t step_launch(Kernel k, const Launch& L, hipStream_t s);
 // Whether the backward has kernels for this type / head size.
 bool backward_supported(int bf16, int D);

@@ -4,7 +4,7 @@
 // Forward, staged:  products (gram items of every frame) -> [combine] -> scan -> products
 //                   (output items of every frame).
 // Forward, fused:   reset of the ticket counter and frame flags -> fused kernel.
-// Step:             bf16 with D = 64 or 128: the column-block kernels step_partial ->
+// Step:             bf16 with D = 64 or 128: the Gram-form kernels step_partial ->
 //                   step_reduce -> step_output; otherwise step_partial -> step_reduce ->
 //                   products (output items of the one frame).
 // Temporal conv:    one launch (the whole block or sequence).

@@ -1,26 +1,22 @@
-// Step mode for bf16 data with D = 64 or 128: one frame from a cached state, the update as
-// written (gen-hub.ru, "NVIDIA SANA-WM: минутное 720p видео с одной видеокарты", section
-// "Архитектура: четыре нетривиальных решения"; streaming by frames: jefxiong.cn digest, item 1):
-//     P = (c K) M,   R = V - gamma P,   M' = gamma M + beta (c K)^T R,   O = Q M'.
-//
-// Columns of M' only depend on the same columns of M (R's column j needs column j of M), so the
-// update splits into independent blocks of 32 value columns. Three launches on the stream:
-//   1. step_partials_kernel, one workgroup per (b, h, column block J, token split p):
-//      P = K M[:, J] on MFMA for each 16-token tile (A = K rows, B = M[:, J] in bf16, held in
-//      registers), then U_p[:, J] = K^T (V[:, J] - gamma c P) accumulated over the split (A = K^T
-//      by transposed LDS reads, B = V[:, J] exact plus the bf16-rounded prediction term),
-//      stored as an fp32 partial. K and V come in 64-token chunks through registers (three in
-//      flight while one is used): each wave loads its 16 K rows in the prediction's A-operand
-//      layout, so the prediction runs from registers, then writes them into LDS unpadded with
-//      an XOR swizzle of each row's 16-byte chunks; one barrier per chunk (LDS double
-//      buffered). The column blocks of one (b, h, split) read the same K rows and are
-//      placed on one XCD (workgroup i runs on XCD i mod 8), so K comes from that XCD's L2
-//      after its first read.
-//   2. step_merge_kernel, one workgroup per (b, h, J, 32 rows): M' = gamma M + beta c sum_p U_p
+// Step mode for bf16 data with D = 64 or 128: one frame from a cached state (gen-hub.ru, "NVIDIA
+// SANA-WM: минутное 720p видео с одной видеокарты", section "Архитектура: четыре нетривиальных
+// решения"; streaming by frames: jefxiong.cn digest, item 1):
+//     R = V - gamma (c K) M,   M' = gamma M + beta (c K)^T R,   O = Q M'.
+// With the residual expanded, (c K)^T R = c (K^T V) - gamma c^2 (K^T K) M, so the part of the
+// update that runs over the frame's tokens is the pair of products G = K^T K and B = K^T V, which
+// split over tokens without the state; the state enters once per split, through a D x D x D
+// product. Three launches on the stream:
+//   1. step_gram_kernel, one workgroup of 8 waves per (b, h, token split p) (one per CU at the
+//      streaming shape): K and V of the split go from global memory straight into LDS (16-byte
+//      direct loads in stages of 112 tokens at D = 128, the next stage loading while one is
+//      used; XOR-swizzled 16-byte chunks), [G_p | B_p] = K_p^T [K_p | V_p] accumulates on v_mfma_f32_32x32x16_bf16
+//      (every operand a transposed LDS read), then U_p = B_p - gamma c G_p M with -gamma c G_p
+//      and M in bf16, stored as an fp32 partial. K and V cross HBM once.
+//   2. step_sum_kernel, one workgroup per (b, h, 32 x 32 tile): M' = gamma M + beta c sum_p U_p
 //      in split order, state_out, and the bf16 transposed copy M'^T.
 //   3. step_output_kernel, one workgroup per (b, h, chunk of at most 256 tokens): M'^T staged
 //      through LDS into registers (the A operand of every tile), O^T = M'^T Q^T per 16-token
-//      tile with 16-byte stores, every Q tile of the chunk loaded before the first product.
+//      tile with 16-byte stores; the chunk's Q loads stay in flight across the staging barrier.
 // Nothing waits on another workgroup inside a launch; the stream orders the three, so results
 // are bitwise reproducible. (A single launch that hands partials and states between
 // workgroups through device-coherent memory was slower: each such hand-off costs a memory
@@ -34,21 +30,25 @@ namespace {
 
 typedef __bf16 bf16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kThreads = 256;   // 4 waves
-constexpr int kCW = 32;         // value columns per partial role
-constexpr int kSC = 64;         // tokens per staged chunk
-constexpr int kRing = 2;        // staged chunks in LDS
-constexpr int kStages = 3;      // chunks in registers (in flight while one is used)
-constexpr int kQD = 4;          // 16-token output tiles per wave (a chunk has at most 16)
+constexpr int kGramThreads = 512;   // Gram kernel: 8 waves, one workgroup per CU
+constexpr int kSumThreads = 256;    // sum kernel: one 32 x 32 tile of 16 fp32 per lane, 4 per thread
+constexpr int kOutThreads = 256;    // output kernel: 4 waves
+constexpr int kQD = 4;              // 16-token output tiles per wave (a chunk has at most 16)
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x16_bf16: lane l = 32 g + r holds A row r and B column r over the contraction
+// slice [8 g, 8 g + 8), and C rows 8 i + 4 g + q (register 4 i + q) of column r
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -64,51 +64,324 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 
-// XOR swizzle of the 16-byte chunks of row r of an unpadded LDS tile with CH chunks per row:
-// chunk c of row r is stored at chunk c ^ swz(r). The masks (functions of the bits b_i of r) make
-// the tile's accesses free of bank conflicts whether the LDS serves 64 banks per clock (16 lanes
-// of a 16-byte access, 32 lanes of an 8-byte one) or 32 (8 and 16 lanes):
-//   CH = 16, 8 (K chunk, D = 128, 64): 16-byte row stores (16 rows, one chunk each) and
-//            transposed reads (rows k0 + 4 g + 0..3, two neighbouring chunks);
-//   CH = 4 (V chunk): transposed reads of two neighbouring chunks (the stores fill whole rows).
-template <int CH> __device__ __forceinline__ int swz(int r) {
-    const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
-    if constexpr (CH == 16) return (b3 ^ b2) | b0 << 1 | b1 << 2 | b2 << 3;
-    else if constexpr (CH == 8) return (b3 ^ b2) | b1 << 1 | (b0 ^ b2) << 2;
-    else return (b1 ^ b2) << 1;
-}
-// The prediction tile [kCW][kSC] (8-byte accesses, 16 rows x 4 units): unit u of row r is
-// stored at unit u ^ (r mod 16).
-__device__ __forceinline__ int pct_off(int row, int col) { return row * kSC + ((((col >> 2) ^ row) & 15) << 2); }
-
-// Lane (r, g) of each 16-lane group receives X[k0 + 4 g + j][c0 + r], j = 0..3, from a swizzled
-// [row][CH chunks] bf16 LDS tile (ds_read_tr16_b64: destination lane i takes element i mod 4 of
-// the four values at the address of source lane 4 j + i / 4, so source lane s points at row
-// k0 + 4 g + s / 4, columns c0 + 4 (s mod 4) .. + 3).
-template <int CH> __device__ __forceinline__ u32x2 read_tr(const bf16* X, int k0, int c0, int r, int g) {
-    const int row = k0 + 4 * g + (r >> 2);
-    const int c = c0 / 8 + ((r & 3) >> 1);
-    const bf16* a = X + row * CH * 8 + ((c ^ swz<CH>(row)) * 8) + 4 * (r & 1);
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a));
-}
-
-// Barrier of the staged loop: this wave's LDS accesses are complete, then s_barrier. Unlike
+// Barrier on LDS accesses only: this wave's LDS accesses are complete, then s_barrier. Unlike
 // __syncthreads() it does not wait for outstanding global loads (its workgroup release fence
-// lowers to vmcnt(0), which would drain the chunks in flight into registers).
+// lowers to vmcnt(0)).
 __device__ __forceinline__ void lds_barrier() { __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int D> struct PartLds {
-    static constexpr int KB = kSC * D * 2;     // K chunk [token][D]
-    static constexpr int VB = kSC * kCW * 2;   // V chunk [token][kCW]
-    static constexpr int BUF = KB + VB;
-    static constexpr int PB = kCW * kSC * 2;   // prediction tile [kCW][kSC] (pct_off)
-    static constexpr int MTOFF = kRing * (BUF + PB);   // M[:, J]^T in bf16: [kCW][D + 8]
-    static constexpr int BYTES = MTOFF + kCW * (D + 8) * 2;
-};
-template <int D> struct OutLds {
-    static constexpr int BYTES = D * D * 2;    // M'^T, swizzled (out_mask)
+// ---------------------------------------------------------------------------- Gram kernel
+// Stage of the split in LDS: K and V of TB tokens, [token][D] bf16 rows without padding (56 KB
+// for the pair). Two stages are resident (separate arrays, so that the compiler can tell reads
+// of one from the direct loads into the other).
+template <int D> struct GramLds {
+    static constexpr int TB = D == 128 ? 112 : 224;   // tokens per stage (a multiple of 16)
+    static constexpr int TILE = TB * D;               // bf16 elements of one K or V stage
 };
 
+// XOR swizzle of the 16-byte chunks of a token row of a [token][D] stage (CH = D / 8 chunks per
+// row): chunk c of row r is stored at chunk c ^ swz(r). The masks keep the transposed reads below
+// (per 16-lane group 4 rows and 2 neighbouring chunks; the four groups of a wave at rows +0 / +4,
+// columns +0 / +16; 8 bytes per lane) free of bank conflicts with 64 or 32 banks per clock.
+template <int CH> __device__ __forceinline__ int gswz(int r) {
+    const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
+    if constexpr (CH == 16) return b0 | b1 << 1 | (b0 ^ b2) << 2 | (b1 ^ b3) << 3;
+    else return b1 | (b0 ^ b2) << 1 | (b0 ^ b1 ^ b3) << 2;
+}
+
+// Lane l = 32 g + r receives X[krow + 4 g + j][c0 + r], j = 0..3, from a swizzled [row][W]
+// bf16 LDS matrix (W elements per row, chunk c of row r stored at chunk c ^ gswz(r)):
+// ds_read_tr16_b64 gives destination lane i of each 16-lane group element i mod 4 of the four
+// b16 values at the address of source lane 4 j + i / 4; so source lane s of group q = l / 16
+// points at row krow + 4 (q / 2) + s / 4, columns c0 + 16 (q mod 2) + 4 (s mod 4) .. + 3. krow is
+// a multiple of 8 and the swizzle depends on the row's low 4 bits only, so the address of a read
+// at row krow + 16 k is a per-lane offset (tr_off, for krow = 0 or 8) plus 16 k rows.
+template <int W> __device__ __forceinline__ int tr_off(int krow, int c0, int lane) {
+    const int q = lane >> 4, s = lane & 15;
+    const int row = krow + 4 * (q >> 1) + (s >> 2);
+    const int col = c0 + 16 * (q & 1) + 4 * (s & 3);
+    return row * W + (((col >> 3) ^ gswz<W / 8>(row)) * 8) + (col & 7);
+}
+__device__ __forceinline__ u32x2 read_tr(const bf16* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+// Element (row, col) of the same swizzled [row][W] layout (col a multiple of 4 for 8-byte and of
+// 8 for 16-byte accesses)
+template <int W> __device__ __forceinline__ int sw_off(int row, int col) {
+    return row * W + (((col >> 3) ^ gswz<W / 8>(row)) * 8) + (col & 7);
+}
+
+// Contraction operand over the 16 rows kr .. kr + 15 (kr a multiple of 16) of a [row][W] matrix
+// for one 32-column block, whose per-lane offsets for rows 0 and 8 are o0 and o8: lane (r, g)
+// holds column c0 + r at rows kr + 4 g + 0..3 (slots 0-3) and kr + 8 + 4 g + 0..3 (slots 4-7).
+// A and B operands use the same row order, so the product sums over the 16 rows.
+template <int W> __device__ __forceinline__ bf16x8 frag(const bf16* X, int kr, int o0, int o8) {
+    return join(read_tr(X + kr * W + o0), read_tr(X + kr * W + o8));
+}
+// The same with the slots of tokens at or past `valid` zeroed (the ragged end of a split; the
+// rows there hold copies of the split's last row, so the other operand stays finite)
+__device__ __forceinline__ bf16x8 mask_tail(bf16x8 x, int krow, int lane, int valid) {
+    const int t0 = krow + 4 * (lane >> 5);
+    const u32x4 v = __builtin_bit_cast(u32x4, x);
+    const uint32_t m0 = (t0 < valid ? 0xFFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
+    const uint32_t m1 = (t0 + 2 < valid ? 0xFFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+    const uint32_t m2 = (t0 + 8 < valid ? 0xFFFFu : 0u) | (t0 + 9 < valid ? 0xFFFF0000u : 0u);
+    const uint32_t m3 = (t0 + 10 < valid ? 0xFFFFu : 0u) | (t0 + 11 < valid ? 0xFFFF0000u : 0u);
+    return __builtin_bit_cast(bf16x8, u32x4{v[0] & m0, v[1] & m1, v[2] & m2, v[3] & m3});
+}
+
+// Role ((b h) * nsplit + p) * HV + hr: split p of (b, h), rows [hr DR, hr DR + DR) of U (DR =
+// D / HV key features; HV = step_halves(D)). The workgroup forms those rows of [G | B] = K^T
+// [K | V] over the split's tokens (DR rows; 2 D columns: D of G, then D of B). Wave w owns RTW x
+// CTW tiles of 32 x 32: local rows 32 RTW (w mod 2), columns 32 CTW (w / 2); waves 0-3 hold G,
+// waves 4-7 hold B. The epilogue writes -gamma c G (transposed) and M to LDS in bf16 and the B
+// waves finish their tiles as U_p = B_p + (-gamma c G_p) M. The partial goes to
+// part[role][tile][lane][16 fp32], tile = local 32-row block * (D / 32) + 32-column block of U.
+template <int D, bool DELTA>
+__global__ __launch_bounds__(kGramThreads, 1) void step_gram_kernel(Launch L) {
+    using GL = GramLds<D>;
+    constexpr int HV = step_halves(D), DR = D / HV;
+    constexpr int TB = GL::TB, CH = D / 8;
+    constexpr int SLOTS = TB * CH;                    // 16-byte slots of one K (or V) stage
+    constexpr int INSTR = 2 * SLOTS / kGramThreads;   // direct loads per thread per stage
+    static_assert(SLOTS % 64 == 0 && (2 * SLOTS) % kGramThreads == 0, "whole wave instructions");
+    static_assert(SLOTS % (64 * INSTR) == 0, "the K / V boundary falls between waves");
+    constexpr int RTW = DR / 64, CTW = D / 64;        // 32 x 32 tiles per wave: rows, columns
+    constexpr int NTL = (DR / 32) * (D / 32);         // tiles of this workgroup's rows of U
+    static_assert(2 * RTW * 4 * CTW * 32 * 32 == 2 * DR * D, "eight waves cover the rows of [G | B]");
+    __shared__ __attribute__((aligned(16))) bf16 st0[2][GL::TILE];   // K, V of even stages
+    __shared__ __attribute__((aligned(16))) bf16 st1[2][GL::TILE];   // K, V of odd stages
+    __shared__ __attribute__((aligned(16))) bf16 ms[DELTA ? D * D : 8];   // M in bf16, [k][n]
+    static_assert(D * DR <= 2 * GL::TILE, "the epilogue's copy of G fits in one stage buffer");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+    const int r = lane & 31, g = lane >> 5;
+    // workgroup i runs on XCD i mod 8; XCD x takes the contiguous stretch [x n8, (x + 1) n8) of
+    // the roles in order, so the two halves of a split read its K and V through one L2 and the
+    // splits of one (b, h) share its state there (the grid is padded to 8 n8 workgroups; the
+    // padding returns at once)
+    const int nrole = L.B * L.H * L.nsplit * HV;
+    const int n8 = (nrole + 7) / 8;
+    const int role = (int)(blockIdx.x % 8) * n8 + (int)(blockIdx.x / 8);
+    if (role >= nrole) return;
+    const int hr = role % HV, bh = role / HV / L.nsplit, p = role / HV % L.nsplit;
+    const int b = bh / L.H, h = bh % L.H;
+    const int t0 = p * L.split_tokens, t1 = min(L.S, t0 + L.split_tokens);
+    const int ntok = t1 - t0, nst = (ntok + TB - 1) / TB;
+    const int64_t io = (int64_t)b * L.sb + (int64_t)h * L.sh;
+    const bf16* kb = (const bf16*)L.k + io;
+    const bf16* vb = (const bf16*)L.v + io;
+
+    // the state, for the epilogue: thread t < D^2 / 32 holds rows 4 (t / (D / 8)) .. + 3, columns
+    // 8 (t mod (D / 8)) .. + 7 of M; loaded first, so that the stage loads queue behind it
+    constexpr int MB = D * D / 32;
+    static_assert(MB <= kGramThreads, "one 4 x 8 block of M per thread");
+    const bool mthread = DELTA && tid < MB;
+    const int mj0 = 4 * (tid / (D / 8)), mn0 = 8 * (tid % (D / 8));
+    f32x4 mx[4][2];
+    if (mthread) {
+        const float* M = L.state_in + (int64_t)bh * D * D + mj0 * D + mn0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) mx[e][hh] = *(const f32x4*)(M + e * D + 4 * hh);
+    }
+
+    // stage n (tokens t0 + n TB ..) into buffer tl: instruction ins of the workgroup fills slots
+    // 64 ins .. 64 ins + 63 of the K | V pair (lane i's 16 bytes land at slot 64 ins + i; the
+    // lane picks the source chunk that the swizzle puts there); rows past the split load its
+    // last row and are zeroed in the operands
+    auto issue = [&](int n, bf16 (&tl)[2][GL::TILE]) {
+        const int s0 = t0 + n * TB;
+#pragma unroll
+        for (int i = 0; i < INSTR; ++i) {
+            const int ins = wave * INSTR + i;
+            const bool isv = ins * 64 >= SLOTS;
+            const int u = ins * 64 + lane - (isv ? SLOTS : 0);
+            const int row = u / CH, c = (u % CH) ^ gswz<CH>(row);
+            const bf16* src = (isv ? vb : kb) + (int64_t)min(s0 + row, t1 - 1) * L.st + c * 8;
+            bf16* dst = &tl[isv ? 1 : 0][(ins * 64 - (isv ? SLOTS : 0)) * 8];
+            __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        }
+    };
+    issue(0, st0);
+    if (mthread) {
+        // M in bf16 for the epilogue's B operand (16-byte rows of the swizzled [k][n] layout);
+        // the stage-0 loads stay in flight (issued after M's)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            *(u32x4*)(ms + sw_off<D>(mj0 + e, mn0)) =
+                u32x4{pack2(mx[e][0][0], mx[e][0][1]), pack2(mx[e][0][2], mx[e][0][3]),
+                      pack2(mx[e][1][0], mx[e][1][1]), pack2(mx[e][1][2], mx[e][1][3])};
+    }
+
+    const int rt0 = RTW * (wave & 1), ct0 = CTW * (wave >> 1);
+    const bool gwave = ct0 < D / 32;            // this wave's block lies in G
+    const bool busy = DELTA || !gwave;          // without the delta term G is not needed
+    // per-lane offsets of the operand reads (rows 0 and 8 of a 16-token step): A = the wave's
+    // key features of K, B = its columns of K (G) or of V (B)
+    const int bc0 = gwave ? 32 * ct0 : 32 * ct0 - D;
+    int oa[RTW][2], ob[CTW][2];
+#pragma unroll
+    for (int a = 0; a < RTW; ++a)
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) oa[a][h8] = tr_off<D>(8 * h8, hr * DR + 32 * (rt0 + a), lane);
+#pragma unroll
+    for (int c = 0; c < CTW; ++c)
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) ob[c][h8] = tr_off<D>(8 * h8, bc0 + 32 * c, lane);
+    f32x16 acc[RTW][CTW];
+#pragma unroll
+    for (int a = 0; a < RTW; ++a)
+#pragma unroll
+        for (int c = 0; c < CTW; ++c)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[a][c][j] = 0.f;
+
+    // stage n from buffer cur, with stage n + 1 loading into nxt meanwhile. The barrier (whose
+    // fence waits for this wave's loads) makes every wave's loads of stage n visible, and every
+    // wave is past its reads of stage n - 1 from nxt before the next loads go there. The loads
+    // of the other buffer are in flight only after the wait, so the compiler, which tells the
+    // two arrays apart, adds no wait for them before the reads of cur.
+    auto stage = [&](int n, bf16 (&cur)[2][GL::TILE], bf16 (&nxt)[2][GL::TILE]) __attribute__((always_inline)) {
+        __syncthreads();
+        if (n + 1 < nst) issue(n + 1, nxt);
+        const int valid = min(TB, ntok - n * TB);
+        if (busy) {
+            const bf16* kt = cur[0];
+            const bf16* bt = gwave ? cur[0] : cur[1];   // B operand: K (G) or V (B)
+            // every 16-token step of the stage; the operands of step kk + 1 are read while the
+            // products of step kk run (two register sets); steps past `valid` add zeros (their
+            // A slots are masked)
+            constexpr int NK = TB / 16;
+            bf16x8 fa[2][RTW], fb[2][CTW];
+            auto load = [&](int kk, int set) __attribute__((always_inline)) {
+                const int kr = 16 * kk;
+#pragma unroll
+                for (int a = 0; a < RTW; ++a) fa[set][a] = mask_tail(frag<D>(kt, kr, oa[a][0], oa[a][1]), kr, lane, valid);
+#pragma unroll
+                for (int c = 0; c < CTW; ++c) fb[set][c] = frag<D>(bt, kr, ob[c][0], ob[c][1]);
+            };
+            load(0, 0);
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                if (kk + 1 < NK) load(kk + 1, (kk + 1) & 1);
+#pragma unroll
+                for (int a = 0; a < RTW; ++a)
+#pragma unroll
+                    for (int c = 0; c < CTW; ++c) acc[a][c] = mfma32(fa[kk & 1][a], fb[kk & 1][c], acc[a][c]);
+            }
+        }
+    };
+    for (int n = 0; n < nst; n += 2) {
+        stage(n, st0, st1);
+        if (n + 1 < nst) stage(n + 1, st1, st0);
+    }
+
+    if constexpr (DELTA) {
+        // every wave is done with the stages: -gamma c G^T into stage buffer 0 as a swizzled
+        // [k][i] bf16 matrix (k the D key features, i this workgroup's DR rows; 8-byte stores of
+        // the C layout's 4 consecutive rows)
+        lds_barrier();
+        bf16* gs = &st0[0][0];
+        const float ngc = -L.gamma[bh] * L.c;
+        if (gwave) {
+#pragma unroll
+            for (int a = 0; a < RTW; ++a)
+#pragma unroll
+                for (int c = 0; c < CTW; ++c)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const f32x16& x = acc[a][c];
+                        *(u32x2*)(gs + sw_off<DR>(32 * (ct0 + c) + r, 32 * (rt0 + a) + 8 * i + 4 * g)) =
+                            u32x2{pack2(ngc * x[4 * i], ngc * x[4 * i + 1]), pack2(ngc * x[4 * i + 2], ngc * x[4 * i + 3])};
+                    }
+        }
+        lds_barrier();
+        if (!gwave) {
+            // U = B + (-gamma c G) M over the D key features, 16 at a time; both operands by
+            // transposed reads in the same row order: A from G^T (rows k, columns i), B from M
+            // (rows k, columns n)
+            int ga[RTW][2], gb[CTW][2];
+#pragma unroll
+            for (int a = 0; a < RTW; ++a)
+#pragma unroll
+                for (int h8 = 0; h8 < 2; ++h8) ga[a][h8] = tr_off<DR>(8 * h8, 32 * (rt0 + a), lane);
+#pragma unroll
+            for (int c = 0; c < CTW; ++c)
+#pragma unroll
+                for (int h8 = 0; h8 < 2; ++h8) gb[c][h8] = tr_off<D>(8 * h8, 32 * (ct0 + c) - D, lane);
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                bf16x8 fa[RTW], fb[CTW];
+#pragma unroll
+                for (int a = 0; a < RTW; ++a) fa[a] = frag<DR>(gs, 16 * ks, ga[a][0], ga[a][1]);
+#pragma unroll
+                for (int c = 0; c < CTW; ++c) fb[c] = frag<D>(ms, 16 * ks, gb[c][0], gb[c][1]);
+#pragma unroll
+                for (int a = 0; a < RTW; ++a)
+#pragma unroll
+                    for (int c = 0; c < CTW; ++c) acc[a][c] = mfma32(fa[a], fb[c], acc[a][c]);
+            }
+        }
+    }
+    if (!gwave) {
+        float* pp = L.part + (int64_t)role * NTL * 1024;
+#pragma unroll
+        for (int a = 0; a < RTW; ++a)
+#pragma unroll
+            for (int c = 0; c < CTW; ++c) {
+                const int tile = (rt0 + a) * (D / 32) + (ct0 + c - D / 32);
+                f32x4* dst = (f32x4*)(pp + (tile * 64 + lane) * 16);
+                const f32x16& x = acc[a][c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i] = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+            }
+    }
+}
+
+// ------------------------------------------------------------------------------ sum kernel
+// One 32 x 32 tile of one (b, h): thread t takes registers 4 (t mod 4) .. + 3 of lane t / 4 of
+// the partial layout, i.e. rows 32 rt + 8 (t mod 4) + 4 g + 0..3 of column 32 ct + r (lane =
+// 32 g + r). M' = gamma M + beta c sum_p U_p, summed in split order.
+template <int D>
+__global__ __launch_bounds__(kSumThreads) void step_sum_kernel(Launch L) {
+    constexpr int NT = (D / 32) * (D / 32), HV = step_halves(D), RTH = D / 32 / HV;
+    constexpr int NTL = NT / HV;                     // tiles of one workgroup's partial
+    const int tid = threadIdx.x, lane = tid >> 2, part = tid & 3;
+    const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
+    const int rt = tile / (D / 32), ct = tile % (D / 32);
+    const int hr = rt / RTH, lt = (rt % RTH) * (D / 32) + ct;   // half and local tile of the partial
+    const int i = 32 * rt + 8 * part + 4 * (lane >> 5), j = 32 * ct + (lane & 31);
+    const int NS = L.nsplit;
+    // partial of split p: role ((b h) NS + p) HV + hr; consecutive splits are HV NTL tiles apart
+    const float* src = L.part + (((int64_t)bh * NS * HV + hr) * NTL + lt) * 1024 + lane * 16 + 4 * part;
+    const float* min_ = L.state_in + (int64_t)bh * D * D;
+    float m0[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) m0[qq] = min_[(i + qq) * D + j];
+    constexpr int BATCH = 8;   // partials in flight
+    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < NS; p0 += BATCH) {
+        f32x4 x[BATCH];
+#pragma unroll
+        for (int e = 0; e < BATCH; ++e) x[e] = *(const f32x4*)(src + (int64_t)min(p0 + e, NS - 1) * HV * NTL * 1024);
+#pragma unroll
+        for (int e = 0; e < BATCH; ++e)
+            if (p0 + e < NS) u += x[e];
+    }
+    const float gm = L.gamma[bh], bc = L.beta[bh] * L.c;
+    float m[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) m[qq] = gm * m0[qq] + bc * u[qq];
+    if (L.state_out) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) L.state_out[(int64_t)bh * D * D + (i + qq) * D + j] = m[qq];
+    }
+    *(u32x2*)((bf16*)L.mt + (int64_t)bh * D * D + j * D + i) = u32x2{pack2(m[0], m[1]), pack2(m[2], m[3])};
+}
+
+// ---------------------------------------------------------------------------- output kernel
 // Output column of row m of 16-row tile jt of the A operand M'^T: tiles 2p and 2p + 1 cover
 // columns 32p .. 32p + 31 so that lane (r, g) of their C tiles holds 8 consecutive columns.
 __device__ __forceinline__ int out_col(int jt, int m) { return 32 * (jt >> 1) + 8 * (m >> 2) + 4 * (jt & 1) + (m & 3); }
@@ -127,216 +400,15 @@ template <int D> __device__ __forceinline__ int out_off(int r, int c) {   // c: 
     return r * D + (((c >> 2) ^ (out_mask<D>(r) & ~1)) << 2);
 }
 __device__ __forceinline__ u32x4 half_swap(u32x4 v, bool sw) { return sw ? u32x4{v[2], v[3], v[0], v[1]} : v; }
-
-// Partial of role ((b h) * nsplit + p) * NJ + J.
-template <int D, bool DELTA>
-__device__ void partial_body(const Launch& L, int role, char* lds) {
-    constexpr int NJ = D / kCW, CHK = D / 8, KSN = D / 32, RT = D / 64;
-    static_assert(kSC * (kCW / 8) == kThreads, "one 16-byte slot of V per thread and chunk");
-    using PL = PartLds<D>;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, g = lane >> 4;
-    const int NS = L.nsplit;
-    const int q = role / NJ, J = role % NJ;
-    const int bh = q / NS, p = q % NS;
-    const int b = bh / L.H, h = bh % L.H;
-    const int t0 = p * L.split_tokens, t1 = min(L.S, t0 + L.split_tokens);
-    const int64_t io = (int64_t)b * L.sb + (int64_t)h * L.sh;
-    const bf16* kb = (const bf16*)L.k + io;
-    const bf16* vb = (const bf16*)L.v + io + kCW * J;
-
-    // M[:, J] (B operand of the prediction) goes through LDS once per workgroup, transposed
-    // and in bf16: thread t < (D / 8) (kCW / 8) loads the 8 x 8 block (rows 8 (t / 4), columns
-    // kCW J + 8 (t mod 4)) with 16-byte loads and stores its columns as rows of mts[j][k]
-    constexpr int NBK = (D / 8) * (kCW / 8);
-    static_assert(NBK <= kThreads, "one 8 x 8 block of M per thread");
-    const bool mthread = DELTA && tid < NBK;
-    f32x4 mx[8][2];
-    if (mthread) {
-        const float* M = L.state_in + (int64_t)bh * D * D + (8 * (tid / (kCW / 8))) * D + kCW * J + 8 * (tid % (kCW / 8));
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) mx[e][hh] = *(const f32x4*)(M + e * D + 4 * hh);
-    }
-
-    // A chunk of tokens c0 .. c0 + kSC - 1 in registers: wave w holds K rows 16 w .. 16 w + 15
-    // as the prediction's A operand (lane (r, g): row 16 w + r, features 32 ks + 8 g .. + 7);
-    // thread t holds the 16 bytes of V that go to slot t of the V tile (row t / 4, stored chunk
-    // t mod 4, the row's chunk (t mod 4) ^ swz(row)). Rows past the split load its last row and
-    // are replaced by zeros, so they add nothing.
-    struct Stage {
-        u32x4 k[KSN];
-        u32x4 v;
-    };
-    const int vrow = tid >> 2, vchunk = (tid & 3) ^ swz<kCW / 8>(tid >> 2);
-    auto load = [&](Stage& st, int c0) {
-        const bf16* kr = kb + (int64_t)min(c0 + 16 * wave + r, t1 - 1) * L.st + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < KSN; ++ks) st.k[ks] = *(const u32x4*)(kr + 32 * ks);
-        st.v = *(const u32x4*)(vb + (int64_t)min(c0 + vrow, t1 - 1) * L.st + vchunk * 8);
-    };
-    Stage sg[kStages];   // chunks n + 1 .. n + kStages are in flight while chunk n is used
-#pragma unroll
-    for (int i = 0; i < kStages; ++i)
-        if (t0 + i * kSC < t1) load(sg[i], t0 + i * kSC);
-
-    bf16x8 bm[DELTA ? 2 : 1][DELTA ? KSN : 1];
-    if constexpr (DELTA) {
-        bf16* mts = (bf16*)(lds + PL::MTOFF);   // [kCW][D + 8]
-        if (mthread) {
-            const int k0 = 8 * (tid / (kCW / 8)), j0 = 8 * (tid % (kCW / 8));
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int hh = c >> 2, qq = c & 3;
-                *(u32x4*)(mts + (j0 + c) * (D + 8) + k0) =
-                    u32x4{pack2(mx[0][hh][qq], mx[1][hh][qq]), pack2(mx[2][hh][qq], mx[3][hh][qq]),
-                          pack2(mx[4][hh][qq], mx[5][hh][qq]), pack2(mx[6][hh][qq], mx[7][hh][qq])};
-            }
-        }
-        lds_barrier();
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int ks = 0; ks < KSN; ++ks)
-                bm[ct][ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(mts + (16 * ct + r) * (D + 8) + 32 * ks + 8 * g));
-    }
-    const float gc = L.gamma[bh] * L.c;
-
-    f32x4 acc[RT][2];
-#pragma unroll
-    for (int it = 0; it < RT; ++it)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) acc[it][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // chunk n: the prediction from the stage's registers, the stage into LDS buffer n % 2 (with
-    // the prediction tile), the stage refilled with chunk n + kStages, one barrier, the U
-    // product. Buffer n % 2 was last read for chunk n - 2, which every wave finished before the
-    // barrier of chunk n - 1.
-    auto chunk = [&](Stage& st, int c0, int n) {
-        const int buf = n & 1;
-        bf16* kc = (bf16*)(lds + buf * PL::BUF);
-        bf16* vc = (bf16*)(lds + buf * PL::BUF + PL::KB);
-        bf16* pct = (bf16*)(lds + kRing * PL::BUF + buf * PL::PB);   // -gamma c P^T: [kCW][kSC]
-        const int tv = t1 - c0;   // tokens of the split left, from this chunk on
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const int krow = 16 * wave + r;
-        u32x4 kx[KSN];
-#pragma unroll
-        for (int ks = 0; ks < KSN; ++ks) kx[ks] = krow < tv ? st.k[ks] : z;
-        if constexpr (DELTA) {
-            // C lane (r, g) holds P[16 wave + 4 g + q][16 ct + r]
-            f32x4 pa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int ks = 0; ks < KSN; ++ks)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) pa[ct] = mfma(__builtin_bit_cast(bf16x8, kx[ks]), bm[ct][ks], pa[ct]);
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-                *(u32x2*)(pct + pct_off(16 * ct + r, 16 * wave + 4 * g)) =
-                    u32x2{pack2(-gc * pa[ct][0], -gc * pa[ct][1]), pack2(-gc * pa[ct][2], -gc * pa[ct][3])};
-        }
-#pragma unroll
-        for (int ks = 0; ks < KSN; ++ks)
-            *(u32x4*)(kc + krow * D + (((4 * ks + g) ^ swz<CHK>(krow)) * 8)) = kx[ks];
-        *(u32x4*)(vc + tid * 8) = vrow < tv ? st.v : z;
-        if (c0 + kStages * kSC < t1) load(st, c0 + kStages * kSC);
-        lds_barrier();
-        // U[i][j] += sum over the chunk's tokens of K[t][i] (V[t][j] - gamma c P[t][j]); the k
-        // order of a 32-token step is tokens {4 g + e} then {16 + 4 g + e}, in A and B alike
-#pragma unroll
-        for (int tg = 0; tg < kSC; tg += 32) {
-            bf16x8 bv[2], bp[2];
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                bv[ct] = join(read_tr<kCW / 8>(vc, tg, 16 * ct, r, g), read_tr<kCW / 8>(vc, tg + 16, 16 * ct, r, g));
-                if constexpr (DELTA) {
-                    bp[ct] = join(*(const u32x2*)(pct + pct_off(16 * ct + r, tg + 4 * g)),
-                                  *(const u32x2*)(pct + pct_off(16 * ct + r, tg + 16 + 4 * g)));
-                }
-            }
-#pragma unroll
-            for (int it = 0; it < RT; ++it) {
-                const int i0 = 16 * (wave * RT + it);
-                const bf16x8 ak = join(read_tr<CHK>(kc, tg, i0, r, g), read_tr<CHK>(kc, tg + 16, i0, r, g));
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    acc[it][ct] = mfma(ak, bv[ct], acc[it][ct]);
-                    if constexpr (DELTA) acc[it][ct] = mfma(ak, bp[ct], acc[it][ct]);
-                }
-            }
-        }
-    };
-    for (int c0 = t0, n = 0; c0 < t1; c0 += kStages * kSC, n += kStages) {
-#pragma unroll
-        for (int i = 0; i < kStages; ++i)
-            if (c0 + i * kSC < t1) chunk(sg[i], c0 + i * kSC, n + i);
-    }
-
-    // partial of split p in the lanes' own order: part[(b h) J][p][tile][lane][4 fp32], tile
-    // (row tile) * 2 + (column tile)
-    float* pp = L.part + ((int64_t)(bh * NJ + J) * NS + p) * D * kCW;
-#pragma unroll
-    for (int it = 0; it < RT; ++it)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-            *(f32x4*)(pp + (((wave * RT + it) * 2 + ct) * 64 + lane) * 4) = acc[it][ct];
-}
-
-template <int D, bool DELTA>
-__global__ __launch_bounds__(kThreads, 2) void step_partials_kernel(Launch L) {
-    constexpr int NJ = D / kCW;
-    __shared__ __attribute__((aligned(16))) char lds[PartLds<D>::BYTES];
-    const int NG = L.B * L.H * L.nsplit;   // (b, h, split) groups
-    // workgroup i runs on XCD i mod 8: the NJ column blocks of a group share an XCD
-    const int xcd = blockIdx.x % 8, k = blockIdx.x / 8;
-    const int q = (k / NJ) * 8 + xcd, J = k % NJ;
-    if (q >= NG) return;
-    partial_body<D, DELTA>(L, q * NJ + J, lds);
-}
-
-// M' = gamma M + beta c sum_p U_p for rows 32 rb .. 32 rb + 31 of column block J of one (b, h);
-// thread t handles tile 4 rb + t / 64 of the partial layout at lane t mod 64: rows
-// 16 (2 rb + t / 128) + 4 g + q, column 32 J + 16 ((t / 64) mod 2) + r.
-template <int D>
-__global__ __launch_bounds__(kThreads) void step_merge_kernel(Launch L) {
-    constexpr int NJ = D / kCW, NRB = D / 32;
-    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
-    const int rb = blockIdx.x % NRB, J = (blockIdx.x / NRB) % NJ, bh = blockIdx.x / (NRB * NJ);
-    const int tile = 4 * rb + (tid >> 6);
-    const int i = 16 * (tile >> 1) + 4 * g, j = kCW * J + 16 * (tile & 1) + r;
-    const int NS = L.nsplit;
-    const float* part = L.part + (int64_t)(bh * NJ + J) * NS * D * kCW + (tile * 64 + lane) * 4;
-    const float* min_ = L.state_in + (int64_t)bh * D * D;
-    float m0[4];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) m0[qq] = min_[(i + qq) * D + j];
-    constexpr int BATCH = 8;   // partials in flight
-    f32x4 u = {0.f, 0.f, 0.f, 0.f};
-    for (int p0 = 0; p0 < NS; p0 += BATCH) {
-        f32x4 x[BATCH];
-#pragma unroll
-        for (int e = 0; e < BATCH; ++e) x[e] = *(const f32x4*)(part + (int64_t)min(p0 + e, NS - 1) * D * kCW);
-#pragma unroll
-        for (int e = 0; e < BATCH; ++e)
-            if (p0 + e < NS) u += x[e];
-    }
-    const float gm = L.gamma[bh], bc = L.beta[bh] * L.c;
-    float m[4];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) m[qq] = gm * m0[qq] + bc * u[qq];
-    if (L.state_out) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) L.state_out[(int64_t)bh * D * D + (i + qq) * D + j] = m[qq];
-    }
-    *(u32x2*)((bf16*)L.mt + (int64_t)bh * D * D + j * D + i) = u32x2{pack2(m[0], m[1]), pack2(m[2], m[3])};
-}
+template <int D> struct OutLds {
+    static constexpr int BYTES = D * D * 2;    // M'^T, swizzled (out_mask)
+};
 
 // O = Q M' for tokens [chunk * chunk_tokens, + chunk_tokens) of one (b, h): wave w takes the
 // 16-token tiles w, w + 4, .. (at most kQD), computed as O^T = M'^T Q^T so that lane (r, g)
 // ends up with 8 consecutive output columns of token r.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void step_output_kernel(Launch L) {
+__global__ __launch_bounds__(kOutThreads, 2) void step_output_kernel(Launch L) {
     constexpr int KSN = D / 32, TJ = D / 16;
     __shared__ __attribute__((aligned(16))) char lds[OutLds<D>::BYTES];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -349,12 +421,12 @@ __global__ __launch_bounds__(kThreads, 2) void step_output_kernel(Launch L) {
     // M'^T loads first, then the chunk's Q rows (B operand: lane (r, g) holds
     // Q[t][32 ks + 8 g .. + 7]) through a buffer resource ending with the frame's last row:
     // rows past S read zero and their stores drop
-    constexpr int NE = D * D / 8, PT = NE / kThreads;
-    static_assert(NE % kThreads == 0, "whole rows per thread");
+    constexpr int NE = D * D / 8, PT = NE / kOutThreads;
+    static_assert(NE % kOutThreads == 0, "whole rows per thread");
     const bf16* mt = (const bf16*)L.mt + (int64_t)bh * D * D;
     u32x4 x[PT];
 #pragma unroll
-    for (int k = 0; k < PT; ++k) x[k] = *(const u32x4*)(mt + (tid + k * kThreads) * 8);
+    for (int k = 0; k < PT; ++k) x[k] = *(const u32x4*)(mt + (tid + k * kOutThreads) * 8);
     const int qstb = (int)L.st * 2, ostb = (int)L.ot * 2;
     const __amdgpu_buffer_rsrc_t rq =
         buffer_over((const bf16*)L.q + (int64_t)b * L.sb + (int64_t)h * L.sh, ((S - 1) * (int)L.st + D) * 2);
@@ -371,10 +443,11 @@ __global__ __launch_bounds__(kThreads, 2) void step_output_kernel(Launch L) {
     bf16* ms = (bf16*)lds;   // M'^T, swizzled
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
-        const int e = tid + k * kThreads, row = e / (D / 8), c = (e % (D / 8)) * 8;
+        const int e = tid + k * kOutThreads, row = e / (D / 8), c = (e % (D / 8)) * 8;
         *(u32x4*)(ms + out_off<D>(row, c)) = half_swap(x[k], out_mask<D>(row) & 1);
     }
-    __syncthreads();
+    // LDS-only barrier: the chunk's Q loads stay in flight, each tile waits for its own rows
+    lds_barrier();
     bf16x8 am[TJ][KSN];
 #pragma unroll
     for (int jt = 0; jt < TJ; ++jt)
@@ -407,25 +480,27 @@ __global__ __launch_bounds__(kThreads, 2) void step_output_kernel(Launch L) {
 }
 
 template <int D> hipError_t launch_d(Kernel k, const Launch& L, hipStream_t s) {
-    constexpr int NJ = D / kCW;
     const int64_t BH = (int64_t)L.B * L.H;
     switch (k) {
     case K_STEP_PARTIAL: {
-        const int64_t n = (BH * L.nsplit + 7) / 8 * 8 * NJ;
-        if (n > 0x7FFFFFFF || L.split_tokens % kSC) return hipErrorInvalidValue;
+        const int64_t n = (BH * L.nsplit * step_halves(D) + 7) / 8 * 8;
+        if (n > 0x7FFFFFFF || L.split_tokens % 16) return hipErrorInvalidValue;
         if (L.use_delta)
-            hipLaunchKernelGGL((step_partials_kernel<D, true>), dim3((unsigned)n), dim3(kThreads), 0, s, L);
+            hipLaunchKernelGGL((step_gram_kernel<D, true>), dim3((unsigned)n), dim3(kGramThreads), 0, s, L);
         else
-            hipLaunchKernelGGL((step_partials_kernel<D, false>), dim3((unsigned)n), dim3(kThreads), 0, s, L);
+            hipLaunchKernelGGL((step_gram_kernel<D, false>), dim3((unsigned)n), dim3(kGramThreads), 0, s, L);
         break;
     }
-    case K_STEP_REDUCE:
-        hipLaunchKernelGGL((step_merge_kernel<D>), dim3((unsigned)(BH * NJ * (D / 32))), dim3(kThreads), 0, s, L);
+    case K_STEP_REDUCE: {
+        const int64_t n = BH * (D / 32) * (D / 32);
+        if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((step_sum_kernel<D>), dim3((unsigned)n), dim3(kSumThreads), 0, s, L);
         break;
+    }
     case K_STEP_OUTPUT: {
         const int64_t n = BH * L.nchunk;
         if (n > 0x7FFFFFFF || L.chunk_tokens > 4 * 16 * kQD) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((step_output_kernel<D>), dim3((unsigned)n), dim3(kThreads), 0, s, L);
+        hipLaunchKernelGGL((step_output_kernel<D>), dim3((unsigned)n), dim3(kOutThreads), 0, s, L);
         break;
     }
     default:

@@ -261,10 +261,11 @@ gdn_status gdn_forward_framewise_fp8(const gdn_problem* p, const void* q, const 
  *                otherwise it receives the new state and may equal state_in exactly
  *   workspace    at least gdn_workspace_size(p, 1) bytes, 256-byte aligned
  * Three launches: partial products over token splits, the state update, the outputs. bf16
- * data with D = 64 or 128 (and S rows of either token stride within 2 GiB) splits the partial
- * products into blocks of 32 value columns (trace kinds STEP_PARTIAL, STEP_REDUCE,
- * STEP_OUTPUT); other types and head sizes use whole-state partials and the forward's output
- * kernel (STEP_PARTIAL, STEP_REDUCE, PRODUCTS). Results are bitwise reproducible.
+ * data with D = 64 or 128 (and S rows of either token stride within 2 GiB) forms, per split,
+ * K^T K and K^T V and from them the split's share of the update (trace kinds STEP_PARTIAL,
+ * STEP_REDUCE, STEP_OUTPUT); other types and head sizes use whole-state partials and the
+ * forward's output kernel (STEP_PARTIAL, STEP_REDUCE, PRODUCTS). Results are bitwise
+ * reproducible.
  */
 gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, const void* v,
                           const float* gamma, const float* beta, const float* state_in,
@@ -284,7 +285,7 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
  * may run at the same time on one GPU race and must be ordered by the caller (one stream, or
  * events). Nothing in the array needs to start at zero: each launch writes what the next reads.
  */
-#define GDN_STEP_SCRATCH_BYTES ((size_t)16 << 20)
+#define GDN_STEP_SCRATCH_BYTES ((size_t)32 << 20)
 gdn_status gdn_step_frame_noalloc(const gdn_problem* p, const void* q, const void* k,
                                   const void* v, const float* gamma, const float* beta,
                                   const float* state_in, void* o, float* state_out,

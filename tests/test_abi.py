@@ -83,9 +83,10 @@ def test_step_workspace_independent_of_frames():
     assert len(sizes) == 1
 
 
-def test_column_block_step_workspace():
+def test_gram_step_workspace():
     # the streaming shape (B 1, H 16, D 128, S 3520, bf16): fp32 partials of 8 token splits of
-    # 448 tokens (512 partial workgroups of 32 value columns), the new state transposed in bf16
+    # 448 tokens (two workgroups per split, one per half of the rows: 256 in all, one per CU),
+    # the new state transposed in bf16
     p = gdn.Problem(1, 16, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 0, 0, 128, 0, 0, 128)
     assert gdn.workspace_size(p, True) == 16 * 8 * 128 * 128 * 4 + 16 * 128 * 128 * 2
     # rows beyond 2 GiB: the whole-state step kernels
@@ -478,9 +479,9 @@ def test_step_noalloc_validation():
     assert call_na(prob(), q=None) == 1
     assert call_na(prob(), si=None) == 1 and "state_in" in msg()
     assert call_na(prob(), q=A + 8) == 5
-    # beyond the static scratch (16 MiB): 256 heads of D = 128 at 3520 tokens need 24 MiB
-    big = gdn.Problem(1, 256, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 256 * 3520 * 128, 3520 * 128,
-                      128, 256 * 3520 * 128, 3520 * 128, 128)
-    assert gdn.workspace_size(big, 1) > (16 << 20)
+    # beyond the static scratch (32 MiB): 512 heads of D = 128 at 3520 tokens need 48 MiB
+    big = gdn.Problem(1, 512, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 512 * 3520 * 128, 3520 * 128,
+                      128, 512 * 3520 * 128, 3520 * 128, 128)
+    assert gdn.workspace_size(big, 1) > (32 << 20)
     assert call_na(big, q=A, k=A << 12, v=A << 13, o=A << 14) == 7
     assert "static scratch" in msg()

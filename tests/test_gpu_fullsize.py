@@ -47,19 +47,22 @@ def f32(bits):
 
 def run_heads(jobs, work):
     """Run work(*job) for each job on a thread pool; at most WORKERS jobs hold their inputs at
-    once. Returns the results in job order."""
+    once. Returns the results in job order.
+
+    BLAS is limited to one thread once, around the whole pool: its threaded kernels are not
+    reentrant, and a limit entered and left per worker would let one worker's exit restore the
+    threaded mode while others are inside a product."""
     from threadpoolctl import threadpool_limits
     gate = threading.Semaphore(WORKERS)
 
     def one(job):
         try:
-            with threadpool_limits(1):
-                return work(*job())
+            return work(*job())
         finally:
             gate.release()
 
     futs = []
-    with ThreadPoolExecutor(WORKERS) as pool:
+    with threadpool_limits(1), ThreadPoolExecutor(WORKERS) as pool:
         for job in jobs:
             gate.acquire()
             futs.append(pool.submit(one, job))
