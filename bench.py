@@ -46,6 +46,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gdn_720p_60s_bf16.json")
 KERNEL_SRC = os.path.join(ROOT, "frame_wise_gated_libgdn_amd", "csrc", "gdn_kernels.hip")
 STEP_PROFILE = os.path.join(ROOT, "profiles", "step_kernels_stream_720p_bf16.json")
 STEP_SRC = os.path.join(ROOT, "frame_wise_gated_libgdn_amd", "csrc", "gdn_step.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_720p_bench.json")
 
 
 def log(*a):
@@ -142,6 +143,28 @@ def traffic_for(kernel, workload, plan):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else round(k["hbm_gb_per_launch"], 3)
+
+
+def counters_for(key=None):
+    """Committed rocprofv3 counters of one kernel of the bench's legs (HBM bytes, L2 hit rate,
+    MFMA busy fraction, clock), or of all of them when key is None; an entry is None when its
+    kernel's source changed since the counters were taken."""
+    try:
+        with open(COUNTERS_FILE) as fh:
+            t = json.load(fh)["kernels"]
+    except (OSError, ValueError, KeyError):
+        return None
+    csrc = os.path.join(ROOT, "frame_wise_gated_libgdn_amd", "csrc")
+
+    def entry(e):
+        if e.get("source_sha256") != source_sha(os.path.join(csrc, e["source"])):
+            return None
+        return {k_: e[k_] for k_ in ("avg_us", "hbm_read_gb", "hbm_write_gb", "l2_hit",
+                                     "mfma_busy", "mfma_busy_at_2400mhz", "bf16_mfma_tflops",
+                                     "clock_ghz")}
+    if key is not None:
+        return entry(t[key]) if key in t else None
+    return {k_: entry(e) for k_, e in t.items()}
 
 
 def copy_calibration(gib):
@@ -720,6 +743,9 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_for(dom + "_kernel", w.name, plan_key),
             "traffic_unit": "GB per launch",
+            # MFMA busy fraction and L2 hit rate of the same kernel from committed counters
+            "mfma_busy": (counters_for("fused_bf16") or {}).get("mfma_busy"),
+            "l2_hit": (counters_for("fused_bf16") or {}).get("l2_hit"),
             "algorithmic_gb_per_launch": round(launch_bytes / 1e9, 4),
             "launch_ms": round(launch_ms, 4),
             "launches_per_step": {k_: a[0] // args.steps for k_, a in per.items()},
@@ -781,6 +807,9 @@ def main():
             result["backward"]["from_saved_states"]["forward_save_ms"]))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if w.name == "gdn_720p_60s_bf16":
+        # per-kernel counters of every leg (rocprofv3 runs of this script, committed summary)
+        result["counters"] = counters_for()
     print(json.dumps(result), flush=True)
 
 
