@@ -17,6 +17,7 @@ import threading
 
 __all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "forward_framewise",
            "forward_framewise_save", "saved_size", "step_frame", "step_frame_noalloc",
+           "prepare_step_frame",
            "backward_framewise", "check_timeout",
            "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES", "GDN_F32",
            "GDN_BF16"]
@@ -30,7 +31,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
           8: "GDN_ERR_HIP", 9: "GDN_ERR_TIMEOUT"}
 KERNEL_NAMES = {0: "products", 1: "combine", 2: "scan", 3: "step_partial", 4: "step_reduce",
                 5: "fused_reset", 6: "fused", 7: "scan_bwd", 8: "bwd", 9: "scan_states",
-                10: "tconv", 11: "attn", 12: "step_output", 13: "bwd_qdo"}
+                10: "tconv", 11: "attn", 12: "step_output", 13: "bwd_qdo", 14: "step_fused"}
 SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
 
 
@@ -433,8 +434,11 @@ def attention_framecausal(q, k, v, *, tokens_per_frame, q_frame0=0, scale=None, 
 
 
 def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_scale=None,
-               out=None, state_out=None, workspace=None, stream=None):
+               out=None, state_out=None, workspace=None, stream=None, schedule="auto",
+               check_timeout=None):
     """One frame: q, k, v [B, H, S, D]; gamma, beta fp32 [B, H]; state fp32 [B, H, D, D].
+    schedule: "staged" keeps the bf16 step's three launches; "auto" / "fused" run them as one
+    where the shape and device allow. check_timeout as in forward_framewise.
     Returns (o, new_state) when commit, else (o, None). state_out may be `state` itself."""
     import torch
     B, H, S, D = q.shape
@@ -451,16 +455,55 @@ def step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True, key_
     _check_f32("beta", beta, (B, H))
     _check_f32("state", state, (B, H, D, D))
     _check_f32("state_out", state_out, (B, H, D, D))
-    p = _problem(q, out, 1, use_delta, key_scale)
+    p = _problem(q, out, 1, use_delta, key_scale, schedule)
     ws, nbytes = _workspace(p, True, workspace, q.device)
     _check(load().gdn_step_frame(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                  _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out), _ptr(ws),
                                  nbytes, _stream(stream)))
+    _after(p, 1, ws, workspace is None, stream, check_timeout)
     return out, state_out
 
 
+def prepare_step_frame(q, k, v, gamma, beta, state, commit=True, *, use_delta=True,
+                       key_scale=None, out=None, state_out=None, workspace=None, stream=None,
+                       schedule="auto"):
+    """step_frame with every argument checked and marshalled once: returns a function of no
+    arguments that enqueues the same gdn_step_frame call again (on the same buffers, whose
+    contents may change between calls) and raises GdnError if it fails. For loops that issue
+    many steps from the host (a streaming server), where the per-call checks of step_frame
+    would cost more host time than the step takes on the GPU."""
+    import torch
+    B, H, S, D = q.shape
+    if k.stride() != q.stride() or v.stride() != q.stride() or k.shape != q.shape \
+            or v.shape != q.shape:
+        raise GdnError(4, "q, k and v must share shape and strides")
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=q.dtype, device=q.device)
+    if commit and state_out is None:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    if not commit:
+        state_out = None
+    _check_f32("gamma", gamma, (B, H))
+    _check_f32("beta", beta, (B, H))
+    _check_f32("state", state, (B, H, D, D))
+    _check_f32("state_out", state_out, (B, H, D, D))
+    p = _problem(q, out, 1, use_delta, key_scale, schedule)
+    ws, nbytes = _workspace(p, True, workspace, q.device)
+    fn = load().gdn_step_frame
+    args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(state),
+            _ptr(out), _ptr(state_out), _ptr(ws), nbytes, _stream(stream))
+    keep = (p, q, k, v, gamma, beta, state, out, state_out, ws)   # alive while the call is
+
+    def call():
+        code = fn(*args)
+        if code:
+            _check(code)
+        return keep[7], keep[8]
+    return call
+
+
 def step_frame_noalloc(q, k, v, gamma, beta, state, commit=True, *, use_delta=True,
-                       key_scale=None, out=None, state_out=None, stream=None):
+                       key_scale=None, out=None, state_out=None, stream=None, schedule="auto"):
     """step_frame through gdn_step_frame_noalloc: the workspace is the library's own static
     device scratch (no workspace argument, nothing allocated by the library; calls on one GPU
     share it and must not overlap). out and state_out, when not given, are allocated here by
@@ -480,7 +523,7 @@ def step_frame_noalloc(q, k, v, gamma, beta, state, commit=True, *, use_delta=Tr
     _check_f32("beta", beta, (B, H))
     _check_f32("state", state, (B, H, D, D))
     _check_f32("state_out", state_out, (B, H, D, D))
-    p = _problem(q, out, 1, use_delta, key_scale)
+    p = _problem(q, out, 1, use_delta, key_scale, schedule)
     _check(load().gdn_step_frame_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                          _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),
                                          _stream(stream)))

@@ -35,6 +35,8 @@ struct Plan {
     bool fused_states;          // backward: the forward states recomputed by the fused forward
     int nsplit, split_tokens;   // partial-product kernel
     int nchunk, chunk_tokens;   // output kernel
+    bool step_one;              // step: the Gram-form work may run in one launch (shape allows)
+    size_t step_ctl_bytes;      // ... its time-out word, epochs and meeting flags
     size_t canon_bytes, part_bytes, mt_bytes;   // staged forward and step
     size_t ctl_bytes, chain_bytes;              // fused forward; chained backward
     size_t crec_bytes, gt_bytes;                // backward
@@ -42,7 +44,7 @@ struct Plan {
         if (mode >= 2)
             return align256(ctl_bytes) + align256(chain_bytes) + align256(canon_bytes) +
                    align256(part_bytes) + align256(mt_bytes) + align256(crec_bytes) + gt_bytes;
-        if (mode == 1 && fused) return align256(part_bytes) + mt_bytes;
+        if (mode == 1 && fused) return align256(step_ctl_bytes) + align256(part_bytes) + mt_bytes;
         return fused ? align256(ctl_bytes) + chain_bytes
                      : align256(canon_bytes) + align256(part_bytes) + mt_bytes;
     }
@@ -101,6 +103,7 @@ bool choose_bwd_chain(const gdn_problem& p) {
 constexpr int kTargetGroups = 2048;  // workgroups wanted per parallel launch (256 CUs x 8)
 constexpr int kStepPartials = 256;   // Gram step: partial workgroups (one per CU)
 constexpr int kStepOutputs = 256;    // Gram step: output workgroups
+constexpr int kStepXcdCUs = 32;      // one-launch step: workgroups per XCD (its CUs)
 
 // mode: 0 forward, 1 step, 2 backward, 3 backward from saved states (no forward recompute)
 Plan make_plan(const gdn_problem& p, int mode) {
@@ -153,6 +156,11 @@ Plan make_plan(const gdn_problem& p, int mode) {
         // the new state transposed in bf16
         const int64_t hv = gdn::step_halves((int)D);
         int64_t ns = (kStepPartials + BH * hv - 1) / (BH * hv);
+        // one launch: the heads spread evenly over the 8 XCDs (B H a multiple of 8), each head's
+        // workgroups on one XCD of 32 CUs, one workgroup per CU (STAGED keeps three launches)
+        const int64_t hpx = BH / 8;
+        pl.step_one = p.schedule != GDN_SCHEDULE_STAGED && BH % 8 == 0 && hpx * hv <= kStepXcdCUs;
+        if (pl.step_one) ns = kStepXcdCUs / (hpx * hv);
         ns = std::max<int64_t>(1, std::min<int64_t>(ns, (S + 127) / 128));
         pl.split_tokens = (int)(((tiles16 + ns - 1) / ns) * 16);
         pl.nsplit = (int)((S + pl.split_tokens - 1) / pl.split_tokens);
@@ -162,6 +170,7 @@ Plan make_plan(const gdn_problem& p, int mode) {
         pl.nchunk = (int)((S + pl.chunk_tokens - 1) / pl.chunk_tokens);
         pl.part_bytes = (size_t)(BH * pl.nsplit * D * D * 4);
         pl.mt_bytes = (size_t)(BH * D * D * 2);
+        pl.step_ctl_bytes = pl.step_one ? gdn::step_one_ctl_bytes(BH, pl.nsplit * hv) : 0;
         pl.canon_bytes = 0;
         pl.chain_bytes = 0;
     }
@@ -409,8 +418,14 @@ gdn_status run(int step_mode, const gdn_problem* p, const void* q, const void* k
     L.gamma = gamma; L.beta = beta; L.state_in = state_in; L.state_out = state_out;
     if (step_mode && pl.fused) {
         L.step_cols = 1;
-        L.part = (float*)ws;
-        L.mt = (char*)ws + align256(pl.part_bytes);
+        // one launch where the device holds its grid (8 XCDs with a CU for each of a head's
+        // workgroups), else the three launches over the same buffers
+        const int64_t W = (int64_t)pl.nsplit * gdn::step_halves((int)D);
+        L.step_one = pl.step_one && gdn::step_one_device_ok((int)(B * H / 8 * W));
+        L.ctl = (int*)ws;
+        L.spin_limit = fused_spin_limit();
+        L.part = (float*)((char*)ws + align256(pl.step_ctl_bytes));
+        L.mt = (char*)ws + align256(pl.step_ctl_bytes) + align256(pl.part_bytes);
         if (S == 1) {
             L.st = std::max<int64_t>(L.st, D);
             L.ot = std::max<int64_t>(L.ot, D);
@@ -724,12 +739,27 @@ gdn_status gdn_check_timeout(const gdn_problem* p, int mode, const void* workspa
     gdn_status s = check_sizes(p, mode == 3 ? 2 : mode);
     if (s != GDN_OK) return s;
     const Plan pl = make_plan(*p, mode);
-    // bounded waits: the fused forward, and the backward's chained schedule (its reverse chain
-    // and, recomputing, the fused forward that rebuilds the states); step mode never waits
-    const bool waits = mode != 1 && (pl.fused || pl.fused_states);
+    // bounded waits: the fused forward, the backward's chained schedule (its reverse chain and,
+    // recomputing, the fused forward that rebuilds the states) and the one-launch step
+    const bool waits = mode == 1 ? pl.fused && pl.step_one : pl.fused || pl.fused_states;
     if (!waits) return GDN_OK;
     if (!workspace) return fail(GDN_ERR_NULL, "workspace is NULL");
     hipError_t e = hipStreamSynchronize((hipStream_t)hip_stream);
+    if (mode == 1) {
+        // the step's time-out word stays set until read here
+        uint64_t word = 0;
+        if (e == hipSuccess) e = hipMemcpy(&word, workspace, sizeof word, hipMemcpyDeviceToHost);
+        const bool timed_out = e == hipSuccess && word == gdn::kStepTimeoutWord;
+        if (timed_out) {
+            const uint64_t zero = 0;
+            e = hipMemcpy(const_cast<void*>(workspace), &zero, sizeof zero, hipMemcpyHostToDevice);
+        }
+        if (e != hipSuccess) return fail(GDN_ERR_HIP, "reading the time-out word failed: %s", hipGetErrorString(e));
+        if (timed_out)
+            return fail(GDN_ERR_TIMEOUT, "a bounded wait of the one-launch step timed out; its "
+                                         "state and outputs are NaN");
+        return GDN_OK;
+    }
     int32_t flag = 0;
     if (e == hipSuccess) e = hipMemcpy(&flag, (const char*)workspace + 4, sizeof flag, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "reading the time-out flag failed: %s", hipGetErrorString(e));

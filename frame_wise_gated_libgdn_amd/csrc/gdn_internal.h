@@ -35,6 +35,8 @@ struct Launch {
                          //   group g of the state is published
     float* chain;        // workspace (fused): published states, [2][B*H][D][D] fp32, [c][n] order
     int step_cols;       // step: the Gram-form kernels of gdn_step.hip (bf16, D = 64 / 128)
+    int step_one;        // step: those kernels' work in one launch (step_fused_kernel); ctl
+                         //   then holds its time-out word, per-head epochs and meeting flags
     float* save_states;  // fused forward, training: fp32 states, [B*H][F + 1][D][D] transposed
                          //   (slot 0 the initial state, slot f + 1 = M_f), or NULL
     void* save_recs;     // ... and the frames' Ghat planes ([B*H][F] records of rec_stride bytes)
@@ -76,7 +78,8 @@ enum Kernel {
     K_TCONV = 10,        // block-causal temporal convolution
     K_ATTN = 11,         // frame-causal softmax attention
     K_STEP_OUTPUT = 12,  // step (Gram-form kernels): outputs of the frame
-    K_BWD_QDO = 13       // backward: C_f = Q_f^T dO_f and dQ_f in one pass over Q and dO
+    K_BWD_QDO = 13,      // backward: C_f = Q_f^T dO_f and dQ_f in one pass over Q and dO
+    K_STEP_FUSED = 14    // step (Gram form): partials, new state and outputs in one launch
 };
 
 // Arguments of the frame-causal softmax attention (gdn_attn.hip). q: [B][H][Tq][D], k, v:
@@ -120,6 +123,14 @@ bool step_cols_supported(int bf16, int D);
 // Workgroups per token split in the Gram step (each forms D / halves rows of the split's update).
 constexpr int step_halves(int D) { return D == 128 ? 2 : 1; }
 hipError_t step_launch(Kernel k, const Launch& L, hipStream_t s);
+// One-launch step: the ctl words it needs for B*H heads of W workgroups each (time-out word,
+// per-head epochs, two meeting flags per workgroup), and whether the current device can hold its
+// grid (8 XCDs, each with at least `per_xcd` CUs for one workgroup each).
+constexpr size_t step_one_ctl_bytes(int64_t BH, int64_t W) { return (size_t)(1 + BH + 2 * BH * W) * 8; }
+bool step_one_device_ok(int per_xcd);
+// Value of the one-launch step's time-out word (64-bit, at byte 0 of its workspace) once a wait
+// gave up; nothing else writes it.
+constexpr uint64_t kStepTimeoutWord = 0x5354455054494D45ull;
 // Whether the backward has kernels for this type / head size.
 bool backward_supported(int bf16, int D);
 

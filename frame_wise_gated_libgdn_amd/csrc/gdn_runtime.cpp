@@ -4,7 +4,8 @@
 // Forward, staged:  products (gram items of every frame) -> [combine] -> scan -> products
 //                   (output items of every frame).
 // Forward, fused:   reset of the ticket counter and frame flags -> fused kernel.
-// Step:             bf16 with D = 64 or 128: the Gram-form kernels step_partial ->
+// Step:             bf16 with D = 64 or 128: the Gram-form kernels, in one launch
+//                   (step_fused) where the heads fill the XCDs, else step_partial ->
 //                   step_reduce -> step_output; otherwise step_partial -> step_reduce ->
 //                   products (output items of the one frame).
 // Temporal conv:    one launch (the whole block or sequence).
@@ -76,6 +77,7 @@ hipError_t run_step(const Launch& L0, hipStream_t s) {
     t_trace_log.clear();
     Launcher run{L0, s};
     const int64_t BH = (int64_t)L0.B * L0.H;
+    if (L0.step_one) return run.go(K_STEP_FUSED, L0, s, BH);
     if (L0.step_cols) {
         GDN_TRY(run.go(K_STEP_PARTIAL, L0, s, BH));
         GDN_TRY(run.go(K_STEP_REDUCE, L0, s, BH));

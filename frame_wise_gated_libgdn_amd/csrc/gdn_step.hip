@@ -23,6 +23,8 @@
 // round trip of microseconds under load, more than a launch boundary.)
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -63,6 +65,9 @@ __device__ __forceinline__ bf16x8 join(u32x2 lo, u32x2 hi) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
+// cache-policy operand of the buffer intrinsics for device-scope loads (sc1): served by the L2
+// of the XCD they run on, never by a CU's own L1, which may hold lines from before a hand-off
+constexpr int kDeviceScope = 16;
 
 // Barrier on LDS accesses only: this wave's LDS accesses are complete, then s_barrier. Unlike
 // __syncthreads() it does not wait for outstanding global loads (its workgroup release fence
@@ -135,9 +140,15 @@ __device__ __forceinline__ bf16x8 mask_tail(bf16x8 x, int krow, int lane, int va
 // CTW tiles of 32 x 32: local rows 32 RTW (w mod 2), columns 32 CTW (w / 2); waves 0-3 hold G,
 // waves 4-7 hold B. The epilogue writes -gamma c G (transposed) and M to LDS in bf16 and the B
 // waves finish their tiles as U_p = B_p + (-gamma c G_p) M. The partial goes to
-// part[role][tile][lane][16 fp32], tile = local 32-row block * (D / 32) + 32-column block of U.
-template <int D, bool DELTA>
-__global__ __launch_bounds__(kGramThreads, 1) void step_gram_kernel(Launch L) {
+// part[role][tile][i][lane][4 fp32] (registers 4 i .. 4 i + 3 of the C layout), tile = local
+// 32-row block * (D / 32) + 32-column block of U.
+// `last()` runs in every wave once the split's last stage has landed, before its products
+// (for global loads into registers that the caller wants in flight early; no LDS access).
+template <int D, bool DELTA, class Hook>
+__device__ __forceinline__ void gram_phase(const Launch& L, int bh, int p, int hr, int role,
+                                           bf16 (&st0)[2][GramLds<D>::TILE],
+                                           bf16 (&st1)[2][GramLds<D>::TILE],
+                                           bf16 (&ms)[DELTA ? D * D : 8], Hook&& last) {
     using GL = GramLds<D>;
     constexpr int HV = step_halves(D), DR = D / HV;
     constexpr int TB = GL::TB, CH = D / 8;
@@ -148,23 +159,11 @@ __global__ __launch_bounds__(kGramThreads, 1) void step_gram_kernel(Launch L) {
     constexpr int RTW = DR / 64, CTW = D / 64;        // 32 x 32 tiles per wave: rows, columns
     constexpr int NTL = (DR / 32) * (D / 32);         // tiles of this workgroup's rows of U
     static_assert(2 * RTW * 4 * CTW * 32 * 32 == 2 * DR * D, "eight waves cover the rows of [G | B]");
-    __shared__ __attribute__((aligned(16))) bf16 st0[2][GL::TILE];   // K, V of even stages
-    __shared__ __attribute__((aligned(16))) bf16 st1[2][GL::TILE];   // K, V of odd stages
-    __shared__ __attribute__((aligned(16))) bf16 ms[DELTA ? D * D : 8];   // M in bf16, [k][n]
     static_assert(D * DR <= 2 * GL::TILE, "the epilogue's copy of G fits in one stage buffer");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int r = lane & 31, g = lane >> 5;
-    // workgroup i runs on XCD i mod 8; XCD x takes the contiguous stretch [x n8, (x + 1) n8) of
-    // the roles in order, so the two halves of a split read its K and V through one L2 and the
-    // splits of one (b, h) share its state there (the grid is padded to 8 n8 workgroups; the
-    // padding returns at once)
-    const int nrole = L.B * L.H * L.nsplit * HV;
-    const int n8 = (nrole + 7) / 8;
-    const int role = (int)(blockIdx.x % 8) * n8 + (int)(blockIdx.x / 8);
-    if (role >= nrole) return;
-    const int hr = role % HV, bh = role / HV / L.nsplit, p = role / HV % L.nsplit;
     const int b = bh / L.H, h = bh % L.H;
     const int t0 = p * L.split_tokens, t1 = min(L.S, t0 + L.split_tokens);
     const int ntok = t1 - t0, nst = (ntok + TB - 1) / TB;
@@ -238,14 +237,18 @@ __global__ __launch_bounds__(kGramThreads, 1) void step_gram_kernel(Launch L) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[a][c][j] = 0.f;
 
-    // stage n from buffer cur, with stage n + 1 loading into nxt meanwhile. The barrier (whose
-    // fence waits for this wave's loads) makes every wave's loads of stage n visible, and every
-    // wave is past its reads of stage n - 1 from nxt before the next loads go there. The loads
-    // of the other buffer are in flight only after the wait, so the compiler, which tells the
-    // two arrays apart, adds no wait for them before the reads of cur.
+    // stage n from buffer cur, with stage n + 1 loading into nxt meanwhile. This wave's direct
+    // loads of stage n are complete (an explicit wait: the barrier's fence waits for LDS
+    // accesses only, and the compiler's own wait is not placed before every stage), so after
+    // the barrier every wave's are, and every wave is past its reads of stage n - 1 from nxt
+    // before the next loads go there. The loads of the other buffer are issued only after the
+    // barrier, so the compiler, which tells the two arrays apart, adds no wait for them before
+    // the reads of cur.
     auto stage = [&](int n, bf16 (&cur)[2][GL::TILE], bf16 (&nxt)[2][GL::TILE]) __attribute__((always_inline)) {
+        __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (n + 1 < nst) issue(n + 1, nxt);
+        else last();
         const int valid = min(TB, ntok - n * TB);
         if (busy) {
             const bf16* kt = cur[0];
@@ -326,36 +329,59 @@ __global__ __launch_bounds__(kGramThreads, 1) void step_gram_kernel(Launch L) {
         }
     }
     if (!gwave) {
+        // register group i of every lane: one contiguous 1 KB per store instruction
         float* pp = L.part + (int64_t)role * NTL * 1024;
 #pragma unroll
         for (int a = 0; a < RTW; ++a)
 #pragma unroll
             for (int c = 0; c < CTW; ++c) {
                 const int tile = (rt0 + a) * (D / 32) + (ct0 + c - D / 32);
-                f32x4* dst = (f32x4*)(pp + (tile * 64 + lane) * 16);
                 const f32x16& x = acc[a][c];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i] = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+                for (int i = 0; i < 4; ++i)
+                    *(f32x4*)(pp + ((tile * 4 + i) * 64 + lane) * 4) = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
             }
     }
 }
 
+template <int D, bool DELTA>
+__global__ __launch_bounds__(kGramThreads, 1) void step_gram_kernel(Launch L) {
+    constexpr int HV = step_halves(D);
+    __shared__ __attribute__((aligned(16))) bf16 st0[2][GramLds<D>::TILE];   // K, V of even stages
+    __shared__ __attribute__((aligned(16))) bf16 st1[2][GramLds<D>::TILE];   // K, V of odd stages
+    __shared__ __attribute__((aligned(16))) bf16 ms[DELTA ? D * D : 8];      // M in bf16, [k][n]
+    // workgroup i runs on XCD i mod 8; XCD x takes the contiguous stretch [x n8, (x + 1) n8) of
+    // the roles in order, so the two halves of a split read its K and V through one L2 and the
+    // splits of one (b, h) share its state there (the grid is padded to 8 n8 workgroups; the
+    // padding returns at once)
+    const int nrole = L.B * L.H * L.nsplit * HV;
+    const int n8 = (nrole + 7) / 8;
+    const int role = (int)(blockIdx.x % 8) * n8 + (int)(blockIdx.x / 8);
+    if (role >= nrole) return;
+    const int hr = role % HV, bh = role / HV / L.nsplit, p = role / HV % L.nsplit;
+    gram_phase<D, DELTA>(L, bh, p, hr, role, st0, st1, ms, [] {});
+}
+
 // ------------------------------------------------------------------------------ sum kernel
-// One 32 x 32 tile of one (b, h): thread t takes registers 4 (t mod 4) .. + 3 of lane t / 4 of
-// the partial layout, i.e. rows 32 rt + 8 (t mod 4) + 4 g + 0..3 of column 32 ct + r (lane =
-// 32 g + r). M' = gamma M + beta c sum_p U_p, summed in split order.
-template <int D>
-__global__ __launch_bounds__(kSumThreads) void step_sum_kernel(Launch L) {
+// One 32 x 32 tile (rt, ct) of the new state of one (b, h), on 256 threads: thread thr takes
+// registers 4 (thr / 64) .. + 3 of lane thr mod 64 of the partial layout, i.e. rows 32 rt +
+// 8 (thr / 64) + 4 g + 0..3 of column 32 ct + r (lane = 32 g + r); a wave reads 1 KB in a row. M' = gamma M + beta c
+// sum_p U_p, summed in split order; state_out (when committing) and the bf16 transposed copy M'^T.
+// COH: the partials were stored by other workgroups of the same launch and are read with
+// device-scope loads; poison: the partials are incomplete, M' is NaN.
+template <int D, bool COH>
+__device__ __forceinline__ void sum_tile(const Launch& L, int bh, int tile, int thr, bool poison) {
     constexpr int NT = (D / 32) * (D / 32), HV = step_halves(D), RTH = D / 32 / HV;
     constexpr int NTL = NT / HV;                     // tiles of one workgroup's partial
-    const int tid = threadIdx.x, lane = tid >> 2, part = tid & 3;
-    const int tile = blockIdx.x % NT, bh = blockIdx.x / NT;
+    const int lane = thr & 63, part = thr >> 6;
     const int rt = tile / (D / 32), ct = tile % (D / 32);
     const int hr = rt / RTH, lt = (rt % RTH) * (D / 32) + ct;   // half and local tile of the partial
     const int i = 32 * rt + 8 * part + 4 * (lane >> 5), j = 32 * ct + (lane & 31);
     const int NS = L.nsplit;
     // partial of split p: role ((b h) NS + p) HV + hr; consecutive splits are HV NTL tiles apart
-    const float* src = L.part + (((int64_t)bh * NS * HV + hr) * NTL + lt) * 1024 + lane * 16 + 4 * part;
+    const float* head = L.part + (int64_t)bh * NS * HV * NTL * 1024;
+    const int src = ((hr * NTL + lt) * 1024 + (part * 64 + lane) * 4) * 4;   // bytes into the head
+    const __amdgpu_buffer_rsrc_t rp = buffer_over(head, NS * HV * NTL * 4096);
     const float* min_ = L.state_in + (int64_t)bh * D * D;
     float m0[4];
 #pragma unroll
@@ -365,7 +391,13 @@ __global__ __launch_bounds__(kSumThreads) void step_sum_kernel(Launch L) {
     for (int p0 = 0; p0 < NS; p0 += BATCH) {
         f32x4 x[BATCH];
 #pragma unroll
-        for (int e = 0; e < BATCH; ++e) x[e] = *(const f32x4*)(src + (int64_t)min(p0 + e, NS - 1) * HV * NTL * 1024);
+        for (int e = 0; e < BATCH; ++e) {
+            const int off = src + min(p0 + e, NS - 1) * HV * NTL * 4096;
+            if constexpr (COH)
+                x[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kDeviceScope));
+            else
+                x[e] = *(const f32x4*)((const char*)head + off);
+        }
 #pragma unroll
         for (int e = 0; e < BATCH; ++e)
             if (p0 + e < NS) u += x[e];
@@ -373,12 +405,18 @@ __global__ __launch_bounds__(kSumThreads) void step_sum_kernel(Launch L) {
     const float gm = L.gamma[bh], bc = L.beta[bh] * L.c;
     float m[4];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) m[qq] = gm * m0[qq] + bc * u[qq];
+    for (int qq = 0; qq < 4; ++qq) m[qq] = poison ? __builtin_nanf("") : gm * m0[qq] + bc * u[qq];
     if (L.state_out) {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) L.state_out[(int64_t)bh * D * D + (i + qq) * D + j] = m[qq];
     }
     *(u32x2*)((bf16*)L.mt + (int64_t)bh * D * D + j * D + i) = u32x2{pack2(m[0], m[1]), pack2(m[2], m[3])};
+}
+
+template <int D>
+__global__ __launch_bounds__(kSumThreads) void step_sum_kernel(Launch L) {
+    constexpr int NT = (D / 32) * (D / 32);
+    sum_tile<D, false>(L, blockIdx.x / NT, blockIdx.x % NT, threadIdx.x, false);
 }
 
 // ---------------------------------------------------------------------------- output kernel
@@ -479,6 +517,187 @@ __global__ __launch_bounds__(kOutThreads, 2) void step_output_kernel(Launch L) {
     }
 }
 
+// ---------------------------------------------------------------------- one-launch step
+// The three phases above in one launch, for shapes where every (b, h) gets its W = nsplit * HV
+// workgroups on one XCD: workgroup i runs on XCD i mod 8 (the hardware hands workgroups to the
+// XCDs in turn), and XCD x takes the heads x hpx .. x hpx + hpx - 1 (hpx = B H / 8), W
+// workgroups each, at most one per CU. Phase A is the Gram kernel's work, then the W
+// workgroups of the head meet; phase B: workgroup r forms the 32 x 32 tiles r, r + W, .. of
+// M' (the sum kernel's work); they meet again; phase C: workgroup r forms the outputs of its
+// chunk of ceil(S / 16 / W) 16-token tiles (the output kernel's work, by 8 waves). Every phase
+// keeps the arithmetic and summation order of its kernel, so the results are those of the
+// three launches, bit for bit.
+//
+// Hand-offs. The partials, M'^T and the meeting flags are written with plain stores, which land
+// in the L2 of the writer's XCD (measured: a flag is seen about 0.4 us after it is stored, 1.1 us
+// with device-scope stores, which write through), and read with device-scope loads, which that
+// L2 serves and a CU's own L1 does not; workgroups of one head share that L2, so nothing waits
+// for HBM. A meeting: every wave waits until its stores have completed, the workgroup meets at a
+// barrier, one lane stores the tag
+//     T_k = (epoch + 1) << 8 | k << 4 | xcc
+// at flag[k][b h][r], and one wave polls the W flags of the head until each holds T_k. The
+// epoch of a head (ctl word 1 + b h) is read at the start and advanced by workgroup 0 of the
+// head after the second meeting, so each launch's tags differ from whatever the buffer held; the
+// XCC id (hardware register) in the tag makes a head whose workgroups landed on different XCDs,
+// whose L2 caches do not see each other's stores, fail to meet instead of reading stale data.
+// Waits are bounded (spin_limit polls; 0 gives up at once): a workgroup that gives up stores
+// kStepTimeout in ctl word 0 and goes on with NaN (a NaN state after the first meeting, NaN
+// outputs after the second), so the kernel always ends. The meetings need the head's W
+// workgroups resident together: the host launches this kernel only where the grid fits one
+// workgroup per CU on every XCD.
+//
+// ctl (64-bit words): [0] time-out word, [1 + b h] epoch of (b, h),
+// [1 + B H + (k B H + b h) W + r] flag of workgroup r at meeting k.
+constexpr uint64_t kStepTimeout = kStepTimeoutWord;
+constexpr int kOutBatch = 2;   // one-launch step: 16-token output tiles per wave and batch
+
+template <int D, bool DELTA>
+__global__ __launch_bounds__(kGramThreads, 1) void step_fused_kernel(Launch L) {
+    constexpr int HV = step_halves(D);
+    constexpr int KSN = D / 32, TJ = D / 16, NT = (D / 32) * (D / 32);
+    constexpr int NW = kGramThreads / 64;
+    __shared__ __attribute__((aligned(16))) bf16 st0[2][GramLds<D>::TILE];
+    __shared__ __attribute__((aligned(16))) bf16 st1[2][GramLds<D>::TILE];
+    __shared__ __attribute__((aligned(16))) bf16 ms[DELTA ? D * D : 8];
+    __shared__ int s_bad;
+    static_assert(D * D <= 2 * GramLds<D>::TILE, "M'^T fits in one stage buffer");
+
+    const int BH = L.B * L.H, W = L.nsplit * HV, hpx = BH / 8;
+    const int xcd = (int)(blockIdx.x % 8), slot = (int)(blockIdx.x / 8);
+    const int bh = xcd * hpx + slot / W, r = slot % W;
+    if (slot >= hpx * W) return;
+    const int p = r / HV, hr = r % HV;
+    const int role = (bh * L.nsplit + p) * HV + hr;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint64_t* ctl = (uint64_t*)L.ctl;
+    uint64_t* flags = ctl + 1 + BH;
+
+    // tags of this launch (wave 0 stores and polls them)
+    uint64_t tag0 = 0;
+    if (wave == 0) {
+        const uint64_t ep = __hip_atomic_load(ctl + 1 + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15u;   // HW_REG_XCC_ID[3:0]
+        tag0 = ((ep + 1) << 8) | xcc;
+    }
+    // meeting k of the head's W workgroups; returns true when a wait gave up. PEND: loads this
+    // wave issued after its last store, left in flight (the counter retires in issue order, so
+    // waiting until at most PEND remain waits for every store); the barrier waits for LDS only
+    auto meet = [&](int k, auto pend) __attribute__((always_inline)) {
+        constexpr int PEND = decltype(pend)::value;
+        if constexpr (PEND == 0) __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
+        else if constexpr (PEND == 4) __asm__ __volatile__("s_waitcnt vmcnt(4)" ::: "memory");
+        else if constexpr (PEND == 8) __asm__ __volatile__("s_waitcnt vmcnt(8)" ::: "memory");
+        else static_assert(PEND < 0, "no wait for this count");
+        lds_barrier();
+        if (wave == 0) {
+            const uint64_t tag = tag0 | ((uint64_t)k << 4);
+            uint64_t* fl = flags + ((int64_t)k * BH + bh) * W;
+            if (lane == 0) __hip_atomic_store(fl + r, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            bool ok = false;   // spin_limit 0: every meeting gives up at once
+            for (int it = 0; it < L.spin_limit; ++it) {
+                const bool mine = lane >= W || __hip_atomic_load(fl + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+                ok = __all(mine);
+                if (ok) break;
+            }
+            if (lane == 0) {
+                if (!ok) __hip_atomic_store(ctl, kStepTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (k == 1 && r == 0)   // every workgroup of the head has read the epoch
+                    __hip_atomic_store(ctl + 1 + bh, (tag0 >> 8), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_bad = !ok;
+            }
+        }
+        lds_barrier();
+        return s_bad != 0;
+    };
+
+    // phase C's Q rows (B operand: lane (q16, g4) holds Q[t][32 ks + 8 g4 .. + 7]); rows past S
+    // read zero
+    const int S = L.S;
+    const int b = bh / L.H, h = bh % L.H;
+    const int q16 = lane & 15, g4 = lane >> 4;
+    const int ctk = ((S + 15) / 16 + W - 1) / W * 16;
+    const int s_beg = r * ctk, s_end = min(S, s_beg + ctk);
+    const int qstb = (int)L.st * 2, ostb = (int)L.ot * 2;
+    const __amdgpu_buffer_rsrc_t rq =
+        buffer_over((const bf16*)L.q + (int64_t)b * L.sb + (int64_t)h * L.sh, ((S - 1) * (int)L.st + D) * 2);
+    const __amdgpu_buffer_rsrc_t ro =
+        buffer_over((bf16*)L.o + (int64_t)b * L.ob + (int64_t)h * L.oh, ((S - 1) * (int)L.ot + D) * 2);
+    u32x4 bq[kOutBatch][KSN];
+    auto load_q = [&](int d0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int d = 0; d < kOutBatch; ++d) {
+            const int row = min(s_beg + 16 * (wave + NW * (d0 + d)) + q16, S);
+#pragma unroll
+            for (int ks = 0; ks < KSN; ++ks)
+                bq[d][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, row * qstb + (32 * ks + 8 * g4) * 2, 0, 0));
+        }
+    };
+
+    // phase A
+    gram_phase<D, DELTA>(L, bh, p, hr, role, st0, st1, ms, [] {});
+    const bool bad1 = meet(0, std::integral_constant<int, 0>());
+
+    // phase B: tiles r, r + W, .. of M', 256 threads each
+    for (int t = r + W * (tid >> 8); t < NT; t += 2 * W) sum_tile<D, true>(L, bh, t, tid & 255, bad1);
+    // phase C's first Q rows load during the second meeting: issued after phase B's stores (the
+    // empty asm keeps the compiler from moving them earlier), which the meeting waits for alone
+    __asm__ __volatile__("" ::: "memory");
+    load_q(0);
+    const bool bad2 = meet(1, std::integral_constant<int, kOutBatch * KSN>());
+
+    // phase C: M'^T through LDS into registers, then the chunk's tiles, kOutBatch per wave at a time
+    constexpr int NE = D * D / 8, PT = NE / kGramThreads;
+    static_assert(NE % kGramThreads == 0, "whole rows of M'^T per thread");
+    const __amdgpu_buffer_rsrc_t rm = buffer_over((const bf16*)L.mt + (int64_t)bh * D * D, D * D * 2);
+    bf16* mst = &st0[0][0];
+    {
+        u32x4 x[PT];
+#pragma unroll
+        for (int k = 0; k < PT; ++k)
+            x[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rm, (tid + k * kGramThreads) * 16, 0, kDeviceScope));
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const int e = tid + k * kGramThreads, row = e / (D / 8), c = (e % (D / 8)) * 8;
+            *(u32x4*)(mst + out_off<D>(row, c)) = half_swap(bad2 ? u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u} : x[k],
+                                                            out_mask<D>(row) & 1);
+        }
+    }
+    lds_barrier();
+    bf16x8 am[TJ][KSN];
+#pragma unroll
+    for (int jt = 0; jt < TJ; ++jt)
+#pragma unroll
+        for (int ks = 0; ks < KSN; ++ks)
+            am[jt][ks] = __builtin_bit_cast(bf16x8, half_swap(*(const u32x4*)(mst + out_off<D>(out_col(jt, q16), 32 * ks + 8 * g4)),
+                                                              out_mask<D>(out_col(jt, q16)) & 1));
+    const int ntile = max(0, (s_end - s_beg + 15) / 16);
+    for (int d0 = 0; NW * d0 < ntile; d0 += kOutBatch) {
+        if (d0 > 0) load_q(d0);
+#pragma unroll
+        for (int d = 0; d < kOutBatch; ++d) {
+            const int st = s_beg + 16 * (wave + NW * (d0 + d));
+            if (st < s_end) {
+                f32x4 acc[TJ];
+#pragma unroll
+                for (int jt = 0; jt < TJ; ++jt) {
+                    acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSN; ++ks) acc[jt] = mfma(am[jt][ks], __builtin_bit_cast(bf16x8, bq[d][ks]), acc[jt]);
+                }
+                const int oo = min(st + q16, S) * ostb;
+#pragma unroll
+                for (int pp = 0; pp < TJ / 2; ++pp) {
+                    const f32x4 y0 = acc[2 * pp], y1 = acc[2 * pp + 1];
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4{pack2(y0[0], y0[1]), pack2(y0[2], y0[3]), pack2(y1[0], y1[1]), pack2(y1[2], y1[3])}, ro,
+                        oo + (32 * pp + 8 * g4) * 2, 0, 0);
+                }
+            }
+        }
+    }
+}
+
 template <int D> hipError_t launch_d(Kernel k, const Launch& L, hipStream_t s) {
     const int64_t BH = (int64_t)L.B * L.H;
     switch (k) {
@@ -497,6 +716,15 @@ template <int D> hipError_t launch_d(Kernel k, const Launch& L, hipStream_t s) {
         hipLaunchKernelGGL((step_sum_kernel<D>), dim3((unsigned)n), dim3(kSumThreads), 0, s, L);
         break;
     }
+    case K_STEP_FUSED: {
+        const int64_t n = BH * L.nsplit * step_halves(D);
+        if (BH % 8 || n > 8 * 32 || L.split_tokens % 16 || !L.ctl) return hipErrorInvalidValue;
+        if (L.use_delta)
+            hipLaunchKernelGGL((step_fused_kernel<D, true>), dim3((unsigned)n), dim3(kGramThreads), 0, s, L);
+        else
+            hipLaunchKernelGGL((step_fused_kernel<D, false>), dim3((unsigned)n), dim3(kGramThreads), 0, s, L);
+        break;
+    }
     case K_STEP_OUTPUT: {
         const int64_t n = BH * L.nchunk;
         if (n > 0x7FFFFFFF || L.chunk_tokens > 4 * 16 * kQD) return hipErrorInvalidValue;
@@ -512,6 +740,23 @@ template <int D> hipError_t launch_d(Kernel k, const Launch& L, hipStream_t s) {
 }  // namespace
 
 bool step_cols_supported(int bf16, int D) { return bf16 && (D == 64 || D == 128); }
+
+bool step_one_device_ok(int per_xcd) {
+    constexpr int kMaxDevices = 64;
+    static int cached[kMaxDevices];   // 0 unknown, else 1 + CUs per XCD (0 when not 8 XCDs)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+    int c = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (c == 0) {
+        int xcc = 0, cu = 0;
+        if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return false;
+        c = 1 + (xcc == 8 ? cu / 8 : 0);
+        __atomic_store_n(&cached[dev], c, __ATOMIC_RELAXED);
+    }
+    return per_xcd >= 1 && c - 1 >= per_xcd;
+}
 
 hipError_t step_launch(Kernel k, const Launch& L, hipStream_t s) {
     if (!L.bf16) return hipErrorInvalidValue;

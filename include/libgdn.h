@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define LIBGDN_ABI_VERSION 10
+#define LIBGDN_ABI_VERSION 11
 
 typedef enum {
     GDN_OK = 0,
@@ -122,7 +122,7 @@ typedef struct {
     float   key_scale;         /* c; <= 0 selects 1/sqrt(D*S) */
     int64_t qkv_stride_b, qkv_stride_h, qkv_stride_t;   /* elements */
     int64_t o_stride_b, o_stride_h, o_stride_t;         /* elements */
-    int32_t schedule;          /* forward only, a gdn_schedule; ignored in step mode */
+    int32_t schedule;          /* a gdn_schedule; step mode: see gdn_step_frame */
 } gdn_problem;
 
 /*
@@ -260,12 +260,19 @@ gdn_status gdn_forward_framewise_fp8(const gdn_problem* p, const void* q, const 
  *   state_out    NULL: the new state is not committed (a denoising pass that will be redone);
  *                otherwise it receives the new state and may equal state_in exactly
  *   workspace    at least gdn_workspace_size(p, 1) bytes, 256-byte aligned
- * Three launches: partial products over token splits, the state update, the outputs. bf16
- * data with D = 64 or 128 (and S rows of either token stride within 2 GiB) forms, per split,
- * K^T K and K^T V and from them the split's share of the update (trace kinds STEP_PARTIAL,
- * STEP_REDUCE, STEP_OUTPUT); other types and head sizes use whole-state partials and the
- * forward's output kernel (STEP_PARTIAL, STEP_REDUCE, PRODUCTS). Results are bitwise
- * reproducible.
+ * bf16 data with D = 64 or 128 (and S rows of either token stride within 2 GiB) forms, per
+ * token split, K^T K and K^T V and from them the split's share of the update, then the new
+ * state, then the outputs. Where B*H is a multiple of 8 with B*H/8 * (2 if D = 128 else 1) <= 32,
+ * p->schedule is not GDN_SCHEDULE_STAGED and the device has 8 XCDs of at least 32 CUs, the
+ * three phases run in one launch (trace kind STEP_FUSED): each head's workgroups share one
+ * XCD and meet twice inside the launch through its L2, waits bounded as in the FUSED forward
+ * (GDN_FUSED_SPIN_LIMIT; 0 makes every meeting give up at once): a wait that gives up leaves
+ * a NaN state and NaN outputs and sets the 64-bit time-out word at byte 0 of the workspace,
+ * which stays set until gdn_check_timeout reads it (the meetings need the head's workgroups on
+ * the GPU together, one per CU).
+ * Otherwise three launches (STEP_PARTIAL, STEP_REDUCE, STEP_OUTPUT); both give the same
+ * results bit for bit. Other types and head sizes use whole-state partials and the forward's
+ * output kernel (STEP_PARTIAL, STEP_REDUCE, PRODUCTS). Results are bitwise reproducible.
  */
 gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, const void* v,
                           const float* gamma, const float* beta, const float* state_in,
@@ -283,7 +290,10 @@ gdn_status gdn_step_frame(const gdn_problem* p, const void* q, const void* k, co
  *   device looks up that device's copy of the array (GDN_ERR_HIP if that fails).
  * Every call on one GPU shares that GPU's array, whatever the stream or host thread: calls that
  * may run at the same time on one GPU race and must be ordered by the caller (one stream, or
- * events). Nothing in the array needs to start at zero: each launch writes what the next reads.
+ * events). Nothing in the array needs to start at zero: each launch writes what the next reads
+ * (the one-launch step's per-head epochs make each launch's meeting flags new whatever the
+ * array held). A time-out of the one-launch step sets the word at byte 0 of the array; it is
+ * not readable through gdn_check_timeout, whose workspace argument it is not.
  */
 #define GDN_STEP_SCRATCH_BYTES ((size_t)32 << 20)
 gdn_status gdn_step_frame_noalloc(const gdn_problem* p, const void* q, const void* k,
@@ -382,9 +392,12 @@ gdn_status gdn_backward_framewise_saved(const gdn_problem* p, const void* q, con
  *   p, mode    the problem and workspace mode of that call (as gdn_workspace_size: 0 forward,
  *              1 step, 2 backward, 3 backward from saved states); they select the schedule
  *   workspace  the workspace passed to that call
- * Returns GDN_OK when the flag is clear or the call's schedule has no bounded wait (STAGED,
- * step mode; nothing is read then), GDN_ERR_TIMEOUT when it is set, GDN_ERR_HIP when the
- * synchronisation or the 4-byte read fails, and the argument errors of gdn_workspace_size.
+ * Step mode (mode 1) with a shape that may run in one launch (see gdn_step_frame): reads the
+ * 64-bit time-out word at byte 0 instead, which the step never clears itself: any step call on
+ * this workspace since the last check that gave up sets it, and this call clears it.
+ * Returns GDN_OK when the flag is clear or the call's schedule has no bounded wait (STAGED, the
+ * other step shapes; nothing is read then), GDN_ERR_TIMEOUT when it is set, GDN_ERR_HIP when
+ * the synchronisation or the read fails, and the argument errors of gdn_workspace_size.
  * It blocks the host: not for use during graph capture.
  */
 gdn_status gdn_check_timeout(const gdn_problem* p, int mode, const void* workspace, void* hip_stream);
@@ -414,7 +427,8 @@ typedef enum {
     GDN_KERNEL_TCONV = 10,        /* block-causal temporal convolution */
     GDN_KERNEL_ATTN = 11,         /* frame-causal softmax attention */
     GDN_KERNEL_STEP_OUTPUT = 12,  /* step, bf16 with D = 64 or 128: outputs of the frame */
-    GDN_KERNEL_BWD_QDO = 13       /* backward: Q_f^T dO_f and dQ in one pass over Q and dO */
+    GDN_KERNEL_BWD_QDO = 13,      /* backward: Q_f^T dO_f and dQ in one pass over Q and dO */
+    GDN_KERNEL_STEP_FUSED = 14    /* step, bf16 with D = 64 or 128: partials, state, outputs */
 } gdn_kernel_kind;
 
 typedef struct {

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.abi_version() == 10
+    assert gdn.abi_version() == 11
     lib = gdn.load()
     for code in range(10):
         assert lib.gdn_status_string(code)
@@ -84,11 +84,21 @@ def test_step_workspace_independent_of_frames():
 
 
 def test_gram_step_workspace():
-    # the streaming shape (B 1, H 16, D 128, S 3520, bf16): fp32 partials of 8 token splits of
-    # 448 tokens (two workgroups per split, one per half of the rows: 256 in all, one per CU),
-    # the new state transposed in bf16
+    # the streaming shape (B 1, H 16, D 128, S 3520, bf16): the one-launch step's control words
+    # (time-out word, 16 epochs, two flags per workgroup; 256 bytes aligned), fp32 partials of 8
+    # token splits of 448 tokens (two workgroups per split, one per half of the rows: 256 in
+    # all, one per CU), the new state transposed in bf16
     p = gdn.Problem(1, 16, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 0, 0, 128, 0, 0, 128)
-    assert gdn.workspace_size(p, True) == 16 * 8 * 128 * 128 * 4 + 16 * 128 * 128 * 2
+    ctl = (1 + 16 + 2 * 16 * 16) * 8
+    ctl = (ctl + 255) // 256 * 256
+    assert gdn.workspace_size(p, True) == ctl + 16 * 8 * 128 * 128 * 4 + 16 * 128 * 128 * 2
+    # STAGED keeps the three launches and needs no control words
+    st = gdn.Problem(1, 16, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 0, 0, 128, 0, 0, 128, 1)
+    assert gdn.workspace_size(st, True) == 16 * 8 * 128 * 128 * 4 + 16 * 128 * 128 * 2
+    # heads not a multiple of 8: three launches, splits filling 256 workgroups (12 heads: 11
+    # splits of 320 tokens)
+    h12 = gdn.Problem(1, 12, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 0, 0, 128, 0, 0, 128)
+    assert gdn.workspace_size(h12, True) == 12 * 11 * 128 * 128 * 4 + 12 * 128 * 128 * 2
     # rows beyond 2 GiB: the whole-state step kernels
     big = gdn.Problem(1, 16, 128, 3520, 1, gdn.GDN_BF16, 1, 0.0, 0, 0, 1 << 20, 0, 0, 128)
     assert gdn.workspace_size(big, True) != gdn.workspace_size(p, True)
