@@ -1095,13 +1095,21 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
             store4(Mt + (16 * cb + r16) * MR + nw + 16 * nb + 4 * g, x[0], x[1], x[2], x[3]);
         }
     __syncthreads();
+    // k slots paired over two steps: in steps 2j and 2j + 1, lane group g holds the 16
+    // consecutive features 64 j + 16 g .. + 15 (the first 8 in step 2j), so that one 16-byte load
+    // brings a lane's E4M3 codes for both steps. Both input types and M^T use this grouping:
+    // each instruction rounds its own partial sum, and the E4M3 path (codes, then the scale on
+    // the fp32 result) equals the bf16 path on the decoded values bit for bit only when the two
+    // group the features alike.
     constexpr int TJ = D / 16, KSN = D / MM::KS;
+    static_assert(KSN % 2 == 0 && MM::KS == 32 && MM::KL == 8, "paired k steps of 32");
+    auto kslot = [&](int ks) { return 64 * (ks >> 1) + 16 * g + 8 * (ks & 1); };
     bf16x8 am[TJ][KSN];
 #pragma unroll
     for (int jt = 0; jt < TJ; ++jt)
 #pragma unroll
         for (int ks = 0; ks < KSN; ++ks)
-            am[jt][ks] = ld_frag<bf16>(Mt + out_col<bf16, D>(jt, r16) * MR + ks * MM::KS + g * MM::KL);
+            am[jt][ks] = ld_frag<bf16>(Mt + out_col<bf16, D>(jt, r16) * MR + kslot(ks));
     // Q tiles read and O tiles written through buffer resources that end with the frame's
     // last row, so tiles past S read zeros and drop their stores without branches; each wave
     // keeps QD tiles of Q in flight (a ring, unrolled so that every slot is a register)
@@ -1114,19 +1122,17 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
         ((S - 1) * (int)L.ot + D) * 2);
     const int qstb = (int)L.st * ESZ, ostb = (int)L.ot * 2;
     const float oscale = FP8 ? L.q_scale[gi] : 1.f;
-    // Q fragments as loaded: 8 bf16 values, or 8 E4M3 codes decoded when used
-    using QRaw = typename std::conditional<FP8, u32x2, u32x4>::type;
-    auto load_q = [&](int s0, QRaw (&bq)[KSN]) {
-        const int vo = (s0 + r16) * qstb + (g * MM::KL) * ESZ;
+    // Q fragments as loaded: per step 8 bf16 values, or per step pair 16 E4M3 codes decoded
+    // when used
+    constexpr int QN = FP8 ? KSN / 2 : KSN;
+    auto load_q = [&](int s0, u32x4 (&bq)[QN]) {
+        const int vo = (s0 + r16) * qstb;
 #pragma unroll
-        for (int ks = 0; ks < KSN; ++ks) {
-            if constexpr (FP8)
-                bq[ks] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, vo + ks * MM::KS, 0, 0));
-            else
-                bq[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, vo + ks * MM::KS * 2, 0, 0));
-        }
+        for (int i = 0; i < QN; ++i)
+            bq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rq, vo + kslot(FP8 ? 2 * i : i) * ESZ, 0, 0));
     };
-    QRaw bq[QD][KSN];
+    u32x4 bq[QD][QN];
 #pragma unroll
     for (int d = 0; d < QD; ++d) load_q(wave * 16 + d * 64, bq[d]);
     for (int s0 = wave * 16; s0 < S; s0 += QD * 64) {
@@ -1136,10 +1142,13 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
             bf16x8 bw[KSN];
 #pragma unroll
             for (int ks = 0; ks < KSN; ++ks) {
-                if constexpr (FP8)
-                    bw[ks] = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(bq[d][ks]));
-                else
+                if constexpr (FP8) {
+                    const u32x4 w = bq[d][ks >> 1];
+                    bw[ks] = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(
+                                                           (ks & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]}));
+                } else {
                     bw[ks] = __builtin_bit_cast(bf16x8, bq[d][ks]);
+                }
             }
             load_q(st + QD * 64, bq[d]);  // the tile QD steps ahead, into the freed slot
             f32x4 acc[TJ];
