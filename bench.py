@@ -109,6 +109,8 @@ def parse():
                     help="forward schedule (auto: the library's choice)")
     ap.add_argument("--copy-calib-gib", type=float, default=0.0,
                     help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--placement-sweep", type=int, default=0,
+                    help="only the 720p forward at this many output placements (for counter runs)")
     ap.add_argument("--stream-only", action="store_true",
                     help="only the streaming step leg (for profiling its kernels); prints its JSON")
     return ap.parse_args()
@@ -633,6 +635,40 @@ def attention_mode(dev, steps, warmup, ev, stream):
     return out
 
 
+def placement_sweep(dev, count, reps=3):
+    """The 720p forward with the same Q, K, V and a new output buffer for each of `count`
+    placements (every earlier buffer kept, so each lands on fresh pages further away in HBM):
+    ms per call at each placement, for counter runs that compare them (dispatches in order)."""
+    import torch
+    import frame_wise_gated_libgdn_amd as gdn
+    import gdn_synth
+    w = gdn_synth.WORKLOADS["gdn_720p_60s_bf16"]
+    q, k, v = gdn_synth.qkv_torch(w, dev)
+    g, b = gdn_synth.gates_torch(w, dev)
+    st = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device=dev)
+    p = gdn.Problem(w.B, w.H, w.D, w.S, w.F, gdn.GDN_BF16, int(w.use_delta), 0.0,
+                    *q.stride()[:3], *q.stride()[:3])
+    ws = torch.empty(gdn.workspace_size(p, False), dtype=torch.uint8, device=dev)
+    outs, rows = [], []
+    base = q.data_ptr()
+    for i in range(count):
+        o = torch.empty_like(q)
+        outs.append(o)
+        gdn.forward_framewise(q, k, v, g, b, out=o, state_out=st, workspace=ws)   # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            gdn.forward_framewise(q, k, v, g, b, out=o, state_out=st, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        rows.append({"placement": i, "o_offset_gb": round((o.data_ptr() - base) / 1e9, 2),
+                     "ms": round(e0.elapsed_time(e1) / reps, 4)})
+        log("placement %d: O at +%.2f GB from Q, %.3f ms" % (i, rows[-1]["o_offset_gb"], rows[-1]["ms"]))
+    return {"workload": w.name, "reps_per_placement": reps, "dispatches_per_placement": reps + 1,
+            "placements": rows}
+
+
 def streaming_ceiling(dev, gib=4.0, reps=10):
     """Bandwidth of a plain torch streaming kernel with the fused kernel's mix of traffic (three
     tensors read, one written: y = a + b * c in one elementwise kernel), for reading `frac`
@@ -672,6 +708,10 @@ def main():
         copy_calibration(args.copy_calib_gib)
         return
     gdn.load()
+    if args.placement_sweep > 0:
+        print(json.dumps({"placement_sweep": placement_sweep(torch.device("cuda:0"),
+                                                             args.placement_sweep)}), flush=True)
+        return
     if args.stream_only:
         ev = HipEvents()
         print(json.dumps({"stream": stream_mode(torch.device("cuda:0"), args.stream_frames, ev,
