@@ -553,6 +553,18 @@ def tconv_mode(dev, steps, warmup, ev, stream, stream_frames=240):
     for f in range(3):
         gdn.temporal_conv(x[:, f:f + 1], wt, bt, c, block_frames=1, out=yf, cache_out=c, stream=stream)
     torch.cuda.synchronize()
+    # frame by frame through prepared calls (arguments marshalled once, as a streaming loop
+    # holding its buffers would), one event between frames
+    calls = [gdn.prepare_temporal_conv(x[:, f:f + 1], wt, bt, c, block_frames=1, out=yf, cache_out=c,
+                                       stream=stream) for f in range(nf)]
+    marks = [ev.new() for _ in range(nf + 1)]
+    ev.record(marks[0], sh)
+    for f in range(nf):
+        calls[f]()
+        ev.record(marks[f + 1], sh)
+    torch.cuda.synchronize()
+    lat = np.array([ev.ms(marks[f], marks[f + 1]) * 1e3 for f in range(nf)])
+    # the same through the checking binding call, each launch bracketed by its own events
     evs = [(ev.new(), ev.new()) for _ in range(nf)]
     kev = [[ev.new(), ev.new()] for _ in range(nf)]
     for f in range(nf):
@@ -562,7 +574,7 @@ def tconv_mode(dev, steps, warmup, ev, stream, stream_frames=240):
         ev.record(evs[f][1], sh)
     gdn.set_trace(None)
     torch.cuda.synchronize()
-    lat = np.array([ev.ms(a, b) * 1e3 for a, b in evs])       # includes the host's launch work
+    blat = np.array([ev.ms(a, b) * 1e3 for a, b in evs])      # includes the host's launch work
     klat = np.array([ev.ms(a, b) * 1e3 for a, b in kev])      # the launch alone
     step_bytes = 4 * w.B * w.S * w.C * 2       # x, cache_in read; y, cache_out written
     del x, y
@@ -574,6 +586,7 @@ def tconv_mode(dev, steps, warmup, ev, stream, stream_frames=240):
             "frac": round(bytes_alg / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "stream": {"frames": nf, "us_per_frame_median": round(float(np.median(lat)), 2),
                        "us_per_frame_p90": round(float(np.percentile(lat, 90)), 2),
+                       "binding_us_per_frame_median": round(float(np.median(blat)), 2),
                        "kernel_us_median": round(float(np.median(klat)), 2),
                        "kernel_gb_s": round(step_bytes / (float(np.median(klat)) * 1e-6) / 1e9, 1),
                        "bytes_per_frame_mb": round(step_bytes / 1e6, 2),

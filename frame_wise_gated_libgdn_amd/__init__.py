@@ -17,7 +17,7 @@ import threading
 
 __all__ = ["GdnError", "Problem", "load", "library_path", "workspace_size", "forward_framewise",
            "forward_framewise_save", "saved_size", "step_frame", "step_frame_noalloc",
-           "prepare_step_frame",
+           "prepare_step_frame", "prepare_temporal_conv",
            "backward_framewise", "check_timeout",
            "abi_version", "set_trace", "read_trace", "KERNEL_NAMES", "SCHEDULES", "GDN_F32",
            "GDN_BF16"]
@@ -404,6 +404,35 @@ def temporal_conv(x, weight, bias=None, cache=None, *, block_frames, out=None, c
     _check(load().gdn_tconv_forward(ctypes.byref(p), _ptr(x), _ptr(weight), _ptr(bias), _ptr(cache),
                                     _ptr(out), _ptr(cache_out), _stream(stream)))
     return out, cache_out
+
+
+def prepare_temporal_conv(x, weight, bias=None, cache=None, *, block_frames, out, cache_out=None,
+                          stream=None):
+    """temporal_conv with every argument checked and marshalled once: returns a function of no
+    arguments that enqueues the same gdn_tconv_forward call again (same buffers; their contents
+    may change between calls) and raises GdnError if it fails. For streaming loops that convolve
+    one block per call from the cache (cache_out may be cache)."""
+    B, T, S, C = x.shape
+    if x.stride(3) != 1 or out.stride(3) != 1:
+        raise GdnError(4, "the channel dimension must be contiguous")
+    for name, t in (("cache", cache), ("cache_out", cache_out)):
+        if t is not None and (t.dtype != x.dtype or tuple(t.shape) != (B, S, C) or not t.is_contiguous()):
+            raise GdnError(4, "%s must be a contiguous %s tensor of shape %s" % (name, x.dtype, (B, S, C)))
+    _check_f32("weight", weight, (C, 3))
+    _check_f32("bias", bias, (C,))
+    p = TconvProblem(B, T, S, C, int(block_frames), _dtype_code(x), x.stride(0), x.stride(1),
+                     x.stride(2), out.stride(0), out.stride(1), out.stride(2))
+    fn = load().gdn_tconv_forward
+    args = (ctypes.byref(p), _ptr(x), _ptr(weight), _ptr(bias), _ptr(cache), _ptr(out),
+            _ptr(cache_out), _stream(stream))
+    keep = (p, x, weight, bias, cache, out, cache_out)   # alive while the call is
+
+    def call():
+        code = fn(*args)
+        if code:
+            _check(code)
+        return keep[5], keep[6]
+    return call
 
 
 def attention_framecausal(q, k, v, *, tokens_per_frame, q_frame0=0, scale=None, out=None,

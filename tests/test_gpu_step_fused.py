@@ -161,3 +161,22 @@ def test_one_launch_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(o, ref_o) and torch.equal(st, ref_s), "replay %d differs" % rep
     gdn.check_timeout(p, 1, ws)
+
+
+def test_prepared_step_call_equals_step_frame():
+    """prepare_step_frame marshals the arguments once; calling it again after the inputs change
+    in place gives what step_frame gives on the new contents."""
+    case = (1, 8, 128, 500, True, "head")
+    _, (q, k, v, g, b, s) = inputs(case)
+    o = torch.empty_like(q)
+    so = torch.empty_like(s)
+    call = gdn.prepare_step_frame(q, k, v, g, b, s, out=o, state_out=so)
+    for rep in range(3):
+        ref_o, ref_s = gdn.step_frame(q, k, v, g, b, s)
+        out, st = call()
+        torch.cuda.synchronize()
+        assert out is o and st is so
+        assert torch.equal(o, ref_o) and torch.equal(so, ref_s), "call %d differs" % rep
+        q.mul_(0.5)   # new contents, same buffers
+    with pytest.raises(gdn.GdnError):
+        gdn.prepare_step_frame(q, k[:, :, :10], v, g, b, s)

@@ -114,6 +114,25 @@ def test_tconv_one_frame_stream_in_place_cache():
     assert torch.equal(c, xd[:, -1])
 
 
+def test_tconv_prepared_calls_stream_like_the_binding():
+    """prepare_temporal_conv per frame (arguments marshalled once), cache updated in place:
+    the frames equal the whole sequence in one call bit for bit."""
+    B, T, S, C = 1, 5, 12, 128
+    x, cache, w, bias = make(B, T, S, C, "bf16", 21)
+    xd, wd, bd = x.to(DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(bias).to(DEV)
+    whole, _ = gdn.temporal_conv(xd, wd, bd, cache.to(DEV), block_frames=1)
+    c = cache.to(DEV).clone()
+    outs = [torch.empty_like(xd[:, :1]) for _ in range(T)]
+    calls = [gdn.prepare_temporal_conv(xd[:, t:t + 1], wd, bd, c, block_frames=1, out=outs[t], cache_out=c)
+             for t in range(T)]
+    for t in range(T):
+        y, cc = calls[t]()
+        assert y is outs[t] and cc is c
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=1), whole)
+    assert torch.equal(c, xd[:, -1])
+
+
 def test_tconv_deterministic():
     x, cache, w, bias = make(1, 33, 4, 128, "bf16", 9)
     args = (x.to(DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(bias).to(DEV), cache.to(DEV))
