@@ -249,6 +249,9 @@ gdn_status check_sizes(const gdn_problem* p, int mode) {
         return fail(GDN_ERR_UNSUPPORTED, "the fused schedule needs a frame's q/k/v rows and its o rows within 2 GiB");
     if (mode == 2 && !gdn::backward_supported(p->dtype == GDN_BF16, D))
         return fail(GDN_ERR_UNSUPPORTED, "the backward needs bf16 data and D = 64 or 128");
+    // the gradient kernels address a frame's rows through 32-bit buffer offsets
+    if (mode == 2 && !fused_rows_fit(*p))
+        return fail(GDN_ERR_UNSUPPORTED, "the backward needs a frame's q/k/v rows and its d_o rows within 2 GiB");
     const int64_t F = step_mode ? 1 : p->frames;
     const int64_t BH = (int64_t)p->batch * p->heads;
     // grid sizes: BH * F * splits must fit a 1-D grid; token indices f*S+s must fit int32 math

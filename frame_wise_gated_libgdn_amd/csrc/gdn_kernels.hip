@@ -1230,6 +1230,7 @@ template <int D> __device__ __forceinline__ u32x2 read_tr4(const bf16* X, int k0
 }
 
 constexpr int kBwdThreads = 512;
+constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt not waited for
 
 template <int D, bool DELTA>
 __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
@@ -1296,18 +1297,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
     bf16* dkf = (bf16*)L.dk + io;
     bf16* dvf = (bf16*)L.dv + io;
 
-    for (int s0 = wave * 16; s0 < S; s0 += NW * 16) {
-        const int s = s0 + r16;
-        const bool in = s < S;
-        // operands are loaded where their use begins, to keep live ranges short
-        bf16x8 bk[KS];
-        u32x4 vv[CP];
+    // the wave's 16-token tiles s0 = 16 wave + 16 NW i; K and V of the next tile load while the
+    // current one is used (one tile ahead in registers). K, V, dK and dV go through buffer
+    // resources that end with the frame's last row: rows at or past S read zero and drop their
+    // stores, with no branches around the loads (the host keeps a frame's rows below 2 GiB)
+    const int fbytes = ((S - 1) * (int)L.st + D) * 2, stb = (int)L.st * 2;
+    const __amdgpu_buffer_rsrc_t rk = buffer_over(kf, fbytes), rv = buffer_over(vf, fbytes);
+    const __amdgpu_buffer_rsrc_t rdk = buffer_over(dkf, fbytes), rdv = buffer_over(dvf, fbytes);
+    auto row_off = [&](int s0) { return s0 + r16 < S ? (s0 + r16) * stb + 16 * g : fbytes; };
+    bf16x8 bk[KS];
+    u32x4 vv[CP];
+    auto load_kv = [&](int s0, bf16x8 (&kr)[KS], u32x4 (&vr)[CP]) __attribute__((always_inline)) {
+        const int off = row_off(s0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            bk[ks] = in ? ld_frag<bf16>(kf + (int64_t)s * L.st + ks * 32 + 8 * g) : zero_frag<bf16>();
+            kr[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, off + 64 * ks, 0, 0));
 #pragma unroll
         for (int p = 0; p < CP; ++p)
-            vv[p] = in ? ld16(vf + (int64_t)s * L.st + 32 * p + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+            vr[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off + 64 * p, 0, 0));
+    };
+    load_kv(wave * 16, bk, vv);
+    // the first tile is complete before the loop: otherwise the compiler's wait at the loop
+    // head, placed for these loads, also waits for the previous tile's stores on every pass
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    for (int s0 = wave * 16; s0 < S; s0 += NW * 16) {
+        const int so = row_off(s0);
+        bf16x8 nk[KS];
+        u32x4 nv[CP];
+        load_kv(s0 + NW * 16, nk, nv);
 
         // P^T and (Kt G)^T: C tiles whose rows are the features out_col(cb, 4 g + q), i.e. for
         // tile pair p, lane (r, g) holds features 32 p + 8 g + (0..7) of token r
@@ -1352,11 +1369,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
                 b2[cb][0] = pack_bf16x2(sc * kk[0], sc * kk[1]);
                 b2[cb][1] = pack_bf16x2(sc * kk[2], sc * kk[3]);
             }
-            if (in) st16(dvf + (int64_t)s * L.st + 32 * p + 8 * g, u32x4{dvw[0], dvw[1], dvw[2], dvw[3]});
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{dvw[0], dvw[1], dvw[2], dvw[3]}, rdv, so + 64 * p, 0, 0);
         }
         // dKt^T, a pair of 16-row tiles (32 features) at a time (not unrolled: it indexes no
         // register array, and unrolling lets the compiler hoist every LDS read)
-#pragma unroll 1
+#pragma unroll
         for (int p = 0; p < CP; ++p) {
             f32x4 ak[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -1382,11 +1399,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kernel(Launch L) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (in)
-                st16(dkf + (int64_t)s * L.st + 32 * p + 8 * g,
-                     u32x4{pack_bf16x2(c * ak[0][0], c * ak[0][1]), pack_bf16x2(c * ak[0][2], c * ak[0][3]),
-                           pack_bf16x2(c * ak[1][0], c * ak[1][1]), pack_bf16x2(c * ak[1][2], c * ak[1][3])});
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{pack_bf16x2(c * ak[0][0], c * ak[0][1]), pack_bf16x2(c * ak[0][2], c * ak[0][3]),
+                      pack_bf16x2(c * ak[1][0], c * ak[1][1]), pack_bf16x2(c * ak[1][2], c * ak[1][3])},
+                rdk, so + 64 * p, 0, 0);
         }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bk[ks] = nk[ks];
+#pragma unroll
+        for (int p = 0; p < CP; ++p) vv[p] = nv[p];
     }
 
     // dgamma, dbeta: wave sums, then a fixed-order sum over waves
@@ -1518,15 +1539,22 @@ __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
         }
     }
 
-    // tokens [c0, c0 + SC) of Q and dO into registers; rows at or beyond t1 are zero
+    // tokens [c0, c0 + SC) of Q and dO into registers; rows at or beyond t1 are zero. Q, dO and
+    // dQ go through buffer resources that end with the frame's last row, and rows past t1 are
+    // addressed at that end: they read zero and drop their stores, with no branches (the host
+    // keeps a frame's rows below 2 GiB), so the compiler can count the accesses in flight
+    const int qbytes = ((S - 1) * (int)L.st + D) * 2, obytes = ((S - 1) * (int)L.ot + D) * 2;
+    const int qstb = (int)L.st * 2, ostb = (int)L.ot * 2;
+    const __amdgpu_buffer_rsrc_t rbq = buffer_over(qf, qbytes), rbo = buffer_over(of, obytes);
+    const __amdgpu_buffer_rsrc_t rbdq = buffer_over(dqf, qbytes);
     u32x4 rq[NLD], ro[NLD];
     auto load = [&](int c0) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int e = tid + i * kQdoThreads, tok = c0 + e / FB, fb = e % FB;
             const bool in = tok < t1;
-            rq[i] = in ? ld16(qf + (int64_t)tok * L.st + fb * 8) : u32x4{0u, 0u, 0u, 0u};
-            ro[i] = in ? ld16(of + (int64_t)tok * L.ot + fb * 8) : u32x4{0u, 0u, 0u, 0u};
+            rq[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rbq, in ? tok * qstb + fb * 16 : qbytes, 0, 0));
+            ro[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rbo, in ? tok * ostb + fb * 16 : obytes, 0, 0));
         }
     };
 
@@ -1538,6 +1566,9 @@ __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
     const int ja0 = RW * wave;
 
     load(t0);
+    // the first chunk is complete before the loop: otherwise the compiler's wait at the loop
+    // head, placed for these loads, also waits for the previous chunk's dQ stores on every pass
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     for (int c0 = t0; c0 < t1; c0 += SC) {
         lds_sync();   // the previous chunk's readers are done (first pass: M_f^T is written)
 #pragma unroll
@@ -1547,7 +1578,8 @@ __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
             st16_sw<D>(Ot, row, fb * 8, ro[i]);
         }
         lds_sync();
-        if (c0 + SC < t1) load(c0 + SC);
+        load(c0 + SC);   // past the end: zeros, no memory access
+        __builtin_amdgcn_sched_barrier(0);   // issued here, a whole chunk ahead of their use
 
         // C += Q^T dO over the chunk's tokens, 32 at a time (k slots 0-7 of lane group g:
         // tokens k0 + 8 g + 0..7, the same in both operands)
@@ -1574,10 +1606,11 @@ __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
         // reads of the swizzled tile are then free of bank conflicts), 32 features at a time
         const int trow = out_col<bf16, 64>(wave, r16);
         const int s = c0 + trow;
+        const int so = s < t1 ? s * qstb + 16 * g : qbytes;
         bf16x8 bo[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bo[ks] = ld16_sw<D>(Ot, trow, ks * 32 + 8 * g);
-#pragma unroll 1
+#pragma unroll
         for (int pp = 0; pp < CP; ++pp) {
             f32x4 aq[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -1589,10 +1622,10 @@ __global__ __launch_bounds__(kQdoThreads, 2) void qdo_kernel(Launch L) {
                     aq[hh] = MM::run(__builtin_bit_cast(bf16x8, u32x4{n0[0], n0[1], n1[0], n1[1]}), bo[ks], aq[hh]);
                 }
             }
-            if (s < t1)
-                st16(dqf + (int64_t)s * L.st + 32 * pp + 8 * g,
-                     u32x4{pack_bf16x2(aq[0][0], aq[0][1]), pack_bf16x2(aq[0][2], aq[0][3]),
-                           pack_bf16x2(aq[1][0], aq[1][1]), pack_bf16x2(aq[1][2], aq[1][3])});
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{pack_bf16x2(aq[0][0], aq[0][1]), pack_bf16x2(aq[0][2], aq[0][3]),
+                      pack_bf16x2(aq[1][0], aq[1][1]), pack_bf16x2(aq[1][2], aq[1][3])},
+                rbdq, so + 64 * pp, 0, 0);
         }
     }
 

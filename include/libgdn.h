@@ -338,8 +338,9 @@ gdn_status gdn_step_frame_noalloc(const gdn_problem* p, const void* q, const voi
  *   dgamma, dbeta  outputs, fp32 [B][H][F]
  *   d_state_in   output fp32 [B][H][D][D], or NULL; may equal d_state_out exactly
  *   workspace    at least gdn_workspace_size(p, 2) bytes, 256-byte aligned
- * Supported: bf16 data with D = 64 or 128 (GDN_ERR_UNSUPPORTED otherwise). No output may
- * overlap an input, the workspace or another output.
+ * Supported: bf16 data with D = 64 or 128, a frame's q/k/v rows within 2 GiB and its d_o rows
+ * within 2 GiB (GDN_ERR_UNSUPPORTED otherwise). No output may overlap an input, the workspace or
+ * another output.
  */
 gdn_status gdn_backward_framewise(const gdn_problem* p, const void* q, const void* k,
                                   const void* v, const float* gamma, const float* beta,

@@ -393,6 +393,20 @@ def test_fused_needs_frame_output_rows_within_2gib():
     assert call(big) == 3 and "2 GiB" in msg()
 
 
+def test_backward_needs_frame_rows_within_2gib():
+    # the gradient kernels read K, V, Q, dO and write dK, dV, dQ through 32-bit buffer offsets
+    for field in ("qkv", "o"):
+        big = prob(F=3)
+        setattr(big, field + "_stride_t", 1 << 25)     # 39 rows of 2^25 bf16 elements: > 2 GiB
+        setattr(big, field + "_stride_h", (1 << 25) * 40 * 3)
+        setattr(big, field + "_stride_b", (1 << 25) * 40 * 3 * 2)
+        n = ctypes.c_size_t(0)
+        assert gdn.load().gdn_workspace_size(ctypes.byref(big), 2, ctypes.byref(n)) == 3
+        assert "2 GiB" in msg()
+        assert call_bwd(big) == 3
+    assert gdn.workspace_size(prob(F=3), 2) > 0
+
+
 def tprob(B=1, T=6, S=5, C=16, tb=2, dtype=gdn.GDN_BF16):
     return gdn.TconvProblem(B, T, S, C, tb, dtype, T * S * C, S * C, C, T * S * C, S * C, C)
 
