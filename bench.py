@@ -435,6 +435,9 @@ def backward_mode(w, dev, steps, ev, stream):
     bs_ms = timed(bwd_saved)
     saved_gb = saved.numel() / 1e9
     del q, k, v, d_o, dq, dk, dv, o, saved, wsf, ws3
+    torch.cuda.empty_cache()
+    ceil_1r = {"kind": CEILING_KINDS[1], "gb_s": round(streaming_ceiling(dev, 1), 1)}
+    ceil_2r = {"kind": CEILING_KINDS[2], "gb_s": round(streaming_ceiling(dev, 2), 1)}
     return {"workload": w.name, "ms_per_call": round(ms, 4),
             "from_saved_states": {"forward_save_ms": round(fs_ms, 4), "saved_gb": round(saved_gb, 3),
                                   "backward_ms": round(bs_ms, 4),
@@ -445,10 +448,25 @@ def backward_mode(w, dev, steps, ev, stream):
             "call": {"bytes_alg_gb": round(bytes_alg / 1e9, 3), "t_roof_ms": round(t_roof, 4),
                      "frac_of_roofline": round(t_roof / ms, 4),
                      "achieved_gb_s": round(bytes_alg / (ms * 1e-3) / 1e9, 1)},
-            "bwd_kernel": {"achieved_gb_s": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1) if bwd_ms else None,
-                           "frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if bwd_ms else None},
-            "qdo_kernel": {"achieved_gb_s": round(qdo_bytes / (qdo_ms * 1e-3) / 1e9, 1) if qdo_ms else None,
-                           "frac": round(qdo_bytes / (qdo_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if qdo_ms else None}}
+            "bwd_kernel": kernel_vs_ceiling(bwd_bytes, bwd_ms, "bwd", ceil_1r),
+            "qdo_kernel": kernel_vs_ceiling(qdo_bytes, qdo_ms, "qdo", ceil_2r)}
+
+
+def kernel_vs_ceiling(alg_bytes, ms, key, ceiling):
+    """A backward kernel's algorithmic rate against the HBM peak; its measured HBM traffic (the
+    committed counters, when they were taken on the current source) per this run's duration,
+    against the torch streaming kernel with its mix of reads and writes."""
+    if not ms:
+        return None
+    c = counters_for(key)
+    hbm = c["hbm_read_gb"] + c["hbm_write_gb"] if c else None
+    out = {"achieved_gb_s": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+           "frac": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "hbm_gb_per_launch": round(hbm, 3) if hbm else None,
+           "hbm_gb_s": round(hbm / (ms * 1e-3), 1) if hbm else None,
+           "ceiling": ceiling}
+    out["frac_of_ceiling"] = round(hbm / (ms * 1e-3) / ceiling["gb_s"], 4) if hbm else None
+    return out
 
 
 def fp8_mode(dev, steps, warmup, ev, stream):
@@ -682,16 +700,30 @@ def placement_sweep(dev, count, reps=3):
             "placements": rows}
 
 
-def streaming_ceiling(dev, gib=4.0, reps=10):
-    """Bandwidth of a plain torch streaming kernel with the fused kernel's mix of traffic (three
-    tensors read, one written: y = a + b * c in one elementwise kernel), for reading `frac`
-    against what a simple kernel reaches on the same device."""
+CEILING_KINDS = {
+    1: "torch bf16 copy y = a: 1 tensor read, 1 written, 4 GiB each",
+    2: "torch bf16 add y = a + b: 2 tensors read, 1 written, 4 GiB each",
+    3: "torch bf16 addcmul y = a + b * c: 3 tensors read, 1 written, 4 GiB each",
+}
+
+
+def streaming_ceiling(dev, nread=3, gib=4.0, reps=10):
+    """Bandwidth of a plain torch streaming kernel that reads `nread` tensors and writes one
+    (one elementwise kernel): the reference for a kernel with the same mix of traffic (the fused
+    forward reads three and writes one; the backward's Q/dO pass two and one; its gradient
+    kernel K, V and dK, dV, one to one)."""
     import torch
     n = int(gib * (1 << 30)) // 2
-    a, b, c, y = (torch.empty(n, dtype=torch.bfloat16, device=dev).normal_() for _ in range(4))
+    xs = [torch.empty(n, dtype=torch.bfloat16, device=dev).normal_() for _ in range(nread)]
+    y = torch.empty(n, dtype=torch.bfloat16, device=dev)
 
     def f():
-        torch.addcmul(a, b, c, out=y)
+        if nread == 1:
+            y.copy_(xs[0])
+        elif nread == 2:
+            torch.add(xs[0], xs[1], out=y)
+        else:
+            torch.addcmul(xs[0], xs[1], xs[2], out=y)
 
     f()
     torch.cuda.synchronize()
@@ -702,9 +734,9 @@ def streaming_ceiling(dev, gib=4.0, reps=10):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    del a, b, c, y
+    del xs, y
     torch.cuda.empty_cache()
-    return 4 * n * 2 / (ms * 1e-3) / 1e9   # a, b, c read, y written
+    return (nread + 1) * n * 2 / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -854,9 +886,9 @@ def main():
     ev.close()
     del q, k, v, o, ws
     torch.cuda.empty_cache()
-    ceil = streaming_ceiling(dev)
+    ceil = streaming_ceiling(dev, 3)
     result["roofline"]["streaming_ceiling"] = {
-        "kind": "torch bf16 addcmul y = a + b * c: 3 tensors read, 1 written, 4 GiB each",
+        "kind": CEILING_KINDS[3],
         "gb_s": round(ceil, 1), "frac_of_ceiling": round(achieved / ceil, 4)}
     log("streaming ceiling (torch addcmul): %.0f GB/s" % ceil)
     if not args.no_stream:
