@@ -664,6 +664,9 @@ gdn_status run_attn(const gdn_attn_problem* p, const void* q, const void* k, con
         !layout_ok(B, H, Tk, D, p->kv_stride_b, p->kv_stride_h, p->kv_stride_t) ||
         !layout_ok(B, H, Tq, D, p->o_stride_b, p->o_stride_h, p->o_stride_t))
         return fail(GDN_ERR_STRIDE, "strides overlap rows or are negative");
+    // the kernel addresses a head's key and value rows through 32-bit offsets from each tile
+    if (((Tk - 1) * p->kv_stride_t + D) * 2 >= ((int64_t)1 << 31))
+        return fail(GDN_ERR_UNSUPPORTED, "a head's key/value rows must lie within 2 GiB");
     for (const void* ptr : {q, k, v, (const void*)o})
         if (!aligned(ptr, 16)) return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
     for (int64_t st : {p->q_stride_b, p->q_stride_h, p->q_stride_t, p->kv_stride_b, p->kv_stride_h,

@@ -4,14 +4,14 @@
 // both directions), o = softmax(scale q k^T) v, per (b, h). Queries may be a later slice of the
 // frames than the keys (a streaming step against the cache of all frames so far).
 //
-// One workgroup of 8 waves takes 256 queries of one (b, h); a wave owns 32 of them and walks the
-// visible keys in tiles of 64. Products run on v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains
+// One workgroup of 8 or 12 waves takes 256 or 384 queries of one (b, h); a wave owns 32 of
+// them and walks the visible keys in tiles of 64. Products run on v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains
 // about 2.4 PFLOP/s, the 16x16x32 form about 1.45): lane l = 32 g + r holds A row r and B column
 // r over the contraction slice [8 g, 8 g + 8), and C rows 8 i + 4 g + q (register 4 i + q) of
 // column r.
 //   * S^T = K Q^T per 32-key block: A = K rows from LDS, B = the wave's Q rows, held in
-//     registers for the whole call; lane (r, g) ends up with the scores of query r for keys
-//     8 i + 4 g + q of each 32-key block (16 per block);
+//     registers for the whole call (in LDS with 12 waves); lane (r, g) ends up with the scores
+//     of query r for keys 8 i + 4 g + q of each 32-key block (16 per block);
 //   * online softmax per query in that layout (exp2 of one fma with scale * log2 e folded in;
 //     the two lanes of a query meet by one lane exchange; the running maximum moves only by
 //     more than 8 in log2 units, so most tiles skip rescaling the accumulators);
@@ -42,12 +42,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kKT = 64;        // keys per tile
 constexpr int kQW = 32;        // queries per wave
-// waves per workgroup (one workgroup per CU, two waves per SIMD). They share each K/V tile, so
-// 8 halve the tile traffic per query against 4; measured on the 880 x 81 sequence and on 720p
-// streaming frames (224 workgroups) 8 were faster throughout (43.3 against 47.0 ms, 100.5 against
-// 117.1 ms at frame 960)
-constexpr int kNW = 8;
-constexpr int kQB = kNW * kQW; // queries per workgroup
+// Waves per workgroup (one workgroup per CU): 8 (two per SIMD, Q in registers) or 12 (three
+// per SIMD, Q in LDS, so that registers fit 168 per lane). They share each K/V tile, so more
+// waves stream fewer tiles per query. Measured on the 880 x 81 sequence and on 720p streaming
+// frames: 8 waves beat 4 throughout (43.3 against 47.0 ms, 100.5 against 117.1 ms at frame
+// 960); 12 beat 8 on the whole sequence (40.3 against 40.9-43.2 ms) but lose on one frame,
+// whose 10 query blocks per head of 384 leave CUs idle (117 against 95-98 ms). The launcher
+// takes 12 when the grid has at least two workgroups per CU.
+constexpr int kQBMax = 12 * kQW;   // queries per workgroup at most
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -85,70 +87,109 @@ template <int D> __device__ __forceinline__ u32x2 read_vt(const bf16* X, int kro
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a));
 }
 
+// byte offset of read_vt's address for rows krow = 8 h (mod 16) and dims c0 = 32 db, within a
+// tile: the 16-key step s adds s 16 D 2 bytes (row bits 4 and up leave the swizzle unchanged)
+template <int D> __device__ __forceinline__ uint32_t vt_off(int h, int db, int lane) {
+    constexpr int CH = D / 8;
+    const int q = lane >> 4, s = lane & 15;
+    const int row = 8 * h + 4 * (q >> 1) + (s >> 2);
+    const int col = 32 * db + 16 * (q & 1) + 4 * (s & 3);
+    return (uint32_t)((row * D + (((col >> 3) ^ swz<CH>(row)) * 8) + (col & 7)) * 2);
+}
+
 // number of keys visible to query row t (keys of frames 0 .. its frame)
 __device__ __forceinline__ int visible(const AttnLaunch& L, int t) {
     const int64_t n = (int64_t)(L.q_frame0 + t / L.S + 1) * L.S;
     return n < L.Tk ? (int)n : L.Tk;
 }
 
-template <int D>
-__global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
+    constexpr int QB = NW * kQW;          // queries per workgroup
+    constexpr bool QLDS = NW > 8;         // Q fragments from LDS instead of registers
     constexpr int KS = D / 16;            // 16-long k steps over the head dim (scores)
     constexpr int DB = D / 32;            // 32-dim blocks of O
     constexpr int KB = kKT / 32;          // 32-key blocks per tile
     constexpr int CH = D / 8;             // 16-byte chunks per row
     constexpr int SLOTS = kKT * CH;       // 16-byte slots of one operand tile
-    constexpr int INSTR = 2 * SLOTS / (64 * kNW);   // load instructions per wave per tile (K and V)
-    static_assert(SLOTS % 64 == 0 && (2 * SLOTS) % (64 * kNW) == 0, "whole instructions per wave");
+    constexpr int NI = 2 * SLOTS / 64;                 // load instructions per tile (K and V)
+    constexpr int INSTR = (NI + NW - 1) / NW;          // at most, per wave (wave w: w, w + NW, ..)
+    static_assert(SLOTS % 64 == 0, "whole instructions");
     // the two buffers are separate arrays and the tile loop is unrolled by two, so that every
     // LDS read names its buffer statically: the compiler can then tell the reads of one buffer
     // from the direct-to-LDS loads into the other, and does not wait for those before them
     __shared__ __attribute__((aligned(16))) bf16 tile0[2][kKT * D];   // [K, V] of even tiles
     __shared__ __attribute__((aligned(16))) bf16 tile1[2][kKT * D];   // [K, V] of odd tiles
+    // with QLDS, each wave's Q rows, [query][dim] swizzled as the K tiles
+    __shared__ __attribute__((aligned(16))) bf16 qs[QLDS ? NW : 1][QLDS ? kQW * D : 8];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, g = lane >> 5;
     // XCD-aware order: workgroup i runs on XCD i mod 8; XCD x takes the contiguous stretch
     // [x n8, (x + 1) n8) of the (b h)-major, query-block-minor order, so that the workgroups
     // resident on one XCD are neighbouring query blocks of the same head and share its K/V tiles
     // through that XCD's L2 (the grid is padded to 8 n8 workgroups; the padding returns at once)
-    const int nqb = (L.Tq + kQB - 1) / kQB;
+    const int nqb = (L.Tq + QB - 1) / QB;
     const int n8 = (L.B * L.H * nqb + 7) / 8;
     const int item = (int)(blockIdx.x % 8) * n8 + (int)(blockIdx.x / 8);
     if (item >= L.B * L.H * nqb) return;
     const int bh = item / nqb, qb = item % nqb;
     const int b = bh / L.H, h = bh % L.H;
-    const int qw0 = qb * kQB + wave * kQW;    // first query of this wave
+    const int qw0 = qb * QB + wave * kQW;    // first query of this wave
 
     // the wave's Q rows as B operands (lane (r, g): query qw0 + r, dims 16 ks + 8 g .. + 7);
     // rows past Tq repeat the last row (never stored)
-    bf16x8 qf[KS];
+    const bf16* qw = qs[QLDS ? wave : 0];
+    bf16x8 qf[QLDS ? 1 : KS];
     int nlim;
     {
         const bf16* qbase = (const bf16*)L.q + (int64_t)b * L.qsb + (int64_t)h * L.qsh;
         const int t = min(qw0 + r, L.Tq - 1);
         nlim = visible(L, t);
+        u32x4 x[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qbase + (int64_t)t * L.qst + 16 * ks + 8 * g));
+        for (int ks = 0; ks < KS; ++ks) x[ks] = *(const u32x4*)(qbase + (int64_t)t * L.qst + 16 * ks + 8 * g);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (QLDS) *(u32x4*)(qs[wave] + r * D + (((2 * ks + g) ^ swz<CH>(r)) * 8)) = x[ks];
+            else qf[ks] = __builtin_bit_cast(bf16x8, x[ks]);
+        }
     }
+    // per-lane byte offsets of the V^T reads (read_vt) for the two halves of a 16-key step and
+    // each 32-dim block
+    uint32_t voff[2][DB];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) voff[hh][db] = vt_off<D>(hh, db, lane);
     // keys every query of the workgroup sees, and the keys any of them sees
-    const int kfull = visible(L, qb * kQB);
-    const int kmax = visible(L, min(qb * kQB + kQB, L.Tq) - 1);
+    const int kfull = visible(L, qb * QB);
+    const int kmax = visible(L, min(qb * QB + QB, L.Tq) - 1);
 
     const bf16* kbase = (const bf16*)L.k + (int64_t)b * L.ksb + (int64_t)h * L.ksh;
     const bf16* vbase = (const bf16*)L.v + (int64_t)b * L.ksb + (int64_t)h * L.ksh;
     // tile of keys k0 .. k0 + kKT - 1 into buffer buf: instruction ins of the workgroup fills
     // slots 64 ins .. 64 ins + 63 of the K | V pair; rows past Tk are loaded clamped (finite
     // values: their scores are masked and their weights are zero)
+    // (a uniform base per tile and a 32-bit offset per lane, recomputed from a lane index the
+    // optimiser cannot see through, so that few registers hold addresses across the tile loop;
+    // the host keeps a head's key rows below 2 GiB)
+    const int kstb = (int)L.kst * 2;
     auto issue = [&](int k0, bf16 (&tl)[2][kKT * D]) {
+        const char* ksrc = (const char*)kbase + (int64_t)k0 * kstb;
+        const char* vsrc = (const char*)vbase + (int64_t)k0 * kstb;
+        const int lim = L.Tk - 1 - k0;
+        int ln = lane;
+        __asm__ __volatile__("" : "+v"(ln));
 #pragma unroll
         for (int i = 0; i < INSTR; ++i) {
-            const int ins = wave * INSTR + i;
+            const int ins = wave + NW * i;
+            if (NI % NW && ins >= NI) break;                 // the same for the whole wave
             const bool isv = ins * 64 >= SLOTS;              // the same for the whole wave
-            const int u = ins * 64 + lane - (isv ? SLOTS : 0);
+            const int u = ins * 64 + ln - (isv ? SLOTS : 0);
             const int row = u / CH, c = (u % CH) ^ swz<CH>(row);
-            const bf16* src = (isv ? vbase : kbase) + (int64_t)min(k0 + row, L.Tk - 1) * L.kst + c * 8;
+            const char* src = (isv ? vsrc : ksrc) + (uint32_t)(min(row, lim) * kstb + c * 16);
             bf16* dst = &tl[isv ? 1 : 0][(ins * 64 - (isv ? SLOTS : 0)) * 8];
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
@@ -184,7 +225,10 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
             for (int kb = 0; kb < KB; ++kb) {
                 const int row = 32 * kb + r;
                 const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(kt + row * D + (((2 * ks + g) ^ swz<CH>(row)) * 8)));
-                sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
+                bf16x8 qb_;
+                if constexpr (QLDS) qb_ = __builtin_bit_cast(bf16x8, *(const u32x4*)(qw + r * D + (((2 * ks + g) ^ swz<CH>(r)) * 8)));
+                else qb_ = qf[ks];
+                sacc[kb] = mfma32(a, qb_, sacc[kb]);
             }
         if (k0 + kKT > kfull) {   // a tile some query does not see completely
 #pragma unroll
@@ -234,8 +278,10 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
                               pack2(x[o + 6], x[o + 7])});
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const u32x2 v0 = read_vt<D>(vt, 16 * s, 32 * db, lane);
-                const u32x2 v1 = read_vt<D>(vt, 16 * s + 8, 32 * db, lane);
+                const u32x2 v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)((const char*)vt + voff[0][db] + s * 16 * D * 2)));
+                const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)((const char*)vt + voff[1][db] + s * 16 * D * 2)));
                 oacc[db] = mfma32(__builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]}), pb, oacc[db]);
             }
         }
@@ -268,12 +314,18 @@ __global__ __launch_bounds__(64 * kNW, 1) void attn_kernel(AttnLaunch L) {
 
 bool attn_supported(int D) { return D == 64 || D == 128; }
 
-template <int D> hipError_t launch_d(const AttnLaunch& L, hipStream_t s) {
-    const int64_t items = (int64_t)L.B * L.H * ((L.Tq + kQB - 1) / kQB);
+template <int D, int NW> hipError_t launch_nw(const AttnLaunch& L, hipStream_t s) {
+    const int64_t items = (int64_t)L.B * L.H * ((L.Tq + NW * kQW - 1) / (NW * kQW));
     const int64_t blocks = (items + 7) / 8 * 8;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_kernel<D>), dim3((unsigned)blocks), dim3(64 * kNW), 0, s, L);
+    hipLaunchKernelGGL((attn_kernel<D, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, L);
     return hipGetLastError();
+}
+
+// 12 waves where the grid then still has at least two workgroups per CU (256 CUs), else 8
+template <int D> hipError_t launch_d(const AttnLaunch& L, hipStream_t s) {
+    const int64_t items12 = (int64_t)L.B * L.H * ((L.Tq + kQBMax - 1) / kQBMax);
+    return items12 >= 2 * 256 ? launch_nw<D, 12>(L, s) : launch_nw<D, 8>(L, s);
 }
 
 hipError_t attn_launch(const AttnLaunch& L, hipStream_t s) {

@@ -198,7 +198,8 @@ typedef struct {
  *            query's own frame must be present)
  *   o        [B][H][Tq][D] bf16, must not overlap q, k or v
  * fp32 softmax and accumulation; the weights enter the value product rounded to bf16. Pointers
- * 16-byte aligned, strides multiples of 8 elements. No workspace. Asynchronous on hip_stream;
+ * 16-byte aligned, strides multiples of 8 elements; a head's Tk key (and value) rows must lie
+ * within 2 GiB (GDN_ERR_UNSUPPORTED otherwise). No workspace. Asynchronous on hip_stream;
  * errors and tracing as gdn_forward_framewise (trace kind GDN_KERNEL_ATTN, units B*H*Tq).
  */
 gdn_status gdn_attention_framecausal(const gdn_attn_problem* p, const void* q, const void* k,

@@ -455,6 +455,11 @@ def test_attention_validation():
     assert call_attn(p) == 3
     assert call_attn(aprob(), o=A + 256) == 6               # o overlaps q
     assert call_attn(aprob(), k=2 * A + 8) == 5
+    big = aprob()                                             # key rows over 2 GiB: 32-bit offsets
+    big.kv_stride_t = 1 << 25
+    big.kv_stride_h = (1 << 25) * 3 * 40
+    big.kv_stride_b = big.kv_stride_h * 2
+    assert call_attn(big) == 3 and "2 GiB" in msg()
 
 
 def test_trace_kinds_match_the_header():

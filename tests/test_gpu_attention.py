@@ -49,6 +49,9 @@ CASES = [
     # several 256-query workgroups per head, ragged last one
     (2, 128, 128, 97, 3, 3, 0, "head"),
     (2, 128, 64, 65, 5, 6, 1, "token"),      # later keys present, masked
+    # grids of at least 512 workgroups of 384 queries take the 12-wave kernel (Q in LDS)
+    (2, 256, 128, 97, 3, 3, 0, "head"),
+    (2, 128, 64, 65, 8, 9, 1, "token"),      # two query blocks per head, ragged, later keys masked
 ]
 
 
@@ -76,6 +79,7 @@ RESCALE_CASES = [
     (1, 2, 64, 77, 3, 4, 1, "head", 16.0, True),     # ragged last key tile, later keys masked
     (2, 3, 64, 40, 5, 5, 0, "token", 16.0, False),
     (1, 1, 128, 130, 2, 6, 3, "head", 12.0, True),   # streaming rows, ragged tiles
+    (2, 256, 128, 40, 3, 3, 0, "head", 8.0, True),   # the 12-wave kernel
 ]
 
 
