@@ -5,10 +5,10 @@
 // frames than the keys (a streaming step against the cache of all frames so far).
 //
 // One workgroup of 8 or 12 waves takes 256 or 384 queries of one (b, h); a wave owns 32 of
-// them and walks the visible keys in tiles of 64. Products run on v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains
-// about 2.4 PFLOP/s, the 16x16x32 form about 1.45): lane l = 32 g + r holds A row r and B column
-// r over the contraction slice [8 g, 8 g + 8), and C rows 8 i + 4 g + q (register 4 i + q) of
-// column r.
+// them and walks the visible keys in tiles of 64. Products run on v_mfma_f32_32x32x16_bf16 (on
+// gfx950 it sustains about 2.4 PFLOP/s, the 16x16x32 form about 1.45): lane l = 32 g + r holds
+// A row r and B column r over the contraction slice [8 g, 8 g + 8), and C rows 8 i + 4 g + q
+// (register 4 i + q) of column r.
 //   * S^T = K Q^T per 32-key block: A = K rows from LDS, B = the wave's Q rows, held in
 //     registers for the whole call (in LDS with 12 waves); lane (r, g) ends up with the scores
 //     of query r for keys 8 i + 4 g + q of each 32-key block (16 per block);
@@ -25,6 +25,9 @@
 // tile lands unpadded, one 1 KB stretch per instruction, and bank conflicts are avoided by the
 // choice of source chunk per lane (an XOR swizzle of each row's 16-byte chunks). Key tiles that
 // every query of the workgroup sees completely skip the mask; the others mask per element.
+// Instruction scheduling is left to the compiler: forcing one wave's softmax to interleave
+// with its next tile's products measured slower (the two waves of a SIMD overlap each other's
+// products and vector work; one wave's vector work does not run in its own products' shadow).
 #include <stdint.h>
 
 #include "gdn_internal.h"
