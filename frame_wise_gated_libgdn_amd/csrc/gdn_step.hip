@@ -11,7 +11,7 @@
 //      direct loads in stages of 112 tokens at D = 128, the next stage loading while one is
 //      used; XOR-swizzled 16-byte chunks), [G_p | B_p] = K_p^T [K_p | V_p] accumulates on v_mfma_f32_32x32x16_bf16
 //      (every operand a transposed LDS read), then U_p = B_p - gamma c G_p M with -gamma c G_p
-//      and M in bf16, stored as an fp32 partial. K and V cross HBM once.
+//      and M in bf16, stored as a partial of 24 bits per value. K and V cross HBM once.
 //   2. step_sum_kernel, one workgroup per (b, h, 32 x 32 tile): M' = gamma M + beta c sum_p U_p
 //      in split order, state_out, and the bf16 transposed copy M'^T.
 //   3. step_output_kernel, one workgroup per (b, h, chunk of at most 256 tokens): M'^T staged
@@ -36,6 +36,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -73,6 +74,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, int
 // streaming shape that ends the one-launch step 1.6 us sooner for the outputs and 0.5 us
 // sooner for the partials, net of their slower read-back.
 constexpr int kDeviceScope = 16;
+
+// The partials travel in 24 bits per value: the top three bytes of each fp32 (sign, exponent and
+// 15 fraction bits), rounded to nearest (ties away from zero), four values in 12 bytes. A
+// partial keeps 16 significant bits, against the 8 of the bf16 operands of the products that
+// form it; the sum of the partials and the state stay fp32. A NaN is truncated and made quiet,
+// so that it stays a NaN whatever its payload; a finite value past the largest 24-bit one
+// rounds to infinity.
+__device__ __forceinline__ u32x3 pack24(f32x4 x) {
+    uint32_t t[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        // through a scalar: a bit cast of a vector lane itself reads lane 0 on this compiler
+        const float f = x[q];
+        const uint32_t b = __builtin_bit_cast(uint32_t, f);
+        t[q] = (b & 0x7FFFFFFFu) > 0x7F800000u ? b >> 8 | 0x4000u : (b + 0x80u) >> 8;
+    }
+    return u32x3{t[0] | t[1] << 24, t[1] >> 8 | t[2] << 16, t[2] >> 16 | t[3] << 8};
+}
+__device__ __forceinline__ f32x4 unpack24(u32x3 d) {
+    const uint32_t t0 = d[0] & 0xFFFFFFu, t1 = d[0] >> 24 | (d[1] & 0xFFFFu) << 8;
+    const uint32_t t2 = d[1] >> 16 | (d[2] & 0xFFu) << 16, t3 = d[2] >> 8;
+    return f32x4{__builtin_bit_cast(float, t0 << 8), __builtin_bit_cast(float, t1 << 8),
+                 __builtin_bit_cast(float, t2 << 8), __builtin_bit_cast(float, t3 << 8)};
+}
+constexpr int kPartBytes = 12;   // bytes per lane and register group of a partial
 
 // Barrier on LDS accesses only: this wave's LDS accesses are complete, then s_barrier. Unlike
 // __syncthreads() it does not wait for outstanding global loads (its workgroup release fence
@@ -145,8 +171,8 @@ __device__ __forceinline__ bf16x8 mask_tail(bf16x8 x, int krow, int lane, int va
 // CTW tiles of 32 x 32: local rows 32 RTW (w mod 2), columns 32 CTW (w / 2); waves 0-3 hold G,
 // waves 4-7 hold B. The epilogue writes -gamma c G (transposed) and M to LDS in bf16 and the B
 // waves finish their tiles as U_p = B_p + (-gamma c G_p) M. The partial goes to
-// part[role][tile][i][lane][4 fp32] (registers 4 i .. 4 i + 3 of the C layout), tile = local
-// 32-row block * (D / 32) + 32-column block of U.
+// part[role][tile][i][lane][12 bytes] (registers 4 i .. 4 i + 3 of the C layout in 24 bits
+// each, pack24), tile = local 32-row block * (D / 32) + 32-column block of U.
 // `last()` runs in every wave once the split's last stage has landed, before its products
 // (for global loads into registers that the caller wants in flight early; no LDS access).
 template <int D, bool DELTA, class Hook>
@@ -334,9 +360,10 @@ __device__ __forceinline__ void gram_phase(const Launch& L, int bh, int p, int h
         }
     }
     if (!gwave) {
-        // register group i of every lane: one contiguous 1 KB per store instruction, written
-        // through (so that the end of the launch need not write them back)
-        const __amdgpu_buffer_rsrc_t rp = buffer_over(L.part + (int64_t)role * NTL * 1024, NTL * 4096);
+        // register group i of every lane: one contiguous 768 bytes per store instruction,
+        // written through (so that the end of the launch need not write them back)
+        constexpr int RB = NTL * 4 * 64 * kPartBytes;   // bytes of one role's partial
+        const __amdgpu_buffer_rsrc_t rp = buffer_over((const char*)L.part + (int64_t)role * RB, RB);
 #pragma unroll
         for (int a = 0; a < RTW; ++a)
 #pragma unroll
@@ -345,9 +372,9 @@ __device__ __forceinline__ void gram_phase(const Launch& L, int bh, int p, int h
                 const f32x16& x = acc[a][c];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        __builtin_bit_cast(u32x4, f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]}), rp,
-                        ((tile * 4 + i) * 64 + lane) * 16, 0, kDeviceScope);
+                    __builtin_amdgcn_raw_buffer_store_b96(
+                        pack24(f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]}), rp,
+                        ((tile * 4 + i) * 64 + lane) * kPartBytes, 0, kDeviceScope);
             }
     }
 }
@@ -387,9 +414,10 @@ __device__ __forceinline__ void sum_tile(const Launch& L, int bh, int tile, int 
     const int i = 32 * rt + 8 * part + 4 * (lane >> 5), j = 32 * ct + (lane & 31);
     const int NS = L.nsplit;
     // partial of split p: role ((b h) NS + p) HV + hr; consecutive splits are HV NTL tiles apart
-    const float* head = L.part + (int64_t)bh * NS * HV * NTL * 1024;
-    const int src = ((hr * NTL + lt) * 1024 + (part * 64 + lane) * 4) * 4;   // bytes into the head
-    const __amdgpu_buffer_rsrc_t rp = buffer_over(head, NS * HV * NTL * 4096);
+    constexpr int RB = NTL * 4 * 64 * kPartBytes;   // bytes of one role's partial
+    const char* head = (const char*)L.part + (int64_t)bh * NS * HV * RB;
+    const int src = (((hr * NTL + lt) * 4 + part) * 64 + lane) * kPartBytes;   // bytes into the head
+    const __amdgpu_buffer_rsrc_t rp = buffer_over(head, NS * HV * RB);
     const float* min_ = L.state_in + (int64_t)bh * D * D;
     float m0[4];
 #pragma unroll
@@ -400,11 +428,11 @@ __device__ __forceinline__ void sum_tile(const Launch& L, int bh, int tile, int 
         f32x4 x[BATCH];
 #pragma unroll
         for (int e = 0; e < BATCH; ++e) {
-            const int off = src + min(p0 + e, NS - 1) * HV * NTL * 4096;
+            const int off = src + min(p0 + e, NS - 1) * HV * RB;
             if constexpr (COH)
-                x[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kDeviceScope));
+                x[e] = unpack24(__builtin_amdgcn_raw_buffer_load_b96(rp, off, 0, kDeviceScope));
             else
-                x[e] = *(const f32x4*)((const char*)head + off);
+                x[e] = unpack24(__builtin_amdgcn_raw_buffer_load_b96(rp, off, 0, 0));
         }
 #pragma unroll
         for (int e = 0; e < BATCH; ++e)
