@@ -14,7 +14,8 @@
 //     of query r for keys 8 i + 4 g + q of each 32-key block (16 per block);
 //   * online softmax per query in that layout (exp2 of one fma with scale * log2 e folded in;
 //     the two lanes of a query meet by one lane exchange; the running maximum moves only by
-//     more than 8 in log2 units, so most tiles skip rescaling the accumulators);
+//     more than 8 in log2 units, so most tiles skip rescaling the accumulators; the normaliser
+//     is the fp32 sum of the bf16 weights the products use);
 //   * O^T += V^T P^T per 16-key step s: B = P^T is registers 8 (s mod 2) .. + 7 of score block
 //     s / 2 as they stand, so k slot t of lane group g is key 16 s + 4 g + (t mod 4) + 8 (t / 4);
 //     the A operand V^T is read in that same order with transposed LDS reads (ds_read_tr16_b64,
@@ -38,6 +39,7 @@ namespace {
 typedef __bf16 bf16;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -59,7 +61,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, bf16x2{(bf16)lo, (bf16)hi});
 }
 
@@ -120,9 +121,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
     static_assert(SLOTS % 64 == 0, "whole instructions");
     // the two buffers are separate arrays and the tile loop is unrolled by two, so that every
     // LDS read names its buffer statically: the compiler can then tell the reads of one buffer
-    // from the direct-to-LDS loads into the other, and does not wait for those before them
-    __shared__ __attribute__((aligned(16))) bf16 tile0[2][kKT * D];   // [K, V] of even tiles
-    __shared__ __attribute__((aligned(16))) bf16 tile1[2][kKT * D];   // [K, V] of odd tiles
+    // from the direct-to-LDS loads into the other, and does not wait for those before them.
+    // Their larger alignment places them first in LDS, below 64 KB, so that every V^T read of
+    // either buffer takes its buffer, half and 16-key step in the instruction's immediate offset
+    // (with the Q rows first, each tile added its 96 KB base to eight lane offsets)
+    __shared__ __attribute__((aligned(1024))) bf16 tile0[2][kKT * D];   // [K, V] of even tiles
+    __shared__ __attribute__((aligned(1024))) bf16 tile1[2][kKT * D];   // [K, V] of odd tiles
     // with QLDS, each wave's Q rows, [query][dim] swizzled as the K tiles
     __shared__ __attribute__((aligned(16))) bf16 qs[QLDS ? NW : 1][QLDS ? kQW * D : 8];
 
@@ -199,6 +203,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
     };
 
     const float c2 = L.scale * 1.4426950408889634f;   // scores in log2 units
+    const bf16x2 ones2 = bf16x2{(bf16)1.f, (bf16)1.f};
     float m = -__builtin_inff(), l = 0.f;
     f32x16 oacc[DB];
 #pragma unroll
@@ -261,24 +266,24 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
             m = mnew;
         }
-        float sum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][j], c2, -m));
-                sacc[kb][j] = p;
-                sum += p;
-            }
-        l += sum;
-        // O^T += V^T P^T, four 16-key steps
+            for (int j = 0; j < 16; ++j) sacc[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][j], c2, -m));
+        // O^T += V^T P^T, four 16-key steps. The normaliser sums the same bf16 weights that the
+        // products take, two per instruction (v_dot2c_f32_bf16 against (1, 1), fp32 sum)
 #pragma unroll
         for (int s = 0; s < kKT / 16; ++s) {
             const int o = 8 * (s & 1);
             const f32x16& x = sacc[s >> 1];
-            const bf16x8 pb = __builtin_bit_cast(
-                bf16x8, u32x4{pack2(x[o], x[o + 1]), pack2(x[o + 2], x[o + 3]), pack2(x[o + 4], x[o + 5]),
-                              pack2(x[o + 6], x[o + 7])});
+            const u32x4 pw = u32x4{pack2(x[o], x[o + 1]), pack2(x[o + 2], x[o + 3]), pack2(x[o + 4], x[o + 5]),
+                                   pack2(x[o + 6], x[o + 7])};
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = pw[e];   // through a scalar: a bit cast of a vector lane itself reads lane 0 on this compiler
+                l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones2, l, false);
+            }
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const u32x2 v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
