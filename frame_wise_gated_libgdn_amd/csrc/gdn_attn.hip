@@ -178,25 +178,33 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
     const bf16* vbase = (const bf16*)L.v + (int64_t)b * L.ksb + (int64_t)h * L.ksh;
     // tile of keys k0 .. k0 + kKT - 1 into buffer buf: instruction ins of the workgroup fills
     // slots 64 ins .. 64 ins + 63 of the K | V pair; rows past Tk are loaded clamped (finite
-    // values: their scores are masked and their weights are zero)
-    // (a uniform base per tile and a 32-bit offset per lane, recomputed from a lane index the
-    // optimiser cannot see through, so that few registers hold addresses across the tile loop;
-    // the host keeps a head's key rows below 2 GiB)
+    // values: their scores are masked and their weights are zero). A uniform base per tile and
+    // a 32-bit offset per lane (the host keeps a head's key rows below 2 GiB): each lane's row
+    // and swizzled chunk offsets are the same for every tile and are computed once, so a load
+    // costs one clamp and one add per tile (recomputing them cost about 30 vector instructions
+    // per tile)
     const int kstb = (int)L.kst * 2;
+    uint32_t roff[INSTR], coff[INSTR];
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+        const int ins = wave + NW * i;
+        const bool isv = ins * 64 >= SLOTS;
+        const int u = ins * 64 + lane - (isv ? SLOTS : 0);
+        const int row = u / CH, c = (u % CH) ^ swz<CH>(row);
+        roff[i] = (uint32_t)(row * kstb);
+        coff[i] = (uint32_t)(c * 16);
+    }
     auto issue = [&](int k0, bf16 (&tl)[2][kKT * D]) {
         const char* ksrc = (const char*)kbase + (int64_t)k0 * kstb;
         const char* vsrc = (const char*)vbase + (int64_t)k0 * kstb;
-        const int lim = L.Tk - 1 - k0;
-        int ln = lane;
-        __asm__ __volatile__("" : "+v"(ln));
+        // the last row's offset, or the tile's last (at most 63 rows on: below 2 GiB)
+        const uint32_t limoff = (uint32_t)(min(L.Tk - 1 - k0, kKT - 1) * kstb);
 #pragma unroll
         for (int i = 0; i < INSTR; ++i) {
             const int ins = wave + NW * i;
             if (NI % NW && ins >= NI) break;                 // the same for the whole wave
             const bool isv = ins * 64 >= SLOTS;              // the same for the whole wave
-            const int u = ins * 64 + ln - (isv ? SLOTS : 0);
-            const int row = u / CH, c = (u % CH) ^ swz<CH>(row);
-            const char* src = (isv ? vsrc : ksrc) + (uint32_t)(min(row, lim) * kstb + c * 16);
+            const char* src = (isv ? vsrc : ksrc) + (min(roff[i], limoff) + coff[i]);
             bf16* dst = &tl[isv ? 1 : 0][(ins * 64 - (isv ? SLOTS : 0)) * 8];
             __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
