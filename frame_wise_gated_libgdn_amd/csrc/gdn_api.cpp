@@ -59,8 +59,14 @@ constexpr int64_t kFusedMinItems = 1024;
 bool fused_rows_fit(const gdn_problem& p) {
     const int64_t esz = p.dtype == GDN_FP8_E4M3 ? 1 : 2;
     const int64_t S = p.tokens_per_frame, D = p.head_dim;
-    const int64_t in_span = ((S - 1) * p.qkv_stride_t + D) * esz;
-    const int64_t out_span = ((S - 1) * p.o_stride_t + D) * 2;
+    // the fused forward also addresses kFusedRowsPast rows past the frame (they read zero and
+    // drop their stores); a single-token tensor is given one row's length as its stride
+    const bool one = S * (int64_t)p.frames == 1;
+    const int64_t st = one ? std::max<int64_t>(p.qkv_stride_t, D) : p.qkv_stride_t;
+    const int64_t ot = one ? std::max<int64_t>(p.o_stride_t, D) : p.o_stride_t;
+    const int64_t rows = S - 1 + gdn::kFusedRowsPast;
+    const int64_t in_span = (rows * st + D) * esz;
+    const int64_t out_span = (rows * ot + D) * 2;
     return p.qkv_stride_t >= 0 && p.o_stride_t >= 0 && in_span < ((int64_t)1 << 31) &&
            out_span < ((int64_t)1 << 31);
 }

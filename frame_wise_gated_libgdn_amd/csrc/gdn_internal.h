@@ -114,6 +114,11 @@ hipError_t run_tconv(const TconvLaunch& L, hipStream_t s);
 // Fused forward: value-column groups pipelined through the frame chain (one flag each per (b, h)).
 constexpr int kChainGroups = 8;
 constexpr int kSpinLimitDefault = 1 << 20;  // polls of about a microsecond each
+// Rows past a frame's last one that the fused forward addresses (the ragged last K/V stage, Q
+// tiles prefetched ahead, O tiles of the last pass), through 32-bit offsets that read zero and
+// drop stores at or past the frame's end. The host keeps (S - 1 + kFusedRowsPast) rows of
+// either stride within 2 GiB, so that no such offset leaves int range or wraps into the frame.
+constexpr int kFusedRowsPast = 464;
 
 // Whether the fused single-pass forward has a kernel for this type / head size.
 bool fused_supported(int bf16, int D);

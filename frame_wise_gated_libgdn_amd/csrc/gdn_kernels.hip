@@ -1115,6 +1115,10 @@ __global__ __launch_bounds__(NT, 2) void fused_kernel(Launch L) {
     // keeps QD tiles of Q in flight (a ring, unrolled so that every slot is a register)
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr int QD = 4;
+    // rows addressed past the frame: Q loads up to 2 QD - 1 tiles of 64 ahead of the last tile
+    // begun before S (plus its 16 rows), O stores up to QD - 1 tiles on, K/V one stage on
+    static_assert((2 * QD - 1) * 64 + 15 < kFusedRowsPast && X::SC <= kFusedRowsPast,
+                  "the host bound covers every row the fused kernel addresses");
     const __amdgpu_buffer_rsrc_t rq =
         buffer_over((const char*)L.q + fo * ESZ, ((S - 1) * (int)L.st + D) * ESZ);
     const __amdgpu_buffer_rsrc_t ro = buffer_over(

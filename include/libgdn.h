@@ -98,9 +98,11 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype;
  *   FUSED   one pass: each (b, h, f) is a workgroup that computes its frame's products, waits
  *           for the state of frame f-1 of the same (b, h), applies the step, publishes M_f and
  *           writes O_f; only Q/K/V/O and the D x D states cross HBM. bf16 (or E4M3) with
- *           D = 64 or 128, and a frame's q/k/v rows ((S-1) * qkv_stride_t + D elements) and o
- *           rows ((S-1) * o_stride_t + D elements) each within 2 GiB (GDN_ERR_UNSUPPORTED
- *           otherwise).
+ *           D = 64 or 128, and a frame's q/k/v rows and o rows each within 2 GiB
+ *           (GDN_ERR_UNSUPPORTED otherwise), counting the 464 rows past the frame that the
+ *           kernel addresses (and reads as zero): (S + 463) * qkv_stride_t + D elements, and
+ *           (S + 463) * o_stride_t + D (a single-token tensor counts a stride of max(stride,
+ *           D)). The same bound applies wherever "a frame's rows within 2 GiB" is asked below.
  *   AUTO    FUSED where supported and B*H*F >= 1024, else STAGED.
  * FUSED waits for the previous frame's state are bounded: after GDN_FUSED_SPIN_LIMIT polls
  * (environment, default 2^20, about a microsecond each) a workgroup gives up, continues with a

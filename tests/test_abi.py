@@ -377,6 +377,24 @@ def test_fused_needs_frame_rows_within_2gib():
     assert call(big) == 3 and "2 GiB" in msg()
 
 
+def test_fused_bound_counts_the_rows_past_the_frame():
+    # the fused kernel addresses up to 464 rows past a frame's last one through 32-bit offsets:
+    # a stride whose 40 rows fit in 2 GiB but whose 40 + 463 rows do not must not select it
+    p = prob(F=3000)
+    big = prob(F=3000)
+    big.qkv_stride_t = 2228224                 # 39 rows: 166 MiB; 39 + 464 rows: 2.09 GiB
+    big.qkv_stride_h = big.qkv_stride_t * 40 * 3000
+    big.qkv_stride_b = big.qkv_stride_h * 2
+    assert gdn.workspace_size(big, False) != gdn.workspace_size(p, False)   # falls back to staged
+    big.schedule = 2
+    assert call(big) == 3 and "2 GiB" in msg()
+    ok = prob(F=3000)
+    ok.qkv_stride_t = 1048576                  # 39 + 464 rows: 1006 MiB, fused
+    ok.qkv_stride_h = ok.qkv_stride_t * 40 * 3000
+    ok.qkv_stride_b = ok.qkv_stride_h * 2
+    assert gdn.workspace_size(ok, False) == gdn.workspace_size(p, False)
+
+
 def test_fused_needs_frame_output_rows_within_2gib():
     # the fused kernel also writes O through 32-bit buffer offsets: a huge o token stride
     # with small q/k/v strides must not select it
