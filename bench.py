@@ -621,23 +621,26 @@ def attention_mode(dev, steps, warmup, ev, stream):
     sh = stream.cuda_stream
 
     def timed(fn, reps):
+        """ms per call: the sum of the call's launches (one, or two with key splits)."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        tr = [[ev.new(), ev.new()] for _ in range(reps)]
+        tr = [[ev.new() for _ in range(4)] for _ in range(reps)]
+        nl = 1
         for i in range(reps):
             gdn.set_trace(tr[i])
             fn()
+            nl = len(gdn.read_trace())
         gdn.set_trace(None)
         torch.cuda.synchronize()
-        return sum(ev.ms(a, b) for a, b in tr) / reps
+        return sum(sum(ev.ms(t[2 * j], t[2 * j + 1]) for j in range(nl)) for t in tr) / reps, nl
 
     out = {}
     w = gdn_synth.WORKLOADS["gdn_880x81_bf16"]
     q, k, v = gdn_synth.qkv_torch(w, dev)
     o = torch.empty_like(q)
-    ms = timed(lambda: gdn.attention_framecausal(q, k, v, tokens_per_frame=w.S, out=o, stream=stream),
-               steps)
+    ms, _ = timed(lambda: gdn.attention_framecausal(q, k, v, tokens_per_frame=w.S, out=o, stream=stream),
+                  steps)
     flops = 4 * w.D * w.S * w.S * w.F * (w.F + 1) // 2 * w.B * w.H
     out["whole_880x81"] = {"workload": w.name, "kernel_ms": round(ms, 4),
                            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
@@ -652,13 +655,19 @@ def attention_mode(dev, steps, warmup, ev, stream):
     per = []
     for f in (60, 240, w.F - 1):
         n = (f + 1) * S
-        ms = timed(lambda: gdn.attention_framecausal(q[:, :, f * S:(f + 1) * S], k[:, :, :n], v[:, :, :n],
-                                                     tokens_per_frame=S, q_frame0=f, out=o, stream=stream),
-                   max(1, min(steps, 5)))
+        qf, kf, vf = q[:, :, f * S:(f + 1) * S], k[:, :, :n], v[:, :, :n]
+        # a workspace lets the call split each query block's keys over more workgroups
+        nb = gdn.attention_workspace_size(gdn.attention_problem(qf, kf, o, S, f))
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        ms, nl = timed(lambda: gdn.attention_framecausal(qf, kf, vf, tokens_per_frame=S, q_frame0=f, out=o,
+                                                         workspace=ws, stream=stream),
+                       max(1, min(steps, 5)))
         flops = 4 * w.D * S * n * w.B * w.H
-        per.append({"frame": f, "kernel_ms": round(ms, 3),
+        per.append({"frame": f, "kernel_ms": round(ms, 3), "launches": nl,
+                    "workspace_mb": round(nb / 1e6, 1),
                     "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                     "kv_cache_gb": round(2 * n * w.D * 2 * w.B * w.H / 1e9, 2)})
+        del ws
     out["stream_720p_frame"] = {"workload": w.name, "per_frame": per,
                                 "gdn_state_mb": round(w.B * w.H * w.D * w.D * 4 / 1e6, 2)}
     del q, k, v, o

@@ -31,7 +31,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_UNSUPP
           8: "GDN_ERR_HIP", 9: "GDN_ERR_TIMEOUT"}
 KERNEL_NAMES = {0: "products", 1: "combine", 2: "scan", 3: "step_partial", 4: "step_reduce",
                 5: "fused_reset", 6: "fused", 7: "scan_bwd", 8: "bwd", 9: "scan_states",
-                10: "tconv", 11: "attn", 12: "step_output", 13: "bwd_qdo", 14: "step_fused"}
+                10: "tconv", 11: "attn", 12: "step_output", 13: "bwd_qdo", 14: "step_fused",
+                15: "attn_combine"}
 SCHEDULES = {"auto": 0, "staged": 1, "fused": 2}
 
 
@@ -116,6 +117,12 @@ def load():
             lib.gdn_tconv_forward.restype = ctypes.c_int
             lib.gdn_attention_framecausal.argtypes = [ctypes.POINTER(AttnProblem)] + [_vp] * 5
             lib.gdn_attention_framecausal.restype = ctypes.c_int
+            lib.gdn_attention_workspace_size.argtypes = [ctypes.POINTER(AttnProblem),
+                                                         ctypes.POINTER(ctypes.c_size_t)]
+            lib.gdn_attention_workspace_size.restype = ctypes.c_int
+            lib.gdn_attention_framecausal_ws.argtypes = ([ctypes.POINTER(AttnProblem)] + [_vp] * 5
+                                                         + [ctypes.c_size_t, _vp])
+            lib.gdn_attention_framecausal_ws.restype = ctypes.c_int
             lib.gdn_forward_framewise_fp8.argtypes = [P] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
             lib.gdn_forward_framewise_fp8.restype = ctypes.c_int
             lib.gdn_backward_framewise.argtypes = [P] + [_vp] * 14 + [_vp, ctypes.c_size_t, _vp]
@@ -435,11 +442,31 @@ def prepare_temporal_conv(x, weight, bias=None, cache=None, *, block_frames, out
     return call
 
 
+def attention_problem(q, k, out, tokens_per_frame, q_frame0=0, scale=None):
+    """The gdn_attn_problem of an attention call on these tensors (o's strides from `out`)."""
+    B, H, Tq, D = q.shape
+    S = int(tokens_per_frame)
+    return AttnProblem(B, H, D, S, Tq // S, k.shape[2] // S, int(q_frame0), GDN_BF16,
+                       0.0 if scale is None else float(scale), *q.stride()[:3], *k.stride()[:3],
+                       *out.stride()[:3])
+
+
+def attention_workspace_size(p: AttnProblem) -> int:
+    """Bytes of workspace that attention_framecausal(..., workspace=) may use for problem p
+    (0: the call would not split its keys)."""
+    n = ctypes.c_size_t(0)
+    _check(load().gdn_attention_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
 def attention_framecausal(q, k, v, *, tokens_per_frame, q_frame0=0, scale=None, out=None,
-                          stream=None):
+                          workspace=None, stream=None):
     """Frame-causal softmax attention (gdn_attention_framecausal). q [B, H, Tq, D], k, v
     [B, H, Tk, D] (bf16, D contiguous, k and v with the same strides); q's rows are frames
-    q_frame0 .. q_frame0 + Tq/S - 1, k's and v's frames 0 .. Tk/S - 1. Returns o like q."""
+    q_frame0 .. q_frame0 + Tq/S - 1, k's and v's frames 0 .. Tk/S - 1. Returns o like q.
+    workspace: a uint8 device tensor of attention_workspace_size bytes lets a single-frame
+    call split its keys over more workgroups (gdn_attention_framecausal_ws); "auto" allocates
+    one when the call would use it."""
     import torch
     B, H, Tq, D = q.shape
     Tk = k.shape[2]
@@ -457,8 +484,18 @@ def attention_framecausal(q, k, v, *, tokens_per_frame, q_frame0=0, scale=None, 
     p = AttnProblem(B, H, D, S, Tq // S, Tk // S, int(q_frame0), GDN_BF16,
                     0.0 if scale is None else float(scale), *q.stride()[:3], *k.stride()[:3],
                     *out.stride()[:3])
-    _check(load().gdn_attention_framecausal(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                            _stream(stream)))
+    if workspace is None:
+        _check(load().gdn_attention_framecausal(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(out), _stream(stream)))
+        return out
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise GdnError(2, "workspace must be a tensor, None or \"auto\"")
+        n = attention_workspace_size(p)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check(load().gdn_attention_framecausal_ws(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(out), _ptr(workspace), workspace.numel(),
+                                               _stream(stream)))
     return out
 
 

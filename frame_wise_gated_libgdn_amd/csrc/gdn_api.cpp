@@ -648,9 +648,8 @@ gdn_status run_tconv(const gdn_tconv_problem* p, const void* x, const float* wei
     return GDN_OK;
 }
 
-gdn_status run_attn(const gdn_attn_problem* p, const void* q, const void* k, const void* v,
-                    void* o, void* stream) {
-    g_msg[0] = '\0';
+// Sizes, layout and limits of an attention problem (no pointers); fills the launch's shape.
+gdn_status attn_shape(const gdn_attn_problem* p, gdn::AttnLaunch& L) {
     if (!p) return fail(GDN_ERR_NULL, "problem descriptor is NULL");
     if (p->batch < 1 || p->heads < 1 || p->tokens_per_frame < 1 || p->q_frames < 1 ||
         p->kv_frames < 1 || p->q_frame0 < 0)
@@ -661,10 +660,10 @@ gdn_status run_attn(const gdn_attn_problem* p, const void* q, const void* k, con
     if (!gdn::attn_supported(p->head_dim))
         return fail(GDN_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", p->head_dim);
     if (p->dtype != GDN_BF16) return fail(GDN_ERR_UNSUPPORTED, "attention takes bf16 data");
-    if (!q || !k || !v || !o) return fail(GDN_ERR_NULL, "q, k, v and o are required");
     const int64_t B = p->batch, H = p->heads, D = p->head_dim, S = p->tokens_per_frame;
     const int64_t Tq = (int64_t)p->q_frames * S, Tk = (int64_t)p->kv_frames * S;
-    if (Tk > ((int64_t)1 << 31) - 1 || B * H * ((Tq + 127) / 128) > ((int64_t)1 << 31) - 1)
+    if (Tk > ((int64_t)1 << 31) - 1 || B * H * ((Tq + 127) / 128) > ((int64_t)1 << 31) - 1 ||
+        B * H * Tq * D * 16 > ((int64_t)1 << 62))
         return fail(GDN_ERR_SHAPE, "problem too large for one call");
     if (!layout_ok(B, H, Tq, D, p->q_stride_b, p->q_stride_h, p->q_stride_t) ||
         !layout_ok(B, H, Tk, D, p->kv_stride_b, p->kv_stride_h, p->kv_stride_t) ||
@@ -673,23 +672,49 @@ gdn_status run_attn(const gdn_attn_problem* p, const void* q, const void* k, con
     // the kernel addresses a head's key and value rows through 32-bit offsets from each tile
     if (((Tk - 1) * p->kv_stride_t + D) * 2 >= ((int64_t)1 << 31))
         return fail(GDN_ERR_UNSUPPORTED, "a head's key/value rows must lie within 2 GiB");
-    for (const void* ptr : {q, k, v, (const void*)o})
-        if (!aligned(ptr, 16)) return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
     for (int64_t st : {p->q_stride_b, p->q_stride_h, p->q_stride_t, p->kv_stride_b, p->kv_stride_h,
                        p->kv_stride_t, p->o_stride_b, p->o_stride_h, p->o_stride_t})
         if (st % 8) return fail(GDN_ERR_ALIGN, "strides must be multiples of 8 elements");
-    const Span so = span_of(o, B, H, Tq, D, p->o_stride_b, p->o_stride_h, p->o_stride_t, 2);
-    for (Span in : {span_of(q, B, H, Tq, D, p->q_stride_b, p->q_stride_h, p->q_stride_t, 2),
-                    span_of(k, B, H, Tk, D, p->kv_stride_b, p->kv_stride_h, p->kv_stride_t, 2),
-                    span_of(v, B, H, Tk, D, p->kv_stride_b, p->kv_stride_h, p->kv_stride_t, 2)})
-        if (overlap(so, in)) return fail(GDN_ERR_ALIAS, "o overlaps q, k or v");
-    gdn::AttnLaunch L{};
+    L = gdn::AttnLaunch{};
     L.B = (int)B; L.H = (int)H; L.D = (int)D; L.S = (int)S; L.Tq = (int)Tq; L.Tk = (int)Tk;
     L.q_frame0 = p->q_frame0;
     L.scale = p->scale > 0.f ? p->scale : (float)(1.0 / std::sqrt((double)D));
     L.qsb = p->q_stride_b; L.qsh = p->q_stride_h; L.qst = p->q_stride_t;
     L.ksb = p->kv_stride_b; L.ksh = p->kv_stride_h; L.kst = p->kv_stride_t;
     L.osb = p->o_stride_b; L.osh = p->o_stride_h; L.ost = p->o_stride_t;
+    return GDN_OK;
+}
+
+// ws == NULL: no key splits (the plain entry point)
+gdn_status run_attn(const gdn_attn_problem* p, const void* q, const void* k, const void* v,
+                    void* o, void* ws, size_t ws_bytes, void* stream) {
+    g_msg[0] = '\0';
+    gdn::AttnLaunch L;
+    gdn_status st = attn_shape(p, L);
+    if (st != GDN_OK) return st;
+    if (!q || !k || !v || !o) return fail(GDN_ERR_NULL, "q, k, v and o are required");
+    const int64_t B = L.B, H = L.H, D = L.D, Tq = L.Tq, Tk = L.Tk;
+    for (const void* ptr : {q, k, v, (const void*)o})
+        if (!aligned(ptr, 16)) return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+    const Span so = span_of(o, B, H, Tq, D, p->o_stride_b, p->o_stride_h, p->o_stride_t, 2);
+    const Span ins[3] = {span_of(q, B, H, Tq, D, p->q_stride_b, p->q_stride_h, p->q_stride_t, 2),
+                         span_of(k, B, H, Tk, D, p->kv_stride_b, p->kv_stride_h, p->kv_stride_t, 2),
+                         span_of(v, B, H, Tk, D, p->kv_stride_b, p->kv_stride_h, p->kv_stride_t, 2)};
+    for (Span in : ins)
+        if (overlap(so, in)) return fail(GDN_ERR_ALIAS, "o overlaps q, k or v");
+    size_t need = 0;
+    gdn::attn_plan(L, ws != nullptr, &need);
+    if (need) {
+        if (ws_bytes < need)
+            return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+        if (!aligned(ws, 256)) return fail(GDN_ERR_ALIGN, "workspace must be 256-byte aligned");
+        const Span sw{(const char*)ws, (const char*)ws + need};
+        if (overlap(sw, so) || overlap(sw, ins[0]) || overlap(sw, ins[1]) || overlap(sw, ins[2]))
+            return fail(GDN_ERR_ALIAS, "the workspace overlaps q, k, v or o");
+        const size_t part_bytes = ((size_t)L.nsplit * B * H * Tq * D * 4 + 255) / 256 * 256;
+        L.part = (float*)ws;
+        L.ml = (float*)((char*)ws + part_bytes);
+    }
     L.q = q; L.k = k; L.v = v; L.o = o;
     const hipError_t e = gdn::run_attn(L, (hipStream_t)stream);
     if (e != hipSuccess) return fail(GDN_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
@@ -838,7 +863,23 @@ gdn_status gdn_tconv_forward(const gdn_tconv_problem* p, const void* x, const fl
 
 gdn_status gdn_attention_framecausal(const gdn_attn_problem* p, const void* q, const void* k,
                                      const void* v, void* o, void* hip_stream) {
-    return run_attn(p, q, k, v, o, hip_stream);
+    return run_attn(p, q, k, v, o, nullptr, 0, hip_stream);
+}
+
+gdn_status gdn_attention_workspace_size(const gdn_attn_problem* p, size_t* bytes_out) {
+    g_msg[0] = '\0';
+    if (!bytes_out) return fail(GDN_ERR_NULL, "bytes_out is NULL");
+    gdn::AttnLaunch L;
+    gdn_status st = attn_shape(p, L);
+    if (st != GDN_OK) return st;
+    gdn::attn_plan(L, true, bytes_out);
+    return GDN_OK;
+}
+
+gdn_status gdn_attention_framecausal_ws(const gdn_attn_problem* p, const void* q, const void* k,
+                                        const void* v, void* o, void* workspace,
+                                        size_t workspace_bytes, void* hip_stream) {
+    return run_attn(p, q, k, v, o, workspace, workspace_bytes, hip_stream);
 }
 
 gdn_status gdn_set_trace(void* const* events, int pairs) {

@@ -31,6 +31,8 @@
 // products and vector work; one wave's vector work does not run in its own products' shadow).
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -38,6 +40,8 @@ namespace {
 
 typedef __bf16 bf16;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -141,11 +145,16 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
     // the longest first keeps the end of the launch short (a list-scheduling model of the
     // 880 x 81 sequence, 32 CUs per XCD: 0.2% over the even split of the work, against 4.2%
     // first to last)
+    // With key splits the order is (b h, split)-major: the resident workgroups of an XCD are
+    // then neighbouring query blocks of one split, which read the same key tiles.
     const int nqb = (L.Tq + QB - 1) / QB;
-    const int n8 = (L.B * L.H * nqb + 7) / 8;
+    const int NS = L.nsplit;
+    const int nitems = L.B * L.H * NS * nqb;
+    const int n8 = (nitems + 7) / 8;
     const int item = (int)(blockIdx.x % 8) * n8 + (int)(blockIdx.x / 8);
-    if (item >= L.B * L.H * nqb) return;
-    const int bh = item / nqb, qb = nqb - 1 - item % nqb;
+    if (item >= nitems) return;
+    const int bhs = item / nqb, qb = nqb - 1 - item % nqb;
+    const int bh = bhs / NS, sp = bhs % NS;
     const int b = bh / L.H, h = bh % L.H;
     const int qw0 = qb * QB + wave * kQW;    // first query of this wave
 
@@ -174,9 +183,14 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int db = 0; db < DB; ++db) voff[hh][db] = vt_off<D>(hh, db, lane);
-    // keys every query of the workgroup sees, and the keys any of them sees
+    // keys every query of the workgroup sees, and the keys any of them sees; this split's
+    // share of the latter, [kbeg, kend), in whole tiles (all of it without splits; with
+    // splits, every query of the block sees every key: the queries form one frame)
     const int kfull = visible(L, qb * QB);
     const int kmax = visible(L, min(qb * QB + QB, L.Tq) - 1);
+    const int ntile = (kmax + kKT - 1) / kKT;
+    const int kbeg = (int)((int64_t)sp * ntile / NS) * kKT;
+    const int kend = min((int)((int64_t)(sp + 1) * ntile / NS) * kKT, kmax);
 
     const bf16* kbase = (const bf16*)L.k + (int64_t)b * L.ksb + (int64_t)h * L.ksh;
     const bf16* vbase = (const bf16*)L.v + (int64_t)b * L.ksb + (int64_t)h * L.ksh;
@@ -229,7 +243,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
         // wave is done reading the other buffer (the previous tile), which the next tile fills
         __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (k0 + kKT < kmax) issue(k0 + kKT, nxt);
+        if (k0 + kKT < kend) issue(k0 + kKT, nxt);
         const bf16* kt = cur[0];
         const bf16* vt = cur[1];
 
@@ -306,17 +320,37 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
             }
         }
     };
-    issue(0, tile0);
-    for (int k0 = 0; k0 < kmax; k0 += 2 * kKT) {
+    if (kbeg < kend) issue(kbeg, tile0);
+    for (int k0 = kbeg; k0 < kend; k0 += 2 * kKT) {
         step(k0, tile0, tile1);
-        if (k0 + kKT < kmax) step(k0 + kKT, tile1, tile0);
+        if (k0 + kKT < kend) step(k0 + kKT, tile1, tile0);
     }
 
-    // normalise and store: lane (r, g) holds O[query qw0 + r][dims 32 db + 8 i + 4 g .. + 3] in
-    // registers 4 i .. 4 i + 3 of block db
-    bf16* obase = (bf16*)L.o + (int64_t)b * L.osb + (int64_t)h * L.osh;
-    const float inv = 1.f / (l + __shfl_xor(l, 32));
+    // lane (r, g) holds O[query qw0 + r][dims 32 db + 8 i + 4 g .. + 3] in registers
+    // 4 i .. 4 i + 3 of block db
+    const float lsum = l + __shfl_xor(l, 32);
     const int t = qw0 + r;
+    if (NS > 1) {
+        // this split's unnormalised O, its maximum (log2 units; the same in both lanes of a
+        // query) and its weight sum, for the merge
+        if (t < L.Tq) {
+            const int64_t row = (int64_t)(sp * L.B * L.H + bh) * L.Tq + t;
+            float* prow = L.part + row * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = 4 * i;
+                    *(f32x4*)(prow + 32 * db + 8 * i + 4 * g) =
+                        f32x4{oacc[db][j], oacc[db][j + 1], oacc[db][j + 2], oacc[db][j + 3]};
+                }
+            if (g == 0) *(f32x2*)(L.ml + 2 * row) = f32x2{m, lsum};
+        }
+        return;
+    }
+    // normalise and store
+    bf16* obase = (bf16*)L.o + (int64_t)b * L.osb + (int64_t)h * L.osh;
+    const float inv = 1.f / lsum;
     if (t < L.Tq) {
         bf16* orow = obase + (int64_t)t * L.ost;
 #pragma unroll
@@ -330,28 +364,102 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnLaunch L) {
     }
 }
 
+// Merge of the key splits: per query row, M = max_s m_s, w_s = 2^(m_s - M),
+// o = sum_s w_s O_s / sum_s w_s l_s in split order, rounded to bf16. 32 lanes per row, 4
+// dimensions each (D = 128; 16 lanes at D = 64), 256 threads per workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnLaunch L) {
+    constexpr int LPR = D / 4;                 // lanes per row
+    constexpr int RPB = 256 / LPR;             // rows per workgroup
+    const int64_t nrow = (int64_t)L.B * L.H * L.Tq;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    if (row >= nrow) return;
+    const int c = 4 * (threadIdx.x % LPR);
+    const int NS = L.nsplit;
+    float M = -__builtin_inff();
+    for (int s = 0; s < NS; ++s) M = __builtin_fmaxf(M, L.ml[2 * (s * nrow + row)]);
+    float den = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < NS; ++s) {
+        const int64_t rs = s * nrow + row;
+        const f32x2 ml = *(const f32x2*)(L.ml + 2 * rs);
+        const float w = __builtin_amdgcn_exp2f(ml[0] - M);
+        den += w * ml[1];
+        acc += w * *(const f32x4*)(L.part + rs * D + c);
+    }
+    const float inv = 1.f / den;
+    const int bh = (int)(row / L.Tq), t = (int)(row % L.Tq);
+    const int b = bh / L.H, h = bh % L.H;
+    bf16* orow = (bf16*)L.o + (int64_t)b * L.osb + (int64_t)h * L.osh + (int64_t)t * L.ost;
+    *(u32x2*)(orow + c) = u32x2{pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv)};
+}
+
 }  // namespace
 
 bool attn_supported(int D) { return D == 64 || D == 128; }
 
+// Waves per workgroup: 12 where the grid then has at least two workgroups per CU (256 CUs),
+// else 8. Key splits (when allowed, for a single-frame call whose grid leaves CUs idle): the
+// count of splits that minimises the estimated length of the launch, rounds of 256 workgroups
+// times the tiles each takes, with each split at least 16 tiles long.
+void attn_plan(AttnLaunch& L, bool allow_split, size_t* ws_bytes) {
+    constexpr int kCUs = 256, kMinTiles = 16, kMaxSplit = 16;
+    auto items = [&](int nw) { return (int64_t)L.B * L.H * ((L.Tq + nw * kQW - 1) / (nw * kQW)); };
+    L.nw = items(12) >= 2 * kCUs ? 12 : 8;
+    L.nsplit = 1;
+    const int64_t S = L.S;
+    if (allow_split && L.Tq == S) {
+        const int64_t kmax = std::min<int64_t>((int64_t)(L.q_frame0 + 1) * S, L.Tk);
+        const int64_t tiles = (kmax + kKT - 1) / kKT;
+        // cost in query-tile units: rounds x (queries per workgroup x tiles per split)
+        double best = (double)((items(L.nw) + kCUs - 1) / kCUs) * L.nw * kQW * tiles;
+        for (int nw : {8, 12})
+            for (int ns = 2; ns <= kMaxSplit && tiles / ns >= kMinTiles; ++ns) {
+                const int64_t n = items(nw) * ns;
+                const double cost = (double)((n + kCUs - 1) / kCUs) * nw * kQW * ((tiles + ns - 1) / ns);
+                if (cost < 0.97 * best) {   // a split must gain more than its merge costs
+                    best = cost;
+                    L.nw = nw;
+                    L.nsplit = ns;
+                }
+            }
+    }
+    const int64_t rows = (int64_t)L.B * L.H * L.Tq;
+    *ws_bytes = L.nsplit > 1 ? (size_t)(((L.nsplit * rows * L.D * 4 + 255) / 256) * 256 + L.nsplit * rows * 8) : 0;
+}
+
 template <int D, int NW> hipError_t launch_nw(const AttnLaunch& L, hipStream_t s) {
-    const int64_t items = (int64_t)L.B * L.H * ((L.Tq + NW * kQW - 1) / (NW * kQW));
+    const int64_t items = (int64_t)L.B * L.H * L.nsplit * ((L.Tq + NW * kQW - 1) / (NW * kQW));
     const int64_t blocks = (items + 7) / 8 * 8;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_kernel<D, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, L);
     return hipGetLastError();
 }
 
-// 12 waves where the grid then still has at least two workgroups per CU (256 CUs), else 8
 template <int D> hipError_t launch_d(const AttnLaunch& L, hipStream_t s) {
-    const int64_t items12 = (int64_t)L.B * L.H * ((L.Tq + kQBMax - 1) / kQBMax);
-    return items12 >= 2 * 256 ? launch_nw<D, 12>(L, s) : launch_nw<D, 8>(L, s);
+    return L.nw == 12 ? launch_nw<D, 12>(L, s) : launch_nw<D, 8>(L, s);
 }
 
 hipError_t attn_launch(const AttnLaunch& L, hipStream_t s) {
+    if (L.nsplit < 1 || (L.nsplit > 1 && (!L.part || !L.ml)) || (L.nw != 8 && L.nw != 12))
+        return hipErrorInvalidValue;
     if (L.D == 128) return launch_d<128>(L, s);
     if (L.D == 64) return launch_d<64>(L, s);
     return hipErrorInvalidValue;
+}
+
+hipError_t attn_combine_launch(const AttnLaunch& L, hipStream_t s) {
+    const int64_t rows = (int64_t)L.B * L.H * L.Tq;
+    const int rpb = 256 / (L.D / 4);
+    const int64_t blocks = (rows + rpb - 1) / rpb;
+    if (blocks > 0x7FFFFFFF || L.nsplit < 2) return hipErrorInvalidValue;
+    if (L.D == 128)
+        hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, s, L);
+    else if (L.D == 64)
+        hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, s, L);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -79,7 +79,8 @@ enum Kernel {
     K_ATTN = 11,         // frame-causal softmax attention
     K_STEP_OUTPUT = 12,  // step (Gram-form kernels): outputs of the frame
     K_BWD_QDO = 13,      // backward: C_f = Q_f^T dO_f and dQ_f in one pass over Q and dO
-    K_STEP_FUSED = 14    // step (Gram form): partials, new state and outputs in one launch
+    K_STEP_FUSED = 14,   // step (Gram form): partials, new state and outputs in one launch
+    K_ATTN_COMBINE = 15  // softmax attention with key splits: merge of the splits' partials
 };
 
 // Arguments of the frame-causal softmax attention (gdn_attn.hip). q: [B][H][Tq][D], k, v:
@@ -91,9 +92,21 @@ struct AttnLaunch {
     int64_t qsb, qsh, qst, ksb, ksh, kst, osb, osh, ost;
     const void *q, *k, *v;
     void* o;
+    // Key splits (gdn_attention_framecausal_ws, single-frame calls): nsplit workgroups share a
+    // query block's key tiles, each writing its unnormalised O (part, fp32 [split][b h][t][D])
+    // and its (maximum, weight sum) (ml, fp32 pairs [split][b h][t]); a second launch merges
+    // them into o. nsplit = 1: one workgroup per block writes o directly. nw: waves per
+    // workgroup (8 or 12), set by attn_plan.
+    int nsplit, nw;
+    float* part;
+    float* ml;
 };
 bool attn_supported(int D);
+// Waves per workgroup and key splits for the call (splits only when allow_split and the
+// queries form one frame); bytes of workspace that the splits need (0 for nsplit = 1).
+void attn_plan(AttnLaunch& L, bool allow_split, size_t* ws_bytes);
 hipError_t attn_launch(const AttnLaunch& L, hipStream_t s);
+hipError_t attn_combine_launch(const AttnLaunch& L, hipStream_t s);
 hipError_t run_attn(const AttnLaunch& L, hipStream_t s);
 
 // Arguments of the temporal convolution (gdn_tconv.hip). x, y: [B][T][S][C] with the strides

@@ -164,12 +164,19 @@ hipError_t run_tconv(const TconvLaunch& L, hipStream_t s) {
 hipError_t run_attn(const AttnLaunch& L, hipStream_t s) {
     t_trace_log.clear();
     const bool armed = !t_trace_events.empty();
-    const bool timed = armed && t_trace_events.size() >= 2;
     hipError_t e = hipSuccess;
-    if (timed && (e = hipEventRecord(t_trace_events[0], s)) != hipSuccess) return e;
-    if ((e = attn_launch(L, s)) != hipSuccess) return e;
-    if (timed && (e = hipEventRecord(t_trace_events[1], s)) != hipSuccess) return e;
-    if (armed) t_trace_log.push_back({(int32_t)K_ATTN, 0, (int64_t)L.B * L.H * L.Tq});
+    // launch i is bracketed by trace events 2i, 2i + 1 when that many are armed
+    auto launch = [&](int i, Kernel kind, hipError_t (*fn)(const AttnLaunch&, hipStream_t)) {
+        const bool timed = armed && t_trace_events.size() >= (size_t)(2 * i + 2);
+        hipError_t r;
+        if (timed && (r = hipEventRecord(t_trace_events[2 * i], s)) != hipSuccess) return r;
+        if ((r = fn(L, s)) != hipSuccess) return r;
+        if (timed && (r = hipEventRecord(t_trace_events[2 * i + 1], s)) != hipSuccess) return r;
+        if (armed) t_trace_log.push_back({(int32_t)kind, 0, (int64_t)L.B * L.H * L.Tq});
+        return hipSuccess;
+    };
+    if ((e = launch(0, K_ATTN, attn_launch)) != hipSuccess) return e;
+    if (L.nsplit > 1 && (e = launch(1, K_ATTN_COMBINE, attn_combine_launch)) != hipSuccess) return e;
     return hipSuccess;
 }
 

@@ -208,6 +208,28 @@ gdn_status gdn_attention_framecausal(const gdn_attn_problem* p, const void* q, c
                                      const void* v, void* o, void* hip_stream);
 
 /*
+ * The same attention with a caller-owned workspace that lets one call split each query
+ * block's keys over several workgroups. A single-frame call (q_frames = 1, a streaming step)
+ * has few query blocks, too few to occupy every compute unit; with splits, each workgroup takes
+ * a share of the block's keys and stores its unnormalised output, running maximum and weight
+ * sum in the workspace, and a second launch merges them (the usual rescaling of a softmax by
+ * its maxima; trace kinds GDN_KERNEL_ATTN, then GDN_KERNEL_ATTN_COMBINE). The result equals the
+ * unsplit one up to the order of fp32 rounding.
+ *   gdn_attention_workspace_size   bytes the call may use (0 when it would not split: more
+ *                                  than one query frame, or a grid that already fills the
+ *                                  device); a pure function of the problem's sizes
+ *   workspace   at least that many bytes, 256-byte aligned, not overlapping q, k, v or o
+ *               (GDN_ERR_WORKSPACE / GDN_ERR_ALIGN / GDN_ERR_ALIAS otherwise); NULL runs the
+ *               call unsplit, exactly as gdn_attention_framecausal. Its contents on entry do
+ *               not matter; calls that share one workspace must not overlap in time.
+ * Other arguments, errors and limits as gdn_attention_framecausal.
+ */
+gdn_status gdn_attention_workspace_size(const gdn_attn_problem* p, size_t* bytes_out);
+gdn_status gdn_attention_framecausal_ws(const gdn_attn_problem* p, const void* q, const void* k,
+                                        const void* v, void* o, void* workspace,
+                                        size_t workspace_bytes, void* hip_stream);
+
+/*
  * Workspace bytes needed by gdn_forward_framewise (mode = 0; also gdn_forward_framewise_save),
  * gdn_step_frame (mode = 1), gdn_backward_framewise (mode = 2) or gdn_backward_framewise_saved
  * (mode = 3) for this problem. The step-mode size does not depend on `frames`. Validates the
@@ -432,7 +454,8 @@ typedef enum {
     GDN_KERNEL_ATTN = 11,         /* frame-causal softmax attention */
     GDN_KERNEL_STEP_OUTPUT = 12,  /* step, bf16 with D = 64 or 128: outputs of the frame */
     GDN_KERNEL_BWD_QDO = 13,      /* backward: Q_f^T dO_f and dQ in one pass over Q and dO */
-    GDN_KERNEL_STEP_FUSED = 14    /* step, bf16 with D = 64 or 128: partials, state, outputs */
+    GDN_KERNEL_STEP_FUSED = 14,   /* step, bf16 with D = 64 or 128: partials, state, outputs */
+    GDN_KERNEL_ATTN_COMBINE = 15  /* softmax attention with key splits: merge of the splits */
 } gdn_kernel_kind;
 
 typedef struct {

@@ -480,6 +480,36 @@ def test_attention_validation():
     assert call_attn(big) == 3 and "2 GiB" in msg()
 
 
+def attn_ws_size(p):
+    n = ctypes.c_size_t(0)
+    code = gdn.load().gdn_attention_workspace_size(None if p is None else ctypes.byref(p), ctypes.byref(n))
+    return code, n.value
+
+
+def call_attn_ws(p, ws, wsb, q=A, k=16 * A, v=32 * A, o=48 * A):
+    return gdn.load().gdn_attention_framecausal_ws(ctypes.byref(p), q, k, v, o, ws, wsb, None)
+
+
+def test_attention_workspace_validation():
+    assert attn_ws_size(None)[0] == 1
+    assert attn_ws_size(aprob(D=32))[0] == 3
+    # a whole sequence fills the device by itself, and several query frames never split
+    assert attn_ws_size(aprob(B=2, H=16, S=880, fq=81, fk=81)) == (0, 0)
+    assert attn_ws_size(aprob(fq=3, fk=3)) == (0, 0)
+    # one 720p frame against 961 frames: 224 workgroups of 256 queries for 256 CUs
+    code, n = attn_ws_size(aprob(B=1, H=16, D=128, S=3520, fq=1, fk=961, f0=960))
+    rows = 16 * 3520
+    assert code == 0 and n > 0 and n % (rows * (128 * 4 + 8)) == 0
+    assert 2 <= n // (rows * (128 * 4 + 8)) <= 16
+    # host checks before any launch: too small, misaligned, overlapping o
+    small = aprob(B=1, H=2, D=128, S=200, fq=1, fk=41, f0=40)
+    code, n = attn_ws_size(small)
+    assert code == 0 and n > 0
+    assert call_attn_ws(small, 64 * A, n - 1) == 7 and "workspace" in msg()
+    assert call_attn_ws(small, 64 * A + 16, n) == 5
+    assert call_attn_ws(small, 48 * A, n) == 6 and "overlaps" in msg()
+
+
 def test_trace_kinds_match_the_header():
     """The binding's trace-kind names, the header's GDN_KERNEL_* values and the library's internal
     launch kinds agree (a new kind must be added in all three)."""

@@ -151,18 +151,89 @@ def test_attention_880x81_full_launch():
 
 
 def test_attention_720p_streaming_step():
-    """One 720p frame (S = 3520, 16 heads) at frame 240 against the cache of frames 0..240;
-    oracle on sampled rows of one head."""
+    """One 720p frame (S = 3520, 16 heads) at frame 240 against the cache of frames 0..240,
+    without and with a workspace (key splits); oracle on sampled rows of one head."""
     w = gdn_synth.WORKLOADS["gdn_720p_60s_bf16"]
     S, f0 = w.S, 240
     q, k, v = gdn_synth.qkv_torch(w, DEV, frames=(0, f0 + 1))
-    o = gdn.attention_framecausal(q[:, :, f0 * S:], k, v, tokens_per_frame=S, q_frame0=f0)
+    qf = q[:, :, f0 * S:]
+    o = gdn.attention_framecausal(qf, k, v, tokens_per_frame=S, q_frame0=f0)
+    assert gdn.attention_workspace_size(gdn.attention_problem(qf, k, o, S, f0)) > 0
+    os_ = gdn.attention_framecausal(qf, k, v, tokens_per_frame=S, q_frame0=f0, workspace="auto")
     torch.cuda.synchronize()
     rows = [0, 17, 1000, 3519]
     h = 9
     kc, vc = k[:, h:h + 1].double().cpu().numpy(), v[:, h:h + 1].double().cpu().numpy()
-    qc = q[:, h:h + 1, f0 * S:].double().cpu().numpy()
+    qc = qf[:, h:h + 1].double().cpu().numpy()
     ref = attention.frame_causal_attention(qc, kc, vc, S, q_frame0=f0, rows=rows)
-    e = rel_err(to_np(o[:, h:h + 1, rows]), ref)
-    say("  sampled rows err %.2e" % e)
-    assert e <= TOL
+    for name, out in (("unsplit", o), ("key splits", os_)):
+        e = rel_err(to_np(out[:, h:h + 1, rows]), ref)
+        say("  %s: sampled rows err %.2e" % (name, e))
+        assert e <= TOL
+    d = rel_err(to_np(os_), to_np(o))
+    say("  key splits against unsplit, all rows: %.2e" % d)
+    assert d <= TOL
+
+
+SPLIT_CASES = [
+    # B, H, D, S, kv_frames, q_frame0, layout: one query frame against a long cache, too few
+    # query blocks to fill the device, so a workspace splits the keys
+    (1, 2, 128, 200, 41, 40, "head"),        # 8200 keys: ragged last key tile; ragged query block
+    (1, 1, 64, 300, 30, 20, "token"),        # cache frames after the query frame present, unseen
+    (2, 3, 128, 520, 12, 11, "head"),        # two query blocks per head
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=["-".join(map(str, c)) for c in SPLIT_CASES])
+def test_attention_key_splits(case):
+    """gdn_attention_framecausal_ws: the keys of each query block split over several
+    workgroups, then merged; against the oracle, with a workspace whose entry contents are
+    NaN (they must not matter), twice in a row."""
+    B, H, D, S, fk, f0, layout = case
+    say("attention key splits", case)
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
+    q = bf16_host(rng, (B, H, S, D))
+    k = bf16_host(rng, (B, H, fk * S, D))
+    v = bf16_host(rng, (B, H, fk * S, D))
+    qd, kd, vd = to_dev(q, layout), to_dev(k, layout), to_dev(v, layout)
+    o = torch.empty(qd.shape, dtype=torch.bfloat16, device=DEV)
+    n = gdn.attention_workspace_size(gdn.attention_problem(qd, kd, o, S, f0))
+    say("  workspace %d bytes" % n)
+    assert n > 0
+    ws = torch.full((n,), 255, dtype=torch.uint8, device=DEV)     # NaN bytes
+    ref = attention.frame_causal_attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                           S, q_frame0=f0)
+    for rep in range(2):
+        gdn.attention_framecausal(qd, kd, vd, tokens_per_frame=S, q_frame0=f0, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        e = rel_err(to_np(o), ref)
+        say("  call %d: o err %.2e" % (rep, e))
+        assert e <= TOL
+
+
+def test_attention_key_splits_12_waves():
+    """A single-frame call whose plan takes 12-wave workgroups with 5 key splits (48 heads of
+    one 384-query block each: 240 workgroups of 50 key tiles, against 8-wave blocks of 256
+    queries that would need more rounds); the oracle on sampled heads and rows."""
+    B, H, D, S, fk, f0 = 1, 48, 128, 384, 41, 40
+    rng = np.random.default_rng(12)
+    q = bf16_host(rng, (B, H, S, D))
+    k = bf16_host(rng, (B, H, fk * S, D))
+    v = bf16_host(rng, (B, H, fk * S, D))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.empty_like(qd)
+    n = gdn.attention_workspace_size(gdn.attention_problem(qd, kd, o, S, f0))
+    rows_total = B * H * S
+    # the plan's split count from the workspace size: part (fp32 O) + (m, l) pairs per split
+    ns = n // (rows_total * (D * 4 + 8))
+    say("  workspace %d bytes: %d splits" % (n, ns))
+    assert ns == 5 and n == ns * rows_total * (D * 4 + 8)
+    gdn.attention_framecausal(qd, kd, vd, tokens_per_frame=S, q_frame0=f0, out=o, workspace="auto")
+    torch.cuda.synchronize()
+    rows = [0, 100, 383]
+    for h in (0, 29, 47):
+        ref = attention.frame_causal_attention(q[:, h:h + 1].double().numpy(), k[:, h:h + 1].double().numpy(),
+                                               v[:, h:h + 1].double().numpy(), S, q_frame0=f0, rows=rows)
+        e = rel_err(to_np(o[:, h:h + 1, rows]), ref)
+        say("  head %d sampled rows err %.2e" % (h, e))
+        assert e <= TOL
