@@ -401,7 +401,8 @@ bool attn_supported(int D) { return D == 64 || D == 128; }
 // Waves per workgroup: 12 where the grid then has at least two workgroups per CU (256 CUs),
 // else 8. Key splits (when allowed, for a single-frame call whose grid leaves CUs idle): the
 // count of splits that minimises the estimated length of the launch, rounds of 256 workgroups
-// times the tiles each takes, with each split at least 16 tiles long.
+// times the tiles each takes, with each split at least 16 tiles long; a 12-wave workgroup's
+// tile counts 0.93 of the 8-wave one's per query (the two measured on one CU's worth of work).
 void attn_plan(AttnLaunch& L, bool allow_split, size_t* ws_bytes) {
     constexpr int kCUs = 256, kMinTiles = 16, kMaxSplit = 16;
     auto items = [&](int nw) { return (int64_t)L.B * L.H * ((L.Tq + nw * kQW - 1) / (nw * kQW)); };
@@ -412,17 +413,23 @@ void attn_plan(AttnLaunch& L, bool allow_split, size_t* ws_bytes) {
         const int64_t kmax = std::min<int64_t>((int64_t)(L.q_frame0 + 1) * S, L.Tk);
         const int64_t tiles = (kmax + kKT - 1) / kKT;
         // cost in query-tile units: rounds x (queries per workgroup x tiles per split)
-        double best = (double)((items(L.nw) + kCUs - 1) / kCUs) * L.nw * kQW * tiles;
+        auto cost = [&](int nw, int ns) {
+            const int64_t n = items(nw) * ns;
+            return (double)((n + kCUs - 1) / kCUs) * nw * kQW * ((tiles + ns - 1) / ns) * (nw == 12 ? 0.93 : 1.0);
+        };
+        double best = 0.;
+        int bnw = 0, bns = 1;
         for (int nw : {8, 12})
-            for (int ns = 2; ns <= kMaxSplit && tiles / ns >= kMinTiles; ++ns) {
-                const int64_t n = items(nw) * ns;
-                const double cost = (double)((n + kCUs - 1) / kCUs) * nw * kQW * ((tiles + ns - 1) / ns);
-                if (cost < 0.97 * best) {   // a split must gain more than its merge costs
-                    best = cost;
-                    L.nw = nw;
-                    L.nsplit = ns;
+            for (int ns = 2; ns <= kMaxSplit && tiles / ns >= kMinTiles; ++ns)
+                if (bnw == 0 || cost(nw, ns) < best) {
+                    best = cost(nw, ns);
+                    bnw = nw;
+                    bns = ns;
                 }
-            }
+        if (bnw && best < 0.97 * cost(L.nw, 1)) {   // a split must gain more than its merge costs
+            L.nw = bnw;
+            L.nsplit = bns;
+        }
     }
     const int64_t rows = (int64_t)L.B * L.H * L.Tq;
     *ws_bytes = L.nsplit > 1 ? (size_t)(((L.nsplit * rows * L.D * 4 + 255) / 256) * 256 + L.nsplit * rows * 8) : 0;
