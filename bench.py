@@ -345,7 +345,8 @@ def stream_mode(dev, nframes, ev, stream, schedule="auto"):
             # these sum to more than a pass), and the rocprofv3 kernel averages of the same
             # workload from the committed summary (null when taken on other kernel source)
             "pass_kernel_us_traced": {k_: round(float(np.median(v_)), 2) for k_, v_ in kus.items()},
-            "pass_kernel_us_rocprof": step_profile()}
+            "pass_kernel_us_rocprof": step_profile(),
+            "same_bytes_torch_us": round(pass_bytes_reference(dev, w.B * w.H * w.S * w.D), 2)}
 
 
 def backward_mode(w, dev, steps, ev, stream):
@@ -517,6 +518,9 @@ def fp8_mode(dev, steps, warmup, ev, stream):
     t_roof = max(bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
     fms = kms.get("fused", 0.0)
     del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    c = counters_for("fused_e4m3")
+    hbm = c["hbm_read_gb"] + c["hbm_write_gb"] if c else None
     return {"workload": w.name, "ms_per_call": round(ms, 4),
             "tokens_per_s": round(w.B * w.F * w.S / (ms * 1e-3), 1),
             "launches": [k_ for k_, _, _ in plan],
@@ -525,7 +529,11 @@ def fp8_mode(dev, steps, warmup, ev, stream):
                      "frac_of_roofline": round(t_roof / ms, 4),
                      "achieved_gb_s": round(bytes_alg / (ms * 1e-3) / 1e9, 1)},
             "fused_kernel": {"achieved_gb_s": round(bytes_alg / (fms * 1e-3) / 1e9, 1) if fms else None,
-                             "frac": round(bytes_alg / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if fms else None}}
+                             "frac": round(bytes_alg / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if fms else None,
+                             # the kernel's measured HBM traffic (committed counters) per this
+                             # run's duration
+                             "hbm_gb_per_launch": round(hbm, 3) if hbm else None,
+                             "hbm_gb_s": round(hbm / (fms * 1e-3), 1) if fms and hbm else None}}
 
 
 def tconv_mode(dev, steps, warmup, ev, stream, stream_frames=240):
@@ -746,6 +754,27 @@ def streaming_ceiling(dev, nread=3, gib=4.0, reps=10):
     del xs, y
     torch.cuda.empty_cache()
     return (nread + 1) * n * 2 / (ms * 1e-3) / 1e9
+
+
+def pass_bytes_reference(dev, n, reps=200):
+    """Time of one torch elementwise kernel that moves a step pass's algorithmic bytes (three
+    bf16 tensors of n elements read, one written), launched back to back: what streaming the
+    same bytes with no dependency between them costs at this size."""
+    import torch
+    xs = [torch.empty(n, dtype=torch.bfloat16, device=dev).normal_() for _ in range(3)]
+    y = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    for _ in range(10):
+        torch.addcmul(xs[0], xs[1], xs[2], out=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.addcmul(xs[0], xs[1], xs[2], out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    del xs, y
+    return us
 
 
 def main():
